@@ -1,0 +1,288 @@
+"""Benchmark of the packed variable-length attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+
+A step is one pass of the whole forward (one launch of the gfx950 kernel through the C ABI)
+over one packed batch that is already resident in HBM. The default workload is sixteen
+8192-token sequences, 16 heads, bf16, full window. It prints one JSON line:
+
+* value: effective attention TFLOP/s, counting 4 * 64 FLOPs per visible (query, key) pair per
+  head, over the wall-clock of exactly K steps (synchronised on both sides);
+* roofline: the same algorithmic FLOPs over the kernel's average duration from HIP events on
+  the launch stream, against MI355X's dense bf16/fp16 matrix peak (2516.6 TFLOP/s =
+  256 CUs x 2.4 GHz x 4096 FLOP/clock); traffic: HBM bytes per launch from rocprofv3 counters
+  (FETCH_SIZE + WRITE_SIZE, each scaled by the reading of a plain copy of known size),
+  recorded in profiles/ with the hash of the kernel source they were taken on (null when the
+  source has changed since);
+* cpu_baseline: the float64 oracle (test infrastructure) on the host cores over a bounded
+  sample of rows of the same workload, in the same unit.
+
+Other modes:
+  --profile-run        short run for rocprofv3 (no CPU baseline) plus one plain 1 GiB copy that
+                       calibrates the byte counters;
+  --summarize DIR      read a rocprofv3 counter-collection directory and print the traffic
+                       summary for profiles/.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0         # HBM3E
+KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flash_amd", "csrc", "vlf_attend.hip")
+KERNEL_NAME = "attend_fwd"
+COPY_BYTES = 1 << 30
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"attend_fwd_{workload}_traffic.txt")
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if absent or taken on
+    a different kernel source."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(workload: str):
+    import torch
+    from variable_length_flash_amd import workloads
+    w = workloads.WORKLOADS[workload]()
+    qkv = workloads.draw_qkv(w)
+    cos, sin = workloads.rope_tables(w)
+    return w, qkv, cos, sin
+
+
+def cpu_baseline(w, qkv, cos, sin, target_s: float, pairs_per_head_total: int):
+    """The oracle as it stands, on a bounded sample of rows of the workload (rows of the first
+    sequences, all heads), scaled to effective TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    from variable_length_flash_amd import binding
+    q32 = qkv.float().numpy()
+    c32, s32 = cos.float().numpy(), sin.float().numpy()
+    cores = oracle.threads(len(os.sched_getaffinity(0)))
+
+    def visible(rows):
+        # pairs the sampled rows compute, all heads
+        total = 0
+        cu = w.cu
+        for t in rows:
+            s = int(np.searchsorted(cu, t, side="right") - 1)
+            L = int(cu[s + 1] - cu[s])
+            i = int(t - cu[s])
+            if w.window == 0:
+                total += L
+            else:
+                total += min(L, i + w.window) - max(0, i - w.window + 1)
+        return total * w.heads
+
+    # calibrate on a few rows, then size the sample to the target time
+    probe = np.arange(0, min(w.tokens, 32), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.attend(q32, c32, s32, w.cu, w.heads, w.window, w.scale, mode="B", dtype=w.dtype,
+                  rows=probe)
+    dt = time.perf_counter() - t0
+    n = int(min(w.tokens, max(64, len(probe) * target_s / max(dt, 1e-6))))
+    rows = np.linspace(0, w.tokens - 1, n).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attend(q32, c32, s32, w.cu, w.heads, w.window, w.scale, mode="B", dtype=w.dtype,
+                  rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = visible(rows)
+    flops = 4 * 64 * pairs
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{n} of {w.tokens} rows spread evenly over the workload, all {w.heads} heads "
+                  f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP effective), oracle mode B "
+                  f"(float64), {dt:.1f} s on {cores} threads",
+    }
+
+
+def run(args):
+    import torch
+
+    import variable_length_flash_amd as vlf
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w, qkv, cos, sin = make_inputs(args.workload)
+    batch = vlf.prepare(w.cu, dev)
+    q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
+    out = torch.empty((w.tokens, w.heads * 64), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
+    pairs = vlf.visible_pairs(w.cu, w.window)
+    flops = 4 * 64 * pairs * w.heads
+    alg_bytes = (3 * w.tokens * w.heads * 64 * 2      # qkv read once
+                 + w.tokens * w.heads * 64 * 2        # out written once
+                 + 4 * w.heads * w.tokens)            # lse written once
+
+    def step():
+        vlf.attend_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    if args.profile_run:
+        # a plain copy of known size on the same stream: the counter runs scale by it
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    value = flops / (wall_ms / 1e3) / 1e12
+    achieved = flops / (kernel_ms / 1e3) / 1e12
+    traffic = read_traffic(args.workload)
+    line = {
+        "metric": "effective attention TFLOP/s (visible pairs) + % of bf16 MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {w.note}",
+            "tokens": w.tokens, "sequences": w.sequences, "heads": w.heads, "head_dim": 64,
+            "window": w.window, "rope_base": w.base, "scale": w.scale, "br": batch.br,
+            "visible_pairs_per_head": pairs, "effective_flop": flops,
+            "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "achieved_hbm_gbs_algorithmic": round(alg_bytes / (kernel_ms / 1e3) / 1e9, 1),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(kernel_ms, 4),
+            "algorithmic_bytes": alg_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.profile_run and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, qkv, cos, sin, args.cpu_seconds, pairs)
+    print(json.dumps(line), flush=True)
+
+
+def summarize(directory: str, workload: str):
+    """Traffic per launch from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each
+    scaled by the same counter's reading for the 1 GiB copy of the profile run."""
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    per = {}  # (counter, kind) -> list of per-dispatch values (KiB)
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        kind = "attend" if KERNEL_NAME in name else ("copy" if "copy" in name.lower() or
+                                                     "elementwise" in name.lower() else None)
+        if kind is None:
+            continue
+        per.setdefault((r["Counter_Name"], kind, r.get("Dispatch_Id", "")), 0.0)
+        per[(r["Counter_Name"], kind, r.get("Dispatch_Id", ""))] += float(r["Counter_Value"])
+    res = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        att = [v for (c, k, _), v in per.items() if c == counter and k == "attend"]
+        cpy = [v for (c, k, _), v in per.items() if c == counter and k == "copy"]
+        if not att or not cpy:
+            raise SystemExit(f"{counter}: attend {len(att)} dispatches, copy {len(cpy)}")
+        # the copy reads and writes COPY_BYTES each; its reading (KiB) calibrates the counter
+        copy_kib = max(cpy)
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        res[counter] = (sum(att) / len(att), copy_kib, factor)
+    fetch = res["FETCH_SIZE"][0] * 1024 * res["FETCH_SIZE"][2]
+    write = res["WRITE_SIZE"][0] * 1024 * res["WRITE_SIZE"][2]
+    print(f"kernel: {KERNEL_NAME}")
+    print(f"workload: {workload}")
+    print(f"kernel_source_sha256_16: {kernel_hash()}")
+    for counter, (att, cpy, factor) in res.items():
+        print(f"{counter}_kib_per_dispatch: {att:.1f}")
+        print(f"{counter}_copy_kib_for_{COPY_BYTES}_bytes: {cpy:.1f}")
+        print(f"{counter}_scale_factor: {factor:.4f}")
+    print(f"hbm_fetch_bytes_per_launch: {fetch:.0f}")
+    print(f"hbm_write_bytes_per_launch: {write:.0f}")
+    print(f"hbm_bytes_per_launch: {fetch + write:.0f}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long",
+                    choices=["tiny", "encoder", "sliding", "many_short", "long"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.workload)
+        return
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * vlf.h — C ABI of libvlf.so: the forward pass of packed variable-length attention with rotary
+ * position embeddings applied inside the kernel and an optional symmetric window, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is the one hanzo-kernel 0.2.42 `src/packed.rs` defines: its module contract
+ * (layouts of qkv, cu, tiles, cos/sin and the window value), the host `layout` function (the tile
+ * table) and the `attend` kernel (rotation, masking, online softmax, outputs and log-sum-exp).
+ *
+ * Conventions for every call:
+ *   - Head dimension is 64. H heads; a token's row of qkv holds 3*H*64 elements: the H query
+ *     heads, then the H key heads, then the H value heads, each head's 64 elements contiguous.
+ *   - cu [S+1] int32: cu[0] = 0, non-decreasing, cu[S] = T. Sequence s owns tokens
+ *     cu[s] .. cu[s+1]-1. Zero-length sequences are allowed.
+ *   - window: 0 = every key of the query's own sequence; W >= 1 = keys j with |i - j| < W
+ *     (i, j positions within the sequence).
+ *   - Status codes are returned; nothing aborts or throws across this boundary. After a
+ *     non-zero status, vlf_last_error() returns a message (per calling thread).
+ *   - Pointers marked "host" are read by the CPU during the call only. Pointers marked
+ *     "device" are HIP device memory owned by the caller; the library keeps no reference after
+ *     the call returns and allocates no device memory.
+ */
+#ifndef VLF_H
+#define VLF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vlf_status {
+    VLF_OK = 0,
+    VLF_EINVAL = -1,       /* malformed argument (cu, sizes, null pointer, window, ...) */
+    VLF_EUNSUPPORTED = -2, /* dtype or tile height the library does not build */
+    VLF_EHIP = -3,         /* the HIP runtime reported an error (launch, device) */
+};
+
+enum vlf_dtype {
+    VLF_F16 = 0,  /* IEEE binary16 */
+    VLF_BF16 = 1, /* bfloat16 */
+};
+
+/* Library ABI version (this header: 1). */
+int32_t vlf_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). The pointer
+ * stays valid until the next call on the same thread. */
+const char *vlf_last_error(void);
+
+/*
+ * Validate cu and size the tile table for `br`-row query tiles.
+ * hanzo-kernel 0.2.42 src/packed.rs, `layout`: every sequence contributes ceil(L_s / br) tiles.
+ *   cu_host    host, [S+1] int32, checked as described above.
+ *   br         tile height >= 1 (vlf_attend runs 64 and 128).
+ *   num_tiles  out: number of tiles (may be 0).
+ *   max_len    out: the longest sequence (0 if none). May be NULL.
+ * Errors: VLF_EINVAL for a malformed cu, br < 1 or a total above INT32_MAX tiles.
+ */
+int vlf_tile_count(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, int32_t *num_tiles,
+                   int32_t *max_len);
+
+/*
+ * Write the tile table: for each sequence s in order and each first row i0 = 0, br, 2*br, ...
+ * below L_s, the pair (s, i0), as consecutive uint32 values (hanzo-kernel 0.2.42
+ * src/packed.rs, `layout`). Zero-length sequences get no tiles.
+ *   tiles_host  host, capacity >= 2 * num_tiles uint32 (num_tiles from vlf_tile_count).
+ *   capacity    number of uint32 slots in tiles_host.
+ * Errors: VLF_EINVAL (bad cu, br < 1, capacity too small).
+ */
+int vlf_tile_table(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, uint32_t *tiles_host,
+                   int64_t capacity);
+
+/*
+ * The number of (query, key) pairs one head computes: for each row i of each sequence, the
+ * keys j of the same sequence with window == 0 or |i - j| < window (the masking of
+ * hanzo-kernel 0.2.42 src/packed.rs `attend`). Effective FLOPs of one call are
+ * 4 * 64 * pairs * H.
+ *   cu_host  host, [S+1]. pairs  out.
+ * Errors: VLF_EINVAL (bad cu, window < 0).
+ */
+int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t window,
+                      uint64_t *pairs);
+
+/*
+ * The forward pass (hanzo-kernel 0.2.42 src/packed.rs, `attend`): for each tile in tiles_dev
+ * and each head h, query rows i0 .. i0+br-1 of sequence s against the keys of s the window
+ * reaches.
+ *
+ *   For a row at position i of sequence s (token t = cu[s] + i) and head h:
+ *     q~ = storage-type rounding of (rot(q_t, i) * scale), rotation and scale in float32;
+ *     k~_j = storage-type rounding of rot(k_{cu[s]+j}, j);
+ *     rot(x, p)[m] = x[m] cos[p][m] - x[m+32] sin[p][m],
+ *     rot(x, p)[m+32] = x[m] sin[p][m] + x[m+32] cos[p][m]   (m < 32);
+ *     scores s_ij = <q~, k~_j> (float32 accumulation) for visible j;
+ *     out[t][h*64 + d] = sum_j softmax_j(s_ij) v_j[d], rounded to the storage type;
+ *     lse[h*T + t]     = ln sum_j exp(s_ij)  (float32, natural log of the scaled scores).
+ *
+ *   qkv        device, [T, 3*H*64] elements of `dtype`, rows contiguous.
+ *   cos, sin   device, [table_rows, 32] elements of `dtype`: entry [p][m] for position p.
+ *   table_rows P; the caller guarantees P >= the longest sequence of cu (vlf_tile_count's
+ *              max_len). Tiles whose sequence is longer than P are skipped, not read.
+ *   cu_dev     device, [S+1] int32, the same values as the cu the tiles were built from.
+ *   tiles_dev  device, [num_tiles, 2] uint32 (sequence, first row) pairs built for the same cu
+ *              and `br` (vlf_tile_table, or any permutation of it: the order is the launch
+ *              order). Tiles naming a sequence >= S or a row beyond the sequence are skipped.
+ *   br         64 or 128: rows per tile, as the table was built.
+ *   T, S, H    tokens, sequences, heads (1 <= H <= 65536; T = 0 or num_tiles = 0 launches
+ *              nothing).
+ *   window     0 or W >= 1 as above.
+ *   scale      multiplies the rotated query before rounding (1/8 for head dimension 64).
+ *   dtype      VLF_BF16 or VLF_F16: storage type of qkv, cos, sin and out.
+ *   out        device, [T, H*64] elements of `dtype`. Every row of every tiled sequence is
+ *              written; nothing else is.
+ *   lse        device, [H, T] float32, written for the same rows.
+ *   stream     hipStream_t to launch on (NULL = the null stream). The call is asynchronous:
+ *              it never synchronises, never allocates, and returns once the launch is queued.
+ *
+ * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, negative sizes, T or
+ * S inconsistent with each other, num_tiles < 0), VLF_EUNSUPPORTED (dtype, br),
+ * VLF_EHIP (launch failure, from hipGetLastError). Device-side contents (cu_dev, tiles_dev)
+ * cannot be checked here; the kernel skips tiles that would read out of range.
+ */
+int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+               const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles, int32_t br,
+               int32_t T, int32_t S, int32_t H, int32_t window, float scale, int32_t dtype,
+               void *out, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VLF_H */

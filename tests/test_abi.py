@@ -1,0 +1,156 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/vlf.h declares, builds
+the tile table and the pair count bit-exactly, and rejects malformed arguments with a status and
+a message before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import variable_length_flash_amd as vlf
+from variable_length_flash_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "vlf.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vlf_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_function():
+    lib = vlf.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.vlf_version() == 1
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIBRARY", str(tmp_path / "absent.so"))
+    with pytest.raises(vlf.VlfError):
+        binding.load_library()
+
+
+def _random_cu(rng, count, lo, hi):
+    lens = rng.integers(lo, hi + 1, size=count)
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), [int(x) for x in lens]
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("br", [1, 16, 64, 128])
+def test_tile_table_bit_exact(seed, br):
+    rng = np.random.default_rng(seed)
+    cu, _ = _random_cu(rng, int(rng.integers(1, 200)), 0, 700)
+    got = vlf.tile_table(cu, br)
+    want = oracle.tile_table(cu, br)
+    assert got.dtype == np.uint32
+    np.testing.assert_array_equal(got, want)
+    n, m = vlf.tile_count(cu, br)
+    assert n == want.shape[0] and m == int(np.diff(cu).max())
+
+
+def test_tile_table_golden():
+    cu = [0, 5, 45, 46, 79, 149]  # the page's lengths 5, 40, 1, 33, 70
+    want = {16: [(0, 0), (1, 0), (1, 16), (1, 32), (2, 0), (3, 0), (3, 16), (3, 32), (4, 0),
+                 (4, 16), (4, 32), (4, 48), (4, 64)],
+            64: [(0, 0), (1, 0), (2, 0), (3, 0), (4, 0), (4, 64)]}
+    for br, pairs in want.items():
+        assert vlf.tile_table(cu, br).tolist() == [list(p) for p in pairs]
+
+
+def test_empty_batches():
+    assert vlf.tile_table([0], 64).shape == (0, 2)
+    assert vlf.tile_table([0, 0, 0], 128).shape == (0, 2)
+    assert vlf.visible_pairs([0], 0) == 0
+    assert vlf.tile_table([0, 0, 3, 3], 64).tolist() == [[1, 0]]
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("window", [0, 1, 2, 9, 64, 128, 129, 10000])
+def test_visible_pairs_exact(seed, window):
+    rng = np.random.default_rng(100 + seed)
+    cu, _ = _random_cu(rng, int(rng.integers(1, 60)), 0, 900)
+    assert vlf.visible_pairs(cu, window) == oracle.visible_pairs(cu, window)
+
+
+def test_visible_pairs_of_the_named_workloads():
+    from variable_length_flash_amd import workloads
+    for make in workloads.WORKLOADS.values():
+        w = make()
+        assert vlf.visible_pairs(w.cu, w.window) == oracle.visible_pairs(w.cu, w.window)
+    assert vlf.visible_pairs(workloads.long().cu, 0) == 16 * 8192 * 8192
+
+
+@pytest.mark.parametrize("cu,S,T,msg", [
+    ([1, 5], 1, 5, "cu[0]"),
+    ([0, 5, 3], 2, 3, "decreases"),
+    ([0, 5, 9], 2, 10, "expected T"),
+    ([0, 5], -1, 5, "negative"),
+])
+def test_bad_cu_is_rejected(cu, S, T, msg):
+    lib = vlf.load_library()
+    arr = np.array(cu, dtype=np.int32)
+    n = ctypes.c_int32()
+    rc = lib.vlf_tile_count(arr.ctypes.data_as(ctypes.c_void_p), S, T, 64, ctypes.byref(n), None)
+    assert rc == binding.VLF_EINVAL
+    assert msg in lib.vlf_last_error().decode()
+
+
+def test_tile_table_capacity_is_checked():
+    lib = vlf.load_library()
+    cu = np.array([0, 300], dtype=np.int32)
+    buf = np.zeros(4, dtype=np.uint32)  # 3 tiles of 128 need 6 slots
+    rc = lib.vlf_tile_table(cu.ctypes.data_as(ctypes.c_void_p), 1, 300, 128,
+                            buf.ctypes.data_as(ctypes.c_void_p), 4)
+    assert rc == binding.VLF_EINVAL and "capacity" in lib.vlf_last_error().decode()
+
+
+def _attend_status(**kw):
+    """Call vlf_attend with fake (never dereferenced) pointers: every case below must be
+    rejected on the host before any launch."""
+    args = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=64, cu=0x4000, tiles=0x5000, nt=4,
+                br=64, T=100, S=2, H=2, window=0, scale=0.125, dtype=binding.VLF_BF16,
+                out=0x6000, lse=0x7000, stream=None)
+    args.update(kw)
+    lib = vlf.load_library()
+    rc = lib.vlf_attend(args["qkv"], args["cos"], args["sin"], args["P"], args["cu"],
+                        args["tiles"], args["nt"], args["br"], args["T"], args["S"], args["H"],
+                        args["window"], args["scale"], args["dtype"], args["out"], args["lse"],
+                        args["stream"])
+    return rc, lib.vlf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=7), binding.VLF_EUNSUPPORTED, "dtype"),
+    (dict(br=32), binding.VLF_EUNSUPPORTED, "br"),
+    (dict(H=0), binding.VLF_EINVAL, "H ="),
+    (dict(H=70000), binding.VLF_EINVAL, "H ="),
+    (dict(window=-1), binding.VLF_EINVAL, "window"),
+    (dict(T=-5), binding.VLF_EINVAL, "negative"),
+    (dict(nt=-1), binding.VLF_EINVAL, "negative"),
+    (dict(S=0), binding.VLF_EINVAL, "no sequence"),
+    (dict(qkv=None), binding.VLF_EINVAL, "null"),
+    (dict(lse=None), binding.VLF_EINVAL, "null"),
+    (dict(tiles=None), binding.VLF_EINVAL, "null"),
+    (dict(P=0), binding.VLF_EINVAL, "rotary"),
+    (dict(scale=float("nan")), binding.VLF_EINVAL, "scale"),
+    (dict(scale=float("inf")), binding.VLF_EINVAL, "scale"),
+])
+def test_attend_rejects_bad_arguments(kw, status, msg):
+    rc, text = _attend_status(**kw)
+    assert rc == status
+    assert msg in text
+
+
+def test_attend_with_no_work_is_a_no_op():
+    # no tiles or no tokens: returns OK without touching the (fake) pointers or the device
+    assert _attend_status(nt=0)[0] == binding.VLF_OK
+    assert _attend_status(T=0, S=0, nt=0, qkv=None, out=None)[0] == binding.VLF_OK

@@ -1,0 +1,202 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle, on the GPU.
+
+Tolerances: max |out - oracle| <= 2e-2 for bf16 inputs and 4e-3 for fp16; max |lse - oracle|
+<= 1e-3. The oracle runs in mode B: the query/key operands rounded to the storage type as the
+subject page's kernel rounds them (hanzo-kernel 0.2.42 src/packed.rs, `attend`'s tile loads);
+the gap to the unrounded definition (mode A) is printed for each case.
+
+Small cases compare every output; the full-size workloads run exactly as bench.py launches
+them and compare sampled rows that cover every sequence's first and last rows, tile and wave
+boundaries and random rows, plus properties of all rows. Guard regions after `out` and `lse`
+must stay untouched.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import variable_length_flash_amd as vlf
+from variable_length_flash_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = {"bf16": 2e-2, "fp16": 4e-3}
+LSE_TOL = 1e-3
+GUARD = 4096
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w, qkv, cos, sin, br=None, window=None):
+    """The HIP path on cuda:0 with NaN-filled outputs and guard regions; returns numpy arrays."""
+    window = w.window if window is None else window
+    dev = torch.device("cuda:0")
+    batch = vlf.prepare(w.cu, dev, br)
+    q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
+    T, H = w.tokens, w.heads
+    out_buf = torch.full((T * H * 64 + GUARD,), float("nan"), dtype=qkv.dtype, device=dev)
+    lse_buf = torch.full((H * T + GUARD,), float("nan"), dtype=torch.float32, device=dev)
+    out = out_buf[:T * H * 64].view(T, H * 64)
+    lse = lse_buf[:H * T].view(H, T)
+    vlf.attend_into(batch, q, c, s, H, window, w.scale, out, lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(out_buf[T * H * 64:]).all(), "out guard region was written"
+    assert torch.isnan(lse_buf[H * T:]).all(), "lse guard region was written"
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def inputs(w):
+    qkv = workloads.draw_qkv(w)
+    cos, sin = workloads.rope_tables(w)
+    return qkv, cos, sin
+
+
+def compare(name, w, got_out, got_lse, qkv, cos, sin, rows=None, window=None):
+    window = w.window if window is None else window
+    q32 = qkv.float().numpy()
+    c32, s32 = cos.float().numpy(), sin.float().numpy()
+    want_out, want_lse = oracle.attend(q32, c32, s32, w.cu, w.heads, window, w.scale, mode="B",
+                                       dtype=w.dtype, rows=rows)
+    a_out, a_lse = oracle.attend(q32, c32, s32, w.cu, w.heads, window, w.scale, mode="A",
+                                 dtype=w.dtype, rows=rows)
+    if rows is not None:
+        got_out, got_lse = got_out[rows], got_lse[:, rows]
+    assert np.isfinite(got_out).all() and np.isfinite(got_lse).all(), "unwritten or non-finite"
+    e_out = float(np.abs(got_out - want_out).max()) if got_out.size else 0.0
+    e_lse = float(np.abs(got_lse - want_lse).max()) if got_lse.size else 0.0
+    a_eo = float(np.abs(got_out - a_out).max()) if got_out.size else 0.0
+    a_el = float(np.abs(got_lse - a_lse).max()) if got_lse.size else 0.0
+    _say(f"[parity] {name}: out {e_out:.2e} (tol {OUT_TOL[w.dtype]:.0e}), lse {e_lse:.2e} "
+         f"(tol {LSE_TOL:.0e}); vs unrounded definition: out {a_eo:.2e}, lse {a_el:.2e}")
+    assert e_out <= OUT_TOL[w.dtype], (name, e_out)
+    assert e_lse <= LSE_TOL, (name, e_lse)
+
+
+LENS = [5, 40, 1, 33, 70]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("br", [64, 128])
+@pytest.mark.parametrize("window", [0, 9, 65])
+def test_page_fixture(dtype, br, window):
+    w = workloads.custom(LENS, 2, dtype=dtype, window=window, table_rows=128, seed=7)
+    qkv, cos, sin = inputs(w)
+    _say(f"case page-fixture {dtype} br={br} W={window}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=br)
+    compare(f"lens {LENS} {dtype} br={br} W={window}", w, out, lse, qkv, cos, sin)
+
+
+def test_tiny_workload():
+    w = workloads.tiny()
+    qkv, cos, sin = inputs(w)
+    _say("case tiny")
+    out, lse = run_gpu(w, qkv, cos, sin)
+    compare("tiny", w, out, lse, qkv, cos, sin)
+
+
+RAGGED = [1, 63, 64, 65, 127, 128, 129, 300, 0, 257, 31, 32, 33, 2]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("window", [0, 1, 2, 31, 32, 33, 64, 65, 128, 200, 1000])
+def test_ragged_tiles_and_windows(dtype, window):
+    w = workloads.custom(RAGGED, 3, dtype=dtype, window=window, base=1e4, table_rows=512,
+                         seed=11)
+    qkv, cos, sin = inputs(w)
+    for br in (64, 128):
+        _say(f"case ragged {dtype} W={window} br={br}")
+        out, lse = run_gpu(w, qkv, cos, sin, br=br)
+        compare(f"ragged {dtype} W={window} br={br}", w, out, lse, qkv, cos, sin)
+
+
+def test_single_key_rows_are_exact():
+    """W = 1: each row sees only itself, so out = v (bit-exact) and lse = <q~, k~>."""
+    w = workloads.custom([1, 7, 130, 64], 2, dtype="bf16", window=1, table_rows=256, seed=5)
+    qkv, cos, sin = inputs(w)
+    out, lse = run_gpu(w, qkv, cos, sin)
+    hd = w.heads * 64
+    np.testing.assert_array_equal(out, qkv[:, 2 * hd:].float().numpy())
+    compare("single-key rows", w, out, lse, qkv, cos, sin)
+
+
+@pytest.mark.parametrize("lens", [[1], [1] * 300, [0, 0, 5, 0], [64] * 9, [128, 1, 128],
+                                  [2048], [0, 777, 0, 0, 1500]])
+def test_edge_batches(lens):
+    w = workloads.custom(lens, 2, dtype="fp16", window=0, table_rows=max(lens + [1]), seed=3)
+    qkv, cos, sin = inputs(w)
+    _say(f"case edge {lens[:6]}")
+    out, lse = run_gpu(w, qkv, cos, sin)
+    compare(f"edge {lens[:6]}{'...' if len(lens) > 6 else ''}", w, out, lse, qkv, cos, sin)
+
+
+def test_empty_batch_launches_nothing():
+    w = workloads.custom([0, 0], 2, dtype="bf16", table_rows=4)
+    qkv, cos, sin = inputs(w)
+    out, lse = run_gpu(w, qkv, cos, sin)
+    assert out.shape == (0, 128) and lse.shape == (2, 0)
+
+
+def test_stream_and_repeat_are_deterministic():
+    """Two launches on a side stream give identical bits."""
+    w = workloads.custom([300, 41, 999], 4, dtype="bf16", window=0, table_rows=1024, seed=9)
+    qkv, cos, sin = inputs(w)
+    dev = torch.device("cuda:0")
+    batch = vlf.prepare(w.cu, dev)
+    q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
+    side = torch.cuda.Stream(dev)
+    outs = []
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            o = torch.empty((w.tokens, w.heads * 64), dtype=qkv.dtype, device=dev)
+            l = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
+            vlf.attend_into(batch, q, c, s, w.heads, 0, w.scale, o, l)
+            outs.append((o, l))
+    side.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def sample_rows(w, br, count, seed):
+    """First / last rows of every sequence, rows at tile and wave boundaries of a spread of
+    tiles, and random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    cu = w.cu
+    for s in range(w.sequences):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b > a:
+            rows.update([a, b - 1])
+    tiles = vlf.tile_table(cu, br)
+    pick = tiles[rng.choice(len(tiles), size=min(len(tiles), 64), replace=False)]
+    for s, i0 in pick:
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        for off in (0, 31, 32, 63, 64, 95, 96, br - 1):
+            if i0 + off < L:
+                rows.add(a + int(i0) + off)
+    extra = max(0, count - len(rows))
+    rows.update(rng.integers(0, w.tokens, size=extra).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["encoder", "sliding", "many_short", "long"])
+def test_full_size_workload(name):
+    w = workloads.WORKLOADS[name]()
+    _say(f"case full-size {name}: T={w.tokens} S={w.sequences} H={w.heads} {w.dtype} "
+         f"W={w.window}")
+    qkv, cos, sin = inputs(w)
+    out, lse = run_gpu(w, qkv, cos, sin)
+    # every row written, finite; each out row lies within the span of the visible values
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    vmax = float(qkv[:, 2 * w.heads * 64:].float().abs().max())
+    assert np.abs(out).max() <= vmax * (1 + 2 ** -7)
+    # lse >= the largest visible score is implied by l >= 1; lse <= max score + ln(keys)
+    br = vlf.choose_br(max(w.lens))
+    seed = {"encoder": 2, "sliding": 3, "many_short": 4, "long": 5}[name]
+    rows = sample_rows(w, br, 1500 if name == "long" else 3000, seed=seed)
+    compare(f"{name} ({len(rows)} sampled rows, all heads)", w, out, lse, qkv, cos, sin,
+            rows=rows)

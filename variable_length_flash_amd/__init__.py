@@ -1,9 +1,10 @@
 """MI355X-native packed variable-length attention forward (RoPE in the kernel, optional
-symmetric window), built around a C-ABI library ``libvlf.so`` of hand-written gfx950 HIP.
+symmetric window), built around the C-ABI library ``libvlf.so`` of hand-written gfx950 HIP.
 
 The binding (``variable_length_flash_amd.binding``) loads the library on first use and fails
 loudly when it is missing: there is no fallback path.
 """
 from .binding import (  # noqa: F401
-    VlfError, attend, attend_into, tile_table, visible_pairs, library_path, load_library,
+    Batch, VlfError, attend, attend_into, choose_br, library_path, load_library, prepare,
+    tile_count, tile_table, visible_pairs,
 )

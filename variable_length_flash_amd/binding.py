@@ -1,5 +1,215 @@
-"""placeholder"""
+"""ctypes binding of libvlf.so (declared in include/vlf.h): argument marshalling only.
+
+Every step of the forward runs in the library's gfx950 kernels. PyTorch supplies device memory
+and the current HIP stream. When the library is missing this module raises; there is no other
+implementation to fall back on.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libvlf.so")
+
+VLF_OK, VLF_EINVAL, VLF_EUNSUPPORTED, VLF_EHIP = 0, -1, -2, -3
+VLF_F16, VLF_BF16 = 0, 1
+HEAD_DIM = 64
+
+# every function include/vlf.h declares
+EXPORTS = ("vlf_version", "vlf_last_error", "vlf_tile_count", "vlf_tile_table",
+           "vlf_visible_pairs", "vlf_attend")
+
+
 class VlfError(RuntimeError):
-    pass
-def attend(*a, **k): raise NotImplementedError
-attend_into = tile_table = visible_pairs = library_path = load_library = attend
+    def __init__(self, status: int, message: str):
+        super().__init__(f"vlf status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def load_library():
+    """Open libvlf.so (built by ``variable_length_flash_amd.build``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise VlfError(VLF_EHIP, f"{LIBRARY} is not built; run python -m "
+                                 "variable_length_flash_amd.build")
+    lib = ctypes.CDLL(LIBRARY)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.vlf_version.argtypes = []
+    lib.vlf_version.restype = i32
+    lib.vlf_last_error.argtypes = []
+    lib.vlf_last_error.restype = ctypes.c_char_p
+    lib.vlf_tile_count.argtypes = [p, i32, i32, i32, p, p]
+    lib.vlf_tile_count.restype = ctypes.c_int
+    lib.vlf_tile_table.argtypes = [p, i32, i32, i32, p, i64]
+    lib.vlf_tile_table.restype = ctypes.c_int
+    lib.vlf_visible_pairs.argtypes = [p, i32, i32, i32, p]
+    lib.vlf_visible_pairs.restype = ctypes.c_int
+    lib.vlf_attend.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32,
+                               ctypes.c_float, i32, p, p, p]
+    lib.vlf_attend.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != VLF_OK:
+        raise VlfError(status, load_library().vlf_last_error().decode())
+
+
+def _host_cu(cu) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(cu, torch.Tensor):
+            cu = cu.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    arr = np.asarray(cu)
+    if arr.ndim != 1 or arr.shape[0] < 1:
+        raise VlfError(VLF_EINVAL, "cu must be a 1-D sequence of S+1 offsets")
+    if arr.size and (arr.min() < np.iinfo(np.int32).min or arr.max() > np.iinfo(np.int32).max):
+        raise VlfError(VLF_EINVAL, "cu does not fit int32")
+    return np.ascontiguousarray(arr, dtype=np.int32)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def tile_count(cu, br: int):
+    """(num_tiles, max_len) for ``br``-row tiles of the packed batch ``cu``."""
+    cu = _host_cu(cu)
+    n, m = ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().vlf_tile_count(_ptr(cu), cu.shape[0] - 1, int(cu[-1]), br,
+                                         ctypes.byref(n), ctypes.byref(m)))
+    return n.value, m.value
+
+
+def tile_table(cu, br: int) -> np.ndarray:
+    """The tile table [NT, 2] uint32 of (sequence, first row) pairs, from the library."""
+    cu = _host_cu(cu)
+    n, _ = tile_count(cu, br)
+    table = np.zeros((n, 2), dtype=np.uint32)
+    _check(load_library().vlf_tile_table(_ptr(cu), cu.shape[0] - 1, int(cu[-1]), br,
+                                          _ptr(table), 2 * n))
+    return table
+
+
+def visible_pairs(cu, window: int) -> int:
+    """(query, key) pairs one head computes for this packed batch and window."""
+    cu = _host_cu(cu)
+    out = ctypes.c_uint64()
+    _check(load_library().vlf_visible_pairs(_ptr(cu), cu.shape[0] - 1, int(cu[-1]), int(window),
+                                            ctypes.byref(out)))
+    return int(out.value)
+
+
+def choose_br(max_len: int) -> int:
+    """64-row tiles when no sequence is longer than 64, else 128."""
+    return 64 if max_len <= 64 else 128
+
+
+@dataclass
+class Batch:
+    """Index tensors of one packed batch on the device: cu and the tile table."""
+    cu_host: np.ndarray
+    cu: "torch.Tensor"
+    tiles: "torch.Tensor"
+    num_tiles: int
+    max_len: int
+    br: int
+
+    @property
+    def tokens(self) -> int:
+        return int(self.cu_host[-1])
+
+    @property
+    def sequences(self) -> int:
+        return int(self.cu_host.shape[0] - 1)
+
+
+def prepare(cu, device=None, br: int | None = None) -> Batch:
+    """Validate ``cu``, build the tile table on the host and copy both to ``device``."""
+    import torch
+    cu_host = _host_cu(cu)
+    device = torch.device("cuda") if device is None else torch.device(device)
+    _, max_len = tile_count(cu_host, 128)
+    br = choose_br(max_len) if br is None else int(br)
+    table = tile_table(cu_host, br)
+    return Batch(cu_host, torch.from_numpy(cu_host).to(device),
+                 torch.from_numpy(table.view(np.int32)).to(device), table.shape[0], max_len, br)
+
+
+_DTYPES = {}
+
+
+def _dtype_code(t):
+    import torch
+    if not _DTYPES:
+        _DTYPES.update({torch.bfloat16: VLF_BF16, torch.float16: VLF_F16})
+    if t not in _DTYPES:
+        raise VlfError(VLF_EUNSUPPORTED, f"dtype {t}; supported: bfloat16, float16")
+    return _DTYPES[t]
+
+
+def attend_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: float, out, lse,
+                stream=None):
+    """Queue the forward on ``stream`` (default: torch's current stream of qkv's device).
+
+    qkv [T, 3*heads*64], cos/sin [P, 32] (same dtype, P >= longest sequence), out [T, heads*64]
+    (same dtype), lse [heads, T] float32; all contiguous on one device.
+    """
+    import torch
+    T = batch.tokens
+    code = _dtype_code(qkv.dtype)
+    for name, t, shape, dt in (("qkv", qkv, (T, 3 * heads * HEAD_DIM), qkv.dtype),
+                               ("out", out, (T, heads * HEAD_DIM), qkv.dtype),
+                               ("lse", lse, (heads, T), torch.float32)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise VlfError(VLF_EINVAL, f"{name}: {tuple(t.shape)} {t.dtype} contiguous="
+                                       f"{t.is_contiguous()}, expected {shape} {dt}")
+    for name, t in (("cos", cos), ("sin", sin)):
+        if t.dim() != 2 or t.shape[1] != HEAD_DIM // 2 or t.dtype != qkv.dtype or \
+                not t.is_contiguous():
+            raise VlfError(VLF_EINVAL, f"{name}: {tuple(t.shape)} {t.dtype}, expected [P, 32] "
+                                       f"{qkv.dtype} contiguous")
+    if cos.shape != sin.shape:
+        raise VlfError(VLF_EINVAL, "cos and sin differ in shape")
+    if cos.shape[0] < batch.max_len:
+        raise VlfError(VLF_EINVAL, f"rotary tables have {cos.shape[0]} rows; the longest "
+                                   f"sequence has {batch.max_len}")
+    dev = qkv.device
+    for name, t in (("cos", cos), ("sin", sin), ("out", out), ("lse", lse),
+                    ("cu", batch.cu), ("tiles", batch.tiles)):
+        if t.device != dev:
+            raise VlfError(VLF_EINVAL, f"{name} is on {t.device}, qkv on {dev}")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(load_library().vlf_attend(
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        batch.tiles.data_ptr(), batch.num_tiles, batch.br, T, batch.sequences, heads,
+        int(window), float(scale), code, out.data_ptr(), lse.data_ptr(), stream))
+
+
+def attend(qkv, cos, sin, cu, heads: int, window: int = 0, scale: float = 0.125,
+           br: int | None = None):
+    """Forward of packed attention; returns (out [T, heads*64], lse [heads, T] float32)."""
+    import torch
+    batch = cu if isinstance(cu, Batch) else prepare(cu, qkv.device, br)
+    T = batch.tokens
+    out = torch.empty((T, heads * HEAD_DIM), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((heads, T), dtype=torch.float32, device=qkv.device)
+    attend_into(batch, qkv, cos, sin, heads, window, scale, out, lse)
+    return out, lse

@@ -1,0 +1,166 @@
+// Host side of libvlf.so: argument checks, the tile table and the visible-pair count.
+//
+// The tile table is the host-built index of hanzo-kernel 0.2.42 src/packed.rs (`layout`): one
+// (sequence, first row) pair per `br` query rows of every sequence, in sequence order. The pair
+// count follows the masking of that page's `attend` kernel: a query at position i sees key j of
+// its own sequence when the window is 0 or |i - j| < window.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/vlf.h"
+#include "vlf_internal.h"
+
+namespace vlf {
+
+static thread_local std::string g_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return status;
+}
+
+// cu[0] = 0, non-decreasing, cu[S] = T. Reports the longest sequence.
+static int check_cu(const int32_t *cu, int32_t S, int32_t T, int32_t *max_len) {
+    if (S < 0 || T < 0)
+        return fail(VLF_EINVAL, "negative size: S=%d T=%d", S, T);
+    if (!cu)
+        return fail(VLF_EINVAL, "cu is NULL");
+    if (cu[0] != 0)
+        return fail(VLF_EINVAL, "cu[0] = %d, expected 0", cu[0]);
+    int32_t longest = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        if (cu[s + 1] < cu[s])
+            return fail(VLF_EINVAL, "cu decreases at s=%d (%d > %d)", s, cu[s], cu[s + 1]);
+        int32_t L = cu[s + 1] - cu[s];
+        if (L > longest)
+            longest = L;
+    }
+    if (cu[S] != T)
+        return fail(VLF_EINVAL, "cu[S] = %d, expected T = %d", cu[S], T);
+    if (max_len)
+        *max_len = longest;
+    return VLF_OK;
+}
+
+static bool supported_br(int32_t br) { return br == 64 || br == 128; }
+
+}  // namespace vlf
+
+using namespace vlf;
+
+extern "C" {
+
+int32_t vlf_version(void) { return 1; }
+
+const char *vlf_last_error(void) { return g_error.c_str(); }
+
+int vlf_tile_count(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, int32_t *num_tiles,
+                   int32_t *max_len) {
+    if (br < 1)
+        return fail(VLF_EINVAL, "br = %d < 1", br);
+    if (!num_tiles)
+        return fail(VLF_EINVAL, "num_tiles is NULL");
+    int32_t longest = 0;
+    int rc = check_cu(cu_host, S, T, &longest);
+    if (rc)
+        return rc;
+    int64_t n = 0;
+    for (int32_t s = 0; s < S; ++s)
+        n += (int64_t)(cu_host[s + 1] - cu_host[s] + br - 1) / br;
+    if (n > INT32_MAX)
+        return fail(VLF_EINVAL, "%lld tiles exceed INT32_MAX", (long long)n);
+    *num_tiles = (int32_t)n;
+    if (max_len)
+        *max_len = longest;
+    return VLF_OK;
+}
+
+int vlf_tile_table(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, uint32_t *tiles_host,
+                   int64_t capacity) {
+    int32_t n = 0;
+    int rc = vlf_tile_count(cu_host, S, T, br, &n, nullptr);
+    if (rc)
+        return rc;
+    if (capacity < 2 * (int64_t)n)
+        return fail(VLF_EINVAL, "capacity %lld < %lld", (long long)capacity, 2 * (long long)n);
+    if (n > 0 && !tiles_host)
+        return fail(VLF_EINVAL, "tiles_host is NULL");
+    int64_t k = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        const int32_t L = cu_host[s + 1] - cu_host[s];
+        for (int32_t i0 = 0; i0 < L; i0 += br) {
+            tiles_host[k++] = (uint32_t)s;
+            tiles_host[k++] = (uint32_t)i0;
+        }
+    }
+    return VLF_OK;
+}
+
+int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t window,
+                      uint64_t *pairs) {
+    if (window < 0)
+        return fail(VLF_EINVAL, "window = %d < 0", window);
+    if (!pairs)
+        return fail(VLF_EINVAL, "pairs is NULL");
+    int rc = check_cu(cu_host, S, T, nullptr);
+    if (rc)
+        return rc;
+    uint64_t total = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        const uint64_t L = (uint64_t)(cu_host[s + 1] - cu_host[s]);
+        if (window == 0 || L <= (uint64_t)window) {
+            total += L * L;  // every key of the sequence
+        } else {
+            // rows see min(L, i + W) - max(0, i - W + 1) keys; summed over i this is
+            // L(2W - 1) - W(W - 1) for L >= W
+            const uint64_t W = (uint64_t)window;
+            total += L * (2 * W - 1) - W * (W - 1);
+        }
+    }
+    *pairs = total;
+    return VLF_OK;
+}
+
+int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+               const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles, int32_t br,
+               int32_t T, int32_t S, int32_t H, int32_t window, float scale, int32_t dtype,
+               void *out, float *lse, void *stream) {
+    if (dtype != VLF_BF16 && dtype != VLF_F16)
+        return fail(VLF_EUNSUPPORTED, "dtype = %d; supported: VLF_F16 (0), VLF_BF16 (1)", dtype);
+    if (!supported_br(br))
+        return fail(VLF_EUNSUPPORTED, "br = %d; supported: 64, 128", br);
+    if (H < 1 || H > 65536)
+        return fail(VLF_EINVAL, "H = %d outside 1 .. 65536", H);
+    if (window < 0)
+        return fail(VLF_EINVAL, "window = %d < 0", window);
+    if (T < 0 || S < 0 || num_tiles < 0 || table_rows < 0)
+        return fail(VLF_EINVAL, "negative size: T=%d S=%d num_tiles=%d table_rows=%d", T, S,
+                    num_tiles, table_rows);
+    if (T > 0 && S == 0)
+        return fail(VLF_EINVAL, "T = %d tokens but no sequence", T);
+    if ((int64_t)T * 3 * H * 64 > ((int64_t)1 << 40))
+        return fail(VLF_EINVAL, "qkv of %lld elements is beyond this library's indexing",
+                    (long long)T * 3 * H * 64);
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(VLF_EINVAL, "scale is not finite");
+    if (T == 0 || num_tiles == 0)
+        return VLF_OK;
+    if (!qkv || !cos || !sin || !cu_dev || !tiles_dev || !out || !lse)
+        return fail(VLF_EINVAL, "null device pointer (qkv=%p cos=%p sin=%p cu=%p tiles=%p "
+                    "out=%p lse=%p)", qkv, cos, sin, (const void *)cu_dev,
+                    (const void *)tiles_dev, out, (void *)lse);
+    if (table_rows == 0)
+        return fail(VLF_EINVAL, "empty rotary tables with %d tokens", T);
+    AttendArgs a{qkv, cos, sin, table_rows, cu_dev, tiles_dev, num_tiles, br, T, S, H,
+                 window, scale, dtype, out, lse, stream};
+    return launch_attend(a);
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Internal declarations shared by the host translation unit (vlf_host.cpp) and the kernel
+// translation unit (vlf_attend.hip). Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace vlf {
+
+// Everything the launcher needs after the host side has validated the arguments.
+struct AttendArgs {
+    const void *qkv;
+    const void *cos;
+    const void *sin;
+    int32_t table_rows;
+    const int32_t *cu;
+    const uint32_t *tiles;
+    int32_t num_tiles;
+    int32_t br;
+    int32_t T, S, H;
+    int32_t window;
+    float scale;
+    int32_t dtype;
+    void *out;
+    float *lse;
+    void *stream;
+};
+
+// Queue the forward kernel; returns a vlf_status.
+int launch_attend(const AttendArgs &a);
+
+// Record the calling thread's error message (printf-style) and return `status`.
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+}  // namespace vlf
