@@ -223,21 +223,22 @@ def run(args):
     print(json.dumps(line), flush=True)
 
 
-def summarize(directory: str, workload: str):
+def summarize(directories, workload: str):
     """Traffic per launch from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each
     scaled by the same counter's reading for the 1 GiB copy of the profile run."""
     rows = []
-    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
-                          recursive=True):
-        with open(path) as f:
-            rows.extend(csv.DictReader(f))
+    for directory in directories:
+        for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                              recursive=True):
+            with open(path) as f:
+                rows.extend(csv.DictReader(f))
     if not rows:
-        raise SystemExit(f"no counter_collection.csv under {directory}")
+        raise SystemExit(f"no counter_collection.csv under {directories}")
     per = {}  # (counter, kind) -> list of per-dispatch values (KiB)
     for r in rows:
         name = r.get("Kernel_Name", "")
-        kind = "attend" if KERNEL_NAME in name else ("copy" if "copy" in name.lower() or
-                                                     "elementwise" in name.lower() else None)
+        kind = "attend" if KERNEL_NAME in name else ("copy" if "copybuffer" in name.lower()
+                                                     else None)
         if kind is None:
             continue
         per.setdefault((r["Counter_Name"], kind, r.get("Dispatch_Id", "")), 0.0)
@@ -276,7 +277,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-run", action="store_true")
-    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--summarize", metavar="DIR", nargs="+")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.workload)
