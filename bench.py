@@ -146,7 +146,7 @@ def run(args):
         sys.exit(2)
     dev = torch.device("cuda:0")
     w, qkv, cos, sin = make_inputs(args.workload)
-    batch = vlf.prepare(w.cu, dev)
+    batch = vlf.prepare(w.cu, dev, args.br)
     q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
     out = torch.empty((w.tokens, w.heads * 64), dtype=q.dtype, device=dev)
     lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
@@ -274,6 +274,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long",
                     choices=["tiny", "encoder", "sliding", "many_short", "long"])
+    ap.add_argument("--br", type=int, default=None, choices=[64, 128, 256],
+                    help="query rows per workgroup (default: chosen from the longest sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-run", action="store_true")

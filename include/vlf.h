@@ -52,7 +52,7 @@ const char *vlf_last_error(void);
  * Validate cu and size the tile table for `br`-row query tiles.
  * hanzo-kernel 0.2.42 src/packed.rs, `layout`: every sequence contributes ceil(L_s / br) tiles.
  *   cu_host    host, [S+1] int32, checked as described above.
- *   br         tile height >= 1 (vlf_attend runs 64 and 128).
+ *   br         tile height >= 1 (vlf_attend runs 64, 128 and 256).
  *   num_tiles  out: number of tiles (may be 0).
  *   max_len    out: the longest sequence (0 if none). May be NULL.
  * Errors: VLF_EINVAL for a malformed cu, br < 1 or a total above INT32_MAX tiles.
@@ -104,7 +104,7 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
  *   tiles_dev  device, [num_tiles, 2] uint32 (sequence, first row) pairs built for the same cu
  *              and `br` (vlf_tile_table, or any permutation of it: the order is the launch
  *              order). Tiles naming a sequence >= S or a row beyond the sequence are skipped.
- *   br         64 or 128: rows per tile, as the table was built.
+ *   br         64, 128 or 256: rows per tile, as the table was built.
  *   T, S, H    tokens, sequences, heads (1 <= H <= 65536; T = 0 or num_tiles = 0 launches
  *              nothing).
  *   window     0 or W >= 1 as above.

@@ -117,8 +117,12 @@ def visible_pairs(cu, window: int) -> int:
 
 
 def choose_br(max_len: int) -> int:
-    """64-row tiles when no sequence is longer than 64, else 128."""
-    return 64 if max_len <= 64 else 128
+    """Query rows per workgroup: 64 when no sequence is longer than 64, 256 from 1024 tokens
+    on (each key tile is rotated once per workgroup, so taller tiles rotate less per query),
+    128 in between."""
+    if max_len <= 64:
+        return 64
+    return 256 if max_len >= 1024 else 128
 
 
 @dataclass

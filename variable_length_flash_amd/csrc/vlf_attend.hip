@@ -14,17 +14,31 @@
 //     max or row sum is a local reduction plus one exchange between lanes l and l ^ 32.
 //   * The query operand (B of that product) is rotated, scaled and rounded in registers and
 //     stays there for the whole key loop.
-//   * Keys are rotated in registers and staged row-major in LDS (rows padded to 144 B so the
-//     16-byte operand reads of 8 consecutive lanes fall on distinct banks).
-//   * Values are staged transposed, V^T [dim][key] (rows padded to 136 B), so the output is
-//     computed transposed too, O^T += V^T P^T: the probabilities leave the score accumulator
-//     registers directly as the B operand (after rounding), with the key order inside each
-//     16-key step permuted to match the accumulator layout; no LDS round trip for P. The O^T
-//     accumulator again gives each lane one query, so the per-row rescale is a lane-local
-//     multiply.
+//   * The key loop is software-pipelined over 64-key tiles. Step t: the scores of tile t+1 run
+//     on the matrix unit while the probabilities of tile t are formed (block A); tile t's output
+//     product runs while its row sum is taken and tile t+2 is rotated and written to LDS
+//     (block B); then tile t+1 is masked (edge tiles only) and its row maximum taken. LDS holds
+//     a ring of three tiles (values of t, keys of t+1, tile t+2 being staged); one barrier per
+//     step.
+//   * Key/value rows come in through raw buffer loads whose descriptors are rebased per tile in
+//     scalar registers: rows past the sequence read as zero in hardware and the per-thread
+//     offsets never change. Loads run two steps ahead in two register sets.
+//   * Over the full window, each query tile starts its sweep at a different key tile and wraps
+//     around, so the workgroups of one (sequence, head) do not all miss L2 on the same tile.
+//   * Keys sit row-major in LDS (rows padded to 144 B: the 16-byte operand reads of 16
+//     consecutive lanes fall on distinct banks).
+//   * Values sit transposed, V^T [dim][key] (rows of 144 B), so the output is computed
+//     transposed too, O^T += V^T P^T: the probabilities leave the score accumulators directly as
+//     the B operand (after rounding). Inside each 16-key step the accumulator holds keys
+//     {0-3, 8-11} in lanes 0-31 and {4-7, 12-15} in lanes 32-63; V^T stores every 16 keys in
+//     that order, so each A operand is one 16-byte LDS read. The lanes staging values write
+//     rows 8 apart in the two wave halves, which puts a wave's 64 stores on 64 distinct banks.
+//     The O^T accumulator gives each lane one query, so the per-row rescale is lane-local.
+//   * The softmax keeps, per row, a reference maximum that is only raised when a tile's maximum
+//     exceeds it by more than TAU (natural-log units); probabilities stay <= e^TAU, and the
+//     rescale of O is skipped for the whole wave when no row needs it. The result is the same
+//     as rescaling at every tile (the reference cancels in O / l and is added back in lse).
 //   * exp is exp2 with log2(e) folded into one FMA per score.
-//   * Masks are evaluated only on tiles that touch a sequence end or a window edge; waves with
-//     no visible pair in a key tile skip it.
 //   * The 1-D grid is remapped so that consecutive work items land on the same XCD (blocks are
 //     dealt round-robin over the 8 XCDs): all tiles of one (sequence, head) share one L2.
 #include <hip/hip_runtime.h>
@@ -39,9 +53,11 @@ namespace {
 constexpr int D = 64;      // head dimension
 constexpr int BC = 64;     // keys per key tile
 constexpr int KS = 72;     // LDS row stride of the rotated key tile, elements (144 B)
-constexpr int VS = 68;     // LDS row stride of the transposed value tile, elements (136 B)
+constexpr int VS = 72;     // LDS row stride of the transposed value tile, elements (144 B)
 constexpr int XCDS = 8;    // accelerator complex dies on MI355X
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float TAU = 8.0f;  // headroom of the reference maximum, natural-log units
+constexpr int RSRC_WORD3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -85,15 +101,17 @@ struct F16 {
     }
 };
 
-// Rotate 8 pairs: x1 holds elements m .. m+7, x2 elements m+32 .. m+39, c / s the table entries
-// for m .. m+7 at the row's position. Each output is one float32 rounding of x1 c - x2 s (or
-// x1 s + x2 c): the products of two storage-type values are exact in float32, so the fma
-// rounds once. Then times `scale` (exact for a power of two) and rounded to the storage type.
-template <class E>
-__device__ __forceinline__ void rotate8(u32x4 x1, u32x4 x2, u32x4 c, u32x4 s, float scale,
-                                        u32x4 &y1, u32x4 &y2) {
+// Rotate 2*W pairs held as W packed words each: x1 has elements m.., x2 elements m+32.., c / s
+// the table entries for m.. at the row's position. Each output is one float32 rounding of
+// x1 c - x2 s (or x1 s + x2 c): the products of two storage-type values are exact in float32,
+// so the fma rounds once. Then times `scale` (a power of two in practice, so exact) and rounded
+// to the storage type.
+template <class E, int W>
+__device__ __forceinline__ void rotate(const uint32_t *x1, const uint32_t *x2, const uint32_t *c,
+                                       const uint32_t *s, float scale, uint32_t *y1,
+                                       uint32_t *y2) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < W; ++k) {
         const float a0 = E::lo(x1[k]), a1 = E::hi(x1[k]);
         const float b0 = E::lo(x2[k]), b1 = E::hi(x2[k]);
         const float c0 = E::lo(c[k]), c1 = E::hi(c[k]);
@@ -117,6 +135,194 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Position of key k (0..63) of a tile inside a V^T row: within each 16 keys, swap bits 2 and 3
+// of the index, so keys {0-3, 8-11} come first and {4-7, 12-15} second.
+__device__ __forceinline__ int vt_slot(int k) {
+    return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)(uint32_t)n, RSRC_WORD3);
+}
+
+__device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// One thread's share of staging a 64-key tile, for NTHR threads.
+//   keys:   KP pairs (m, m+32) of key row kk, m = pp .. pp+KP-1;
+//   values: key rows 2kp and 2kp+1 (kp = lane % 32), VD dims in chunks of 4; the chunk index C
+//           (dims 4C .. 4C+3) has bit 1 equal to the wave half, so the two halves of a wave
+//           write V^T rows 8 apart.
+template <int NTHR>
+struct Staging {
+    static constexpr int KP = 2048 / NTHR;    // key pairs per thread (64 keys x 32 pairs)
+    static constexpr int KW = KP / 2;         // packed words per operand
+    static constexpr int TPK = 32 / KP;       // threads per key row
+    static constexpr int VC = 512 / NTHR;     // 4-dim value chunks per thread (16 x 32 pairs)
+    int kk, pp, kp;
+    int vchunk[VC];
+    int koff, toff, voff;                     // byte offsets inside the tile's descriptors
+
+    __device__ void init(int tid, int64_t ld) {
+        kk = tid / TPK;
+        pp = (tid % TPK) * KP;
+        const int lane = tid & 63, w = tid >> 6, half = lane >> 5;
+        kp = lane & 31;
+        constexpr int per = VC;  // chunks per (wave, half) = 8 / waves
+#pragma unroll
+        for (int q = 0; q < VC; ++q) {
+            const int k = w * per + q;  // 0..7 over the waves of the block
+            vchunk[q] = (k & 1) | (half << 1) | ((k >> 1) << 2);
+        }
+        koff = (int)(kk * ld * 2) + pp * 2;
+        toff = kk * 64 + pp * 2;
+        voff = (int)(2 * kp * ld * 2);
+    }
+};
+
+template <int NTHR>
+struct TileRegs {
+    uint32_t x1[Staging<NTHR>::KW], x2[Staging<NTHR>::KW];
+    uint32_t c[Staging<NTHR>::KW], s[Staging<NTHR>::KW];
+    u32x2 va[Staging<NTHR>::VC], vb[Staging<NTHR>::VC];
+};
+
+template <int NTHR>
+__device__ __forceinline__ void stage_load(TileRegs<NTHR> &r, const Staging<NTHR> &sg, int j0,
+                                           int len, int P, const uint16_t *kbase,
+                                           const uint16_t *vbase, const uint16_t *cos_t,
+                                           const uint16_t *sin_t, int64_t ld) {
+    using S = Staging<NTHR>;
+    const int64_t row_bytes = ld * 2;
+    const __amdgpu_buffer_rsrc_t kr = rsrc(kbase + (int64_t)j0 * ld, (int64_t)(len - j0) * row_bytes);
+    const __amdgpu_buffer_rsrc_t vr = rsrc(vbase + (int64_t)j0 * ld, (int64_t)(len - j0) * row_bytes);
+    const __amdgpu_buffer_rsrc_t cr = rsrc(cos_t + (int64_t)j0 * 32, (int64_t)(P - j0) * 64);
+    const __amdgpu_buffer_rsrc_t sr = rsrc(sin_t + (int64_t)j0 * 32, (int64_t)(P - j0) * 64);
+#pragma unroll
+    for (int w = 0; w < S::KW; w += 2) {
+        const u32x2 a = load8(kr, sg.koff + 4 * w);
+        const u32x2 b = load8(kr, sg.koff + 64 + 4 * w);
+        const u32x2 cc = load8(cr, sg.toff + 4 * w);
+        const u32x2 ss = load8(sr, sg.toff + 4 * w);
+        r.x1[w] = a[0], r.x1[w + 1] = a[1];
+        r.x2[w] = b[0], r.x2[w + 1] = b[1];
+        r.c[w] = cc[0], r.c[w + 1] = cc[1];
+        r.s[w] = ss[0], r.s[w + 1] = ss[1];
+    }
+#pragma unroll
+    for (int q = 0; q < S::VC; ++q) {
+        r.va[q] = load8(vr, sg.voff + sg.vchunk[q] * 8);
+        r.vb[q] = load8(vr, sg.voff + (int)row_bytes + sg.vchunk[q] * 8);
+    }
+}
+
+template <class E, int NTHR>
+__device__ __forceinline__ void stage_store(const TileRegs<NTHR> &r, const Staging<NTHR> &sg,
+                                            uint16_t *ks, uint16_t *vt) {
+    using S = Staging<NTHR>;
+    uint32_t y1[S::KW], y2[S::KW];
+    rotate<E, S::KW>(r.x1, r.x2, r.c, r.s, 1.0f, y1, y2);
+#pragma unroll
+    for (int w = 0; w < S::KW; w += 2) {
+        *(u32x2 *)(ks + sg.kk * KS + sg.pp + 2 * w) = u32x2{y1[w], y1[w + 1]};
+        *(u32x2 *)(ks + sg.kk * KS + 32 + sg.pp + 2 * w) = u32x2{y2[w], y2[w + 1]};
+    }
+    const int slot = vt_slot(2 * sg.kp);
+#pragma unroll
+    for (int q = 0; q < S::VC; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t wa = r.va[q][e >> 1], wb = r.vb[q][e >> 1];
+            const uint32_t a = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
+            const uint32_t b = (e & 1) ? (wb & 0xffff0000u) : (wb << 16);
+            *(uint32_t *)(vt + (4 * sg.vchunk[q] + e) * VS + slot) = a | b;
+        }
+    }
+}
+
+// Query operand of one 32-row block: rows rotated, scaled, rounded; rows past the sequence are
+// zero. Lane (n, g) holds, for k-step c, dims 16c + 8g .. 16c + 8g + 7 of its query.
+template <class E>
+__device__ __forceinline__ void query_operand(const uint16_t *qkv, const uint16_t *cos_t,
+                                              const uint16_t *sin_t, int64_t ld, int start,
+                                              int qi, int len, int h, int g, float scale,
+                                              u32x4 (&qop)[4]) {
+    if (qi < len) {
+        const uint16_t *qr = qkv + (int64_t)(start + qi) * ld + h * D;
+        const u32x4 xa = *(const u32x4 *)(qr + 8 * g);
+        const u32x4 xb = *(const u32x4 *)(qr + 16 + 8 * g);
+        const u32x4 xc = *(const u32x4 *)(qr + 32 + 8 * g);
+        const u32x4 xd = *(const u32x4 *)(qr + 48 + 8 * g);
+        const uint16_t *cr = cos_t + qi * 32, *sr = sin_t + qi * 32;
+        const u32x4 ca = *(const u32x4 *)(cr + 8 * g), cb = *(const u32x4 *)(cr + 16 + 8 * g);
+        const u32x4 sa = *(const u32x4 *)(sr + 8 * g), sb = *(const u32x4 *)(sr + 16 + 8 * g);
+        uint32_t y[4][4];
+        const uint32_t xa_[4] = {xa[0], xa[1], xa[2], xa[3]}, xc_[4] = {xc[0], xc[1], xc[2], xc[3]};
+        const uint32_t xb_[4] = {xb[0], xb[1], xb[2], xb[3]}, xd_[4] = {xd[0], xd[1], xd[2], xd[3]};
+        const uint32_t ca_[4] = {ca[0], ca[1], ca[2], ca[3]}, sa_[4] = {sa[0], sa[1], sa[2], sa[3]};
+        const uint32_t cb_[4] = {cb[0], cb[1], cb[2], cb[3]}, sb_[4] = {sb[0], sb[1], sb[2], sb[3]};
+        rotate<E, 4>(xa_, xc_, ca_, sa_, scale, y[0], y[2]);
+        rotate<E, 4>(xb_, xd_, cb_, sb_, scale, y[1], y[3]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            qop[c] = u32x4{y[c][0], y[c][1], y[c][2], y[c][3]};
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            qop[c] = u32x4{0, 0, 0, 0};
+    }
+}
+
+// Scores of one key tile for one 32-row block: S^T = K~ Q~^T from the key tile in LDS. Block 0
+// holds keys 0..31 of the tile, block 1 keys 32..63; lane (n, g), register i holds key
+// 8(i/4) + 4g + (i%4) of the block for query n.
+template <class E>
+__device__ __forceinline__ void scores(const uint16_t *kt, const u32x4 (&qop)[4], int n, int g,
+                                       f32x16 &s0, f32x16 &s1) {
+    const uint16_t *k0 = kt + n * KS + 8 * g;
+    const uint16_t *k1 = kt + (32 + n) * KS + 8 * g;
+    u32x4 a[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        a[2 * c] = *(const u32x4 *)(k0 + 16 * c);
+        a[2 * c + 1] = *(const u32x4 *)(k1 + 16 * c);
+    }
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        s0 = E::mfma(a[2 * c], qop[c], s0);
+        s1 = E::mfma(a[2 * c + 1], qop[c], s1);
+    }
+}
+
+// Masks the scores of the 64-key tile at j0 for query qi (keys past the sequence and outside
+// the window weigh nothing).
+__device__ __forceinline__ void mask_scores(f32x16 &s0, f32x16 &s1, int j0, int len, int window,
+                                            int qi, int g) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int ja = j0 + 8 * (i >> 2) + 4 * g + (i & 3), jb = ja + 32;
+        const int da = qi > ja ? qi - ja : ja - qi;
+        const int db = qi > jb ? qi - jb : jb - qi;
+        const bool va = ja < len && (window == 0 || da < window);
+        const bool vb = jb < len && (window == 0 || db < window);
+        s0[i] = va ? s0[i] : -__builtin_inff();
+        s1[i] = vb ? s1[i] : -__builtin_inff();
+    }
+}
+
+// Row maximum over the 64-key tile, shared by lanes n and n + 32.
+__device__ __forceinline__ float row_max(const f32x16 &s0, const f32x16 &s1) {
+    float mx = __builtin_fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+        mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
+    return pair_max(mx);
+}
+
 template <class E, int NW>
 __global__ void __launch_bounds__(NW * 64)
 attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
@@ -126,8 +332,9 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            int32_t window, float scale) {
     constexpr int BR = 32 * NW;
     constexpr int NTHR = 64 * NW;
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BC * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+    constexpr int RING = 3;  // key/value tiles in LDS: t (values), t+1 (keys), t+2 (being staged)
+    __shared__ __attribute__((aligned(16))) uint16_t ks[RING][BC * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[RING][D * VS];
 
     // XCD-aware work index: block b runs on XCD b % 8; give each XCD a contiguous range.
     const int nb = (int)gridDim.x;
@@ -152,27 +359,8 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, g = lane >> 5;
-    const int qi = i0 + 32 * wv + n;  // this lane's query position
-
-    // ---- query operand: rotated, scaled, rounded; rows past the sequence are zero.
-    // Lane (n, g) holds, for k-step c, dims 16c + 8g .. 16c + 8g + 7 of query n.
-    u32x4 qop[4];
-    if (qi < len) {
-        const uint16_t *qr = qkv + (int64_t)(start + qi) * ld + h * D;
-        const u32x4 xa = *(const u32x4 *)(qr + 8 * g);
-        const u32x4 xb = *(const u32x4 *)(qr + 16 + 8 * g);
-        const u32x4 xc = *(const u32x4 *)(qr + 32 + 8 * g);
-        const u32x4 xd = *(const u32x4 *)(qr + 48 + 8 * g);
-        const uint16_t *cr = cos_t + qi * 32, *sr = sin_t + qi * 32;
-        const u32x4 ca = *(const u32x4 *)(cr + 8 * g), cb = *(const u32x4 *)(cr + 16 + 8 * g);
-        const u32x4 sa = *(const u32x4 *)(sr + 8 * g), sb = *(const u32x4 *)(sr + 16 + 8 * g);
-        rotate8<E>(xa, xc, ca, sa, scale, qop[0], qop[2]);
-        rotate8<E>(xb, xd, cb, sb, scale, qop[1], qop[3]);
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            qop[c] = u32x4{0, 0, 0, 0};
-    }
+    const int w0 = i0 + 32 * wv;  // first row of this wave
+    const int qi = w0 + n;        // this lane's query position
 
     // ---- the key span this tile's window reaches (whole key tiles of BC)
     int lo = 0, hi = len;
@@ -182,138 +370,143 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         if ((int64_t)i0 + BR + window - 1 < len)
             hi = i0 + BR + window - 1;
     }
-
-    const int w0 = i0 + 32 * wv;            // first row of this wave
-    const bool wave_live = w0 < len;
-    const int w1 = min(w0 + 31, len - 1);   // last real row of this wave
-
-    float m_run = -__builtin_inff();  // running max of this row's scores
-    float l_run = 0.f;                // this lane's share of the row's exp-sum
-    f32x16 o0 = {}, o1 = {};          // O^T: dims 0..31 and 32..63 of query n
+    const int ntiles = (hi - lo + BC - 1) / BC;
+    // Over the full window every query tile of a sequence reads every key tile: start each at
+    // a different key tile (and wrap around) so the workgroups of one (sequence, head), which
+    // run side by side on one XCD, do not all miss L2 on the same tile at the same time. The
+    // online softmax does not depend on the order of the keys.
+    const int offset = window > 0 ? 0 : (int)((int64_t)(i0 / BR) * ntiles / ((len + BR - 1) / BR));
+    // first key of the t-th tile in this workgroup's order (t < ntiles + 4); past the span any
+    // in-span tile will do, as those tiles are staged but never used
+    auto key = [&](int t) {
+        int u = t + offset;
+        if (u >= ntiles)
+            u -= ntiles;
+        if (u >= ntiles)
+            u = 0;
+        return lo + u * BC;
+    };
 
     const uint16_t *kbase = qkv + (int64_t)start * ld + hd + h * D;
     const uint16_t *vbase = qkv + (int64_t)start * ld + 2 * hd + h * D;
 
-    for (int j0 = lo; j0 < hi; j0 += BC) {
-        // ---- stage the key tile (rotated) and the value tile (transposed); zero past the end
-        for (int u = tid; u < BC * 4; u += NTHR) {
-            const int kk = u >> 2, pp = u & 3;
-            const int j = j0 + kk;
-            u32x4 y1 = {0, 0, 0, 0}, y2 = {0, 0, 0, 0};
-            if (j < len) {
-                const uint16_t *kr = kbase + (int64_t)j * ld;
-                const u32x4 x1 = *(const u32x4 *)(kr + 8 * pp);
-                const u32x4 x2 = *(const u32x4 *)(kr + 32 + 8 * pp);
-                const u32x4 c = *(const u32x4 *)(cos_t + j * 32 + 8 * pp);
-                const u32x4 s = *(const u32x4 *)(sin_t + j * 32 + 8 * pp);
-                rotate8<E>(x1, x2, c, s, 1.0f, y1, y2);
-            }
-            *(u32x4 *)(ks + kk * KS + 8 * pp) = y1;
-            *(u32x4 *)(ks + kk * KS + 32 + 8 * pp) = y2;
-        }
-        for (int u = tid; u < (BC / 2) * 8; u += NTHR) {
-            const int kp = u >> 3, dc = u & 7;
-            const int j = j0 + 2 * kp;
-            u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-            const uint16_t *vr = vbase + (int64_t)j * ld + 8 * dc;
-            if (j < len)
-                va = *(const u32x4 *)vr;
-            if (j + 1 < len)
-                vb = *(const u32x4 *)(vr + ld);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t a = (e & 1) ? (va[e >> 1] >> 16) : (va[e >> 1] & 0xffffu);
-                const uint32_t bb = (e & 1) ? (vb[e >> 1] & 0xffff0000u) : (vb[e >> 1] << 16);
-                *(uint32_t *)(vt + (8 * dc + e) * VS + 2 * kp) = a | bb;
-            }
-        }
-        __syncthreads();
+    // ---- prologue: tiles 0 and 1 staged in LDS, tiles 2 and 3 in flight to registers
+    Staging<NTHR> sg;
+    sg.init(tid, ld);
+    TileRegs<NTHR> ra, rb;
+    stage_load<NTHR>(ra, sg, key(0), len, P, kbase, vbase, cos_t, sin_t, ld);
+    stage_load<NTHR>(rb, sg, key(1), len, P, kbase, vbase, cos_t, sin_t, ld);
+    u32x4 qop[4];
+    query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
+    stage_store<E, NTHR>(ra, sg, ks[0], vt[0]);
+    stage_load<NTHR>(ra, sg, key(2), len, P, kbase, vbase, cos_t, sin_t, ld);
+    stage_store<E, NTHR>(rb, sg, ks[1], vt[1]);
+    stage_load<NTHR>(rb, sg, key(3), len, P, kbase, vbase, cos_t, sin_t, ld);
+    __syncthreads();
 
-        bool any = wave_live;
-        if (window > 0)
-            any = any && (j0 <= w1 + window - 1) && (j0 + BC - 1 >= w0 - window + 1);
-        if (any) {
-            // ---- S^T = K~ Q~^T: block 0 keys j0 .. j0+31, block 1 keys j0+32 .. j0+63.
-            // Lane (n, g), register i holds key 8(i/4) + 4g + (i%4) of the block, query n.
-            f32x16 s0 = {}, s1 = {};
-            const uint16_t *k0 = ks + n * KS + 8 * g;
-            const uint16_t *k1 = ks + (32 + n) * KS + 8 * g;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                s0 = E::mfma(*(const u32x4 *)(k0 + 16 * c), qop[c], s0);
-                s1 = E::mfma(*(const u32x4 *)(k1 + 16 * c), qop[c], s1);
-            }
+    // A tile needs masks when it reaches past the sequence or some pair of this wave's rows
+    // and its keys lies outside the window.
+    auto edge = [&](int j0) {
+        return (j0 + BC > len) ||
+               (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window));
+    };
 
-            const bool edge = (j0 + BC > len) ||
-                              (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window));
-            if (edge) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int j = j0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    const int ja = j, jb = j + 32;
-                    const int da = qi > ja ? qi - ja : ja - qi;
-                    const int db = qi > jb ? qi - jb : jb - qi;
-                    const bool va = ja < len && (window == 0 || da < window);
-                    const bool vb = jb < len && (window == 0 || db < window);
-                    s0[i] = va ? s0[i] : -__builtin_inff();
-                    s1[i] = vb ? s1[i] : -__builtin_inff();
-                }
-            }
+    float m_ref = -__builtin_inff();  // reference maximum, natural-log units
+    float l_run = 0.f;                // this lane's share of the row's exp-sum
+    f32x16 o0 = {}, o1 = {};          // O^T: dims 0..31 and 32..63 of query n
+    f32x16 sa0, sa1, sb0, sb1;        // scores of the current and the next key tile
 
-            // ---- online softmax for query n
-            float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-            for (int i = 1; i < 16; ++i)
-                mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-            mx = pair_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            // no visible key yet: any finite reference keeps exp2(-inf) = 0
-            const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * LOG2E);
-            m_run = m_new;
-            const float mb = m_ref * LOG2E;
-            float rs = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], LOG2E, -mb));
-                s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], LOG2E, -mb));
-                rs += s0[i] + s1[i];
-            }
-            l_run = l_run * alpha + rs;
+    scores<E>(ks[0], qop, n, g, sa0, sa1);
+    if (edge(key(0)))
+        mask_scores(sa0, sa1, key(0), len, window, qi, g);
+    float mx = row_max(sa0, sa1);
+
+    // One key tile t: c0/c1 hold its masked scores and mx their row maximum; n0/n1 receive the
+    // scores of tile t+1. LDS ring slots: values of t in `cur`, keys of t+1 in the next slot;
+    // tile t+2 (register set `st`) is staged into the slot after, then set `st` receives tile
+    // t+4. Past the span, staging writes a slot no later tile reads, and the loads read zeros
+    // or rows inside the sequence.
+    auto step = [&](f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, TileRegs<NTHR> &st, int t,
+                    int cur) {
+        const int nxt = cur == RING - 1 ? 0 : cur + 1;
+        const int fut = nxt == RING - 1 ? 0 : nxt + 1;
+        const int j1 = key(t + 1);
+
+        // raise the reference maximum where this tile exceeds it by more than TAU; lanes that
+        // keep it scale by exactly 1 (their m_ref may still be -inf, where the difference
+        // would be NaN); a first reference scales the zero state by 0
+        const bool raise = mx > m_ref + TAU;  // false while nothing is visible
+        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * LOG2E) : 1.0f;
+        m_ref = raise ? mx : m_ref;
+        l_run *= alpha;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 o0[i] *= alpha;
                 o1[i] *= alpha;
             }
-
-            // ---- P rounded to the storage type, as the B operand of 16-key steps: step kc
-            // takes registers 8(kc%2) .. 8(kc%2)+7 of block kc/2, i.e. keys
-            // 16kc + 8(e/4) + 4g + (e%4) for slot e.
-            u32x4 pk[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                pk[0][k] = E::pack(s0[2 * k], s0[2 * k + 1]);
-                pk[1][k] = E::pack(s0[8 + 2 * k], s0[8 + 2 * k + 1]);
-                pk[2][k] = E::pack(s1[2 * k], s1[2 * k + 1]);
-                pk[3][k] = E::pack(s1[8 + 2 * k], s1[8 + 2 * k + 1]);
-            }
-
-            // ---- O^T += V^T P^T; the A operand for lane (n, g) at step kc is V^T row (dim) n
-            // (or 32 + n), keys 16kc + 4g + 0..3 and 16kc + 8 + 4g + 0..3.
-            const uint16_t *v0 = vt + n * VS + 4 * g;
-            const uint16_t *v1 = vt + (32 + n) * VS + 4 * g;
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                const u32x2 a0 = *(const u32x2 *)(v0 + 16 * kc);
-                const u32x2 a1 = *(const u32x2 *)(v0 + 16 * kc + 8);
-                const u32x2 b0 = *(const u32x2 *)(v1 + 16 * kc);
-                const u32x2 b1 = *(const u32x2 *)(v1 + 16 * kc + 8);
-                o0 = E::mfma(u32x4{a0[0], a0[1], a1[0], a1[1]}, pk[kc], o0);
-                o1 = E::mfma(u32x4{b0[0], b0[1], b1[0], b1[1]}, pk[kc], o1);
-            }
         }
+        // no visible key yet: any finite reference keeps exp2(-inf) = 0
+        const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
+
+        // ---- block A: the scores of tile t+1 on the matrix unit while the probabilities of
+        // tile t are formed and rounded: the B operand of 16-key step kc takes registers
+        // 8(kc%2) .. 8(kc%2)+7 of block kc/2, i.e. keys 16kc + 8(e/4) + 4g + (e%4).
+        scores<E>(ks[nxt], qop, n, g, n0, n1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            c0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(c0[i], LOG2E, -mb));
+            c1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(c1[i], LOG2E, -mb));
+        }
+        u32x4 pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            pk[0][k] = E::pack(c0[2 * k], c0[2 * k + 1]);
+            pk[1][k] = E::pack(c0[8 + 2 * k], c0[8 + 2 * k + 1]);
+            pk[2][k] = E::pack(c1[2 * k], c1[2 * k + 1]);
+            pk[3][k] = E::pack(c1[8 + 2 * k], c1[8 + 2 * k + 1]);
+        }
+
+        // ---- block B: O^T += V^T P^T for tile t while the row sum is taken and tile t+2 is
+        // rotated and staged. The A operand for lane (n, g) at step kc is V^T row (dim) n (or
+        // 32 + n), slots 16kc + 8g .. +7 = keys 16kc + 4g + 0..3 and 16kc + 8 + 4g + 0..3.
+        const uint16_t *v0 = vt[cur] + n * VS + 8 * g;
+        const uint16_t *v1 = vt[cur] + (32 + n) * VS + 8 * g;
+        u32x4 va[8];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            va[2 * kc] = *(const u32x4 *)(v0 + 16 * kc);
+            va[2 * kc + 1] = *(const u32x4 *)(v1 + 16 * kc);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            o0 = E::mfma(va[2 * kc], pk[kc], o0);
+            o1 = E::mfma(va[2 * kc + 1], pk[kc], o1);
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            rs += c0[i] + c1[i];
+        l_run += rs;
+        stage_store<E, NTHR>(st, sg, ks[fut], vt[fut]);
+        stage_load<NTHR>(st, sg, key(t + 4), len, P, kbase, vbase, cos_t, sin_t, ld);
+
+        // ---- masks (edge tiles only) and row maximum of tile t+1
+        if (edge(j1))
+            mask_scores(n0, n1, j1, len, window, qi, g);
+        mx = row_max(n0, n1);
         __syncthreads();
+    };
+
+    int t = 0, cur = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(sa0, sa1, sb0, sb1, ra, t, cur);
+        cur = cur == RING - 1 ? 0 : cur + 1;
+        step(sb0, sb1, sa0, sa1, rb, t + 1, cur);
+        cur = cur == RING - 1 ? 0 : cur + 1;
     }
+    if (t < ntiles)
+        step(sa0, sa1, sb0, sb1, ra, t, cur);
 
     // ---- epilogue: out = O / l, lse = m + ln l, for rows inside the sequence
     const float l_tot = pair_sum(l_run);
@@ -330,7 +523,7 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
             *(u32x2 *)(orow + 32 + 8 * q + 4 * g) = wb;
         }
         if (g == 0)
-            lse[(int64_t)h * T + start + qi] = m_run + logf(l_tot);
+            lse[(int64_t)h * T + start + qi] = m_ref + logf(l_tot);
     }
 }
 
@@ -356,12 +549,20 @@ int launch_typed(const AttendArgs &a) {
     return VLF_OK;
 }
 
+template <class E>
+int launch_br(const AttendArgs &a) {
+    switch (a.br) {  // the host side admits 64, 128 and 256 only
+    case 64: return launch_typed<E, 2>(a);
+    case 128: return launch_typed<E, 4>(a);
+    case 256: return launch_typed<E, 8>(a);
+    default: return fail(VLF_EUNSUPPORTED, "br = %d", a.br);
+    }
+}
+
 }  // namespace
 
 int launch_attend(const AttendArgs &a) {
-    if (a.dtype == VLF_BF16)
-        return a.br == 128 ? launch_typed<BF16, 4>(a) : launch_typed<BF16, 2>(a);
-    return a.br == 128 ? launch_typed<F16, 4>(a) : launch_typed<F16, 2>(a);
+    return a.dtype == VLF_BF16 ? launch_br<BF16>(a) : launch_br<F16>(a);
 }
 
 }  // namespace vlf

@@ -49,7 +49,7 @@ static int check_cu(const int32_t *cu, int32_t S, int32_t T, int32_t *max_len) {
     return VLF_OK;
 }
 
-static bool supported_br(int32_t br) { return br == 64 || br == 128; }
+static bool supported_br(int32_t br) { return br == 64 || br == 128 || br == 256; }
 
 }  // namespace vlf
 
@@ -135,7 +135,7 @@ int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_
     if (dtype != VLF_BF16 && dtype != VLF_F16)
         return fail(VLF_EUNSUPPORTED, "dtype = %d; supported: VLF_F16 (0), VLF_BF16 (1)", dtype);
     if (!supported_br(br))
-        return fail(VLF_EUNSUPPORTED, "br = %d; supported: 64, 128", br);
+        return fail(VLF_EUNSUPPORTED, "br = %d; supported: 64, 128, 256", br);
     if (H < 1 || H > 65536)
         return fail(VLF_EINVAL, "H = %d outside 1 .. 65536", H);
     if (window < 0)
