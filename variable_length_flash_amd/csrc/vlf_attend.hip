@@ -189,32 +189,65 @@ struct TileRegs {
     u32x2 va[Staging<NTHR>::VC], vb[Staging<NTHR>::VC];
 };
 
-template <int NTHR>
-__device__ __forceinline__ void stage_load(TileRegs<NTHR> &r, const Staging<NTHR> &sg, int j0,
-                                           int len, int P, const uint16_t *kbase,
-                                           const uint16_t *vbase, const uint16_t *cos_t,
-                                           const uint16_t *sin_t, int64_t ld) {
+// Where a workgroup's key/value rows and table rows come from. With FIXED, one descriptor per
+// source covers the whole sequence (32-bit offsets reach every row) and a tile's row offset is
+// added to the per-thread offsets; otherwise the descriptors are rebased on every tile.
+template <bool FIXED>
+struct Sources {
+    const uint16_t *kbase, *vbase, *cos_t, *sin_t;
+    int len, P;
+    int64_t ld;
+    int row_bytes;
+    __amdgpu_buffer_rsrc_t kr, vr, cr, sr;  // FIXED only
+
+    __device__ void init(const uint16_t *k, const uint16_t *v, const uint16_t *c,
+                         const uint16_t *sn, int len_, int P_, int64_t ld_) {
+        kbase = k, vbase = v, cos_t = c, sin_t = sn, len = len_, P = P_, ld = ld_;
+        row_bytes = (int)(ld * 2);
+        if (FIXED) {
+            kr = rsrc(kbase, (int64_t)len * row_bytes);
+            vr = rsrc(vbase, (int64_t)len * row_bytes);
+            cr = rsrc(cos_t, (int64_t)P * 64);
+            sr = rsrc(sin_t, (int64_t)P * 64);
+        }
+    }
+};
+
+template <int NTHR, bool FIXED>
+__device__ __forceinline__ void stage_load(TileRegs<NTHR> &r, const Staging<NTHR> &sg,
+                                           const Sources<FIXED> &src, int j0) {
     using S = Staging<NTHR>;
-    const int64_t row_bytes = ld * 2;
-    const __amdgpu_buffer_rsrc_t kr = rsrc(kbase + (int64_t)j0 * ld, (int64_t)(len - j0) * row_bytes);
-    const __amdgpu_buffer_rsrc_t vr = rsrc(vbase + (int64_t)j0 * ld, (int64_t)(len - j0) * row_bytes);
-    const __amdgpu_buffer_rsrc_t cr = rsrc(cos_t + (int64_t)j0 * 32, (int64_t)(P - j0) * 64);
-    const __amdgpu_buffer_rsrc_t sr = rsrc(sin_t + (int64_t)j0 * 32, (int64_t)(P - j0) * 64);
+    __amdgpu_buffer_rsrc_t kr, vr, cr, sr;
+    int kdelta, tdelta;
+    if (FIXED) {
+        kr = src.kr, vr = src.vr, cr = src.cr, sr = src.sr;
+        kdelta = j0 * src.row_bytes;
+        tdelta = j0 * 64;
+    } else {
+        kr = rsrc(src.kbase + (int64_t)j0 * src.ld, (int64_t)(src.len - j0) * src.row_bytes);
+        vr = rsrc(src.vbase + (int64_t)j0 * src.ld, (int64_t)(src.len - j0) * src.row_bytes);
+        cr = rsrc(src.cos_t + (int64_t)j0 * 32, (int64_t)(src.P - j0) * 64);
+        sr = rsrc(src.sin_t + (int64_t)j0 * 32, (int64_t)(src.P - j0) * 64);
+        kdelta = 0;
+        tdelta = 0;
+    }
+    const int koff = sg.koff + kdelta, toff = sg.toff + tdelta;
 #pragma unroll
     for (int w = 0; w < S::KW; w += 2) {
-        const u32x2 a = load8(kr, sg.koff + 4 * w);
-        const u32x2 b = load8(kr, sg.koff + 64 + 4 * w);
-        const u32x2 cc = load8(cr, sg.toff + 4 * w);
-        const u32x2 ss = load8(sr, sg.toff + 4 * w);
+        const u32x2 a = load8(kr, koff + 4 * w);
+        const u32x2 b = load8(kr, koff + 64 + 4 * w);
+        const u32x2 cc = load8(cr, toff + 4 * w);
+        const u32x2 ss = load8(sr, toff + 4 * w);
         r.x1[w] = a[0], r.x1[w + 1] = a[1];
         r.x2[w] = b[0], r.x2[w + 1] = b[1];
         r.c[w] = cc[0], r.c[w + 1] = cc[1];
         r.s[w] = ss[0], r.s[w + 1] = ss[1];
     }
+    const int va = sg.voff + kdelta, vb = sg.voff + src.row_bytes + kdelta;
 #pragma unroll
     for (int q = 0; q < S::VC; ++q) {
-        r.va[q] = load8(vr, sg.voff + sg.vchunk[q] * 8);
-        r.vb[q] = load8(vr, sg.voff + (int)row_bytes + sg.vchunk[q] * 8);
+        r.va[q] = load8(vr, va + sg.vchunk[q] * 8);
+        r.vb[q] = load8(vr, vb + sg.vchunk[q] * 8);
     }
 }
 
@@ -323,7 +356,7 @@ __device__ __forceinline__ float row_max(const f32x16 &s0, const f32x16 &s1) {
     return pair_max(mx);
 }
 
-template <class E, int NW>
+template <class E, int NW, bool FIXED>
 __global__ void __launch_bounds__(NW * 64)
 attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
@@ -393,15 +426,17 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     // ---- prologue: tiles 0 and 1 staged in LDS, tiles 2 and 3 in flight to registers
     Staging<NTHR> sg;
     sg.init(tid, ld);
+    Sources<FIXED> src;
+    src.init(kbase, vbase, cos_t, sin_t, len, P, ld);
     TileRegs<NTHR> ra, rb;
-    stage_load<NTHR>(ra, sg, key(0), len, P, kbase, vbase, cos_t, sin_t, ld);
-    stage_load<NTHR>(rb, sg, key(1), len, P, kbase, vbase, cos_t, sin_t, ld);
+    stage_load(ra, sg, src, key(0));
+    stage_load(rb, sg, src, key(1));
     u32x4 qop[4];
     query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
     stage_store<E, NTHR>(ra, sg, ks[0], vt[0]);
-    stage_load<NTHR>(ra, sg, key(2), len, P, kbase, vbase, cos_t, sin_t, ld);
+    stage_load(ra, sg, src, key(2));
     stage_store<E, NTHR>(rb, sg, ks[1], vt[1]);
-    stage_load<NTHR>(rb, sg, key(3), len, P, kbase, vbase, cos_t, sin_t, ld);
+    stage_load(rb, sg, src, key(3));
     __syncthreads();
 
     // A tile needs masks when it reaches past the sequence or some pair of this wave's rows
@@ -489,7 +524,7 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
             rs += c0[i] + c1[i];
         l_run += rs;
         stage_store<E, NTHR>(st, sg, ks[fut], vt[fut]);
-        stage_load<NTHR>(st, sg, key(t + 4), len, P, kbase, vbase, cos_t, sin_t, ld);
+        stage_load(st, sg, src, key(t + 4));
 
         // ---- masks (edge tiles only) and row maximum of tile t+1
         if (edge(j1))
@@ -527,7 +562,7 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     }
 }
 
-template <class E, int NW>
+template <class E, int NW, bool FIXED>
 int launch_typed(const AttendArgs &a) {
     const int64_t blocks = (int64_t)a.num_tiles * a.H;
     if (blocks > INT32_MAX)
@@ -542,19 +577,19 @@ int launch_typed(const AttendArgs &a) {
                     (void *)&a.tiles, (void *)&out,   (void *)&a.lse, (void *)&num_tiles,
                     (void *)&T,   (void *)&S,         (void *)&H,  (void *)&P,
                     (void *)&W,   (void *)&scale};
-    hipError_t e = hipLaunchKernel((const void *)attend_fwd<E, NW>, dim3((unsigned)blocks),
+    hipError_t e = hipLaunchKernel((const void *)attend_fwd<E, NW, FIXED>, dim3((unsigned)blocks),
                                    dim3(NW * 64), args, 0, (hipStream_t)a.stream);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "attend launch failed: %s", hipGetErrorString(e));
     return VLF_OK;
 }
 
-template <class E>
+template <class E, bool FIXED>
 int launch_br(const AttendArgs &a) {
     switch (a.br) {  // the host side admits 64, 128 and 256 only
-    case 64: return launch_typed<E, 2>(a);
-    case 128: return launch_typed<E, 4>(a);
-    case 256: return launch_typed<E, 8>(a);
+    case 64: return launch_typed<E, 2, FIXED>(a);
+    case 128: return launch_typed<E, 4, FIXED>(a);
+    case 256: return launch_typed<E, 8, FIXED>(a);
     default: return fail(VLF_EUNSUPPORTED, "br = %d", a.br);
     }
 }
@@ -562,7 +597,13 @@ int launch_br(const AttendArgs &a) {
 }  // namespace
 
 int launch_attend(const AttendArgs &a) {
-    return a.dtype == VLF_BF16 ? launch_br<BF16>(a) : launch_br<F16>(a);
+    // Whole-sequence descriptors need every row of the longest sequence (at most min(P, T)
+    // rows) plus a tile past it to be reachable with a 31-bit byte offset.
+    const int64_t rows = (int64_t)(a.table_rows < a.T ? a.table_rows : a.T) + 2 * BC;
+    const bool fixed = rows * 3 * a.H * D * 2 < ((int64_t)1 << 31);
+    if (a.dtype == VLF_BF16)
+        return fixed ? launch_br<BF16, true>(a) : launch_br<BF16, false>(a);
+    return fixed ? launch_br<F16, true>(a) : launch_br<F16, false>(a);
 }
 
 }  // namespace vlf
