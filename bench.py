@@ -2,18 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
 
-A step is one pass of the whole forward (one launch of the gfx950 kernel through the C ABI)
-over one packed batch that is already resident in HBM. The default workload is sixteen
-8192-token sequences, 16 heads, bf16, full window. It prints one JSON line:
+A step is one pass of the whole forward through the C ABI over one packed batch that is
+already resident in HBM: for batches that pre-rotate keys (the default for long sequences) the
+key-tile kernel (vlf_rotate_keys) and then the forward over the tiles (vlf_attend_rotated),
+otherwise the one forward kernel (vlf_attend without a workspace). The default workload is
+sixteen 8192-token sequences, 16 heads, bf16, full window. It prints one JSON line:
 
 * value: effective attention TFLOP/s, counting 4 * 64 FLOPs per visible (query, key) pair per
   head, over the wall-clock of exactly K steps (synchronised on both sides);
-* roofline: the same algorithmic FLOPs over the kernel's average duration from HIP events on
-  the launch stream, against MI355X's dense bf16/fp16 matrix peak (2516.6 TFLOP/s =
-  256 CUs x 2.4 GHz x 4096 FLOP/clock); traffic: HBM bytes per launch from rocprofv3 counters
-  (FETCH_SIZE + WRITE_SIZE, each scaled by the reading of a plain copy of known size),
-  recorded in profiles/ with the hash of the kernel source they were taken on (null when the
-  source has changed since);
+* roofline: for the dominant kernel (the forward), the same algorithmic FLOPs over that
+  kernel's average duration from HIP events recorded around it on its launch stream, against
+  MI355X's dense bf16/fp16 matrix peak (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clock);
+  traffic: HBM bytes per launch from rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled
+  by the reading of a plain copy of known size), recorded in profiles/ with the hash of the
+  kernel source they were taken on (null when the source has changed since);
 * cpu_baseline: the float64 oracle (test infrastructure) on the host cores over a bounded
   sample of rows of the same workload, in the same unit.
 
@@ -40,7 +42,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0         # HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flash_amd", "csrc", "vlf_attend.hip")
-KERNEL_NAME = "attend_fwd"
+KERNELS = {"direct": "attend_fwd", "prerotate": "attend_pre", "rotate": "prep_tiles"}
 COPY_BYTES = 1 << 30
 
 
@@ -49,14 +51,14 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"attend_fwd_{workload}_traffic.txt")
+def traffic_file(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
 
 
-def read_traffic(workload: str):
+def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None if absent or taken on
     a different kernel source."""
-    path = traffic_file(workload)
+    path = traffic_file(kernel, workload)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -146,34 +148,51 @@ def run(args):
         sys.exit(2)
     dev = torch.device("cuda:0")
     w, qkv, cos, sin = make_inputs(args.workload)
-    batch = vlf.prepare(w.cu, dev, args.br)
+    prerotate = None if args.path == "auto" else args.path == "prerotate"
+    batch = vlf.prepare(w.cu, dev, args.br, prerotate, w.window)
+    path = "prerotate" if batch.prerotate else "direct"
+    kernel = KERNELS[path]
     q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
     out = torch.empty((w.tokens, w.heads * 64), dtype=q.dtype, device=dev)
     lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
+    ws = vlf.new_workspace(batch, w.heads, dev)
     pairs = vlf.visible_pairs(w.cu, w.window)
     flops = 4 * 64 * pairs * w.heads
     alg_bytes = (3 * w.tokens * w.heads * 64 * 2      # qkv read once
                  + w.tokens * w.heads * 64 * 2        # out written once
                  + 4 * w.heads * w.tokens)            # lse written once
+    stream = torch.cuda.current_stream(dev)
 
-    def step():
-        vlf.attend_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse)
+    def step(ev=None):
+        # ev: three events recorded before, between and after the step's kernels
+        if ev is not None:
+            ev[0].record(stream)
+        if batch.prerotate:
+            vlf.rotate_keys(batch, q, c, s, w.heads, ws)
+            if ev is not None:
+                ev[1].record(stream)
+            vlf.attend_rotated_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse, ws)
+        else:
+            if ev is not None:
+                ev[1].record(stream)
+            vlf.attend_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse)
+        if ev is not None:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
+    for k in range(args.steps):
+        step(events[k])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    kernel_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    rotate_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
 
     if args.profile_run:
         # a plain copy of known size on the same stream: the counter runs scale by it
@@ -184,7 +203,11 @@ def run(args):
 
     value = flops / (wall_ms / 1e3) / 1e12
     achieved = flops / (kernel_ms / 1e3) / 1e12
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(kernel, args.workload)
+    # the key-tile kernel reads every key and value row once and writes each used block once
+    key_tiles = sum(-(-int(L) // 64) for L in w.lens)
+    rotate_bytes = (2 * w.tokens * w.heads * 64 * 2 + 2 * sum(w.lens) * 32 * 2
+                    + key_tiles * w.heads * 16384)
     line = {
         "metric": "effective attention TFLOP/s (visible pairs) + % of bf16 MFMA peak, 1 GPU",
         "value": round(value, 2),
@@ -202,11 +225,18 @@ def run(args):
             "workload": f"{args.workload}: {w.note}",
             "tokens": w.tokens, "sequences": w.sequences, "heads": w.heads, "head_dim": 64,
             "window": w.window, "rope_base": w.base, "scale": w.scale, "br": batch.br,
+            "path": path,
+            "kernel_ms": {kernel: round(kernel_ms, 4),
+                          **({KERNELS["rotate"]: round(rotate_ms, 4)} if batch.prerotate
+                             else {})},
+            **({"rotate_hbm_gbs_algorithmic": round(rotate_bytes / (rotate_ms / 1e3) / 1e9, 1)}
+               if batch.prerotate else {}),
             "visible_pairs_per_head": pairs, "effective_flop": flops,
             "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "achieved_hbm_gbs_algorithmic": round(alg_bytes / (kernel_ms / 1e3) / 1e9, 1),
         },
         "roofline": {
+            "kernel": kernel,
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -223,7 +253,7 @@ def run(args):
     print(json.dumps(line), flush=True)
 
 
-def summarize(directories, workload: str):
+def summarize(directories, workload: str, kernel: str):
     """Traffic per launch from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each
     scaled by the same counter's reading for the 1 GiB copy of the profile run."""
     rows = []
@@ -237,8 +267,8 @@ def summarize(directories, workload: str):
     per = {}  # (counter, kind) -> list of per-dispatch values (KiB)
     for r in rows:
         name = r.get("Kernel_Name", "")
-        kind = "attend" if KERNEL_NAME in name else ("copy" if "copybuffer" in name.lower()
-                                                     else None)
+        kind = "attend" if kernel in name else ("copy" if "copybuffer" in name.lower()
+                                                else None)
         if kind is None:
             continue
         per.setdefault((r["Counter_Name"], kind, r.get("Dispatch_Id", "")), 0.0)
@@ -255,7 +285,7 @@ def summarize(directories, workload: str):
         res[counter] = (sum(att) / len(att), copy_kib, factor)
     fetch = res["FETCH_SIZE"][0] * 1024 * res["FETCH_SIZE"][2]
     write = res["WRITE_SIZE"][0] * 1024 * res["WRITE_SIZE"][2]
-    print(f"kernel: {KERNEL_NAME}")
+    print(f"kernel: {kernel}")
     print(f"workload: {workload}")
     print(f"kernel_source_sha256_16: {kernel_hash()}")
     for counter, (att, cpy, factor) in res.items():
@@ -276,13 +306,18 @@ def main():
                     choices=["tiny", "encoder", "sliding", "many_short", "long"])
     ap.add_argument("--br", type=int, default=None, choices=[64, 128, 256],
                     help="query rows per workgroup (default: chosen from the longest sequence)")
+    ap.add_argument("--path", default="auto", choices=["auto", "direct", "prerotate"],
+                    help="direct: every workgroup rotates its key tiles; prerotate: key-tile "
+                         "workspace (default: chosen from the longest sequence)")
+    ap.add_argument("--kernel", default=KERNELS["prerotate"], choices=sorted(KERNELS.values()),
+                    help="kernel whose counters --summarize reads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", nargs="+")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.workload)
+        summarize(args.summarize, args.workload, args.kernel)
         return
     run(args)
 

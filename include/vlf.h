@@ -19,6 +19,10 @@
  *   - Pointers marked "host" are read by the CPU during the call only. Pointers marked
  *     "device" are HIP device memory owned by the caller; the library keeps no reference after
  *     the call returns and allocates no device memory.
+ *   - Two ways to run the forward share every result bit for bit: with a workspace the keys
+ *     are rotated once per call into 64-key tile images that every query tile then streams
+ *     (the faster choice when sequences span several query tiles); without one every
+ *     workgroup rotates the key tiles it reads.
  */
 #ifndef VLF_H
 #define VLF_H
@@ -41,7 +45,7 @@ enum vlf_dtype {
     VLF_BF16 = 1, /* bfloat16 */
 };
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2). */
 int32_t vlf_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). The pointer
@@ -83,6 +87,17 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
                       uint64_t *pairs);
 
 /*
+ * Device workspace vlf_attend needs to pre-rotate keys for T tokens in S sequences and H heads:
+ * H * (floor(T / 64) + S) blocks of 16384 bytes. Key tile u (keys 64u .. 64u+63) of sequence s
+ * and head h occupies block h * (floor(T / 64) + S) + floor(cu[s] / 64) + s + u; these indices
+ * never collide for a valid cu. A block holds two 8192-byte images: the rotated, rounded keys
+ * [key][dim] and the values transposed [dim][key], 64 rows of 128 bytes each.
+ *   bytes  out: the size (0 when T, S or H is 0).
+ * Errors: VLF_EINVAL (negative size, H > 65536, null bytes).
+ */
+int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
+
+/*
  * The forward pass (hanzo-kernel 0.2.42 src/packed.rs, `attend`): for each tile in tiles_dev
  * and each head h, query rows i0 .. i0+br-1 of sequence s against the keys of s the window
  * reaches.
@@ -110,6 +125,13 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
  *   window     0 or W >= 1 as above.
  *   scale      multiplies the rotated query before rounding (1/8 for head dimension 64).
  *   dtype      VLF_BF16 or VLF_F16: storage type of qkv, cos, sin and out.
+ *   workspace  device or NULL. With workspace_bytes >= vlf_workspace_bytes(T, S, H), the call
+ *              first rotates every key tile once into it (vlf_rotate_keys, then
+ *              vlf_attend_rotated: two kernels on `stream`); its
+ *              previous contents are ignored and overwritten, so calls that may overlap in
+ *              time need separate workspaces. NULL (and workspace_bytes 0): no workspace is
+ *              used.
+ *   workspace_bytes  size of `workspace` in bytes.
  *   out        device, [T, H*64] elements of `dtype`. Every row of every tiled sequence is
  *              written; nothing else is.
  *   lse        device, [H, T] float32, written for the same rows.
@@ -117,14 +139,41 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
  *              it never synchronises, never allocates, and returns once the launch is queued.
  *
  * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, negative sizes, T or
- * S inconsistent with each other, num_tiles < 0), VLF_EUNSUPPORTED (dtype, br),
+ * S inconsistent with each other, num_tiles < 0, a workspace smaller than vlf_workspace_bytes or
+ * a size without a pointer), VLF_EUNSUPPORTED (dtype, br),
  * VLF_EHIP (launch failure, from hipGetLastError). Device-side contents (cu_dev, tiles_dev)
  * cannot be checked here; the kernel skips tiles that would read out of range.
  */
 int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
                const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles, int32_t br,
                int32_t T, int32_t S, int32_t H, int32_t window, float scale, int32_t dtype,
-               void *out, float *lse, void *stream);
+               void *workspace, int64_t workspace_bytes, void *out, float *lse, void *stream);
+
+/*
+ * The first half of vlf_attend with a workspace: rotate every key tile of cu once and write it,
+ * with its values, into `workspace` (the blocks vlf_workspace_bytes describes; the rotation and
+ * rounding of k~ in vlf_attend's formula). Arguments as in vlf_attend. One kernel on `stream`;
+ * asynchronous; allocates nothing.
+ * Errors: VLF_EINVAL (null pointer with work to do, H out of range, negative sizes, T or S
+ * inconsistent, workspace missing or smaller than vlf_workspace_bytes), VLF_EUNSUPPORTED
+ * (dtype), VLF_EHIP (launch failure).
+ */
+int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                    const int32_t *cu_dev, int32_t T, int32_t S, int32_t H, int32_t dtype,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * The second half of vlf_attend with a workspace: the forward over key tiles a previous
+ * vlf_rotate_keys wrote into `workspace` for the same qkv, cos, sin, cu and H (queued earlier on
+ * the same stream, or otherwise complete). Arguments and results as in vlf_attend; `workspace`
+ * is read, not written, and may be shared by calls that overlap in time. One kernel on `stream`.
+ * Errors: as vlf_attend; the workspace is required.
+ */
+int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                       const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
+                       int32_t br, int32_t T, int32_t S, int32_t H, int32_t window, float scale,
+                       int32_t dtype, const void *workspace, int64_t workspace_bytes, void *out,
+                       float *lse, void *stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     lib = vlf.load_library()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.vlf_version() == 1
+    assert lib.vlf_version() == 2
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -118,13 +118,13 @@ def _attend_status(**kw):
     rejected on the host before any launch."""
     args = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=64, cu=0x4000, tiles=0x5000, nt=4,
                 br=64, T=100, S=2, H=2, window=0, scale=0.125, dtype=binding.VLF_BF16,
-                out=0x6000, lse=0x7000, stream=None)
+                ws=None, ws_bytes=0, out=0x6000, lse=0x7000, stream=None)
     args.update(kw)
     lib = vlf.load_library()
     rc = lib.vlf_attend(args["qkv"], args["cos"], args["sin"], args["P"], args["cu"],
                         args["tiles"], args["nt"], args["br"], args["T"], args["S"], args["H"],
-                        args["window"], args["scale"], args["dtype"], args["out"], args["lse"],
-                        args["stream"])
+                        args["window"], args["scale"], args["dtype"], args["ws"],
+                        args["ws_bytes"], args["out"], args["lse"], args["stream"])
     return rc, lib.vlf_last_error().decode()
 
 
@@ -143,6 +143,11 @@ def _attend_status(**kw):
     (dict(P=0), binding.VLF_EINVAL, "rotary"),
     (dict(scale=float("nan")), binding.VLF_EINVAL, "scale"),
     (dict(scale=float("inf")), binding.VLF_EINVAL, "scale"),
+    # T=100, S=2, H=2 need 2 * (1 + 2) blocks of 16 KiB
+    (dict(ws=0x8000, ws_bytes=6 * 16384 - 1), binding.VLF_EINVAL, "workspace of"),
+    (dict(ws=0x8000, ws_bytes=0), binding.VLF_EINVAL, "workspace of"),
+    (dict(ws=None, ws_bytes=4096), binding.VLF_EINVAL, "without a workspace"),
+    (dict(ws=0x8000, ws_bytes=-1), binding.VLF_EINVAL, "workspace_bytes"),
 ])
 def test_attend_rejects_bad_arguments(kw, status, msg):
     rc, text = _attend_status(**kw)
@@ -154,3 +159,70 @@ def test_attend_with_no_work_is_a_no_op():
     # no tiles or no tokens: returns OK without touching the (fake) pointers or the device
     assert _attend_status(nt=0)[0] == binding.VLF_OK
     assert _attend_status(T=0, S=0, nt=0, qkv=None, out=None)[0] == binding.VLF_OK
+
+
+@pytest.mark.parametrize("T,S,H", [(0, 0, 1), (1, 1, 1), (63, 1, 1), (64, 1, 1), (100, 2, 2),
+                                   (131072, 16, 16), (33000, 1024, 16), (5, 5, 65536)])
+def test_workspace_bytes(T, S, H):
+    # H * (floor(T / 64) + S) blocks of 16 KiB; nothing when there is no token
+    want = 0 if T == 0 else H * (T // 64 + S) * 16384
+    assert vlf.workspace_bytes(T, S, H) == want
+
+
+@pytest.mark.parametrize("lens", [[1], [64], [65], [5, 40, 1, 33, 70], [0, 64, 0, 128, 1],
+                                  [63, 1, 63, 1, 200], [8192] * 3])
+def test_workspace_blocks_are_disjoint_and_inside(lens):
+    """The block of key tile u of sequence s is floor(cu[s] / 64) + s + u: distinct for all
+    (s, u) and below floor(T / 64) + S (so inside vlf_workspace_bytes)."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, S = int(cu[-1]), len(lens)
+    blocks = [int(cu[s]) // 64 + s + u for s in range(S) for u in range(-(-lens[s] // 64))]
+    assert len(set(blocks)) == len(blocks)
+    assert all(0 <= b < T // 64 + S for b in blocks)
+    assert vlf.workspace_bytes(T, S, 1) >= (max(blocks) + 1) * 16384
+
+
+@pytest.mark.parametrize("T,S,H,msg", [(-1, 1, 1, "negative"), (1, 1, 70000, "above")])
+def test_workspace_bytes_rejects(T, S, H, msg):
+    lib = vlf.load_library()
+    out = ctypes.c_int64()
+    assert lib.vlf_workspace_bytes(T, S, H, ctypes.byref(out)) == binding.VLF_EINVAL
+    assert msg in lib.vlf_last_error().decode()
+
+
+def _rotate_status(**kw):
+    args = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=64, cu=0x4000, T=100, S=2, H=2,
+                dtype=binding.VLF_BF16, ws=0x8000, ws_bytes=6 * 16384, stream=None)
+    args.update(kw)
+    lib = vlf.load_library()
+    rc = lib.vlf_rotate_keys(args["qkv"], args["cos"], args["sin"], args["P"], args["cu"],
+                             args["T"], args["S"], args["H"], args["dtype"], args["ws"],
+                             args["ws_bytes"], args["stream"])
+    return rc, lib.vlf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=3), binding.VLF_EUNSUPPORTED, "dtype"),
+    (dict(H=0), binding.VLF_EINVAL, "H ="),
+    (dict(T=-1), binding.VLF_EINVAL, "negative"),
+    (dict(S=0), binding.VLF_EINVAL, "no sequence"),
+    (dict(ws=None, ws_bytes=0), binding.VLF_EINVAL, "needs a workspace"),
+    (dict(ws_bytes=6 * 16384 - 16), binding.VLF_EINVAL, "workspace of"),
+    (dict(cu=None), binding.VLF_EINVAL, "null"),
+    (dict(P=0), binding.VLF_EINVAL, "rotary"),
+])
+def test_rotate_keys_rejects_bad_arguments(kw, status, msg):
+    rc, text = _rotate_status(**kw)
+    assert rc == status
+    assert msg in text
+
+
+def test_rotate_keys_with_no_tokens_is_a_no_op():
+    assert _rotate_status(T=0, S=0, qkv=None, ws=None, ws_bytes=0)[0] == binding.VLF_OK
+
+
+def test_attend_rotated_needs_a_workspace():
+    lib = vlf.load_library()
+    rc = lib.vlf_attend_rotated(0x1000, 0x2000, 0x3000, 64, 0x4000, 0x5000, 4, 64, 100, 2, 2, 0,
+                                0.125, binding.VLF_BF16, None, 0, 0x6000, 0x7000, None)
+    assert rc == binding.VLF_EINVAL and "needs a workspace" in lib.vlf_last_error().decode()

@@ -33,18 +33,19 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, qkv, cos, sin, br=None, window=None):
-    """The HIP path on cuda:0 with NaN-filled outputs and guard regions; returns numpy arrays."""
+def run_gpu(w, qkv, cos, sin, br=None, window=None, prerotate=None, workspace=None):
+    """The HIP path on cuda:0 with NaN-filled outputs and guard regions; returns numpy arrays.
+    ``prerotate`` picks the path (None: the binding's default for the batch)."""
     window = w.window if window is None else window
     dev = torch.device("cuda:0")
-    batch = vlf.prepare(w.cu, dev, br)
+    batch = vlf.prepare(w.cu, dev, br, prerotate, window)
     q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
     T, H = w.tokens, w.heads
     out_buf = torch.full((T * H * 64 + GUARD,), float("nan"), dtype=qkv.dtype, device=dev)
     lse_buf = torch.full((H * T + GUARD,), float("nan"), dtype=torch.float32, device=dev)
     out = out_buf[:T * H * 64].view(T, H * 64)
     lse = lse_buf[:H * T].view(H, T)
-    vlf.attend_into(batch, q, c, s, H, window, w.scale, out, lse)
+    vlf.attend_into(batch, q, c, s, H, window, w.scale, out, lse, workspace=workspace)
     torch.cuda.synchronize()
     assert torch.isnan(out_buf[T * H * 64:]).all(), "out guard region was written"
     assert torch.isnan(lse_buf[H * T:]).all(), "lse guard region was written"
@@ -81,15 +82,20 @@ def compare(name, w, got_out, got_lse, qkv, cos, sin, rows=None, window=None):
 LENS = [5, 40, 1, 33, 70]
 
 
+PATHS = [False, True]  # prerotate: every workgroup rotates its key tiles / key-tile workspace
+
+
+@pytest.mark.parametrize("prerotate", PATHS)
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("br", [64, 128, 256])
 @pytest.mark.parametrize("window", [0, 9, 65])
-def test_page_fixture(dtype, br, window):
+def test_page_fixture(dtype, br, window, prerotate):
     w = workloads.custom(LENS, 2, dtype=dtype, window=window, table_rows=128, seed=7)
     qkv, cos, sin = inputs(w)
-    _say(f"case page-fixture {dtype} br={br} W={window}")
-    out, lse = run_gpu(w, qkv, cos, sin, br=br)
-    compare(f"lens {LENS} {dtype} br={br} W={window}", w, out, lse, qkv, cos, sin)
+    _say(f"case page-fixture {dtype} br={br} W={window} prerotate={prerotate}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=prerotate)
+    compare(f"lens {LENS} {dtype} br={br} W={window} pre={int(prerotate)}", w, out, lse, qkv,
+            cos, sin)
 
 
 def test_tiny_workload():
@@ -110,21 +116,25 @@ def test_ragged_tiles_and_windows(dtype, window):
                          seed=11)
     qkv, cos, sin = inputs(w)
     for br in (64, 128, 256):
-        _say(f"case ragged {dtype} W={window} br={br}")
-        out, lse = run_gpu(w, qkv, cos, sin, br=br)
-        compare(f"ragged {dtype} W={window} br={br}", w, out, lse, qkv, cos, sin)
+        for pre in PATHS:
+            _say(f"case ragged {dtype} W={window} br={br} prerotate={pre}")
+            out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=pre)
+            compare(f"ragged {dtype} W={window} br={br} pre={int(pre)}", w, out, lse, qkv, cos,
+                    sin)
 
 
+@pytest.mark.parametrize("prerotate", PATHS)
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("br", [64, 128, 256])
-def test_single_key_rows_are_exact(dtype, br):
+def test_single_key_rows_are_exact(dtype, br, prerotate):
     """W = 1: each row sees only itself, so out = v (bit-exact) and lse = <q~, k~>, one float32
     dot product of the rounded operands. Agreement with the oracle's float64 dot product of its
     own rounded operands to float32 accumulation error (far below one storage-type ulp of a
     single operand) shows the kernel's rotated, scaled and rounded operands are the oracle's."""
     w = workloads.custom([1, 7, 130, 64, 300], 2, dtype=dtype, window=1, table_rows=512, seed=5)
     qkv, cos, sin = inputs(w)
-    out, lse = run_gpu(w, qkv, cos, sin, br=br)
+    _say(f"case single-key {dtype} br={br} prerotate={prerotate}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=prerotate)
     hd = w.heads * 64
     np.testing.assert_array_equal(out, qkv[:, 2 * hd:].float().numpy())
     _, want = oracle.attend(qkv.float().numpy(), cos.float().numpy(), sin.float().numpy(), w.cu,
@@ -134,14 +144,49 @@ def test_single_key_rows_are_exact(dtype, br):
     assert err < 2e-5
 
 
+@pytest.mark.parametrize("prerotate", PATHS)
 @pytest.mark.parametrize("lens", [[1], [1] * 300, [0, 0, 5, 0], [64] * 9, [128, 1, 128],
                                   [2048], [0, 777, 0, 0, 1500]])
-def test_edge_batches(lens):
+def test_edge_batches(lens, prerotate):
     w = workloads.custom(lens, 2, dtype="fp16", window=0, table_rows=max(lens + [1]), seed=3)
     qkv, cos, sin = inputs(w)
-    _say(f"case edge {lens[:6]}")
-    out, lse = run_gpu(w, qkv, cos, sin)
-    compare(f"edge {lens[:6]}{'...' if len(lens) > 6 else ''}", w, out, lse, qkv, cos, sin)
+    _say(f"case edge {lens[:6]} prerotate={prerotate}")
+    out, lse = run_gpu(w, qkv, cos, sin, prerotate=prerotate)
+    compare(f"edge {lens[:6]}{'...' if len(lens) > 6 else ''} pre={int(prerotate)}", w, out,
+            lse, qkv, cos, sin)
+
+
+@pytest.mark.parametrize("name,br,window", [("ragged", 64, 0), ("ragged", 128, 33),
+                                            ("ragged", 256, 200), ("encoder", 128, 0),
+                                            ("sliding", 256, 128), ("long", 256, 0)])
+def test_paths_agree_bit_for_bit(name, br, window):
+    """Both paths stage the same rounded operands and run the same arithmetic in the same
+    order; only where the rotated keys come from differs, so every output bit must agree."""
+    if name == "ragged":
+        w = workloads.custom(RAGGED, 3, dtype="bf16", window=window, table_rows=512, seed=13)
+    else:
+        w = workloads.WORKLOADS[name]()
+    qkv, cos, sin = inputs(w)
+    _say(f"case paths agree {name} br={br} W={window}")
+    a_out, a_lse = run_gpu(w, qkv, cos, sin, br=br, window=window, prerotate=False)
+    b_out, b_lse = run_gpu(w, qkv, cos, sin, br=br, window=window, prerotate=True)
+    np.testing.assert_array_equal(a_out, b_out)
+    np.testing.assert_array_equal(a_lse, b_lse)
+
+
+def test_workspace_is_rewritten_on_every_call():
+    """A reused workspace (filled with NaN bit patterns, then reused by a smaller batch) gives
+    the same result as a fresh one: every block a tile reads is written in the same call."""
+    dev = torch.device("cuda:0")
+    big = workloads.custom([700, 1300, 64], 2, dtype="bf16", window=0, table_rows=2048, seed=21)
+    small = workloads.custom([300, 65, 1], 2, dtype="bf16", window=0, table_rows=2048, seed=22)
+    ws = torch.full((vlf.workspace_bytes(big.tokens, big.sequences, big.heads),), 0xFF,
+                    dtype=torch.uint8, device=dev)
+    for w in (big, small):
+        qkv, cos, sin = inputs(w)
+        _say(f"case workspace reuse T={w.tokens}")
+        out, lse = run_gpu(w, qkv, cos, sin, prerotate=True, workspace=ws)
+        compare(f"workspace reuse T={w.tokens}", w, out, lse, qkv, cos, sin)
 
 
 def test_empty_batch_launches_nothing():

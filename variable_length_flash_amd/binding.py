@@ -21,7 +21,8 @@ HEAD_DIM = 64
 
 # every function include/vlf.h declares
 EXPORTS = ("vlf_version", "vlf_last_error", "vlf_tile_count", "vlf_tile_table",
-           "vlf_visible_pairs", "vlf_attend")
+           "vlf_visible_pairs", "vlf_workspace_bytes", "vlf_attend", "vlf_rotate_keys",
+           "vlf_attend_rotated")
 
 
 class VlfError(RuntimeError):
@@ -57,9 +58,15 @@ def load_library():
     lib.vlf_tile_table.restype = ctypes.c_int
     lib.vlf_visible_pairs.argtypes = [p, i32, i32, i32, p]
     lib.vlf_visible_pairs.restype = ctypes.c_int
+    lib.vlf_workspace_bytes.argtypes = [i32, i32, i32, p]
+    lib.vlf_workspace_bytes.restype = ctypes.c_int
     lib.vlf_attend.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32,
-                               ctypes.c_float, i32, p, p, p]
+                               ctypes.c_float, i32, p, i64, p, p, p]
     lib.vlf_attend.restype = ctypes.c_int
+    lib.vlf_attend_rotated.argtypes = lib.vlf_attend.argtypes
+    lib.vlf_attend_rotated.restype = ctypes.c_int
+    lib.vlf_rotate_keys.argtypes = [p, p, p, i32, p, i32, i32, i32, i32, p, i64, p]
+    lib.vlf_rotate_keys.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -116,6 +123,24 @@ def visible_pairs(cu, window: int) -> int:
     return int(out.value)
 
 
+def workspace_bytes(tokens: int, sequences: int, heads: int) -> int:
+    """Bytes of the key-tile workspace (include/vlf.h, vlf_workspace_bytes)."""
+    out = ctypes.c_int64()
+    _check(load_library().vlf_workspace_bytes(int(tokens), int(sequences), int(heads),
+                                              ctypes.byref(out)))
+    return int(out.value)
+
+
+def choose_prerotate(max_len: int, br: int, window: int = 0) -> bool:
+    """Rotate keys once into a workspace when one query tile's key span is at least three
+    query tiles long (the longest sequence, or the window's reach br + 2W - 1): each key tile
+    is then read by three or more workgroups per head, and streaming the pre-rotated images
+    beats rotating them again in every workgroup. Where each key tile is read about once or
+    twice (short sequences, narrow windows) the workspace only adds traffic."""
+    span = max_len if window <= 0 else min(max_len, br + 2 * window - 1)
+    return span >= 3 * br
+
+
 def choose_br(max_len: int) -> int:
     """Query rows per workgroup: 64 when no sequence is longer than 64, 256 from 1024 tokens
     on (each key tile is rotated once per workgroup, so taller tiles rotate less per query),
@@ -134,6 +159,7 @@ class Batch:
     num_tiles: int
     max_len: int
     br: int
+    prerotate: bool = False
 
     @property
     def tokens(self) -> int:
@@ -144,16 +170,35 @@ class Batch:
         return int(self.cu_host.shape[0] - 1)
 
 
-def prepare(cu, device=None, br: int | None = None) -> Batch:
-    """Validate ``cu``, build the tile table on the host and copy both to ``device``."""
+def prepare(cu, device=None, br: int | None = None, prerotate: bool | None = None,
+            window: int = 0) -> Batch:
+    """Validate ``cu``, build the tile table on the host and copy both to ``device``.
+
+    ``br`` (query rows per tile) and ``prerotate`` (use a key-tile workspace) default to
+    ``choose_br`` and ``choose_prerotate`` of the longest sequence and ``window`` (the window
+    the batch will be run with; it only informs that choice)."""
     import torch
     cu_host = _host_cu(cu)
     device = torch.device("cuda") if device is None else torch.device(device)
     _, max_len = tile_count(cu_host, 128)
     br = choose_br(max_len) if br is None else int(br)
+    prerotate = (choose_prerotate(max_len, br, window) if prerotate is None
+                 else bool(prerotate))
     table = tile_table(cu_host, br)
     return Batch(cu_host, torch.from_numpy(cu_host).to(device),
-                 torch.from_numpy(table.view(np.int32)).to(device), table.shape[0], max_len, br)
+                 torch.from_numpy(table.view(np.int32)).to(device), table.shape[0], max_len, br,
+                 prerotate)
+
+
+def new_workspace(batch: Batch, heads: int, device=None):
+    """A uint8 device tensor sized for ``batch`` and ``heads`` (None when the batch does not
+    pre-rotate)."""
+    import torch
+    if not batch.prerotate:
+        return None
+    device = batch.cu.device if device is None else torch.device(device)
+    return torch.empty(workspace_bytes(batch.tokens, batch.sequences, heads),
+                       dtype=torch.uint8, device=device)
 
 
 _DTYPES = {}
@@ -168,19 +213,16 @@ def _dtype_code(t):
     return _DTYPES[t]
 
 
-def attend_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: float, out, lse,
-                stream=None):
-    """Queue the forward on ``stream`` (default: torch's current stream of qkv's device).
-
-    qkv [T, 3*heads*64], cos/sin [P, 32] (same dtype, P >= longest sequence), out [T, heads*64]
-    (same dtype), lse [heads, T] float32; all contiguous on one device.
-    """
+def _check_inputs(batch: Batch, qkv, cos, sin, heads: int, out=None, lse=None):
+    """Shapes, dtypes, contiguity and devices of the call's tensors; returns the dtype code."""
     import torch
     T = batch.tokens
     code = _dtype_code(qkv.dtype)
-    for name, t, shape, dt in (("qkv", qkv, (T, 3 * heads * HEAD_DIM), qkv.dtype),
-                               ("out", out, (T, heads * HEAD_DIM), qkv.dtype),
-                               ("lse", lse, (heads, T), torch.float32)):
+    checks = [("qkv", qkv, (T, 3 * heads * HEAD_DIM), qkv.dtype)]
+    if out is not None:
+        checks += [("out", out, (T, heads * HEAD_DIM), qkv.dtype),
+                   ("lse", lse, (heads, T), torch.float32)]
+    for name, t, shape, dt in checks:
         if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
             raise VlfError(VLF_EINVAL, f"{name}: {tuple(t.shape)} {t.dtype} contiguous="
                                        f"{t.is_contiguous()}, expected {shape} {dt}")
@@ -195,23 +237,82 @@ def attend_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: flo
         raise VlfError(VLF_EINVAL, f"rotary tables have {cos.shape[0]} rows; the longest "
                                    f"sequence has {batch.max_len}")
     dev = qkv.device
-    for name, t in (("cos", cos), ("sin", sin), ("out", out), ("lse", lse),
-                    ("cu", batch.cu), ("tiles", batch.tiles)):
+    tensors = [("cos", cos), ("sin", sin), ("cu", batch.cu), ("tiles", batch.tiles)]
+    if out is not None:
+        tensors += [("out", out), ("lse", lse)]
+    for name, t in tensors:
         if t.device != dev:
             raise VlfError(VLF_EINVAL, f"{name} is on {t.device}, qkv on {dev}")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    return code
+
+
+def _workspace_args(workspace, dev):
+    import torch
+    if workspace is None:
+        return None, 0
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or \
+            workspace.device != dev:
+        raise VlfError(VLF_EINVAL, f"workspace: {workspace.dtype} on {workspace.device}, "
+                                   f"expected contiguous uint8 on {dev}")
+    return workspace.data_ptr(), workspace.numel()
+
+
+def _stream(stream, dev):
+    import torch
+    return torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+
+
+def attend_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: float, out, lse,
+                stream=None, workspace=None):
+    """Queue the forward on ``stream`` (default: torch's current stream of qkv's device).
+
+    qkv [T, 3*heads*64], cos/sin [P, 32] (same dtype, P >= longest sequence), out [T, heads*64]
+    (same dtype), lse [heads, T] float32; all contiguous on one device. ``workspace``: a
+    contiguous uint8 device tensor of at least ``workspace_bytes`` (from ``new_workspace``);
+    when None and the batch pre-rotates, one is allocated for this call.
+    """
+    code = _check_inputs(batch, qkv, cos, sin, heads, out, lse)
+    dev = qkv.device
+    if workspace is None and batch.prerotate:
+        workspace = new_workspace(batch, heads, dev)
+    ws_ptr, ws_bytes = _workspace_args(workspace, dev)
     _check(load_library().vlf_attend(
         qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
-        batch.tiles.data_ptr(), batch.num_tiles, batch.br, T, batch.sequences, heads,
-        int(window), float(scale), code, out.data_ptr(), lse.data_ptr(), stream))
+        batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
+        int(window), float(scale), code, ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
+        _stream(stream, dev)))
+
+
+def rotate_keys(batch: Batch, qkv, cos, sin, heads: int, workspace, stream=None):
+    """Queue the rotation of every key tile into ``workspace`` (include/vlf.h,
+    vlf_rotate_keys): the first half of ``attend_into`` with a workspace."""
+    code = _check_inputs(batch, qkv, cos, sin, heads)
+    dev = qkv.device
+    ws_ptr, ws_bytes = _workspace_args(workspace, dev)
+    _check(load_library().vlf_rotate_keys(
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        batch.tokens, batch.sequences, heads, code, ws_ptr, ws_bytes, _stream(stream, dev)))
+
+
+def attend_rotated_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: float,
+                        out, lse, workspace, stream=None):
+    """Queue the forward over a workspace ``rotate_keys`` filled for the same inputs
+    (include/vlf.h, vlf_attend_rotated): the second half of ``attend_into``."""
+    code = _check_inputs(batch, qkv, cos, sin, heads, out, lse)
+    dev = qkv.device
+    ws_ptr, ws_bytes = _workspace_args(workspace, dev)
+    _check(load_library().vlf_attend_rotated(
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
+        int(window), float(scale), code, ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
+        _stream(stream, dev)))
 
 
 def attend(qkv, cos, sin, cu, heads: int, window: int = 0, scale: float = 0.125,
-           br: int | None = None):
+           br: int | None = None, prerotate: bool | None = None):
     """Forward of packed attention; returns (out [T, heads*64], lse [heads, T] float32)."""
     import torch
-    batch = cu if isinstance(cu, Batch) else prepare(cu, qkv.device, br)
+    batch = cu if isinstance(cu, Batch) else prepare(cu, qkv.device, br, prerotate, window)
     T = batch.tokens
     out = torch.empty((T, heads * HEAD_DIM), dtype=qkv.dtype, device=qkv.device)
     lse = torch.empty((heads, T), dtype=torch.float32, device=qkv.device)

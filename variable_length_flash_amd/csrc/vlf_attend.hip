@@ -66,6 +66,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Storage-type helpers: widen the low / high element of a packed pair, round a pair of floats
 // to the storage type (round-to-nearest-even), and the 32x32x16 matrix instruction.
@@ -356,6 +357,91 @@ __device__ __forceinline__ float row_max(const f32x16 &s0, const f32x16 &s1) {
     return pair_max(mx);
 }
 
+// ---- pre-rotated key tiles --------------------------------------------------------------------
+// A workspace block holds key tile u of sequence s for head h as two 8 KB LDS images: the
+// rotated, rounded keys K~ [key][dim] and the values V^T [dim][slot] (slots in the order of
+// vt_slot). Each image has 64 rows of 128 B; 16-byte chunk c of row r is stored at chunk
+// c ^ ((r >> 1) & 7), so the operand reads of 16 consecutive lanes (rows n .. n+15, one chunk
+// each) cover all 16 chunk positions of two 128-byte rows and fall on distinct banks. The block
+// index floor(cu[s] / 64) + s + u keeps the sequences' blocks apart without a prefix sum.
+constexpr int IMG = 8192;     // bytes of one 64 x 64 image
+constexpr int BLK = 2 * IMG;  // bytes of one key tile's block
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// One workgroup per (block, head) writes that block: keys rotated and rounded exactly as the
+// staging of the other path does, values transposed; keys past the sequence are zero.
+template <class E>
+__global__ void __launch_bounds__(256)
+prep_tiles(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+           const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+           uint8_t *__restrict__ ws, int32_t NB, int32_t T, int32_t S, int32_t H, int32_t P) {
+    __shared__ uint16_t vrow[64][72];
+    const int h = (int)(blockIdx.x / (uint32_t)NB);
+    const int b = (int)(blockIdx.x - (uint32_t)h * (uint32_t)NB);
+    // the sequence owning block b: the largest s with floor(cu[s] / 64) + s <= b
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] / 64 + mid <= b)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int s = lo;
+    const int start = cu[s];
+    const int len = cu[s + 1] - start;
+    if (start < 0 || len <= 0 || len > P || (int64_t)start + len > T)
+        return;
+    const int u = b - (start / 64 + s);
+    if (u < 0 || u >= (len + BC - 1) / BC)
+        return;  // a block no tile of this sequence uses (uniform over the workgroup)
+    const int j0 = BC * u;
+    const int nvalid = min(BC, len - j0);
+    const int64_t ld = 3LL * H * D;
+    const int tid = (int)threadIdx.x;
+    uint8_t *blk = ws + ((int64_t)h * NB + b) * BLK;
+
+    // thread (r, q): key row r, pairs m = 8q .. 8q+7 (dims m and m+32), value dims 16q .. 16q+15
+    const int r = tid >> 2, q = tid & 3;
+    u32x4 x1 = {0, 0, 0, 0}, x2 = {0, 0, 0, 0}, c = {0, 0, 0, 0}, sn = {0, 0, 0, 0};
+    u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+    if (r < nvalid) {
+        const uint16_t *krow = qkv + (int64_t)(start + j0 + r) * ld + H * D + h * D;
+        const uint16_t *vrw = krow + H * D;
+        x1 = *(const u32x4 *)(krow + 8 * q);
+        x2 = *(const u32x4 *)(krow + 32 + 8 * q);
+        c = *(const u32x4 *)(cos_t + (j0 + r) * 32 + 8 * q);
+        sn = *(const u32x4 *)(sin_t + (j0 + r) * 32 + 8 * q);
+        va = *(const u32x4 *)(vrw + 16 * q);
+        vb = *(const u32x4 *)(vrw + 16 * q + 8);
+    }
+    uint32_t y1[4], y2[4];
+    {
+        const uint32_t a_[4] = {x1[0], x1[1], x1[2], x1[3]}, b_[4] = {x2[0], x2[1], x2[2], x2[3]};
+        const uint32_t c_[4] = {c[0], c[1], c[2], c[3]}, s_[4] = {sn[0], sn[1], sn[2], sn[3]};
+        rotate<E, 4>(a_, b_, c_, s_, 1.0f, y1, y2);
+    }
+    *(u32x4 *)(blk + r * 128 + 16 * (q ^ swz(r))) = u32x4{y1[0], y1[1], y1[2], y1[3]};
+    *(u32x4 *)(blk + r * 128 + 16 * ((4 + q) ^ swz(r))) = u32x4{y2[0], y2[1], y2[2], y2[3]};
+    *(u32x4 *)&vrow[r][16 * q] = va;
+    *(u32x4 *)&vrow[r][16 * q + 8] = vb;
+    __syncthreads();
+    // V^T: thread (d, q) writes chunks 2q and 2q+1 of row d; chunk ch holds slots 8ch .. 8ch+7
+    const int d = tid >> 2;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int ch = 2 * q + e;
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k0 = vt_slot(8 * ch + 2 * j), k1 = vt_slot(8 * ch + 2 * j + 1);
+            w[j] = (uint32_t)vrow[k0][d] | ((uint32_t)vrow[k1][d] << 16);
+        }
+        *(u32x4 *)(blk + IMG + d * 128 + 16 * (ch ^ swz(d))) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
 template <class E, int NW, bool FIXED>
 __global__ void __launch_bounds__(NW * 64)
 attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
@@ -409,14 +495,11 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     // run side by side on one XCD, do not all miss L2 on the same tile at the same time. The
     // online softmax does not depend on the order of the keys.
     const int offset = window > 0 ? 0 : (int)((int64_t)(i0 / BR) * ntiles / ((len + BR - 1) / BR));
-    // first key of the t-th tile in this workgroup's order (t < ntiles + 4); past the span any
-    // in-span tile will do, as those tiles are staged but never used
+    // first key of the t-th tile in this workgroup's order (t <= ntiles)
     auto key = [&](int t) {
         int u = t + offset;
         if (u >= ntiles)
             u -= ntiles;
-        if (u >= ntiles)
-            u = 0;
         return lo + u * BC;
     };
 
@@ -429,14 +512,19 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     Sources<FIXED> src;
     src.init(kbase, vbase, cos_t, sin_t, len, P, ld);
     TileRegs<NTHR> ra, rb;
+    // (tiles past the span are neither loaded nor staged: a sequence of one key tile costs one)
     stage_load(ra, sg, src, key(0));
-    stage_load(rb, sg, src, key(1));
+    if (ntiles > 1)
+        stage_load(rb, sg, src, key(1));
     u32x4 qop[4];
     query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
     stage_store<E, NTHR>(ra, sg, ks[0], vt[0]);
-    stage_load(ra, sg, src, key(2));
-    stage_store<E, NTHR>(rb, sg, ks[1], vt[1]);
-    stage_load(rb, sg, src, key(3));
+    if (ntiles > 2)
+        stage_load(ra, sg, src, key(2));
+    if (ntiles > 1)
+        stage_store<E, NTHR>(rb, sg, ks[1], vt[1]);
+    if (ntiles > 3)
+        stage_load(rb, sg, src, key(3));
     __syncthreads();
 
     // A tile needs masks when it reaches past the sequence or some pair of this wave's rows
@@ -459,8 +547,8 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     // One key tile t: c0/c1 hold its masked scores and mx their row maximum; n0/n1 receive the
     // scores of tile t+1. LDS ring slots: values of t in `cur`, keys of t+1 in the next slot;
     // tile t+2 (register set `st`) is staged into the slot after, then set `st` receives tile
-    // t+4. Past the span, staging writes a slot no later tile reads, and the loads read zeros
-    // or rows inside the sequence.
+    // t+4. Past the span nothing is loaded or staged; the scores of a tile past the span read
+    // a stale slot and are never used.
     auto step = [&](f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, TileRegs<NTHR> &st, int t,
                     int cur) {
         const int nxt = cur == RING - 1 ? 0 : cur + 1;
@@ -523,8 +611,10 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         for (int i = 0; i < 16; ++i)
             rs += c0[i] + c1[i];
         l_run += rs;
-        stage_store<E, NTHR>(st, sg, ks[fut], vt[fut]);
-        stage_load(st, sg, src, key(t + 4));
+        if (t + 2 < ntiles)
+            stage_store<E, NTHR>(st, sg, ks[fut], vt[fut]);
+        if (t + 4 < ntiles)
+            stage_load(st, sg, src, key(t + 4));
 
         // ---- masks (edge tiles only) and row maximum of tile t+1
         if (edge(j1))
@@ -562,6 +652,286 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     }
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Wait until at most N of this wave's tile copies are in flight and its LDS reads have returned,
+// then the workgroup barrier. The empty asm statements keep the compiler from moving memory
+// accesses across; no release fence is wanted here (one would wait for every copy in flight).
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);  // vmcnt(N) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The forward over pre-rotated key tiles. Same arithmetic, order and outputs as attend_fwd;
+// the key loop streams each 16 KB block straight into a four-slot LDS ring with buffer loads
+// that write LDS (no registers, no ALU work): tile t+3 is requested at the start of step t into
+// the slot tile t-1 left (every wave passed the barrier after its last read), and the end of
+// step t waits for tile t+2, so each copy has two steps to land.
+template <class E, int NW>
+__global__ void __launch_bounds__(NW * 64)
+attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+           const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+           const uint32_t *__restrict__ tiles, const uint8_t *__restrict__ ws,
+           uint16_t *__restrict__ out, float *__restrict__ lse, int32_t num_tiles, int32_t T,
+           int32_t S, int32_t H, int32_t P, int32_t NB, int32_t window, float scale) {
+    constexpr int BR = 32 * NW;
+    constexpr int RING = 4;
+    constexpr int PIECES = 16 / NW;  // 16-byte copies per thread per tile
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[RING * BLK];
+
+    const int nb = (int)gridDim.x;
+    const int b = (int)blockIdx.x;
+    const int xcd = b % XCDS, slot = b / XCDS;
+    const int per = nb / XCDS, extra = nb % XCDS;
+    const int work = xcd * per + min(xcd, extra) + slot;
+    const int h = work / num_tiles;
+    const int tile = work - h * num_tiles;
+
+    const uint32_t seq = tiles[2 * tile];
+    const int i0 = (int)tiles[2 * tile + 1];
+    if (seq >= (uint32_t)S)
+        return;
+    const int start = cu[seq];
+    const int len = cu[seq + 1] - start;
+    if (i0 < 0 || i0 >= len || len > P || start < 0 || (int64_t)start + len > T)
+        return;
+
+    const int64_t ld = 3LL * H * D;
+    const int hd = H * D;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int w0 = i0 + 32 * wv;
+    const int qi = w0 + n;
+
+    int lo = 0, hi = len;
+    if (window > 0) {
+        if (i0 + 1 > window)
+            lo = (i0 + 1 - window) / BC * BC;
+        if ((int64_t)i0 + BR + window - 1 < len)
+            hi = i0 + BR + window - 1;
+    }
+    const int ntiles = (hi - lo + BC - 1) / BC;
+    const int offset = window > 0 ? 0 : (int)((int64_t)(i0 / BR) * ntiles / ((len + BR - 1) / BR));
+    auto key = [&](int t) {
+        int u = t + offset;
+        if (u >= ntiles)
+            u -= ntiles;
+        return lo + u * BC;
+    };
+
+    // copies of tile t (t < ntiles) into ring slot sl: piece j of wave wv covers bytes
+    // 1024 (NW j + wv) .. +1023 of the block, 16 per lane
+    const uint8_t *wblock = ws + ((int64_t)h * NB + start / BC + (int)seq) * BLK;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int voff = 16 * lane;
+    auto copy = [&](int t, int sl) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(wblock + (int64_t)(key(t) / BC) * BLK), 0, BLK, RSRC_WORD3);
+#pragma unroll
+        for (int j = 0; j < PIECES; ++j) {
+            const int off = 1024 * (NW * j + wvu);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void *)((lds_u8 *)ring + sl * BLK + off), 16, voff, off, 0, 0);
+        }
+    };
+
+    u32x4 qop[4];
+    query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
+    asm volatile("" ::: "memory");
+    copy(0, 0);
+    if (ntiles > 1)
+        copy(1, 1);
+    if (ntiles > 2) {
+        copy(2, 2);
+        ring_barrier<PIECES>();
+    } else {
+        ring_barrier<0>();
+    }
+
+    // byte offset of operand chunk 2kc + g of row n (and of row 32 + n, 4096 further on)
+    int cof[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+        cof[kc] = n * 128 + 16 * ((2 * kc + g) ^ swz(n));
+
+    auto edge = [&](int j0) {
+        return (j0 + BC > len) ||
+               (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window));
+    };
+    auto kscores = [&](int sl, f32x16 &s0, f32x16 &s1) {
+        const uint8_t *kt = ring + sl * BLK;
+        u32x4 a[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            a[2 * c] = *(const u32x4 *)(kt + cof[c]);
+            a[2 * c + 1] = *(const u32x4 *)(kt + 4096 + cof[c]);
+        }
+        s0 = f32x16{};
+        s1 = f32x16{};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            s0 = E::mfma(a[2 * c], qop[c], s0);
+            s1 = E::mfma(a[2 * c + 1], qop[c], s1);
+        }
+    };
+
+    float m_ref = -__builtin_inff();
+    float l_run = 0.f;
+    f32x16 o0 = {}, o1 = {};
+    f32x16 sa0, sa1, sb0, sb1;
+
+    kscores(0, sa0, sa1);
+    if (edge(key(0)))
+        mask_scores(sa0, sa1, key(0), len, window, qi, g);
+    float mx = row_max(sa0, sa1);
+
+    // Step t with tile t in slot cur (cur = t % 4, a constant after unrolling): as in
+    // attend_fwd, plus the copy of tile t+3 and the ring wait.
+    auto step = [&](f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, int t, int cur) {
+        const int nxt = (cur + 1) & 3;
+        const bool more = t + 3 < ntiles;
+        if (more)
+            copy(t + 3, (cur + 3) & 3);
+        const int j1 = key(t + 1);
+
+        const bool raise = mx > m_ref + TAU;
+        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * LOG2E) : 1.0f;
+        m_ref = raise ? mx : m_ref;
+        l_run *= alpha;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                o0[i] *= alpha;
+                o1[i] *= alpha;
+            }
+        }
+        const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
+
+        // past the last tile the scores read a slot no copy is headed for; they are not used
+        kscores(nxt, n0, n1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            c0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(c0[i], LOG2E, -mb));
+            c1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(c1[i], LOG2E, -mb));
+        }
+        u32x4 pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            pk[0][k] = E::pack(c0[2 * k], c0[2 * k + 1]);
+            pk[1][k] = E::pack(c0[8 + 2 * k], c0[8 + 2 * k + 1]);
+            pk[2][k] = E::pack(c1[2 * k], c1[2 * k + 1]);
+            pk[3][k] = E::pack(c1[8 + 2 * k], c1[8 + 2 * k + 1]);
+        }
+        const uint8_t *vt = ring + cur * BLK + IMG;
+        u32x4 va[8];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            va[2 * kc] = *(const u32x4 *)(vt + cof[kc]);
+            va[2 * kc + 1] = *(const u32x4 *)(vt + 4096 + cof[kc]);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            o0 = E::mfma(va[2 * kc], pk[kc], o0);
+            o1 = E::mfma(va[2 * kc + 1], pk[kc], o1);
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            rs += c0[i] + c1[i];
+        l_run += rs;
+        if (t + 1 < ntiles && edge(j1))
+            mask_scores(n0, n1, j1, len, window, qi, g);
+        mx = row_max(n0, n1);
+        if (more)
+            ring_barrier<PIECES>();
+        else
+            ring_barrier<0>();
+    };
+
+    int t = 0;
+    for (; t + 3 < ntiles; t += 4) {
+        step(sa0, sa1, sb0, sb1, t, 0);
+        step(sb0, sb1, sa0, sa1, t + 1, 1);
+        step(sa0, sa1, sb0, sb1, t + 2, 2);
+        step(sb0, sb1, sa0, sa1, t + 3, 3);
+    }
+    if (t < ntiles)
+        step(sa0, sa1, sb0, sb1, t, 0);
+    if (t + 1 < ntiles)
+        step(sb0, sb1, sa0, sa1, t + 1, 1);
+    if (t + 2 < ntiles)
+        step(sa0, sa1, sb0, sb1, t + 2, 2);
+
+    const float l_tot = pair_sum(l_run);
+    if (qi < len) {
+        const float inv = 1.0f / l_tot;
+        uint16_t *orow = out + (int64_t)(start + qi) * hd + h * D;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2 wa = {E::pack(o0[4 * q] * inv, o0[4 * q + 1] * inv),
+                              E::pack(o0[4 * q + 2] * inv, o0[4 * q + 3] * inv)};
+            const u32x2 wb = {E::pack(o1[4 * q] * inv, o1[4 * q + 1] * inv),
+                              E::pack(o1[4 * q + 2] * inv, o1[4 * q + 3] * inv)};
+            *(u32x2 *)(orow + 8 * q + 4 * g) = wa;
+            *(u32x2 *)(orow + 32 + 8 * q + 4 * g) = wb;
+        }
+        if (g == 0)
+            lse[(int64_t)h * T + start + qi] = m_ref + logf(l_tot);
+    }
+}
+
+// Blocks of the key-tile workspace per head: floor(T / 64) + S.
+int64_t tile_blocks(const AttendArgs &a) { return (int64_t)(a.T / BC) + a.S; }
+
+template <class E>
+int launch_rotate(const AttendArgs &a) {
+    const int64_t NB = tile_blocks(a);
+    const int64_t blocks = NB * a.H;
+    if (blocks > INT32_MAX)
+        return fail(VLF_EINVAL, "%lld workgroups exceed the grid limit", (long long)blocks);
+    const uint16_t *qkv = (const uint16_t *)a.qkv;
+    const uint16_t *cs = (const uint16_t *)a.cos;
+    const uint16_t *sn = (const uint16_t *)a.sin;
+    uint8_t *ws = (uint8_t *)a.workspace;
+    int32_t nb32 = (int32_t)NB, T = a.T, S = a.S, H = a.H, P = a.table_rows;
+    void *args[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&ws,
+                    (void *)&nb32, (void *)&T, (void *)&S,  (void *)&H,   (void *)&P};
+    hipError_t e = hipLaunchKernel((const void *)prep_tiles<E>, dim3((unsigned)blocks),
+                                   dim3(256), args, 0, (hipStream_t)a.stream);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "key tile launch failed: %s", hipGetErrorString(e));
+    return VLF_OK;
+}
+
+template <class E, int NW>
+int launch_pre(const AttendArgs &a) {
+    const int64_t blocks = (int64_t)a.num_tiles * a.H;
+    if (blocks > INT32_MAX || tile_blocks(a) * a.H > INT32_MAX)
+        return fail(VLF_EINVAL, "%lld workgroups exceed the grid limit", (long long)blocks);
+    const uint16_t *qkv = (const uint16_t *)a.qkv;
+    const uint16_t *cs = (const uint16_t *)a.cos;
+    const uint16_t *sn = (const uint16_t *)a.sin;
+    const uint8_t *ws = (const uint8_t *)a.workspace;
+    uint16_t *out = (uint16_t *)a.out;
+    int32_t nb32 = (int32_t)tile_blocks(a), num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H;
+    int32_t P = a.table_rows, W = a.window;
+    float scale = a.scale;
+    void *args[] = {(void *)&qkv, (void *)&cs,  (void *)&sn,    (void *)&a.cu,
+                    (void *)&a.tiles, (void *)&ws, (void *)&out, (void *)&a.lse,
+                    (void *)&num_tiles, (void *)&T, (void *)&S,   (void *)&H,
+                    (void *)&P,   (void *)&nb32, (void *)&W,   (void *)&scale};
+    hipError_t e = hipLaunchKernel((const void *)attend_pre<E, NW>, dim3((unsigned)blocks),
+                                   dim3(NW * 64), args, 0, (hipStream_t)a.stream);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "attend launch failed: %s", hipGetErrorString(e));
+    return VLF_OK;
+}
+
 template <class E, int NW, bool FIXED>
 int launch_typed(const AttendArgs &a) {
     const int64_t blocks = (int64_t)a.num_tiles * a.H;
@@ -584,6 +954,16 @@ int launch_typed(const AttendArgs &a) {
     return VLF_OK;
 }
 
+template <class E>
+int launch_pre_br(const AttendArgs &a) {
+    switch (a.br) {  // the host side admits 64, 128 and 256 only
+    case 64: return launch_pre<E, 2>(a);
+    case 128: return launch_pre<E, 4>(a);
+    case 256: return launch_pre<E, 8>(a);
+    default: return fail(VLF_EUNSUPPORTED, "br = %d", a.br);
+    }
+}
+
 template <class E, bool FIXED>
 int launch_br(const AttendArgs &a) {
     switch (a.br) {  // the host side admits 64, 128 and 256 only
@@ -596,12 +976,20 @@ int launch_br(const AttendArgs &a) {
 
 }  // namespace
 
-int launch_attend(const AttendArgs &a) {
+int launch_attend(const AttendArgs &a, Launch what) {
+    const bool bf = a.dtype == VLF_BF16;
+    if (what == Launch::kRotate || what == Launch::kBoth) {
+        const int rc = bf ? launch_rotate<BF16>(a) : launch_rotate<F16>(a);
+        if (rc || what == Launch::kRotate)
+            return rc;
+    }
+    if (what != Launch::kDirect)
+        return bf ? launch_pre_br<BF16>(a) : launch_pre_br<F16>(a);
     // Whole-sequence descriptors need every row of the longest sequence (at most min(P, T)
     // rows) plus a tile past it to be reachable with a 31-bit byte offset.
     const int64_t rows = (int64_t)(a.table_rows < a.T ? a.table_rows : a.T) + 2 * BC;
     const bool fixed = rows * 3 * a.H * D * 2 < ((int64_t)1 << 31);
-    if (a.dtype == VLF_BF16)
+    if (bf)
         return fixed ? launch_br<BF16, true>(a) : launch_br<BF16, false>(a);
     return fixed ? launch_br<F16, true>(a) : launch_br<F16, false>(a);
 }

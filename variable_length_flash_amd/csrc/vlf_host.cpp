@@ -51,13 +51,19 @@ static int check_cu(const int32_t *cu, int32_t S, int32_t T, int32_t *max_len) {
 
 static bool supported_br(int32_t br) { return br == 64 || br == 128 || br == 256; }
 
+int64_t workspace_bytes(int32_t T, int32_t S, int32_t H) {
+    if (T <= 0 || S <= 0 || H <= 0)
+        return 0;
+    return (int64_t)H * ((int64_t)(T / 64) + S) * 16384;
+}
+
 }  // namespace vlf
 
 using namespace vlf;
 
 extern "C" {
 
-int32_t vlf_version(void) { return 1; }
+int32_t vlf_version(void) { return 2; }
 
 const char *vlf_last_error(void) { return g_error.c_str(); }
 
@@ -128,39 +134,113 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
     return VLF_OK;
 }
 
-int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-               const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles, int32_t br,
-               int32_t T, int32_t S, int32_t H, int32_t window, float scale, int32_t dtype,
-               void *out, float *lse, void *stream) {
+int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes) {
+    if (!bytes)
+        return fail(VLF_EINVAL, "bytes is NULL");
+    if (T < 0 || S < 0 || H < 0)
+        return fail(VLF_EINVAL, "negative size: T=%d S=%d H=%d", T, S, H);
+    if (H > 65536)
+        return fail(VLF_EINVAL, "H = %d above 65536", H);
+    *bytes = workspace_bytes(T, S, H);
+    return VLF_OK;
+}
+
+// Checks shared by the three launching calls. `work`: the call launches something (pointers
+// are checked only then); `need_ws`: the call cannot run without a workspace.
+static int check_launch(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                        const int32_t *cu_dev, int32_t T, int32_t S, int32_t H, int32_t dtype,
+                        const void *workspace, int64_t ws_bytes, bool work, bool need_ws) {
     if (dtype != VLF_BF16 && dtype != VLF_F16)
         return fail(VLF_EUNSUPPORTED, "dtype = %d; supported: VLF_F16 (0), VLF_BF16 (1)", dtype);
-    if (!supported_br(br))
-        return fail(VLF_EUNSUPPORTED, "br = %d; supported: 64, 128, 256", br);
     if (H < 1 || H > 65536)
         return fail(VLF_EINVAL, "H = %d outside 1 .. 65536", H);
-    if (window < 0)
-        return fail(VLF_EINVAL, "window = %d < 0", window);
-    if (T < 0 || S < 0 || num_tiles < 0 || table_rows < 0)
-        return fail(VLF_EINVAL, "negative size: T=%d S=%d num_tiles=%d table_rows=%d", T, S,
-                    num_tiles, table_rows);
+    if (T < 0 || S < 0 || table_rows < 0)
+        return fail(VLF_EINVAL, "negative size: T=%d S=%d table_rows=%d", T, S, table_rows);
     if (T > 0 && S == 0)
         return fail(VLF_EINVAL, "T = %d tokens but no sequence", T);
     if ((int64_t)T * 3 * H * 64 > ((int64_t)1 << 40))
         return fail(VLF_EINVAL, "qkv of %lld elements is beyond this library's indexing",
                     (long long)T * 3 * H * 64);
-    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-        return fail(VLF_EINVAL, "scale is not finite");
-    if (T == 0 || num_tiles == 0)
+    if (ws_bytes < 0)
+        return fail(VLF_EINVAL, "workspace_bytes = %lld < 0", (long long)ws_bytes);
+    if (!workspace && ws_bytes > 0)
+        return fail(VLF_EINVAL, "workspace_bytes = %lld without a workspace",
+                    (long long)ws_bytes);
+    if (need_ws && !workspace && work)
+        return fail(VLF_EINVAL, "this call needs a workspace");
+    if (workspace && ws_bytes < workspace_bytes(T, S, H))
+        return fail(VLF_EINVAL, "workspace of %lld bytes; T=%d S=%d H=%d need %lld",
+                    (long long)ws_bytes, T, S, H, (long long)workspace_bytes(T, S, H));
+    if (!work)
         return VLF_OK;
-    if (!qkv || !cos || !sin || !cu_dev || !tiles_dev || !out || !lse)
-        return fail(VLF_EINVAL, "null device pointer (qkv=%p cos=%p sin=%p cu=%p tiles=%p "
-                    "out=%p lse=%p)", qkv, cos, sin, (const void *)cu_dev,
-                    (const void *)tiles_dev, out, (void *)lse);
+    if (!qkv || !cos || !sin || !cu_dev)
+        return fail(VLF_EINVAL, "null device pointer (qkv=%p cos=%p sin=%p cu=%p)", qkv, cos,
+                    sin, (const void *)cu_dev);
     if (table_rows == 0)
         return fail(VLF_EINVAL, "empty rotary tables with %d tokens", T);
-    AttendArgs a{qkv, cos, sin, table_rows, cu_dev, tiles_dev, num_tiles, br, T, S, H,
-                 window, scale, dtype, out, lse, stream};
-    return launch_attend(a);
+    return VLF_OK;
+}
+
+static int attend_common(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                         const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
+                         int32_t br, int32_t T, int32_t S, int32_t H, int32_t window,
+                         float scale, int32_t dtype, const void *workspace, int64_t ws_bytes,
+                         void *out, float *lse, void *stream, Launch what) {
+    if (dtype != VLF_BF16 && dtype != VLF_F16)
+        return fail(VLF_EUNSUPPORTED, "dtype = %d; supported: VLF_F16 (0), VLF_BF16 (1)", dtype);
+    if (!supported_br(br))
+        return fail(VLF_EUNSUPPORTED, "br = %d; supported: 64, 128, 256", br);
+    if (window < 0)
+        return fail(VLF_EINVAL, "window = %d < 0", window);
+    if (num_tiles < 0)
+        return fail(VLF_EINVAL, "negative size: num_tiles=%d", num_tiles);
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(VLF_EINVAL, "scale is not finite");
+    const bool work = T > 0 && num_tiles > 0;
+    int rc = check_launch(qkv, cos, sin, table_rows, cu_dev, T, S, H, dtype, workspace, ws_bytes,
+                          work, what == Launch::kRotated);
+    if (rc)
+        return rc;
+    if (!work)
+        return VLF_OK;
+    if (!tiles_dev || !out || !lse)
+        return fail(VLF_EINVAL, "null device pointer (tiles=%p out=%p lse=%p)",
+                    (const void *)tiles_dev, out, (void *)lse);
+    AttendArgs a{qkv,    cos,   sin,   table_rows, cu_dev, tiles_dev, num_tiles,
+                 br,     T,     S,     H,          window, scale,     dtype,
+                 const_cast<void *>(workspace), out, lse, stream};
+    return launch_attend(a, what);
+}
+
+int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+               const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles, int32_t br,
+               int32_t T, int32_t S, int32_t H, int32_t window, float scale, int32_t dtype,
+               void *workspace, int64_t workspace_bytes_, void *out, float *lse, void *stream) {
+    return attend_common(qkv, cos, sin, table_rows, cu_dev, tiles_dev, num_tiles, br, T, S, H,
+                         window, scale, dtype, workspace, workspace_bytes_, out, lse, stream,
+                         workspace ? Launch::kBoth : Launch::kDirect);
+}
+
+int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                       const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
+                       int32_t br, int32_t T, int32_t S, int32_t H, int32_t window, float scale,
+                       int32_t dtype, const void *workspace, int64_t workspace_bytes_, void *out,
+                       float *lse, void *stream) {
+    return attend_common(qkv, cos, sin, table_rows, cu_dev, tiles_dev, num_tiles, br, T, S, H,
+                         window, scale, dtype, workspace, workspace_bytes_, out, lse, stream,
+                         Launch::kRotated);
+}
+
+int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                    const int32_t *cu_dev, int32_t T, int32_t S, int32_t H, int32_t dtype,
+                    void *workspace, int64_t workspace_bytes_, void *stream) {
+    int rc = check_launch(qkv, cos, sin, table_rows, cu_dev, T, S, H, dtype, workspace,
+                          workspace_bytes_, T > 0, true);
+    if (rc || T == 0)
+        return rc;
+    AttendArgs a{qkv, cos, sin, table_rows, cu_dev, nullptr, 0,       0,       T,     S,
+                 H,   0,   1.f, dtype,      workspace, nullptr, nullptr, stream};
+    return launch_attend(a, Launch::kRotate);
 }
 
 }  // extern "C"

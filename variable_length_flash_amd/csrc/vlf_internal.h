@@ -20,13 +20,25 @@ struct AttendArgs {
     int32_t window;
     float scale;
     int32_t dtype;
+    void *workspace;  // NULL: every workgroup rotates the key tiles it reads
     void *out;
     float *lse;
     void *stream;
 };
 
-// Queue the forward kernel; returns a vlf_status.
-int launch_attend(const AttendArgs &a);
+// Bytes of the key-tile workspace for T tokens, S sequences and H heads.
+int64_t workspace_bytes(int32_t T, int32_t S, int32_t H);
+
+// What launch_attend queues.
+enum class Launch {
+    kDirect,   // the forward, every workgroup rotating the key tiles it reads
+    kRotate,   // the key-tile workspace only
+    kRotated,  // the forward over a workspace written before
+    kBoth,     // kRotate, then kRotated
+};
+
+// Queue the forward kernels; returns a vlf_status.
+int launch_attend(const AttendArgs &a, Launch what);
 
 // Record the calling thread's error message (printf-style) and return `status`.
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
