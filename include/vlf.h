@@ -88,10 +88,12 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
 
 /*
  * Device workspace vlf_attend needs to pre-rotate keys for T tokens in S sequences and H heads:
- * H * (floor(T / 64) + S) blocks of 16384 bytes. Key tile u (keys 64u .. 64u+63) of sequence s
- * and head h occupies block h * (floor(T / 64) + S) + floor(cu[s] / 64) + s + u; these indices
- * never collide for a valid cu. A block holds two 8192-byte images: the rotated, rounded keys
- * [key][dim] and the values transposed [dim][key], 64 rows of 128 bytes each.
+ * NB = floor(T / 64) + S blocks of 16384 bytes per head, then H * NB float32 values, in all
+ * H * NB * 16388 bytes. Key tile u (keys 64u .. 64u+63) of sequence s and head h occupies block
+ * h * NB + floor(cu[s] / 64) + s + u; these indices never collide for a valid cu. A block holds
+ * two 8192-byte images: the rotated, rounded keys [key][dim] and the values transposed
+ * [dim][key], 64 rows of 128 bytes each. The float32 at the same index bounds the Euclidean norm
+ * of the block's rounded keys from above.
  *   bytes  out: the size (0 when T, S or H is 0).
  * Errors: VLF_EINVAL (negative size, H > 65536, null bytes).
  */

@@ -143,8 +143,8 @@ def _attend_status(**kw):
     (dict(P=0), binding.VLF_EINVAL, "rotary"),
     (dict(scale=float("nan")), binding.VLF_EINVAL, "scale"),
     (dict(scale=float("inf")), binding.VLF_EINVAL, "scale"),
-    # T=100, S=2, H=2 need 2 * (1 + 2) blocks of 16 KiB
-    (dict(ws=0x8000, ws_bytes=6 * 16384 - 1), binding.VLF_EINVAL, "workspace of"),
+    # T=100, S=2, H=2 need 2 * (1 + 2) blocks of 16 KiB plus 6 norm bounds
+    (dict(ws=0x8000, ws_bytes=6 * 16388 - 1), binding.VLF_EINVAL, "workspace of"),
     (dict(ws=0x8000, ws_bytes=0), binding.VLF_EINVAL, "workspace of"),
     (dict(ws=None, ws_bytes=4096), binding.VLF_EINVAL, "without a workspace"),
     (dict(ws=0x8000, ws_bytes=-1), binding.VLF_EINVAL, "workspace_bytes"),
@@ -164,8 +164,9 @@ def test_attend_with_no_work_is_a_no_op():
 @pytest.mark.parametrize("T,S,H", [(0, 0, 1), (1, 1, 1), (63, 1, 1), (64, 1, 1), (100, 2, 2),
                                    (131072, 16, 16), (33000, 1024, 16), (5, 5, 65536)])
 def test_workspace_bytes(T, S, H):
-    # H * (floor(T / 64) + S) blocks of 16 KiB; nothing when there is no token
-    want = 0 if T == 0 else H * (T // 64 + S) * 16384
+    # H * (floor(T / 64) + S) blocks of 16 KiB and as many float32 norm bounds; nothing when
+    # there is no token
+    want = 0 if T == 0 else H * (T // 64 + S) * (16384 + 4)
     assert vlf.workspace_bytes(T, S, H) == want
 
 
@@ -192,7 +193,7 @@ def test_workspace_bytes_rejects(T, S, H, msg):
 
 def _rotate_status(**kw):
     args = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=64, cu=0x4000, T=100, S=2, H=2,
-                dtype=binding.VLF_BF16, ws=0x8000, ws_bytes=6 * 16384, stream=None)
+                dtype=binding.VLF_BF16, ws=0x8000, ws_bytes=6 * 16388, stream=None)
     args.update(kw)
     lib = vlf.load_library()
     rc = lib.vlf_rotate_keys(args["qkv"], args["cos"], args["sin"], args["P"], args["cu"],
@@ -207,7 +208,7 @@ def _rotate_status(**kw):
     (dict(T=-1), binding.VLF_EINVAL, "negative"),
     (dict(S=0), binding.VLF_EINVAL, "no sequence"),
     (dict(ws=None, ws_bytes=0), binding.VLF_EINVAL, "needs a workspace"),
-    (dict(ws_bytes=6 * 16384 - 16), binding.VLF_EINVAL, "workspace of"),
+    (dict(ws_bytes=6 * 16388 - 4), binding.VLF_EINVAL, "workspace of"),
     (dict(cu=None), binding.VLF_EINVAL, "null"),
     (dict(P=0), binding.VLF_EINVAL, "rotary"),
 ])

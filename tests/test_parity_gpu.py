@@ -159,9 +159,11 @@ def test_edge_batches(lens, prerotate):
 @pytest.mark.parametrize("name,br,window", [("ragged", 64, 0), ("ragged", 128, 33),
                                             ("ragged", 256, 200), ("encoder", 128, 0),
                                             ("sliding", 256, 128), ("long", 256, 0)])
-def test_paths_agree_bit_for_bit(name, br, window):
-    """Both paths stage the same rounded operands and run the same arithmetic in the same
-    order; only where the rotated keys come from differs, so every output bit must agree."""
+def test_paths_agree(name, br, window):
+    """Both paths stage the same rounded operands and run the same products. They may keep
+    different reference maxima (the workspace path skips the row maximum where a norm bound
+    shows it cannot matter), so the probabilities are rounded at different scales: lse, from
+    the same unrounded sums, agrees to float32 rounding; out to about one bf16 ulp."""
     if name == "ragged":
         w = workloads.custom(RAGGED, 3, dtype="bf16", window=window, table_rows=512, seed=13)
     else:
@@ -170,8 +172,10 @@ def test_paths_agree_bit_for_bit(name, br, window):
     _say(f"case paths agree {name} br={br} W={window}")
     a_out, a_lse = run_gpu(w, qkv, cos, sin, br=br, window=window, prerotate=False)
     b_out, b_lse = run_gpu(w, qkv, cos, sin, br=br, window=window, prerotate=True)
-    np.testing.assert_array_equal(a_out, b_out)
-    np.testing.assert_array_equal(a_lse, b_lse)
+    d_out = float(np.abs(a_out - b_out).max()) if a_out.size else 0.0
+    d_lse = float(np.abs(a_lse - b_lse).max()) if a_lse.size else 0.0
+    _say(f"[paths] {name} br={br} W={window}: out {d_out:.2e}, lse {d_lse:.2e}")
+    assert d_lse <= 2e-5 and d_out <= 8e-3, (d_out, d_lse)
 
 
 def test_workspace_is_rewritten_on_every_call():

@@ -71,6 +71,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Storage-type helpers: widen the low / high element of a packed pair, round a pair of floats
 // to the storage type (round-to-nearest-even), and the 32x32x16 matrix instruction.
 struct BF16 {
+    // headroom of the workspace path's reference maximum (natural-log units): probabilities stay
+    // below e^16, far inside bfloat16's range
+    static constexpr float TAU_PRE = 16.0f;
     static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
     static __device__ __forceinline__ float hi(uint32_t w) {
         return __uint_as_float(w & 0xffff0000u);
@@ -86,6 +89,8 @@ struct BF16 {
 };
 
 struct F16 {
+    // e^10 < 65504 (the largest binary16 value), so a rounded probability cannot overflow
+    static constexpr float TAU_PRE = 10.0f;
     static __device__ __forceinline__ float lo(uint32_t w) {
         return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
     }
@@ -369,14 +374,21 @@ constexpr int BLK = 2 * IMG;  // bytes of one key tile's block
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
+// Margin on a computed norm: the float32 sum of 64 squares and v_sqrt_f32 are each within a few
+// ulp, so a factor 1 + 2^-10 makes the result an upper bound of the exact norm.
+constexpr float NORM_MARGIN = 1.0f + 1.0f / 1024.0f;
+
 // One workgroup per (block, head) writes that block: keys rotated and rounded exactly as the
-// staging of the other path does, values transposed; keys past the sequence are zero.
+// staging of the other path does, values transposed; keys past the sequence are zero. It also
+// writes an upper bound of the largest Euclidean norm among the block's rounded keys into the
+// norm array that follows the blocks (index h * NB + block).
 template <class E>
 __global__ void __launch_bounds__(256)
 prep_tiles(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            uint8_t *__restrict__ ws, int32_t NB, int32_t T, int32_t S, int32_t H, int32_t P) {
     __shared__ uint16_t vrow[64][72];
+    __shared__ float wmax[4];
     const int h = (int)(blockIdx.x / (uint32_t)NB);
     const int b = (int)(blockIdx.x - (uint32_t)h * (uint32_t)NB);
     // the sequence owning block b: the largest s with floor(cu[s] / 64) + s <= b
@@ -426,7 +438,30 @@ prep_tiles(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     *(u32x4 *)(blk + r * 128 + 16 * ((4 + q) ^ swz(r))) = u32x4{y2[0], y2[1], y2[2], y2[3]};
     *(u32x4 *)&vrow[r][16 * q] = va;
     *(u32x4 *)&vrow[r][16 * q + 8] = vb;
+    // squared norm of key row r (its 64 rounded elements sit in lanes 4r .. 4r+3), then the
+    // largest over the wave's 16 rows
+    float sq = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float a0 = E::lo(y1[k]), a1 = E::hi(y1[k]), b0 = E::lo(y2[k]), b1 = E::hi(y2[k]);
+        sq = __builtin_fmaf(a0, a0, sq);
+        sq = __builtin_fmaf(a1, a1, sq);
+        sq = __builtin_fmaf(b0, b0, sq);
+        sq = __builtin_fmaf(b1, b1, sq);
+    }
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1)
+        sq = fmaxf(sq, __shfl_xor(sq, off));
+    if ((tid & 63) == 0)
+        wmax[tid >> 6] = sq;
     __syncthreads();
+    if (tid == 0) {
+        const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        float *norms = (float *)(ws + (int64_t)H * NB * BLK);
+        norms[(int64_t)h * NB + b] = __builtin_sqrtf(m) * NORM_MARGIN;
+    }
     // V^T: thread (d, q) writes chunks 2q and 2q+1 of row d; chunk ch holds slots 8ch .. 8ch+7
     const int d = tid >> 2;
 #pragma unroll
@@ -742,6 +777,23 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 
     u32x4 qop[4];
     query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
+    // upper bound of this row's rounded query norm (lanes n and n + 32 hold 32 elements each)
+    float qn;
+    {
+        float sq = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float a0 = E::lo(qop[c][w]), a1 = E::hi(qop[c][w]);
+                sq = __builtin_fmaf(a0, a0, sq);
+                sq = __builtin_fmaf(a1, a1, sq);
+            }
+        qn = __builtin_sqrtf(pair_sum(sq)) * NORM_MARGIN;
+    }
+    // the blocks' key norm bounds: every score of tile t is at most qn * knorm[key(t) / BC]
+    const float *knorm = (const float *)(ws + (int64_t)H * NB * BLK) + (int64_t)h * NB +
+                         start / BC + (int)seq;
     asm volatile("" ::: "memory");
     copy(0, 0);
     if (ntiles > 1)
@@ -785,21 +837,12 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     f32x16 o0 = {}, o1 = {};
     f32x16 sa0, sa1, sb0, sb1;
 
-    kscores(0, sa0, sa1);
-    if (edge(key(0)))
-        mask_scores(sa0, sa1, key(0), len, window, qi, g);
-    float mx = row_max(sa0, sa1);
-
-    // Step t with tile t in slot cur (cur = t % 4, a constant after unrolling): as in
-    // attend_fwd, plus the copy of tile t+3 and the ring wait.
-    auto step = [&](f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, int t, int cur) {
-        const int nxt = (cur + 1) & 3;
-        const bool more = t + 3 < ntiles;
-        if (more)
-            copy(t + 3, (cur + 3) & 3);
-        const int j1 = key(t + 1);
-
-        const bool raise = mx > m_ref + TAU;
+    // Raise the reference maximum where tile scores (maximum mx) exceed it by more than
+    // TAU_PRE, rescaling l and O (whole wave skipped when no row needs it). Lanes that keep it
+    // scale by exactly 1 (their m_ref may still be -inf, where the difference would be NaN); a
+    // first reference scales the zero state by 0.
+    auto raise_ref = [&](float mx) {
+        const bool raise = mx > m_ref + E::TAU_PRE;
         const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * LOG2E) : 1.0f;
         m_ref = raise ? mx : m_ref;
         l_run *= alpha;
@@ -810,9 +853,25 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
                 o1[i] *= alpha;
             }
         }
+    };
+
+    kscores(0, sa0, sa1);
+    if (edge(key(0)))
+        mask_scores(sa0, sa1, key(0), len, window, qi, g);
+    raise_ref(row_max(sa0, sa1));
+
+    // Step t with tile t in slot cur (cur = t % 4, a constant after unrolling): as in
+    // attend_fwd, plus the copy of tile t+3 and the ring wait, but the reference is raised for
+    // tile t+1 at the end of step t (after tile t's output product), so that the body from the
+    // scores of t+1 to the row sum of t is one branch-free stretch for the scheduler.
+    auto step = [&](f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, int t, int cur) {
+        const int nxt = (cur + 1) & 3;
+        const bool more = t + 3 < ntiles;
+        if (more)
+            copy(t + 3, (cur + 3) & 3);
+        const int j1 = key(t + 1);
         const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
 
-        // past the last tile the scores read a slot no copy is headed for; they are not used
         kscores(nxt, n0, n1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -844,9 +903,17 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         for (int i = 0; i < 16; ++i)
             rs += c0[i] + c1[i];
         l_run += rs;
-        if (t + 1 < ntiles && edge(j1))
-            mask_scores(n0, n1, j1, len, window, qi, g);
-        mx = row_max(n0, n1);
+        // past the last tile the scores of "tile t+1" come from a stale slot: never used
+        if (t + 1 < ntiles) {
+            if (edge(j1))
+                mask_scores(n0, n1, j1, len, window, qi, g);
+            // the row maximum only matters when it could raise the reference: skip it for the
+            // whole wave when the norm bound keeps every row's scores within TAU_PRE of its
+            // reference
+            const bool bounded = qn * knorm[j1 / BC] <= m_ref + E::TAU_PRE;
+            if (__builtin_amdgcn_ballot_w64(!bounded))
+                raise_ref(row_max(n0, n1));
+        }
         if (more)
             ring_barrier<PIECES>();
         else

@@ -54,7 +54,7 @@ static bool supported_br(int32_t br) { return br == 64 || br == 128 || br == 256
 int64_t workspace_bytes(int32_t T, int32_t S, int32_t H) {
     if (T <= 0 || S <= 0 || H <= 0)
         return 0;
-    return (int64_t)H * ((int64_t)(T / 64) + S) * 16384;
+    return (int64_t)H * ((int64_t)(T / 64) + S) * (16384 + 4);
 }
 
 }  // namespace vlf
