@@ -312,7 +312,7 @@ def main():
     ap.add_argument("--kernel", default=KERNELS["prerotate"], choices=sorted(KERNELS.values()),
                     help="kernel whose counters --summarize reads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", nargs="+")
     args = ap.parse_args()

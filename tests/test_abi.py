@@ -227,3 +227,20 @@ def test_attend_rotated_needs_a_workspace():
     rc = lib.vlf_attend_rotated(0x1000, 0x2000, 0x3000, 64, 0x4000, 0x5000, 4, 64, 100, 2, 2, 0,
                                 0.125, binding.VLF_BF16, None, 0, 0x6000, 0x7000, None)
     assert rc == binding.VLF_EINVAL and "needs a workspace" in lib.vlf_last_error().decode()
+
+
+@pytest.mark.parametrize("max_len,window,br", [(1, 0, 64), (64, 0, 64), (65, 0, 128),
+                                               (1023, 0, 128), (1024, 0, 256), (8192, 0, 256),
+                                               (8192, 128, 128), (8192, 512, 128),
+                                               (8192, 513, 256), (64, 128, 64)])
+def test_choose_br(max_len, window, br):
+    assert vlf.choose_br(max_len, window) == br
+
+
+@pytest.mark.parametrize("max_len,br,window,pre", [(8192, 256, 0, True), (512, 128, 0, True),
+                                                   (383, 128, 0, False), (8192, 128, 128, False),
+                                                   (8192, 128, 129, True), (64, 64, 0, False)])
+def test_choose_prerotate(max_len, br, window, pre):
+    # the workspace pays when a query tile's key span (the sequence, or br + 2W - 1) is at
+    # least three query tiles
+    assert vlf.choose_prerotate(max_len, br, window) is pre

@@ -141,12 +141,15 @@ def choose_prerotate(max_len: int, br: int, window: int = 0) -> bool:
     return span >= 3 * br
 
 
-def choose_br(max_len: int) -> int:
-    """Query rows per workgroup: 64 when no sequence is longer than 64, 256 from 1024 tokens
-    on (each key tile is rotated once per workgroup, so taller tiles rotate less per query),
-    128 in between."""
+def choose_br(max_len: int, window: int = 0) -> int:
+    """Query rows per workgroup: 64 when no sequence is longer than 64 (one key tile per
+    query tile: the unpipelined kernel); 128 under a window of at most 512 (a query tile's key
+    span is br + 2W - 1, so taller tiles compute more masked pairs); otherwise 256 from 1024
+    tokens on (fewer, longer key loops) and 128 in between."""
     if max_len <= 64:
         return 64
+    if 0 < window <= 512:
+        return 128
     return 256 if max_len >= 1024 else 128
 
 
@@ -181,7 +184,7 @@ def prepare(cu, device=None, br: int | None = None, prerotate: bool | None = Non
     cu_host = _host_cu(cu)
     device = torch.device("cuda") if device is None else torch.device(device)
     _, max_len = tile_count(cu_host, 128)
-    br = choose_br(max_len) if br is None else int(br)
+    br = choose_br(max_len, window) if br is None else int(br)
     prerotate = (choose_prerotate(max_len, br, window) if prerotate is None
                  else bool(prerotate))
     table = tile_table(cu_host, br)

@@ -478,7 +478,7 @@ prep_tiles(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 }
 
 template <class E, int NW, bool FIXED>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            const uint32_t *__restrict__ tiles, uint16_t *__restrict__ out,
@@ -707,7 +707,7 @@ __device__ __forceinline__ void ring_barrier() {
 // the slot tile t-1 left (every wave passed the barrier after its last read), and the end of
 // step t waits for tile t+2, so each copy has two steps to land.
 template <class E, int NW>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            const uint32_t *__restrict__ tiles, const uint8_t *__restrict__ ws,
@@ -999,6 +999,141 @@ int launch_pre(const AttendArgs &a) {
     return VLF_OK;
 }
 
+// Query tiles of 64 rows (two waves) with a single key-tile slot: each key tile is loaded,
+// rotated, staged and consumed in turn, without attend_fwd's software pipeline. Registers and
+// LDS (18 KB) stay small, so many workgroups share a CU, which is what batches of short
+// sequences need: most of their tiles see one key tile and are bound by load latency, not by
+// the matrix unit. Same arithmetic as attend_fwd, tile by tile.
+template <class E, bool FIXED>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
+attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+           const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+           const uint32_t *__restrict__ tiles, uint16_t *__restrict__ out,
+           float *__restrict__ lse, int32_t num_tiles, int32_t T, int32_t S, int32_t H, int32_t P,
+           int32_t window, float scale) {
+    constexpr int BR = 64;
+    constexpr int NTHR = 128;
+    __shared__ __attribute__((aligned(16))) uint16_t ks[BC * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+
+    const int nb = (int)gridDim.x;
+    const int b = (int)blockIdx.x;
+    const int xcd = b % XCDS, slot = b / XCDS;
+    const int per = nb / XCDS, extra = nb % XCDS;
+    const int work = xcd * per + min(xcd, extra) + slot;
+    const int h = work / num_tiles;
+    const int tile = work - h * num_tiles;
+
+    const uint32_t seq = tiles[2 * tile];
+    const int i0 = (int)tiles[2 * tile + 1];
+    if (seq >= (uint32_t)S)
+        return;
+    const int start = cu[seq];
+    const int len = cu[seq + 1] - start;
+    if (i0 < 0 || i0 >= len || len > P || start < 0 || (int64_t)start + len > T)
+        return;
+
+    const int64_t ld = 3LL * H * D;
+    const int hd = H * D;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int w0 = i0 + 32 * wv;
+    const int qi = w0 + n;
+
+    int lo = 0, hi = len;
+    if (window > 0) {
+        if (i0 + 1 > window)
+            lo = (i0 + 1 - window) / BC * BC;
+        if ((int64_t)i0 + BR + window - 1 < len)
+            hi = i0 + BR + window - 1;
+    }
+    const int ntiles = (hi - lo + BC - 1) / BC;
+
+    Staging<NTHR> sg;
+    sg.init(tid, ld);
+    Sources<FIXED> src;
+    src.init(qkv + (int64_t)start * ld + hd + h * D, qkv + (int64_t)start * ld + 2 * hd + h * D,
+             cos_t, sin_t, len, P, ld);
+    TileRegs<NTHR> r;
+    stage_load(r, sg, src, lo);
+    u32x4 qop[4];
+    query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
+
+    float m_ref = -__builtin_inff();
+    float l_run = 0.f;
+    f32x16 o0 = {}, o1 = {};
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = lo + t * BC;
+        if (t > 0) {
+            stage_load(r, sg, src, j0);
+            __syncthreads();  // every wave is done with the previous tile
+        }
+        stage_store<E, NTHR>(r, sg, ks, vt);
+        __syncthreads();
+        f32x16 s0, s1;
+        scores<E>(ks, qop, n, g, s0, s1);
+        if ((j0 + BC > len) ||
+            (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window)))
+            mask_scores(s0, s1, j0, len, window, qi, g);
+        const float mx = row_max(s0, s1);
+        const bool raise = mx > m_ref + TAU;
+        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * LOG2E) : 1.0f;
+        m_ref = raise ? mx : m_ref;
+        l_run *= alpha;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                o0[i] *= alpha;
+                o1[i] *= alpha;
+            }
+        }
+        const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], LOG2E, -mb));
+            s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], LOG2E, -mb));
+        }
+        u32x4 pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            pk[0][k] = E::pack(s0[2 * k], s0[2 * k + 1]);
+            pk[1][k] = E::pack(s0[8 + 2 * k], s0[8 + 2 * k + 1]);
+            pk[2][k] = E::pack(s1[2 * k], s1[2 * k + 1]);
+            pk[3][k] = E::pack(s1[8 + 2 * k], s1[8 + 2 * k + 1]);
+        }
+        const uint16_t *v0 = vt + n * VS + 8 * g;
+        const uint16_t *v1 = vt + (32 + n) * VS + 8 * g;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            o0 = E::mfma(*(const u32x4 *)(v0 + 16 * kc), pk[kc], o0);
+            o1 = E::mfma(*(const u32x4 *)(v1 + 16 * kc), pk[kc], o1);
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            rs += s0[i] + s1[i];
+        l_run += rs;
+    }
+
+    const float l_tot = pair_sum(l_run);
+    if (qi < len) {
+        const float inv = 1.0f / l_tot;
+        uint16_t *orow = out + (int64_t)(start + qi) * hd + h * D;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2 wa = {E::pack(o0[4 * q] * inv, o0[4 * q + 1] * inv),
+                              E::pack(o0[4 * q + 2] * inv, o0[4 * q + 3] * inv)};
+            const u32x2 wb = {E::pack(o1[4 * q] * inv, o1[4 * q + 1] * inv),
+                              E::pack(o1[4 * q + 2] * inv, o1[4 * q + 3] * inv)};
+            *(u32x2 *)(orow + 8 * q + 4 * g) = wa;
+            *(u32x2 *)(orow + 32 + 8 * q + 4 * g) = wb;
+        }
+        if (g == 0)
+            lse[(int64_t)h * T + start + qi] = m_ref + logf(l_tot);
+    }
+}
+
 template <class E, int NW, bool FIXED>
 int launch_typed(const AttendArgs &a) {
     const int64_t blocks = (int64_t)a.num_tiles * a.H;
@@ -1014,8 +1149,14 @@ int launch_typed(const AttendArgs &a) {
                     (void *)&a.tiles, (void *)&out,   (void *)&a.lse, (void *)&num_tiles,
                     (void *)&T,   (void *)&S,         (void *)&H,  (void *)&P,
                     (void *)&W,   (void *)&scale};
-    hipError_t e = hipLaunchKernel((const void *)attend_fwd<E, NW, FIXED>, dim3((unsigned)blocks),
-                                   dim3(NW * 64), args, 0, (hipStream_t)a.stream);
+    // 64-row tiles take the unpipelined kernel (short sequences), taller ones the pipeline
+    const void *fn;
+    if constexpr (NW == 2)
+        fn = (const void *)attend_one<E, FIXED>;
+    else
+        fn = (const void *)attend_fwd<E, NW, FIXED>;
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(NW * 64), args, 0,
+                                   (hipStream_t)a.stream);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "attend launch failed: %s", hipGetErrorString(e));
     return VLF_OK;
