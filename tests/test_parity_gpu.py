@@ -10,6 +10,7 @@ them and compare sampled rows that cover every sequence's first and last rows, t
 boundaries and random rows, plus properties of all rows. Guard regions after `out` and `lse`
 must stay untouched.
 """
+import functools
 import math
 import sys
 
@@ -258,3 +259,54 @@ def test_full_size_workload(name):
     rows = sample_rows(w, br, 1500 if name == "long" else 3000, seed=seed)
     compare(f"{name} ({len(rows)} sampled rows, all heads)", w, out, lse, qkv, cos, sin,
             rows=rows)
+
+
+@functools.lru_cache(maxsize=1)
+def _tie_inputs(seed=31, length=64):
+    """fp16 inputs whose key rotations land exactly on binary16 ties after the float32
+    rounding the page prescribes (float32 fma, then the cast), while the exact value is off the
+    tie: a fused fma-and-narrow would round those keys the other way. One head, one sequence;
+    queries and values random. Returns (qkv [L, 192] float16, cos, sin [L, 32] float16)."""
+    rng = np.random.default_rng(seed)
+    need = length * 32
+    found = []
+    while sum(len(f[0]) for f in found) < need:
+        n = 1 << 21
+        x1 = rng.standard_normal(n).astype(np.float16).astype(np.float64)
+        x2 = rng.standard_normal(n).astype(np.float16).astype(np.float64)
+        c = rng.uniform(-1, 1, n).astype(np.float16).astype(np.float64)
+        s = rng.uniform(-1, 1, n).astype(np.float16).astype(np.float64)
+        exact = x1 * c - x2 * s               # exact: products of binary16 values fit float64
+        y = exact.astype(np.float32)
+        bits = y.view(np.uint32)
+        normal = (np.abs(y) >= 2.0 ** -14) & (np.abs(y) < 60000)
+        tie = normal & ((bits & 0x1FFF) == 0x1000) & (exact != y.astype(np.float64))
+        k = np.nonzero(tie)[0]
+        found.append((x1[k], x2[k], c[k], s[k]))
+    x1, x2, c, s = (np.concatenate([f[i] for f in found])[:need].reshape(length, 32)
+                    for i in range(4))
+    qkv = np.zeros((length, 3 * 64), dtype=np.float16)
+    qkv[:, :64] = rng.standard_normal((length, 64)).astype(np.float16)
+    qkv[:, 64:96] = x1
+    qkv[:, 96:128] = x2
+    qkv[:, 128:] = rng.standard_normal((length, 64)).astype(np.float16)
+    return (torch.from_numpy(qkv), torch.from_numpy(c.astype(np.float16)),
+            torch.from_numpy(s.astype(np.float16)))
+
+
+@pytest.mark.parametrize("prerotate", PATHS)
+@pytest.mark.parametrize("br", [64, 128, 256])
+def test_key_rotation_ties_round_like_the_page(br, prerotate):
+    """Every key element sits on a binary16 tie after its float32 rounding. With W = 1 each row
+    sees only itself: out = v bit for bit and lse = <q~, k~> to float32 accumulation error, so
+    a key rounded the other way (about one binary16 ulp times |q~|, ~1e-4) cannot pass."""
+    qkv, cos, sin = _tie_inputs()
+    w = workloads.custom([64], 1, dtype="fp16", window=1, table_rows=64, seed=0)
+    _say(f"case key ties br={br} prerotate={prerotate}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=prerotate)
+    np.testing.assert_array_equal(out, qkv[:, 128:].float().numpy())
+    _, want = oracle.attend(qkv.float().numpy(), cos.float().numpy(), sin.float().numpy(), w.cu,
+                            1, 1, w.scale, mode="B", dtype="fp16")
+    err = float(np.abs(lse - want).max())
+    _say(f"[parity] key ties br={br} pre={int(prerotate)}: lse {err:.2e} (tol 2e-5)")
+    assert err < 2e-5

@@ -122,12 +122,37 @@ __device__ __forceinline__ void rotate(const uint32_t *x1, const uint32_t *x2, c
         const float b0 = E::lo(x2[k]), b1 = E::hi(x2[k]);
         const float c0 = E::lo(c[k]), c1 = E::hi(c[k]);
         const float s0 = E::lo(s[k]), s1 = E::hi(s[k]);
-        const float p0 = __builtin_fmaf(a0, c0, -(b0 * s0)) * scale;
-        const float p1 = __builtin_fmaf(a1, c1, -(b1 * s1)) * scale;
-        const float q0 = __builtin_fmaf(a0, s0, b0 * c0) * scale;
-        const float q1 = __builtin_fmaf(a1, s1, b1 * c1) * scale;
+        float p0 = __builtin_fmaf(a0, c0, -(b0 * s0)) * scale;
+        float p1 = __builtin_fmaf(a1, c1, -(b1 * s1)) * scale;
+        float q0 = __builtin_fmaf(a0, s0, b0 * c0) * scale;
+        float q1 = __builtin_fmaf(a1, s1, b1 * c1) * scale;
+        // Materialise the float32 results: the storage-type rounding must see them. Left to
+        // itself the compiler fuses an fma with the narrowing (v_fma_mix*_f16), which rounds
+        // the exact value once and differs wherever the float32 result is a binary16 tie.
+        asm volatile("" : "+v"(p0), "+v"(p1), "+v"(q0), "+v"(q1));
         y1[k] = E::pack(p0, p1);
         y2[k] = E::pack(q0, q1);
+    }
+}
+
+// out row = O / l: a float32 division per element, then the storage-type rounding (the float32
+// quotient is materialised first so that no fused operation rounds the exact quotient instead).
+// Lane (n, g) holds dims 8q + 4g .. +3 (o0) and 32 + 8q + 4g .. +3 (o1) of its query.
+template <class E>
+__device__ __forceinline__ void store_out(const f32x16 &o0, const f32x16 &o1, float l,
+                                          uint16_t *orow, int g) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float a[4], b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = o0[4 * q + e] / l;
+            b[e] = o1[4 * q + e] / l;
+        }
+        asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+        asm volatile("" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+        *(u32x2 *)(orow + 8 * q + 4 * g) = u32x2{E::pack(a[0], a[1]), E::pack(a[2], a[3])};
+        *(u32x2 *)(orow + 32 + 8 * q + 4 * g) = u32x2{E::pack(b[0], b[1]), E::pack(b[2], b[3])};
     }
 }
 
@@ -671,17 +696,8 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     // ---- epilogue: out = O / l, lse = m + ln l, for rows inside the sequence
     const float l_tot = pair_sum(l_run);
     if (qi < len) {
-        const float inv = 1.0f / l_tot;
         uint16_t *orow = out + (int64_t)(start + qi) * hd + h * D;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x2 wa = {E::pack(o0[4 * q] * inv, o0[4 * q + 1] * inv),
-                              E::pack(o0[4 * q + 2] * inv, o0[4 * q + 3] * inv)};
-            const u32x2 wb = {E::pack(o1[4 * q] * inv, o1[4 * q + 1] * inv),
-                              E::pack(o1[4 * q + 2] * inv, o1[4 * q + 3] * inv)};
-            *(u32x2 *)(orow + 8 * q + 4 * g) = wa;
-            *(u32x2 *)(orow + 32 + 8 * q + 4 * g) = wb;
-        }
+        store_out<E>(o0, o1, l_tot, orow, g);
         if (g == 0)
             lse[(int64_t)h * T + start + qi] = m_ref + logf(l_tot);
     }
@@ -936,17 +952,8 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 
     const float l_tot = pair_sum(l_run);
     if (qi < len) {
-        const float inv = 1.0f / l_tot;
         uint16_t *orow = out + (int64_t)(start + qi) * hd + h * D;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x2 wa = {E::pack(o0[4 * q] * inv, o0[4 * q + 1] * inv),
-                              E::pack(o0[4 * q + 2] * inv, o0[4 * q + 3] * inv)};
-            const u32x2 wb = {E::pack(o1[4 * q] * inv, o1[4 * q + 1] * inv),
-                              E::pack(o1[4 * q + 2] * inv, o1[4 * q + 3] * inv)};
-            *(u32x2 *)(orow + 8 * q + 4 * g) = wa;
-            *(u32x2 *)(orow + 32 + 8 * q + 4 * g) = wb;
-        }
+        store_out<E>(o0, o1, l_tot, orow, g);
         if (g == 0)
             lse[(int64_t)h * T + start + qi] = m_ref + logf(l_tot);
     }
@@ -1118,17 +1125,8 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 
     const float l_tot = pair_sum(l_run);
     if (qi < len) {
-        const float inv = 1.0f / l_tot;
         uint16_t *orow = out + (int64_t)(start + qi) * hd + h * D;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x2 wa = {E::pack(o0[4 * q] * inv, o0[4 * q + 1] * inv),
-                              E::pack(o0[4 * q + 2] * inv, o0[4 * q + 3] * inv)};
-            const u32x2 wb = {E::pack(o1[4 * q] * inv, o1[4 * q + 1] * inv),
-                              E::pack(o1[4 * q + 2] * inv, o1[4 * q + 3] * inv)};
-            *(u32x2 *)(orow + 8 * q + 4 * g) = wa;
-            *(u32x2 *)(orow + 32 + 8 * q + 4 * g) = wb;
-        }
+        store_out<E>(o0, o1, l_tot, orow, g);
         if (g == 0)
             lse[(int64_t)h * T + start + qi] = m_ref + logf(l_tot);
     }
