@@ -42,7 +42,14 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0         # HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flash_amd", "csrc", "vlf_attend.hip")
-KERNELS = {"direct": "attend_fwd", "prerotate": "attend_pre", "rotate": "prep_tiles"}
+KERNEL_NAMES = ("attend_pre_o4", "attend_pre", "attend_fwd", "attend_one", "prep_tiles")
+
+
+def forward_kernel(prerotate: bool, br: int) -> str:
+    """The library's forward kernel for a path and tile height (vlf_attend.hip's launchers)."""
+    if prerotate:
+        return "attend_pre_o4" if br == 256 else "attend_pre"
+    return "attend_one" if br == 64 else "attend_fwd"
 COPY_BYTES = 1 << 30
 
 
@@ -151,7 +158,7 @@ def run(args):
     prerotate = None if args.path == "auto" else args.path == "prerotate"
     batch = vlf.prepare(w.cu, dev, args.br, prerotate, w.window)
     path = "prerotate" if batch.prerotate else "direct"
-    kernel = KERNELS[path]
+    kernel = forward_kernel(batch.prerotate, batch.br)
     q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
     out = torch.empty((w.tokens, w.heads * 64), dtype=q.dtype, device=dev)
     lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
@@ -227,8 +234,7 @@ def run(args):
             "window": w.window, "rope_base": w.base, "scale": w.scale, "br": batch.br,
             "path": path,
             "kernel_ms": {kernel: round(kernel_ms, 4),
-                          **({KERNELS["rotate"]: round(rotate_ms, 4)} if batch.prerotate
-                             else {})},
+                          **({"prep_tiles": round(rotate_ms, 4)} if batch.prerotate else {})},
             **({"rotate_hbm_gbs_algorithmic": round(rotate_bytes / (rotate_ms / 1e3) / 1e9, 1)}
                if batch.prerotate else {}),
             "visible_pairs_per_head": pairs, "effective_flop": flops,
@@ -267,8 +273,8 @@ def summarize(directories, workload: str, kernel: str):
     per = {}  # (counter, kind) -> list of per-dispatch values (KiB)
     for r in rows:
         name = r.get("Kernel_Name", "")
-        kind = "attend" if kernel in name else ("copy" if "copybuffer" in name.lower()
-                                                else None)
+        kind = "attend" if f"::{kernel}<" in name else ("copy" if "copybuffer" in name.lower()
+                                                        else None)
         if kind is None:
             continue
         per.setdefault((r["Counter_Name"], kind, r.get("Dispatch_Id", "")), 0.0)
@@ -309,7 +315,7 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "direct", "prerotate"],
                     help="direct: every workgroup rotates its key tiles; prerotate: key-tile "
                          "workspace (default: chosen from the longest sequence)")
-    ap.add_argument("--kernel", default=KERNELS["prerotate"], choices=sorted(KERNELS.values()),
+    ap.add_argument("--kernel", default="attend_pre_o4", choices=KERNEL_NAMES,
                     help="kernel whose counters --summarize reads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
