@@ -1032,7 +1032,10 @@ attend_pre_o4(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
             hi = i0 + BR + window - 1;
     }
     const int ntiles = (hi - lo + BC - 1) / BC;
-    const int offset = window > 0 ? 0 : (int)((int64_t)(i0 / BR) * ntiles / ((len + BR - 1) / BR));
+    // every query tile sweeps its keys in order: the tiles of one (sequence, head) then read
+    // the same blocks at about the same time, which keeps two such pairs per XCD within its L2
+    // (the staggered start of attend_fwd measured 1% slower here)
+    const int offset = 0;
     auto key = [&](int t) {
         int u = t + offset;
         if (u >= ntiles)
