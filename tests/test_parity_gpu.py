@@ -310,3 +310,28 @@ def test_key_rotation_ties_round_like_the_page(br, prerotate):
     err = float(np.abs(lse - want).max())
     _say(f"[parity] key ties br={br} pre={int(prerotate)}: lse {err:.2e} (tol 2e-5)")
     assert err < 2e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("factor", [6.0, 12.0])
+@pytest.mark.parametrize("window", [0, 300])
+def test_outlying_key_norms(dtype, factor, window):
+    """A few keys scaled far beyond the rest loosen the norm bound of every score in their
+    tiles' sweeps. With the factor 6 a bfloat16 row's reference on the 256-row workspace path
+    can sit some 30 above its largest score (probabilities near e^-30); with 12, and for every
+    fp16 row whose bound is loose, the kernel first sweeps the scores for the exact row
+    maximum. Every row must match the oracle on both paths and at every tile height."""
+    w = workloads.custom([700, 300, 65], 2, dtype=dtype, window=window, table_rows=1024,
+                         seed=41)
+    qkv, cos, sin = inputs(w)
+    x = qkv.float()
+    H = w.heads
+    for t in (3, 350, 699, 830, 1007):
+        x[t, H * 64:2 * H * 64] *= factor
+    qkv = x.to(qkv.dtype)
+    for br in (64, 128, 256):
+        for pre in PATHS:
+            _say(f"case outlying keys {dtype} x{factor} W={window} br={br} prerotate={pre}")
+            out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=pre)
+            compare(f"outlying keys {dtype} x{factor} W={window} br={br} pre={int(pre)}", w,
+                    out, lse, qkv, cos, sin)

@@ -74,6 +74,9 @@ struct BF16 {
     // headroom of the workspace path's reference maximum (natural-log units): probabilities stay
     // below e^16, far inside bfloat16's range
     static constexpr float TAU_PRE = 16.0f;
+    // a fixed reference may sit up to this far above a row's largest score: bfloat16 has
+    // float32's exponent range, so e^-40 times the probabilities stays normal
+    static constexpr float FIX_SLACK = 40.0f;
     static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
     static __device__ __forceinline__ float hi(uint32_t w) {
         return __uint_as_float(w & 0xffff0000u);
@@ -91,6 +94,9 @@ struct BF16 {
 struct F16 {
     // e^10 < 65504 (the largest binary16 value), so a rounded probability cannot overflow
     static constexpr float TAU_PRE = 10.0f;
+    // a fixed reference never exceeds a row's largest score: the largest probability stays at
+    // least 1, as with the running maximum, and small ones keep binary16's normal range
+    static constexpr float FIX_SLACK = 0.0f;
     static __device__ __forceinline__ float lo(uint32_t w) {
         return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
     }
@@ -378,6 +384,20 @@ __device__ __forceinline__ void mask_scores(f32x16 &s0, f32x16 &s1, int j0, int 
     }
 }
 
+// Maximum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+        x = __builtin_fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// Whether a key-sweep step is the first of its sweep (attend_pre_o4).
+template <bool F>
+struct FirstStep {
+    static constexpr bool value = F;
+};
+
 // Row maximum over the 64-key tile, shared by lanes n and n + 32.
 __device__ __forceinline__ float row_max(const f32x16 &s0, const f32x16 &s1) {
     float mx = __builtin_fmaxf(s0[0], s1[0]);
@@ -402,6 +422,92 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // Margin on a computed norm: the float32 sum of 64 squares and v_sqrt_f32 are each within a few
 // ulp, so a factor 1 + 2^-10 makes the result an upper bound of the exact norm.
 constexpr float NORM_MARGIN = 1.0f + 1.0f / 1024.0f;
+
+// ---- the fixed reference maximum of the workspace path ----------------------------------------
+// A sweep over pre-rotated key tiles fixes each row's reference maximum before its loop, so no
+// step takes a row maximum or rescales the accumulators (the reference cancels in O / l and
+// returns in lse = m_ref + ln l). Every score of the row is at most bq = |q~| times the largest
+// key norm among the swept blocks (both upper bounds), so a reference at or above bq - TAU_PRE
+// keeps each probability within e^TAU_PRE. With m0 any value no larger than the row's largest
+// score, max(m0, bq - TAU_PRE) also keeps the row's largest probability at least e^-FIX_SLACK
+// when bq - TAU_PRE - m0 <= FIX_SLACK. Where that fails for a row, its wave first sweeps the
+// scores alone for the exact row maximum and takes that as the reference.
+
+// Largest key norm bound among the ntiles blocks from knorm[kb]: the first 128 are read before
+// the caller's copies start (kn0, kn1), the rest after.
+__device__ __forceinline__ void key_norm_reads(const float *knorm, int kb, int ntiles, int lane,
+                                               float &kn0, float &kn1) {
+    kn0 = lane < ntiles ? knorm[kb + lane] : 0.f;
+    kn1 = lane + 64 < ntiles ? knorm[kb + lane + 64] : 0.f;
+}
+__device__ __forceinline__ float key_norm_max(const float *knorm, int kb, int ntiles, int lane,
+                                              float kn0, float kn1) {
+    float kmax = __builtin_fmaxf(kn0, kn1);
+    for (int u = lane + 128; u < ntiles; u += 64)
+        kmax = __builtin_fmaxf(kmax, knorm[kb + u]);
+    return wave_max(kmax);
+}
+
+// Score of row qi with its own key (always visible), from the workspace block that holds it;
+// -inf for rows past the sequence. Shared by lanes n and n + 32.
+template <class E>
+__device__ __forceinline__ float own_score(const uint8_t *wblock, const u32x4 (&qop)[4], int qi,
+                                           int len, int g) {
+    float d = 0.f;
+    if (qi < len) {
+        const int r = qi % BC;
+        const uint8_t *krow = wblock + (int64_t)(qi / BC) * BLK + r * 128;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 kw = *(const u32x4 *)(krow + 16 * ((2 * c + g) ^ swz(r)));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                d = __builtin_fmaf(E::lo(qop[c][w]), E::lo(kw[w]), d);
+                d = __builtin_fmaf(E::hi(qop[c][w]), E::hi(kw[w]), d);
+            }
+        }
+    }
+    d = pair_sum(d);
+    return qi < len ? d : -__builtin_inff();
+}
+
+// The reference of each row of a wave: m_tile is the row maximum of one swept tile (masked),
+// s_own the row's own score, bq its score bound. `exact` returns the exact row maximum.
+template <class E, class Exact>
+__device__ __forceinline__ float fixed_reference(float m_tile, float s_own, float bq, bool valid,
+                                                 Exact exact) {
+    const float m0 = __builtin_fmaxf(m_tile, s_own);
+    const bool ok = !valid || bq - E::TAU_PRE - m0 <= E::FIX_SLACK;
+    if (__builtin_amdgcn_ballot_w64(!ok))
+        return exact();
+    return __builtin_fmaxf(m0, bq - E::TAU_PRE);
+}
+
+// Exact row maximum over tiles key(0) .. key(ntiles - 1): the scores alone, each tile's key
+// image read from its workspace block in global memory (the same bytes and products as the
+// sweep's, so the same scores).
+template <class E, class KeyF, class EdgeF>
+__device__ __forceinline__ float exact_row_max(const uint8_t *wblock,
+                                                         const u32x4 (&qop)[4],
+                                                         const int (&cof)[4], int ntiles,
+                                                         KeyF key, EdgeF edge, int len,
+                                                         int window, int qi, int g) {
+    float mx = -__builtin_inff();
+    for (int u = 0; u < ntiles; ++u) {
+        const int ju = key(u);
+        const uint8_t *kg = wblock + (int64_t)(ju / BC) * BLK;
+        f32x16 a0 = {}, a1 = {};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            a0 = E::mfma(*(const u32x4 *)(kg + cof[c]), qop[c], a0);
+            a1 = E::mfma(*(const u32x4 *)(kg + 4096 + cof[c]), qop[c], a1);
+        }
+        if (edge(ju))
+            mask_scores(a0, a1, ju, len, window, qi, g);
+        mx = __builtin_fmaxf(mx, row_max(a0, a1));
+    }
+    return mx;
+}
 
 // One workgroup per (block, head) writes that block: keys rotated and rounded exactly as the
 // staging of the other path does, values transposed; keys past the sequence are zero. It also
@@ -810,16 +916,20 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     // the blocks' key norm bounds: every score of tile t is at most qn * knorm[key(t) / BC]
     const float *knorm = (const float *)(ws + (int64_t)H * NB * BLK) + (int64_t)h * NB +
                          start / BC + (int)seq;
+    float kn0, kn1;
+    key_norm_reads(knorm, lo / BC, ntiles, lane, kn0, kn1);
     asm volatile("" ::: "memory");
     copy(0, 0);
     if (ntiles > 1)
         copy(1, 1);
-    if (ntiles > 2) {
+    if (ntiles > 2)
         copy(2, 2);
+    // upper bound of every score of this row
+    const float bq = qn * key_norm_max(knorm, lo / BC, ntiles, lane, kn0, kn1);
+    if (ntiles > 2)
         ring_barrier<PIECES>();
-    } else {
+    else
         ring_barrier<0>();
-    }
 
     // byte offset of operand chunk 2kc + g of row n (and of row 32 + n, 4096 further on)
     int cof[4];
@@ -848,46 +958,29 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         }
     };
 
-    float m_ref = -__builtin_inff();
     float l_run = 0.f;
     f32x16 o0 = {}, o1 = {};
     f32x16 sa0, sa1, sb0, sb1;
-
-    // Raise the reference maximum where tile scores (maximum mx) exceed it by more than
-    // TAU_PRE, rescaling l and O (whole wave skipped when no row needs it). Lanes that keep it
-    // scale by exactly 1 (their m_ref may still be -inf, where the difference would be NaN); a
-    // first reference scales the zero state by 0.
-    auto raise_ref = [&](float mx) {
-        const bool raise = mx > m_ref + E::TAU_PRE;
-        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * LOG2E) : 1.0f;
-        m_ref = raise ? mx : m_ref;
-        l_run *= alpha;
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                o0[i] *= alpha;
-                o1[i] *= alpha;
-            }
-        }
-    };
-
     kscores(0, sa0, sa1);
     if (edge(key(0)))
         mask_scores(sa0, sa1, key(0), len, window, qi, g);
-    raise_ref(row_max(sa0, sa1));
+    const float m_ref =
+        fixed_reference<E>(row_max(sa0, sa1), own_score<E>(wblock, qop, qi, len, g), bq,
+                           qi < len, [&] {
+                               return exact_row_max<E>(wblock, qop, cof, ntiles, key, edge, len,
+                                                       window, qi, g);
+                           });
+    const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
 
-    // Step t with tile t in slot cur (cur = t % 4, a constant after unrolling): as in
-    // attend_fwd, plus the copy of tile t+3 and the ring wait, but the reference is raised for
-    // tile t+1 at the end of step t (after tile t's output product), so that the body from the
-    // scores of t+1 to the row sum of t is one branch-free stretch for the scheduler.
+    // Step t with tile t in slot cur (cur = t % 4, a constant after unrolling): the scores of
+    // tile t+1 alongside the softmax and output product of tile t, the copy of tile t+3 and the
+    // ring wait. With the reference fixed the body is one branch-free stretch.
     auto step = [&](f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, int t, int cur) {
         const int nxt = (cur + 1) & 3;
         const bool more = t + 3 < ntiles;
         if (more)
             copy(t + 3, (cur + 3) & 3);
         const int j1 = key(t + 1);
-        const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
-
         kscores(nxt, n0, n1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -919,17 +1012,11 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         for (int i = 0; i < 16; ++i)
             rs += c0[i] + c1[i];
         l_run += rs;
+        // keep the sum in its step (the compiler would defer it and hold the probabilities)
+        asm volatile("" : "+v"(l_run));
         // past the last tile the scores of "tile t+1" come from a stale slot: never used
-        if (t + 1 < ntiles) {
-            if (edge(j1))
-                mask_scores(n0, n1, j1, len, window, qi, g);
-            // the row maximum only matters when it could raise the reference: skip it for the
-            // whole wave when the norm bound keeps every row's scores within TAU_PRE of its
-            // reference
-            const bool bounded = qn * knorm[j1 / BC] <= m_ref + E::TAU_PRE;
-            if (__builtin_amdgcn_ballot_w64(!bounded))
-                raise_ref(row_max(n0, n1));
-        }
+        if (t + 1 < ntiles && edge(j1))
+            mask_scores(n0, n1, j1, len, window, qi, g);
         if (more)
             ring_barrier<PIECES>();
         else
@@ -1072,19 +1159,22 @@ attend_pre_o4(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
     }
     const float *knorm = (const float *)(ws + (int64_t)H * NB * BLK) + (int64_t)h * NB +
                          start / BC + (int)seq;
+    float kn0, kn1;
+    key_norm_reads(knorm, lo / BC, ntiles, lane, kn0, kn1);
     asm volatile("" ::: "memory");
     // tiles 0 .. 2 in flight; tile 0 must land before step 0
     copy(0, 0);
     if (ntiles > 1)
         copy(1, 1);
-    if (ntiles > 2) {
+    if (ntiles > 2)
         copy(2, 2);
+    const float bq = qn * key_norm_max(knorm, lo / BC, ntiles, lane, kn0, kn1);
+    if (ntiles > 2)
         ring_barrier<2 * PIECES>();
-    } else if (ntiles > 1) {
+    else if (ntiles > 1)
         ring_barrier<PIECES>();
-    } else {
+    else
         ring_barrier<0>();
-    }
     int cof[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
@@ -1093,36 +1183,41 @@ attend_pre_o4(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
         return (j0 + BC > len) ||
                (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window));
     };
+    // reference maximum fixed at the first step
     float m_ref = -__builtin_inff();
+    const float s_own = own_score<E>(wblock, qop, qi, len, g);
     float l_run = 0.f;
     f32x16 o0 = {}, o1 = {};
-    auto step = [&](int t, int cur) {
+    auto step = [&](int t, int cur, auto mode) __attribute__((always_inline)) {
+        constexpr bool first = decltype(mode)::value;
         if (t + 3 < ntiles)
             copy(t + 3, (cur + 3) & 3);
         const int j0 = key(t);
         const uint8_t *kt = ring + cur * BLK;
+        // all operand reads of the key image first, then the products
+        u32x4 kop[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            kop[2 * c] = *(const u32x4 *)(kt + cof[c]);
+            kop[2 * c + 1] = *(const u32x4 *)(kt + 4096 + cof[c]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s0 = {}, s1 = {};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            s0 = E::mfma(*(const u32x4 *)(kt + cof[c]), qop[c], s0);
-            s1 = E::mfma(*(const u32x4 *)(kt + 4096 + cof[c]), qop[c], s1);
+            s0 = E::mfma(kop[2 * c], qop[c], s0);
+            s1 = E::mfma(kop[2 * c + 1], qop[c], s1);
         }
+        const uint8_t *vt = kt + IMG;
+        const u32x4 va0 = *(const u32x4 *)(vt + cof[0]);
+        const u32x4 vb0 = *(const u32x4 *)(vt + 4096 + cof[0]);
+        __builtin_amdgcn_sched_barrier(0);
         if (edge(j0))
             mask_scores(s0, s1, j0, len, window, qi, g);
-        if (__builtin_amdgcn_ballot_w64(!(qn * knorm[j0 / BC] <= m_ref + E::TAU_PRE))) {
-            const float mx = row_max(s0, s1);
-            const bool raise = mx > m_ref + E::TAU_PRE;
-            const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * LOG2E) : 1.0f;
-            m_ref = raise ? mx : m_ref;
-            l_run *= alpha;
-            if (__builtin_amdgcn_ballot_w64(raise)) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    o0[i] *= alpha;
-                    o1[i] *= alpha;
-                }
-            }
-        }
+        if constexpr (first)
+            m_ref = fixed_reference<E>(row_max(s0, s1), s_own, bq, qi < len, [&] {
+                return exact_row_max<E>(wblock, qop, cof, ntiles, key, edge, len, window, qi, g);
+            });
         const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -1143,9 +1238,13 @@ attend_pre_o4(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
         for (int i = 0; i < 16; ++i)
             rs += s0[i] + s1[i];
         l_run += rs;
-        const uint8_t *vt = kt + IMG;
+        // keep the sum in its step: otherwise the compiler defers the sums of several steps to
+        // the loop's end and spills their probabilities meanwhile
+        asm volatile("" : "+v"(l_run));
+        o0 = E::mfma(va0, pk[0], o0);
+        o1 = E::mfma(vb0, pk[0], o1);
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
+        for (int kc = 1; kc < 4; ++kc) {
             o0 = E::mfma(*(const u32x4 *)(vt + cof[kc]), pk[kc], o0);
             o1 = E::mfma(*(const u32x4 *)(vt + 4096 + cof[kc]), pk[kc], o1);
         }
@@ -1158,19 +1257,20 @@ attend_pre_o4(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
         else
             ring_barrier<0>();
     };
-    int t = 0;
+    step(0, 0, FirstStep<true>{});
+    int t = 1;
     for (; t + 3 < ntiles; t += 4) {
-        step(t, 0);
-        step(t + 1, 1);
-        step(t + 2, 2);
-        step(t + 3, 3);
+        step(t, 1, FirstStep<false>{});
+        step(t + 1, 2, FirstStep<false>{});
+        step(t + 2, 3, FirstStep<false>{});
+        step(t + 3, 0, FirstStep<false>{});
     }
     if (t < ntiles)
-        step(t, 0);
+        step(t, 1, FirstStep<false>{});
     if (t + 1 < ntiles)
-        step(t + 1, 1);
+        step(t + 1, 2, FirstStep<false>{});
     if (t + 2 < ntiles)
-        step(t + 2, 2);
+        step(t + 2, 3, FirstStep<false>{});
     const float l_tot = pair_sum(l_run);
     if (qi < len) {
         uint16_t *orow = out + (int64_t)(start + qi) * hd + h * D;
