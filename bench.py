@@ -42,13 +42,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0         # HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flash_amd", "csrc", "vlf_attend.hip")
-KERNEL_NAMES = ("attend_pre_o4", "attend_pre", "attend_fwd", "attend_one", "prep_tiles")
+KERNEL_NAMES = ("attend_pre_ph", "attend_pre", "attend_fwd", "attend_one", "prep_tiles")
 
 
 def forward_kernel(prerotate: bool, br: int) -> str:
     """The library's forward kernel for a path and tile height (vlf_attend.hip's launchers)."""
     if prerotate:
-        return "attend_pre_o4" if br == 256 else "attend_pre"
+        return "attend_pre_ph" if br == 256 else "attend_pre"
     return "attend_one" if br == 64 else "attend_fwd"
 COPY_BYTES = 1 << 30
 
@@ -315,7 +315,7 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "direct", "prerotate"],
                     help="direct: every workgroup rotates its key tiles; prerotate: key-tile "
                          "workspace (default: chosen from the longest sequence)")
-    ap.add_argument("--kernel", default="attend_pre_o4", choices=KERNEL_NAMES,
+    ap.add_argument("--kernel", default="attend_pre_ph", choices=KERNEL_NAMES,
                     help="kernel whose counters --summarize reads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)

@@ -19,10 +19,13 @@
  *   - Pointers marked "host" are read by the CPU during the call only. Pointers marked
  *     "device" are HIP device memory owned by the caller; the library keeps no reference after
  *     the call returns and allocates no device memory.
- *   - Two ways to run the forward share every result bit for bit: with a workspace the keys
- *     are rotated once per call into 64-key tile images that every query tile then streams
- *     (the faster choice when sequences span several query tiles); without one every
- *     workgroup rotates the key tiles it reads.
+ *   - There are two ways to run the forward. With a workspace, the keys are rotated once per
+ *     call into 64-key tile images that every query tile then streams; this is the faster
+ *     choice when sequences span several query tiles. Without one, every workgroup rotates the
+ *     key tiles it reads. Both round the same operands and run the same products. They may
+ *     subtract different reference maxima before the exp, which cancel in the results, so the
+ *     probabilities are rounded at different scales: lse agrees to float32 rounding and out
+ *     to about one storage-type ulp.
  */
 #ifndef VLF_H
 #define VLF_H

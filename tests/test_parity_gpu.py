@@ -161,9 +161,9 @@ def test_edge_batches(lens, prerotate):
                                             ("ragged", 256, 200), ("encoder", 128, 0),
                                             ("sliding", 256, 128), ("long", 256, 0)])
 def test_paths_agree(name, br, window):
-    """Both paths stage the same rounded operands and run the same products. They may keep
-    different reference maxima (the workspace path skips the row maximum where a norm bound
-    shows it cannot matter), so the probabilities are rounded at different scales: lse, from
+    """Both paths stage the same rounded operands and run the same products. They keep
+    different reference maxima (the workspace path fixes each row's reference from a norm
+    bound before its key loop), so the probabilities are rounded at different scales: lse, from
     the same unrounded sums, agrees to float32 rounding; out to about one bf16 ulp."""
     if name == "ragged":
         w = workloads.custom(RAGGED, 3, dtype="bf16", window=window, table_rows=512, seed=13)

@@ -392,9 +392,9 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
-// Whether a key-sweep step is the first of its sweep (attend_pre_o4).
+// Which wave group a sweep of attend_pre_ph runs for (true: the late group).
 template <bool F>
-struct FirstStep {
+struct LateGroup {
     static constexpr bool value = F;
 };
 
@@ -1069,20 +1069,18 @@ int launch_rotate(const AttendArgs &a) {
     return VLF_OK;
 }
 
-// The workspace path at 256 rows: eight waves, four waves per SIMD (two workgroups per CU, 2 x
-// 64 KB of LDS). Step t computes the scores of tile t, its softmax and its output product in
-// order, without attend_pre's score ping-pong; that frees the registers for the doubled
-// occupancy, and the other waves on a SIMD cover each wave's load and dependency latencies
-// (measured 4.6% faster than the ping-pong at two waves per SIMD on the long workload).
-// Tile t+3 is copied at the start of step t into the slot tile t-1 left; the end of step t
-// waits for tile t+1 only, so every copy has three steps to land.
+// The workspace path at 256 rows in two wave groups half a step apart (waves 0-3 and 4-7, one
+// of each on every SIMD): while one group runs a phase of matrix products (tile t's output
+// product, tile t+1's scores) the other runs a softmax phase, so the vector instructions of one
+// wave issue while the matrix unit works for the other (a wave's own products and vector work
+// do not overlap). Four waves per SIMD (two workgroups per CU, 2 x 64 KB of LDS).
 template <class E>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
-attend_pre_o4(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
-          const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
-          const uint32_t *__restrict__ tiles, const uint8_t *__restrict__ ws,
-          uint16_t *__restrict__ out, float *__restrict__ lse, int32_t num_tiles, int32_t T,
-          int32_t S, int32_t H, int32_t P, int32_t NB, int32_t window, float scale) {
+attend_pre_ph(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+              const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+              const uint32_t *__restrict__ tiles, const uint8_t *__restrict__ ws,
+              uint16_t *__restrict__ out, float *__restrict__ lse, int32_t num_tiles, int32_t T,
+              int32_t S, int32_t H, int32_t P, int32_t NB, int32_t window, float scale) {
     constexpr int NW = 8;
     constexpr int BR = 32 * NW;
     constexpr int RING = 4;
@@ -1183,48 +1181,49 @@ attend_pre_o4(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
         return (j0 + BC > len) ||
                (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window));
     };
-    // reference maximum fixed at the first step
-    float m_ref = -__builtin_inff();
+    // the two groups: waves 0-3 and 4-7 (one of each on every SIMD)
+    const bool late = __builtin_amdgcn_readfirstlane(wv) >= 4;
+    float m_ref = -__builtin_inff(), mb = 0.f;
     const float s_own = own_score<E>(wblock, qop, qi, len, g);
     float l_run = 0.f;
-    f32x16 o0 = {}, o1 = {};
-    auto step = [&](int t, int cur, auto mode) __attribute__((always_inline)) {
-        constexpr bool first = decltype(mode)::value;
-        if (t + 3 < ntiles)
-            copy(t + 3, (cur + 3) & 3);
+    f32x16 o0 = {}, o1 = {}, s0, s1;
+    u32x4 pk[4];
+    auto plain_barrier = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // scores of the key tile in slot sl into s0, s1
+    auto scores = [&](int sl) __attribute__((always_inline)) {
+        const uint8_t *kt = ring + sl * BLK;
+        s0 = f32x16{};
+        s1 = f32x16{};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            s0 = E::mfma(*(const u32x4 *)(kt + cof[c]), qop[c], s0);
+            s1 = E::mfma(*(const u32x4 *)(kt + 4096 + cof[c]), qop[c], s1);
+        }
+    };
+    // tile 0's scores and the reference
+    auto first = [&]() __attribute__((always_inline)) {
+        scores(0);
+        if (edge(key(0)))
+            mask_scores(s0, s1, key(0), len, window, qi, g);
+        m_ref = fixed_reference<E>(row_max(s0, s1), s_own, bq, qi < len, [&] {
+            return exact_row_max<E>(wblock, qop, cof, ntiles, key, edge, len, window, qi, g);
+        });
+        mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
+    };
+    // softmax of tile t (scores in s0, s1; tile 0 was masked by first()): pk and the row sum
+    auto softmax = [&](int t) __attribute__((always_inline)) {
         const int j0 = key(t);
-        const uint8_t *kt = ring + cur * BLK;
-        // all operand reads of the key image first, then the products
-        u32x4 kop[8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            kop[2 * c] = *(const u32x4 *)(kt + cof[c]);
-            kop[2 * c + 1] = *(const u32x4 *)(kt + 4096 + cof[c]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 s0 = {}, s1 = {};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            s0 = E::mfma(kop[2 * c], qop[c], s0);
-            s1 = E::mfma(kop[2 * c + 1], qop[c], s1);
-        }
-        const uint8_t *vt = kt + IMG;
-        const u32x4 va0 = *(const u32x4 *)(vt + cof[0]);
-        const u32x4 vb0 = *(const u32x4 *)(vt + 4096 + cof[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (edge(j0))
+        if (t > 0 && edge(j0))
             mask_scores(s0, s1, j0, len, window, qi, g);
-        if constexpr (first)
-            m_ref = fixed_reference<E>(row_max(s0, s1), s_own, bq, qi < len, [&] {
-                return exact_row_max<E>(wblock, qop, cof, ntiles, key, edge, len, window, qi, g);
-            });
-        const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], LOG2E, -mb));
             s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], LOG2E, -mb));
         }
-        u32x4 pk[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             pk[0][k] = E::pack(s0[2 * k], s0[2 * k + 1]);
@@ -1232,45 +1231,87 @@ attend_pre_o4(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
             pk[2][k] = E::pack(s1[2 * k], s1[2 * k + 1]);
             pk[3][k] = E::pack(s1[8 + 2 * k], s1[8 + 2 * k + 1]);
         }
-        // row sum before the output product: the unrounded probabilities die earlier
         float rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             rs += s0[i] + s1[i];
         l_run += rs;
-        // keep the sum in its step: otherwise the compiler defers the sums of several steps to
-        // the loop's end and spills their probabilities meanwhile
+        // keep the sum in its phase (the compiler would defer it and hold the probabilities)
         asm volatile("" : "+v"(l_run));
-        o0 = E::mfma(va0, pk[0], o0);
-        o1 = E::mfma(vb0, pk[0], o1);
+    };
+    // output product of tile t (pk, slot cur), then the scores of tile t+1 (next slot)
+    // The products run at a raised wave priority: the arbiter then issues them ahead of the
+    // other group's vector work and the matrix unit idles less (measured 2.5% faster).
+    auto product = [&](int t, int cur) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        const uint8_t *vt = ring + cur * BLK + IMG;
 #pragma unroll
-        for (int kc = 1; kc < 4; ++kc) {
+        for (int kc = 0; kc < 4; ++kc) {
             o0 = E::mfma(*(const u32x4 *)(vt + cof[kc]), pk[kc], o0);
             o1 = E::mfma(*(const u32x4 *)(vt + 4096 + cof[kc]), pk[kc], o1);
         }
-        // tile t+1 must have landed (t+2, t+3 may stay in flight)
-        const int later = min(2, max(0, ntiles - (t + 2)));
-        if (later == 2)
-            ring_barrier<2 * PIECES>();
-        else if (later == 1)
+        if (t + 1 < ntiles)
+            scores((cur + 1) & 3);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // end of phase 2t+1: tile t+2 has landed (tile t+3, copied at phase 2t, may be in flight)
+    auto odd_end = [&](int t) __attribute__((always_inline)) {
+        if (t + 3 < ntiles)
             ring_barrier<PIECES>();
         else
             ring_barrier<0>();
     };
-    step(0, 0, FirstStep<true>{});
-    int t = 1;
-    for (; t + 3 < ntiles; t += 4) {
-        step(t, 1, FirstStep<false>{});
-        step(t + 1, 2, FirstStep<false>{});
-        step(t + 2, 3, FirstStep<false>{});
-        step(t + 3, 0, FirstStep<false>{});
-    }
-    if (t < ntiles)
-        step(t, 1, FirstStep<false>{});
-    if (t + 1 < ntiles)
-        step(t + 1, 2, FirstStep<false>{});
-    if (t + 2 < ntiles)
-        step(t + 2, 3, FirstStep<false>{});
+    // Global phase 2t: the early group runs tile t's product (and tile t+1's scores), the late
+    // group tile t's softmax; phase 2t+1: early softmax of t+1, late product of t. Every phase
+    // ends at a barrier. Tile t+3 is copied at phase 2t into the slot of tile t-1, whose last
+    // reads (the late group's product of t-1) ended with phase 2t-1; it is first read at phase
+    // 2t+4 and waited for at the end of phase 2t+3.
+    auto run = [&](auto late_group) __attribute__((always_inline)) {
+        constexpr bool LATE = decltype(late_group)::value;
+        auto phases = [&](int t, int cur) __attribute__((always_inline)) {
+            if (t + 3 < ntiles)
+                copy(t + 3, (cur + 3) & 3);
+            if constexpr (LATE)
+                softmax(t);
+            else
+                product(t, cur);
+            plain_barrier();
+            if constexpr (LATE) {
+                product(t, cur);
+            } else {
+                if (t + 1 < ntiles)
+                    softmax(t + 1);
+            }
+            odd_end(t);
+        };
+        // phases -2 and -1
+        if constexpr (LATE) {
+            plain_barrier();
+            first();
+        } else {
+            first();
+            plain_barrier();
+            softmax(0);
+        }
+        odd_end(-1);
+        int t = 0;
+        for (; t + 3 < ntiles; t += 4) {
+            phases(t, 0);
+            phases(t + 1, 1);
+            phases(t + 2, 2);
+            phases(t + 3, 3);
+        }
+        if (t < ntiles)
+            phases(t, 0);
+        if (t + 1 < ntiles)
+            phases(t + 1, 1);
+        if (t + 2 < ntiles)
+            phases(t + 2, 2);
+    };
+    if (late)
+        run(LateGroup<true>{});
+    else
+        run(LateGroup<false>{});
     const float l_tot = pair_sum(l_run);
     if (qi < len) {
         uint16_t *orow = out + (int64_t)(start + qi) * hd + h * D;
@@ -1299,7 +1340,7 @@ int launch_pre(const AttendArgs &a) {
                     (void *)&P,   (void *)&nb32, (void *)&W,   (void *)&scale};
     const void *fn;
     if constexpr (NW == 8)
-        fn = (const void *)attend_pre_o4<E>;
+        fn = (const void *)attend_pre_ph<E>;
     else
         fn = (const void *)attend_pre<E, NW>;
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(NW * 64), args, 0,
