@@ -335,3 +335,28 @@ def test_outlying_key_norms(dtype, factor, window):
             out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=pre)
             compare(f"outlying keys {dtype} x{factor} W={window} br={br} pre={int(pre)}", w,
                     out, lse, qkv, cos, sin)
+
+
+@functools.lru_cache(maxsize=1)
+def _wide_inputs():
+    """88 sequences of 1024 tokens, 64 heads, bf16, tables of 90112 rows: qkv spans 2.2 GB, so
+    byte offsets from its start pass 2^31 and the direct path builds a buffer descriptor per
+    key tile instead of one per sequence (its whole-sequence form needs every offset below
+    2^31)."""
+    w = workloads.custom([1024] * 88, 64, dtype="bf16", window=0, base=1.6e5, table_rows=90112,
+                         seed=23)
+    qkv, cos, sin = inputs(w)
+    return w, qkv, cos, sin
+
+
+@pytest.mark.parametrize("window", [0, 300])
+def test_offsets_past_2gib(window):
+    w, qkv, cos, sin = _wide_inputs()
+    assert qkv.numel() * 2 > 2 ** 31
+    w_rows = sample_rows(w, 128, 1200, seed=9)
+    assert w_rows[-1] == w.tokens - 1
+    for br, pre in ((64, False), (128, False), (256, False), (256, True)):
+        _say(f"case offsets past 2 GiB W={window} br={br} prerotate={pre}")
+        out, lse = run_gpu(w, qkv, cos, sin, br=br, window=window, prerotate=pre)
+        compare(f"qkv of 2.2 GB W={window} br={br} pre={int(pre)} ({len(w_rows)} rows)", w, out,
+                lse, qkv, cos, sin, rows=w_rows, window=window)
