@@ -147,7 +147,7 @@ def run(args):
     import variable_length_flash_amd as vlf
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+        print(f"bench.py measures one GPU; the library has no multi-GPU path (asked for "
               f"--gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
@@ -241,22 +241,30 @@ def run(args):
             "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "achieved_hbm_gbs_algorithmic": round(alg_bytes / (kernel_ms / 1e3) / 1e9, 1),
         },
-        "roofline": {
-            "kernel": kernel,
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "kernel_ms": round(kernel_ms, 4),
-            "algorithmic_bytes": alg_bytes,
-        },
+        "roofline": roofline(kernel, flops, alg_bytes, kernel_ms, traffic),
         "cpu_baseline": None,
     }
     if not args.profile_run and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, qkv, cos, sin, args.cpu_seconds, pairs)
     print(json.dumps(line), flush=True)
+
+
+def roofline(kernel: str, flops: float, alg_bytes: int, kernel_ms: float, traffic):
+    """The forward kernel against its bound: the matrix unit when the workload's arithmetic
+    intensity (effective FLOP per algorithmic byte) is above the ridge of the bf16 peak and HBM,
+    else HBM, with algorithmic bytes per launch over the kernel's average duration."""
+    seconds = kernel_ms / 1e3
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    common = {"kernel": kernel, "traffic": traffic, "kernel_ms": round(kernel_ms, 4),
+              "algorithmic_bytes": alg_bytes, "algorithmic_flop": flops,
+              "intensity_flop_per_byte": round(flops / alg_bytes, 1)}
+    if flops / alg_bytes >= ridge:
+        achieved = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), **common}
+    achieved = alg_bytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), **common}
 
 
 def summarize(directories, workload: str, kernel: str):
