@@ -360,3 +360,19 @@ def test_offsets_past_2gib(window):
         out, lse = run_gpu(w, qkv, cos, sin, br=br, window=window, prerotate=pre)
         compare(f"qkv of 2.2 GB W={window} br={br} pre={int(pre)} ({len(w_rows)} rows)", w, out,
                 lse, qkv, cos, sin, rows=w_rows, window=window)
+
+
+@pytest.mark.parametrize("window", [0, 1000])
+def test_fp16_long_sequences_on_the_workspace_path(window):
+    """Two sequences of 8192 tokens in fp16 on the workspace path. Its fixed reference may sit
+    no higher than a row's largest score for binary16, so with N(0, 1) inputs a share of waves
+    takes the exact-maximum sweep; sampled rows against the oracle."""
+    w = workloads.custom([8192, 8192], 4, dtype="fp16", window=window, base=1.6e5,
+                         table_rows=8192, seed=29)
+    qkv, cos, sin = inputs(w)
+    rows = sample_rows(w, 256, 900, seed=17)
+    for br in (128, 256):
+        _say(f"case fp16 long workspace W={window} br={br}")
+        out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=True)
+        compare(f"fp16 2 x 8192 W={window} br={br} pre=1 ({len(rows)} rows)", w, out, lse, qkv,
+                cos, sin, rows=rows)
