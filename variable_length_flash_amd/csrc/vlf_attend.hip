@@ -828,8 +828,11 @@ __device__ __forceinline__ void ring_barrier() {
 // that write LDS (no registers, no ALU work): tile t+3 is requested at the start of step t into
 // the slot tile t-1 left (every wave passed the barrier after its last read), and the end of
 // step t waits for tile t+2, so each copy has two steps to land.
+// At 64 rows (two waves) the compiler keeps part of the loop state in AGPRs and the kernel runs
+// one wave per SIMD; the binding never takes the workspace path at that height (its key span
+// is too short to repay the key tiles), so only an explicit request runs it.
 template <class E, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 1 : 2)))
 attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            const uint32_t *__restrict__ tiles, const uint8_t *__restrict__ ws,
