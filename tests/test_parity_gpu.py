@@ -376,3 +376,35 @@ def test_fp16_long_sequences_on_the_workspace_path(window):
         out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=True)
         compare(f"fp16 2 x 8192 W={window} br={br} pre=1 ({len(rows)} rows)", w, out, lse, qkv,
                 cos, sin, rows=rows)
+
+
+@pytest.mark.parametrize("prerotate", PATHS)
+@pytest.mark.parametrize("br", [64, 128, 256])
+def test_tile_order_and_foreign_entries(br, prerotate):
+    """The tile table is the launch order and may be any permutation of the canonical one; its
+    entries naming a sequence past S or a first row at or past the sequence end (including
+    2^32 - 1, read as -1) are skipped without writing anything."""
+    import dataclasses
+    lens = [300, 0, 77, 513, 1, 129]
+    w = workloads.custom(lens, 3, dtype="bf16", window=0, table_rows=600, seed=37)
+    qkv, cos, sin = inputs(w)
+    dev = torch.device("cuda:0")
+    batch = vlf.prepare(w.cu, dev, br, prerotate, 0)
+    canon = vlf.tile_table(w.cu, br).astype(np.int64)
+    rng = np.random.default_rng(br + 7 * int(prerotate))
+    foreign = np.array([[len(lens), 0], [len(lens) + 5, 0], [0, 300], [0, 300 + 64],
+                        [2, 77], [4, 2 ** 32 - 1], [1, 0]], dtype=np.int64)
+    table = np.concatenate([canon, foreign])[rng.permutation(len(canon) + len(foreign))]
+    tiles = torch.from_numpy(table.astype(np.uint32).view(np.int32)).to(dev).contiguous()
+    batch = dataclasses.replace(batch, tiles=tiles, num_tiles=len(table))
+    T, H = w.tokens, w.heads
+    out_buf = torch.full((T * H * 64 + GUARD,), float("nan"), dtype=qkv.dtype, device=dev)
+    lse_buf = torch.full((H * T + GUARD,), float("nan"), dtype=torch.float32, device=dev)
+    out = out_buf[:T * H * 64].view(T, H * 64)
+    lse = lse_buf[:H * T].view(H, T)
+    _say(f"case shuffled table br={br} prerotate={prerotate}")
+    vlf.attend_into(batch, qkv.to(dev), cos.to(dev), sin.to(dev), H, 0, w.scale, out, lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(out_buf[T * H * 64:]).all() and torch.isnan(lse_buf[H * T:]).all()
+    compare(f"shuffled table with foreign entries br={br} pre={int(prerotate)}", w,
+            out.float().cpu().numpy(), lse.cpu().numpy(), qkv, cos, sin)
