@@ -229,18 +229,28 @@ def test_attend_rotated_needs_a_workspace():
     assert rc == binding.VLF_EINVAL and "needs a workspace" in lib.vlf_last_error().decode()
 
 
-@pytest.mark.parametrize("max_len,window,br", [(1, 0, 64), (64, 0, 64), (65, 0, 128),
-                                               (1023, 0, 128), (1024, 0, 256), (8192, 0, 256),
-                                               (8192, 128, 128), (8192, 512, 128),
-                                               (8192, 513, 256), (64, 128, 64)])
-def test_choose_br(max_len, window, br):
-    assert vlf.choose_br(max_len, window) == br
+@pytest.mark.parametrize("max_len,window,typical,br", [
+    (1, 0, None, 64), (64, 0, None, 64), (65, 0, None, 128), (447, 0, None, 128),
+    (448, 0, None, 256), (8192, 0, None, 256), (8192, 128, None, 128), (8192, 512, None, 128),
+    (8192, 513, None, 256), (64, 128, None, 64),
+    # the typical length decides, not the longest sequence
+    (512, 0, 343.0, 128), (512, 0, 512.0, 256), (8192, 0, 300.0, 128), (65, 0, 30.0, 128)])
+def test_choose_br(max_len, window, typical, br):
+    assert vlf.choose_br(max_len, window, typical) == br
 
 
-@pytest.mark.parametrize("max_len,br,window,pre", [(8192, 256, 0, True), (512, 128, 0, True),
-                                                   (383, 128, 0, False), (8192, 128, 128, False),
-                                                   (8192, 128, 129, True), (64, 64, 0, False)])
-def test_choose_prerotate(max_len, br, window, pre):
-    # the workspace pays when a query tile's key span (the sequence, or br + 2W - 1) is at
-    # least three query tiles
-    assert vlf.choose_prerotate(max_len, br, window) is pre
+@pytest.mark.parametrize("length,br,window,pre", [
+    (8192, 256, 0, True), (512, 128, 0, True), (383, 128, 0, False), (343, 128, 0, False),
+    (8192, 128, 128, False), (8192, 128, 129, True), (64, 64, 0, False), (448, 256, 0, True),
+    (447, 256, 0, False), (2048, 256, 600, True)])
+def test_choose_prerotate(length, br, window, pre):
+    # the workspace pays when a query tile's key span (the typical length, or br + 2W - 1) is
+    # three query tiles at 128 rows, or 448 tokens at 256 rows
+    assert vlf.choose_prerotate(length, br, window) is pre
+
+
+@pytest.mark.parametrize("lens,want", [([], 0.0), ([0, 0], 0.0), ([5], 5.0), ([100, 156],
+                                       (100 ** 2 + 156 ** 2) / 256), ([512] * 32, 512.0)])
+def test_typical_length(lens, want):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    assert vlf.typical_length(cu) == pytest.approx(want)

@@ -254,7 +254,7 @@ def test_full_size_workload(name):
     vmax = float(qkv[:, 2 * w.heads * 64:].float().abs().max())
     assert np.abs(out).max() <= vmax * (1 + 2 ** -7)
     # lse >= the largest visible score is implied by l >= 1; lse <= max score + ln(keys)
-    br = vlf.choose_br(max(w.lens), w.window)
+    br = vlf.choose_br(max(w.lens), w.window, vlf.typical_length(w.cu))
     seed = {"encoder": 2, "sliding": 3, "many_short": 4, "long": 5}[name]
     rows = sample_rows(w, br, 1500 if name == "long" else 3000, seed=seed)
     compare(f"{name} ({len(rows)} sampled rows, all heads)", w, out, lse, qkv, cos, sin,

@@ -7,5 +7,5 @@ loudly when it is missing: there is no fallback path.
 from .binding import (  # noqa: F401
     Batch, VlfError, attend, attend_into, attend_rotated_into, choose_br, choose_prerotate,
     library_path, load_library, new_workspace, prepare, rotate_keys, tile_count, tile_table,
-    visible_pairs, workspace_bytes,
+    typical_length, visible_pairs, workspace_bytes,
 )

@@ -131,26 +131,38 @@ def workspace_bytes(tokens: int, sequences: int, heads: int) -> int:
     return int(out.value)
 
 
-def choose_prerotate(max_len: int, br: int, window: int = 0) -> bool:
-    """Rotate keys once into a workspace when one query tile's key span is at least three
-    query tiles long (the longest sequence, or the window's reach br + 2W - 1): each key tile
-    is then read by three or more workgroups per head, and streaming the pre-rotated images
-    beats rotating them again in every workgroup. Where each key tile is read about once or
-    twice (short sequences, narrow windows) the workspace only adds traffic."""
-    span = max_len if window <= 0 else min(max_len, br + 2 * window - 1)
-    return span >= 3 * br
+def typical_length(cu) -> float:
+    """The sequence length an average token sits in: sum(L^2) / sum(L) over the batch (0 for
+    an empty batch). Work per token grows with its sequence's length, so this, not the longest
+    sequence, is what the tile height and path choices below weigh."""
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    total = int(lens.sum())
+    return float((lens * lens).sum()) / total if total > 0 else 0.0
 
 
-def choose_br(max_len: int, window: int = 0) -> int:
+def choose_prerotate(length: float, br: int, window: int = 0) -> bool:
+    """Rotate keys once into a workspace when one query tile's key span (``length``, the
+    batch's typical length, or the window's reach br + 2W - 1) is long enough for each key tile
+    to be read by several workgroups per head: three query tiles at 64 and 128 rows, 448 tokens
+    (1.75 tiles) at 256 rows, whose workspace kernel is the most efficient one. Below that,
+    streaming pre-rotated images does not repay the pass that writes them (measured on batches
+    of 256-4096-token sequences, the encoder and the sliding-window workloads)."""
+    span = length if window <= 0 else min(length, br + 2 * window - 1)
+    return span >= (3 * br if br < 256 else 7 * br // 4)
+
+
+def choose_br(max_len: int, window: int = 0, typical: float | None = None) -> int:
     """Query rows per workgroup: 64 when no sequence is longer than 64 (one key tile per
     query tile: the unpipelined kernel); 128 under a window of at most 512 (a query tile's key
-    span is br + 2W - 1, so taller tiles compute more masked pairs); otherwise 256 from 1024
-    tokens on (fewer, longer key loops) and 128 in between."""
+    span is br + 2W - 1, so taller tiles compute more masked pairs); otherwise 256 when the
+    typical length (``typical``, default ``max_len``; see ``typical_length``) reaches 448
+    tokens (fewer, longer key loops on the most efficient kernel) and 128 below."""
+    typical = max_len if typical is None else typical
     if max_len <= 64:
         return 64
     if 0 < window <= 512:
         return 128
-    return 256 if max_len >= 1024 else 128
+    return 256 if typical >= 448 else 128
 
 
 @dataclass
@@ -178,14 +190,15 @@ def prepare(cu, device=None, br: int | None = None, prerotate: bool | None = Non
     """Validate ``cu``, build the tile table on the host and copy both to ``device``.
 
     ``br`` (query rows per tile) and ``prerotate`` (use a key-tile workspace) default to
-    ``choose_br`` and ``choose_prerotate`` of the longest sequence and ``window`` (the window
-    the batch will be run with; it only informs that choice)."""
+    ``choose_br`` and ``choose_prerotate`` of the longest sequence, the typical length and
+    ``window`` (the window the batch will be run with; it only informs that choice)."""
     import torch
     cu_host = _host_cu(cu)
     device = torch.device("cuda") if device is None else torch.device(device)
     _, max_len = tile_count(cu_host, 128)
-    br = choose_br(max_len, window) if br is None else int(br)
-    prerotate = (choose_prerotate(max_len, br, window) if prerotate is None
+    typical = typical_length(cu_host)
+    br = choose_br(max_len, window, typical) if br is None else int(br)
+    prerotate = (choose_prerotate(typical, br, window) if prerotate is None
                  else bool(prerotate))
     table = tile_table(cu_host, br)
     return Batch(cu_host, torch.from_numpy(cu_host).to(device),
