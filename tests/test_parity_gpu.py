@@ -220,6 +220,35 @@ def test_stream_and_repeat_are_deterministic():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+def test_explicit_stream_keeps_its_workspace():
+    """A launch on an explicit stream (torch stream or raw handle) while another stream is
+    current: the workspace the binding allocates belongs to the launch stream, so an allocation
+    of the same size made right after on the current stream, and overwritten there, cannot be
+    handed that memory while the kernels still read it."""
+    w = workloads.custom([300, 41, 999], 4, dtype="bf16", window=0, table_rows=1024, seed=9)
+    qkv, cos, sin = inputs(w)
+    dev = torch.device("cuda:0")
+    batch = vlf.prepare(w.cu, dev)
+    assert batch.prerotate
+    q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
+    nbytes = vlf.workspace_bytes(w.tokens, w.sequences, w.heads)
+    ref_o = torch.empty((w.tokens, w.heads * 64), dtype=qkv.dtype, device=dev)
+    ref_l = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
+    vlf.attend_into(batch, q, c, s, w.heads, 0, w.scale, ref_o, ref_l)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    for handle in (side, side.cuda_stream):
+        o = torch.empty_like(ref_o)
+        l = torch.empty_like(ref_l)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        vlf.attend_into(batch, q, c, s, w.heads, 0, w.scale, o, l, stream=handle)
+        clobber = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        clobber.fill_(0xFF)
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), f"stream={type(handle)}"
+
+
 def sample_rows(w, br, count, seed):
     """First / last rows of every sequence, rows at tile and wave boundaries of a spread of
     tiles, and random rows."""

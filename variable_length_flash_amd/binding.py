@@ -135,7 +135,7 @@ def typical_length(cu) -> float:
     """The sequence length an average token sits in: sum(L^2) / sum(L) over the batch (0 for
     an empty batch). Work per token grows with its sequence's length, so this, not the longest
     sequence, is what the tile height and path choices below weigh."""
-    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    lens = np.diff(_host_cu(cu).astype(np.int64))
     total = int(lens.sum())
     return float((lens * lens).sum()) / total if total > 0 else 0.0
 
@@ -273,9 +273,19 @@ def _workspace_args(workspace, dev):
     return workspace.data_ptr(), workspace.numel()
 
 
-def _stream(stream, dev):
+def _torch_stream(stream, dev):
+    """The launch stream as a torch stream: torch's current stream of ``dev`` (None), a
+    torch.cuda.Stream, or a raw hipStream_t handle."""
     import torch
-    return torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=dev)
+
+
+def _stream(stream, dev):
+    return _torch_stream(stream, dev).cuda_stream
 
 
 def attend_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: float, out, lse,
@@ -287,16 +297,21 @@ def attend_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: flo
     contiguous uint8 device tensor of at least ``workspace_bytes`` (from ``new_workspace``);
     when None and the batch pre-rotates, one is allocated for this call.
     """
+    import torch
     code = _check_inputs(batch, qkv, cos, sin, heads, out, lse)
     dev = qkv.device
+    launch = _torch_stream(stream, dev)
     if workspace is None and batch.prerotate:
-        workspace = new_workspace(batch, heads, dev)
+        # allocated on the launch stream: when this call returns the block goes back to that
+        # stream's pool, so its next user is ordered after these kernels
+        with torch.cuda.stream(launch):
+            workspace = new_workspace(batch, heads, dev)
     ws_ptr, ws_bytes = _workspace_args(workspace, dev)
     _check(load_library().vlf_attend(
         qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
         batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
         int(window), float(scale), code, ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
-        _stream(stream, dev)))
+        launch.cuda_stream))
 
 
 def rotate_keys(batch: Batch, qkv, cos, sin, heads: int, workspace, stream=None):
