@@ -254,3 +254,15 @@ def test_choose_prerotate(length, br, window, pre):
 def test_typical_length(lens, want):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     assert vlf.typical_length(cu) == pytest.approx(want)
+
+
+def test_tile_count_and_table_at_int32_extremes():
+    # one sequence of INT32_MAX - 1 tokens: tile counts for tile heights near INT32_MAX, where
+    # the row arithmetic must not wrap in 32 bits
+    big = 2 ** 31 - 2
+    cu = np.array([0, big], dtype=np.int32)
+    for br, want in ((2 ** 31 - 1, 1), (2 ** 30, 2), (big, 1), (big - 1, 2)):
+        assert vlf.tile_count(cu, br)[0] == want, br
+        table = vlf.tile_table(cu, br)
+        assert table.shape == (want, 2)
+        assert table[:, 1].tolist() == [i * br for i in range(want)]

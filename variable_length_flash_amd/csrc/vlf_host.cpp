@@ -79,7 +79,7 @@ int vlf_tile_count(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, int
         return rc;
     int64_t n = 0;
     for (int32_t s = 0; s < S; ++s)
-        n += (int64_t)(cu_host[s + 1] - cu_host[s] + br - 1) / br;
+        n += ((int64_t)(cu_host[s + 1] - cu_host[s]) + br - 1) / br;
     if (n > INT32_MAX)
         return fail(VLF_EINVAL, "%lld tiles exceed INT32_MAX", (long long)n);
     *num_tiles = (int32_t)n;
@@ -101,7 +101,7 @@ int vlf_tile_table(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, uin
     int64_t k = 0;
     for (int32_t s = 0; s < S; ++s) {
         const int32_t L = cu_host[s + 1] - cu_host[s];
-        for (int32_t i0 = 0; i0 < L; i0 += br) {
+        for (int64_t i0 = 0; i0 < L; i0 += br) {
             tiles_host[k++] = (uint32_t)s;
             tiles_host[k++] = (uint32_t)i0;
         }
