@@ -42,13 +42,18 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0         # HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flash_amd", "csrc", "vlf_attend.hip")
-KERNEL_NAMES = ("attend_pre_ph", "attend_pre", "attend_fwd", "attend_one", "prep_tiles")
+KERNEL_NAMES = ("attend_pre_ph", "attend_pre", "attend_fwd", "attend_one", "attend_slide",
+                "prep_tiles")
 
 
-def forward_kernel(prerotate: bool, br: int) -> str:
-    """The library's forward kernel for a path and tile height (vlf_attend.hip's launchers)."""
+def forward_kernel(prerotate: bool, br: int, window: int) -> str:
+    """The library's forward kernel for a path, tile height and window (vlf_attend.hip's
+    launchers)."""
+    from variable_length_flash_amd import binding
     if prerotate:
         return "attend_pre_ph" if br == 256 else "attend_pre"
+    if br == 256 and binding.window_fits_ring(window):
+        return "attend_slide"
     return "attend_one" if br == 64 else "attend_fwd"
 COPY_BYTES = 1 << 30
 
@@ -158,7 +163,7 @@ def run(args):
     prerotate = None if args.path == "auto" else args.path == "prerotate"
     batch = vlf.prepare(w.cu, dev, args.br, prerotate, w.window)
     path = "prerotate" if batch.prerotate else "direct"
-    kernel = forward_kernel(batch.prerotate, batch.br)
+    kernel = forward_kernel(batch.prerotate, batch.br, w.window)
     q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
     out = torch.empty((w.tokens, w.heads * 64), dtype=q.dtype, device=dev)
     lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)

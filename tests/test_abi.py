@@ -231,8 +231,11 @@ def test_attend_rotated_needs_a_workspace():
 
 @pytest.mark.parametrize("max_len,window,typical,br", [
     (1, 0, None, 64), (64, 0, None, 64), (65, 0, None, 128), (447, 0, None, 128),
-    (448, 0, None, 256), (8192, 0, None, 256), (8192, 128, None, 128), (8192, 512, None, 128),
+    (448, 0, None, 256), (8192, 0, None, 256), (8192, 512, None, 128),
     (8192, 513, None, 256), (64, 128, None, 64),
+    # windows of at most 129 keys: 256-row tiles on the key ring once sequences fill them
+    (8192, 1, None, 256), (8192, 128, None, 256), (8192, 129, None, 256), (8192, 130, None, 128),
+    (8192, 128, 255.0, 128), (300, 128, 256.0, 256),
     # the typical length decides, not the longest sequence
     (512, 0, 343.0, 128), (512, 0, 512.0, 256), (8192, 0, 300.0, 128), (65, 0, 30.0, 128)])
 def test_choose_br(max_len, window, typical, br):
@@ -242,11 +245,27 @@ def test_choose_br(max_len, window, typical, br):
 @pytest.mark.parametrize("length,br,window,pre", [
     (8192, 256, 0, True), (512, 128, 0, True), (383, 128, 0, False), (343, 128, 0, False),
     (8192, 128, 128, False), (8192, 128, 129, True), (64, 64, 0, False), (448, 256, 0, True),
-    (447, 256, 0, False), (2048, 256, 600, True)])
+    (447, 256, 0, False), (2048, 256, 600, True), (8192, 256, 128, False),
+    (8192, 256, 129, False), (8192, 256, 130, True)])
 def test_choose_prerotate(length, br, window, pre):
     # the workspace pays when a query tile's key span (the typical length, or br + 2W - 1) is
     # three query tiles at 128 rows, or 448 tokens at 256 rows
     assert vlf.choose_prerotate(length, br, window) is pre
+
+
+def test_window_fits_ring():
+    # brute force: the key tiles a 256-row tile at i0 (a multiple of 256, far from either
+    # sequence end) reaches under window W, against the eight-slot ring
+    for window in range(0, 400):
+        i0 = 4096
+        if window == 0:
+            want = False
+        else:
+            lo = (i0 + 1 - window) // 64 * 64
+            hi = i0 + 256 + window - 1
+            want = -(-(hi - lo) // 64) <= 8
+        assert binding.window_fits_ring(window) is want, window
+    assert binding.window_fits_ring(129) and not binding.window_fits_ring(130)
 
 
 @pytest.mark.parametrize("lens,want", [([], 0.0), ([0, 0], 0.0), ([5], 5.0), ([100, 156],

@@ -407,6 +407,61 @@ def test_fp16_long_sequences_on_the_workspace_path(window):
                 cos, sin, rows=rows)
 
 
+RUN_LENS = [9000, 0, 7001, 1, 300, 5000, 129, 64, 65]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("window", [1, 64, 127, 128, 129])
+def test_window_runs_keep_keys(dtype, window):
+    """Direct path, 256-row tiles, windows of at most 129 keys: one workgroup per CU walks a run
+    of (head, tile) items and keeps the window's key tiles in LDS from one item to the next.
+    1408 items, so every run spans several and crosses sequences (an empty one, one-row and
+    one-tile ones) and heads."""
+    w = workloads.custom(RUN_LENS, 16, dtype=dtype, window=window, base=1.6e5, table_rows=9000,
+                         seed=43)
+    qkv, cos, sin = inputs(w)
+    _say(f"case window runs {dtype} W={window}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=256, prerotate=False)
+    compare(f"window runs {dtype} W={window}", w, out, lse, qkv, cos, sin)
+
+
+@pytest.mark.parametrize("order", ["shuffled", "reversed", "doubled"])
+def test_window_runs_in_any_table_order(order):
+    """The kept key tiles follow the table order: a shuffled table (with entries that name no
+    tile), a reversed one and one that lists every tile twice in a row give the canonical
+    results."""
+    import dataclasses
+    lens = [3000, 0, 77, 2000, 1, 129, 700]
+    w = workloads.custom(lens, 24, dtype="bf16", window=100, table_rows=3000, seed=47)
+    qkv, cos, sin = inputs(w)
+    dev = torch.device("cuda:0")
+    batch = vlf.prepare(w.cu, dev, 256, False, w.window)
+    canon = vlf.tile_table(w.cu, 256).astype(np.int64)
+    if order == "shuffled":
+        foreign = np.array([[len(lens), 0], [0, 3000], [2, 77], [4, 2 ** 32 - 1], [1, 0]],
+                           dtype=np.int64)
+        table = np.concatenate([canon, foreign])
+        table = table[np.random.default_rng(5).permutation(len(table))]
+    elif order == "reversed":
+        table = canon[::-1]
+    else:
+        table = np.repeat(canon, 2, axis=0)
+    tiles = torch.from_numpy(np.ascontiguousarray(table).astype(np.uint32).view(np.int32))
+    batch = dataclasses.replace(batch, tiles=tiles.to(dev).contiguous(), num_tiles=len(table))
+    T, H = w.tokens, w.heads
+    out_buf = torch.full((T * H * 64 + GUARD,), float("nan"), dtype=qkv.dtype, device=dev)
+    lse_buf = torch.full((H * T + GUARD,), float("nan"), dtype=torch.float32, device=dev)
+    out = out_buf[:T * H * 64].view(T, H * 64)
+    lse = lse_buf[:H * T].view(H, T)
+    _say(f"case window runs, {order} table")
+    vlf.attend_into(batch, qkv.to(dev), cos.to(dev), sin.to(dev), H, w.window, w.scale, out,
+                    lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(out_buf[T * H * 64:]).all() and torch.isnan(lse_buf[H * T:]).all()
+    compare(f"window runs, {order} table", w, out.float().cpu().numpy(), lse.cpu().numpy(),
+            qkv, cos, sin)
+
+
 @pytest.mark.parametrize("prerotate", PATHS)
 @pytest.mark.parametrize("br", [64, 128, 256])
 def test_tile_order_and_foreign_entries(br, prerotate):

@@ -147,22 +147,38 @@ def choose_prerotate(length: float, br: int, window: int = 0) -> bool:
     (1.75 tiles) at 256 rows, whose workspace kernel is the most efficient one. Below that,
     streaming pre-rotated images does not repay the pass that writes them (measured on batches
     of 256-4096-token sequences, the encoder and the sliding-window workloads)."""
+    if br == 256 and window_fits_ring(window):
+        return False  # the direct path keeps such a window's keys in LDS (attend_slide)
     span = length if window <= 0 else min(length, br + 2 * window - 1)
     return span >= (3 * br if br < 256 else 7 * br // 4)
 
 
 def choose_br(max_len: int, window: int = 0, typical: float | None = None) -> int:
     """Query rows per workgroup: 64 when no sequence is longer than 64 (one key tile per
-    query tile: the unpipelined kernel); 128 under a window of at most 512 (a query tile's key
-    span is br + 2W - 1, so taller tiles compute more masked pairs); otherwise 256 when the
-    typical length (``typical``, default ``max_len``; see ``typical_length``) reaches 448
-    tokens (fewer, longer key loops on the most efficient kernel) and 128 below."""
+    query tile: the unpipelined kernel). Under a window of at most 129 keys, 256 when the
+    typical length (``typical``, default ``max_len``; see ``typical_length``) fills a 256-row
+    tile (the direct path then walks consecutive tiles with the window's keys held in LDS).
+    Otherwise 128 under a window of at most 512 (a query tile's key span is br + 2W - 1, so
+    taller tiles compute more masked pairs), and for full windows 256 when the typical length
+    reaches 448 tokens (fewer, longer key loops on the most efficient kernel), 128 below."""
     typical = max_len if typical is None else typical
     if max_len <= 64:
         return 64
+    if window_fits_ring(window) and typical >= 256:
+        return 256
     if 0 < window <= 512:
         return 128
     return 256 if typical >= 448 else 128
+
+
+def window_fits_ring(window: int) -> bool:
+    """Whether the direct path runs 256-row tiles under ``window`` on its LDS-resident key
+    ring (attend_slide): a tile's keys, from i0 - 64 ceil((W - 1) / 64) to i0 + 256 + W - 2,
+    must span at most eight 64-key tiles, which holds for 1 <= W <= 129."""
+    if window < 1:
+        return False
+    back = -(-(window - 1) // 64) * 64
+    return -(-(back + 256 + window - 1) // 64) <= 8
 
 
 @dataclass

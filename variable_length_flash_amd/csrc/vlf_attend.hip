@@ -312,37 +312,60 @@ __device__ __forceinline__ void stage_store(const TileRegs<NTHR> &r, const Stagi
     }
 }
 
+// Raw inputs of one lane's query operand: dims 8g .. 8g+7, 16+8g .., 32+8g .., 48+8g .. of the
+// query row and the table entries for dims 8g .., 16+8g .. at its position (zero past the
+// sequence).
+struct QueryRaw {
+    u32x4 x[4], c[2], s[2];
+};
+
+__device__ __forceinline__ void query_load(QueryRaw &r, const uint16_t *qkv,
+                                           const uint16_t *cos_t, const uint16_t *sin_t,
+                                           int64_t ld, int start, int qi, int len, int h, int g) {
+    u32x4 x0 = {0, 0, 0, 0}, x1 = x0, x2 = x0, x3 = x0, c0 = x0, c1 = x0, s0 = x0, s1 = x0;
+    if (qi < len) {
+        const uint16_t *qr = qkv + (int64_t)(start + qi) * ld + h * D + 8 * g;
+        x0 = *(const u32x4 *)qr;
+        x1 = *(const u32x4 *)(qr + 16);
+        x2 = *(const u32x4 *)(qr + 32);
+        x3 = *(const u32x4 *)(qr + 48);
+        const uint16_t *cr = cos_t + qi * 32 + 8 * g, *sr = sin_t + qi * 32 + 8 * g;
+        c0 = *(const u32x4 *)cr;
+        c1 = *(const u32x4 *)(cr + 16);
+        s0 = *(const u32x4 *)sr;
+        s1 = *(const u32x4 *)(sr + 16);
+    }
+    r.x[0] = x0, r.x[1] = x1, r.x[2] = x2, r.x[3] = x3;
+    r.c[0] = c0, r.c[1] = c1, r.s[0] = s0, r.s[1] = s1;
+}
+
 // Query operand of one 32-row block: rows rotated, scaled, rounded; rows past the sequence are
-// zero. Lane (n, g) holds, for k-step c, dims 16c + 8g .. 16c + 8g + 7 of its query.
+// zero (a zero row rotates to zero). Lane (n, g) holds, for k-step c, dims 16c + 8g .. 16c +
+// 8g + 7 of its query.
+template <class E>
+__device__ __forceinline__ void query_make(const QueryRaw &r, float scale, u32x4 (&qop)[4]) {
+    uint32_t y[4][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t x1[4] = {r.x[k][0], r.x[k][1], r.x[k][2], r.x[k][3]};
+        const uint32_t x2[4] = {r.x[k + 2][0], r.x[k + 2][1], r.x[k + 2][2], r.x[k + 2][3]};
+        const uint32_t c[4] = {r.c[k][0], r.c[k][1], r.c[k][2], r.c[k][3]};
+        const uint32_t s[4] = {r.s[k][0], r.s[k][1], r.s[k][2], r.s[k][3]};
+        rotate<E, 4>(x1, x2, c, s, scale, y[k], y[k + 2]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        qop[c] = u32x4{y[c][0], y[c][1], y[c][2], y[c][3]};
+}
+
 template <class E>
 __device__ __forceinline__ void query_operand(const uint16_t *qkv, const uint16_t *cos_t,
                                               const uint16_t *sin_t, int64_t ld, int start,
                                               int qi, int len, int h, int g, float scale,
                                               u32x4 (&qop)[4]) {
-    if (qi < len) {
-        const uint16_t *qr = qkv + (int64_t)(start + qi) * ld + h * D;
-        const u32x4 xa = *(const u32x4 *)(qr + 8 * g);
-        const u32x4 xb = *(const u32x4 *)(qr + 16 + 8 * g);
-        const u32x4 xc = *(const u32x4 *)(qr + 32 + 8 * g);
-        const u32x4 xd = *(const u32x4 *)(qr + 48 + 8 * g);
-        const uint16_t *cr = cos_t + qi * 32, *sr = sin_t + qi * 32;
-        const u32x4 ca = *(const u32x4 *)(cr + 8 * g), cb = *(const u32x4 *)(cr + 16 + 8 * g);
-        const u32x4 sa = *(const u32x4 *)(sr + 8 * g), sb = *(const u32x4 *)(sr + 16 + 8 * g);
-        uint32_t y[4][4];
-        const uint32_t xa_[4] = {xa[0], xa[1], xa[2], xa[3]}, xc_[4] = {xc[0], xc[1], xc[2], xc[3]};
-        const uint32_t xb_[4] = {xb[0], xb[1], xb[2], xb[3]}, xd_[4] = {xd[0], xd[1], xd[2], xd[3]};
-        const uint32_t ca_[4] = {ca[0], ca[1], ca[2], ca[3]}, sa_[4] = {sa[0], sa[1], sa[2], sa[3]};
-        const uint32_t cb_[4] = {cb[0], cb[1], cb[2], cb[3]}, sb_[4] = {sb[0], sb[1], sb[2], sb[3]};
-        rotate<E, 4>(xa_, xc_, ca_, sa_, scale, y[0], y[2]);
-        rotate<E, 4>(xb_, xd_, cb_, sb_, scale, y[1], y[3]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            qop[c] = u32x4{y[c][0], y[c][1], y[c][2], y[c][3]};
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            qop[c] = u32x4{0, 0, 0, 0};
-    }
+    QueryRaw r;
+    query_load(r, qkv, cos_t, sin_t, ld, start, qi, len, h, g);
+    query_make<E>(r, scale, qop);
 }
 
 // Scores of one key tile for one 32-row block: S^T = K~ Q~^T from the key tile in LDS. Block 0
@@ -1479,6 +1502,384 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     }
 }
 
+// ---- windows that fit in LDS: query tiles walked in table order, keys kept between them -------
+// With a window of at most 129 keys, the keys that a 256-row query tile reaches span at most
+// eight 64-key tiles, and the next query tile of the same sequence shares all but four of them.
+// attend_slide runs one 8-wave workgroup per CU over a contiguous run of the (head, tile) items:
+// an 8-slot LDS ring holds the current item's key tiles (key tile u of the sequence in slot
+// u % 8, as block images), each new key tile is rotated and staged once per run instead of once
+// per query tile that reads it, and the next item's new key tiles and query rows are loaded into
+// registers while the current item computes. Each wave sweeps only the key tiles its own 32 rows
+// reach. The arithmetic per key tile is that of attend_one.
+
+// A thread's share of staging one key tile, by role (t = tid % 256):
+//   keys:   key row t / 4, dims 8 (t % 4) .. +7 and 32 + 8 (t % 4) .. +7, and their table entries;
+//   values: keys 2 (t / 8) and 2 (t / 8) + 1, dims 8 (t % 8) .. +7.
+// Eight consecutive lanes read one 128-byte row (keys: two 64-byte halves).
+struct SlideKeys {
+    u32x4 x1, x2, c, s;
+};
+struct SlideVals {
+    u32x4 va, vb;
+};
+
+// Where the current item's key and value rows come from.
+struct SlideSrc {
+    const uint16_t *kbase, *vbase, *cos_t, *sin_t;
+    int64_t ld;
+    int len, P, row_bytes;
+    int koff, toff, voff;  // this thread's byte offsets inside a tile
+};
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Loads of the key tile at j0 (< len). Descriptors are rebased on the tile and end at the
+// sequence (table) end, so rows past it read as zero.
+__device__ __forceinline__ void slide_load_keys(SlideKeys &r, const SlideSrc &q, int j0) {
+    const __amdgpu_buffer_rsrc_t kr =
+        rsrc(q.kbase + (int64_t)j0 * q.ld, (int64_t)(q.len - j0) * q.row_bytes);
+    const __amdgpu_buffer_rsrc_t cr = rsrc(q.cos_t + (int64_t)j0 * 32, (int64_t)(q.P - j0) * 64);
+    const __amdgpu_buffer_rsrc_t sr = rsrc(q.sin_t + (int64_t)j0 * 32, (int64_t)(q.P - j0) * 64);
+    r.x1 = load16(kr, q.koff);
+    r.x2 = load16(kr, q.koff + 64);
+    r.c = load16(cr, q.toff);
+    r.s = load16(sr, q.toff);
+}
+__device__ __forceinline__ void slide_load_vals(SlideVals &r, const SlideSrc &q, int j0) {
+    const __amdgpu_buffer_rsrc_t vr =
+        rsrc(q.vbase + (int64_t)j0 * q.ld, (int64_t)(q.len - j0) * q.row_bytes);
+    r.va = load16(vr, q.voff);
+    r.vb = load16(vr, q.voff + q.row_bytes);
+}
+
+// Rotates and rounds the keys into the block image at blk (the layout prep_tiles writes).
+template <class E>
+__device__ __forceinline__ void slide_store_keys(const SlideKeys &r, uint8_t *blk, int t) {
+    const int kr = t >> 2, q = t & 3;
+    uint32_t a[4], b[4], c[4], s[4], y1[4], y2[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        a[k] = r.x1[k], b[k] = r.x2[k], c[k] = r.c[k], s[k] = r.s[k];
+    rotate<E, 4>(a, b, c, s, 1.0f, y1, y2);
+    *(u32x4 *)(blk + kr * 128 + 16 * (q ^ swz(kr))) = u32x4{y1[0], y1[1], y1[2], y1[3]};
+    *(u32x4 *)(blk + kr * 128 + 16 * ((4 + q) ^ swz(kr))) = u32x4{y2[0], y2[1], y2[2], y2[3]};
+}
+
+// Transposes the values into the V^T image: row d, slot p holds key vt_slot(p); keys 2kp and
+// 2kp + 1 sit in slots p and p + 1, one 32-bit word per dim.
+__device__ __forceinline__ void slide_store_vals(const SlideVals &r, uint8_t *blk, int t) {
+    const int kp = t >> 3, c = t & 7;
+    const int p = vt_slot(2 * kp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int d = 8 * c + e;
+        const uint32_t wa = r.va[e >> 1], wb = r.vb[e >> 1];
+        const uint32_t lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
+        const uint32_t hi = (e & 1) ? (wb & 0xffff0000u) : (wb << 16);
+        *(uint32_t *)(blk + IMG + d * 128 + 16 * ((p >> 3) ^ swz(d)) + 2 * (p & 7)) = lo | hi;
+    }
+}
+
+// Masks the scores of the key tile at j0 to the keys lo <= j < hi: register i of block b holds
+// key j0 + 32b + 8(i/4) + 4g + i%4 (one subtraction, one comparison and one select each).
+__device__ __forceinline__ void mask_band(f32x16 &s0, f32x16 &s1, int lo, int hi, int j0,
+                                          int g) {
+    const int a = lo - j0 - 4 * g;
+    const uint32_t span = (uint32_t)max(hi - lo, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int o = 8 * (i >> 2) + (i & 3);
+        s0[i] = (uint32_t)(o - a) < span ? s0[i] : -__builtin_inff();
+        s1[i] = (uint32_t)(o + 32 - a) < span ? s1[i] : -__builtin_inff();
+    }
+}
+
+// One (head, query tile) item of attend_slide, with the key tiles [ta, tb) its window reaches.
+struct SlideItem {
+    int h, seq, i0, start, len, ta, tb;
+    bool ok;
+};
+
+template <class E>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+             const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+             const uint32_t *__restrict__ tiles, uint16_t *__restrict__ out,
+             float *__restrict__ lse, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
+             int32_t P, int32_t window, float scale) {
+    constexpr int NW = 8;
+    constexpr int BR = 32 * NW;
+    constexpr int RING = 8;  // key tiles held in LDS
+    constexpr int DESC = 64; // items described in LDS at a time
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[RING * BLK];
+    __shared__ int32_t desc[DESC][8];  // seq (-1: skip), i0, start, len, h, ta, tb
+
+    // this workgroup's run of items u = h * num_tiles + tile (the host keeps the count below
+    // 2^31)
+    const int items = num_tiles * H;
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int ua = (int)((int64_t)items * b / G), ub = (int)((int64_t)items * (b + 1) / G);
+    if (ua >= ub)
+        return;
+
+    const int64_t ld = 3LL * H * D;
+    const int hd = H * D;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int t = tid & 255, gp = __builtin_amdgcn_readfirstlane(wv) >> 2;
+    int cof[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+        cof[kc] = n * 128 + 16 * ((2 * kc + g) ^ swz(n));
+
+    // ---- item descriptors, DESC at a time (one lane each)
+    int base = ua;
+    auto fill = [&](int from) {
+        if (tid < DESC) {
+            int32_t e[8] = {-1, 0, 0, 0, 0, 0, 0, 0};
+            const int u = from + tid;
+            if (u < ub) {
+                const int h = u / num_tiles;
+                const int tile = u - h * num_tiles;
+                const uint32_t seq = tiles[2 * tile];
+                const int i0 = (int)tiles[2 * tile + 1];
+                if (seq < (uint32_t)S) {
+                    const int start = cu[seq];
+                    const int len = cu[seq + 1] - start;
+                    int lo = 0, hi = len;
+                    if (window > 0) {
+                        if (i0 + 1 > window)
+                            lo = (i0 + 1 - window) / BC * BC;
+                        if ((int64_t)i0 + BR + window - 1 < len)
+                            hi = i0 + BR + window - 1;
+                    }
+                    // a tile that does not match cu, or reaches more key tiles than the ring
+                    // holds (the host admits no such window), reads and writes nothing
+                    if (i0 >= 0 && i0 < len && len <= P && start >= 0 &&
+                        (int64_t)start + len <= T && (hi + BC - 1) / BC - lo / BC <= RING) {
+                        e[0] = (int)seq, e[1] = i0, e[2] = start, e[3] = len;
+                        e[5] = lo / BC, e[6] = (hi + BC - 1) / BC;
+                    }
+                }
+                e[4] = h;
+            }
+            *(u32x4 *)&desc[tid][0] = u32x4{(uint32_t)e[0], (uint32_t)e[1], (uint32_t)e[2],
+                                            (uint32_t)e[3]};
+            *(u32x4 *)&desc[tid][4] = u32x4{(uint32_t)e[4], (uint32_t)e[5], (uint32_t)e[6], 0u};
+        }
+        base = from;
+    };
+    auto decode = [&](int u, SlideItem &it) {
+        const int k = u - base;
+        it.seq = __builtin_amdgcn_readfirstlane(desc[k][0]);
+        it.i0 = __builtin_amdgcn_readfirstlane(desc[k][1]);
+        it.start = __builtin_amdgcn_readfirstlane(desc[k][2]);
+        it.len = __builtin_amdgcn_readfirstlane(desc[k][3]);
+        it.h = __builtin_amdgcn_readfirstlane(desc[k][4]);
+        it.ta = __builtin_amdgcn_readfirstlane(desc[k][5]);
+        it.tb = __builtin_amdgcn_readfirstlane(desc[k][6]);
+        it.ok = it.seq >= 0;
+    };
+
+    // The ring holds key tiles [ra, rb) of (rseq, rh). An item keeps them when it belongs to
+    // the same (sequence, head) and its range starts inside them; its new tiles are then
+    // [max(rb, ta), tb), all within eight consecutive tiles, so no kept tile shares a slot
+    // with a new one.
+    int rseq = -1, rh = -1, ra = 0, rb = 0;
+    auto keeps = [&](const SlideItem &it) {
+        return it.seq == rseq && it.h == rh && it.ta >= ra && it.ta <= rb;
+    };
+    auto fresh = [&](const SlideItem &it, int &na, int &nb) {
+        na = nb = 0;
+        if (!it.ok)
+            return;
+        na = keeps(it) ? max(rb, it.ta) : it.ta;
+        nb = max(na, it.tb);
+    };
+    auto advance = [&](const SlideItem &it) {
+        if (!it.ok)
+            return;  // nothing was staged or read
+        rb = keeps(it) ? max(it.tb, rb) : it.tb;
+        ra = it.ta;
+        rseq = it.seq;
+        rh = it.h;
+    };
+
+    SlideSrc src;
+    src.cos_t = cos_t;
+    src.sin_t = sin_t;
+    src.ld = ld;
+    src.P = P;
+    src.row_bytes = (int)(ld * 2);
+    src.koff = (t >> 2) * src.row_bytes + 16 * (t & 3);
+    src.toff = (t >> 2) * 64 + 16 * (t & 3);
+    src.voff = 2 * (t >> 3) * src.row_bytes + 16 * (t & 7);
+    auto set_src = [&](const SlideItem &it) {
+        src.kbase = qkv + (int64_t)it.start * ld + hd + it.h * D;
+        src.vbase = src.kbase + hd;
+        src.len = it.len;
+    };
+
+    // New tiles travel in pairs (x, x + 1): waves 0-3 take the keys of x and the values of
+    // x + 1, waves 4-7 the other way round, so each thread holds one of each per pair.
+    SlideKeys kk[2];
+    SlideVals vv[2];
+    QueryRaw qr;
+    auto load_pair = [&](SlideKeys &k, SlideVals &v, int x, int nb) {
+        const int tk = x + gp, tv = x + 1 - gp;
+        if (tk < nb)
+            slide_load_keys(k, src, tk * BC);
+        if (tv < nb)
+            slide_load_vals(v, src, tv * BC);
+    };
+    auto store_pair = [&](const SlideKeys &k, const SlideVals &v, int x, int nb) {
+        const int tk = x + gp, tv = x + 1 - gp;
+        if (tk < nb)
+            slide_store_keys<E>(k, ring + (tk & (RING - 1)) * BLK, t);
+        if (tv < nb)
+            slide_store_vals(v, ring + (tv & (RING - 1)) * BLK, t);
+    };
+    // issue the loads of an item's first four new key tiles and of its query rows
+    auto prefetch = [&](const SlideItem &it, int na, int nb) {
+        if (it.ok) {
+            set_src(it);
+            load_pair(kk[0], vv[0], na, nb);
+            load_pair(kk[1], vv[1], na + 2, nb);
+        }
+        // (an item that reads nothing loads zero rows)
+        query_load(qr, qkv, cos_t, sin_t, ld, it.start, it.ok ? it.i0 + 32 * wv + n : 0,
+                   it.ok ? it.len : 0, it.h, g);
+    };
+
+    fill(ua);
+    __syncthreads();
+    SlideItem cur, nxt, nn;
+    int na, nb;
+    decode(ua, cur);
+    nxt.ok = false;
+    if (ua + 1 < ub)
+        decode(ua + 1, nxt);
+    fresh(cur, na, nb);
+    prefetch(cur, na, nb);
+
+    for (int u = ua; u < ub; ++u) {
+        // ---- stage the item's new key tiles (every wave is done with the previous item)
+        __syncthreads();
+        if (cur.ok) {
+            store_pair(kk[0], vv[0], na, nb);
+            store_pair(kk[1], vv[1], na + 2, nb);
+            // a cold ring (first item of a run or of a sequence) needs more than four
+            for (int x = na + 4; x < nb; x += 4) {
+                load_pair(kk[0], vv[0], x, nb);
+                load_pair(kk[1], vv[1], x + 2, nb);
+                store_pair(kk[0], vv[0], x, nb);
+                store_pair(kk[1], vv[1], x + 2, nb);
+            }
+        }
+        advance(cur);
+        u32x4 qop[4];
+        query_make<E>(qr, scale, qop);
+        // the next item's loads (into the registers just consumed) fly while this one computes
+        int na2 = 0, nb2 = 0;
+        if (u + 1 < ub) {
+            fresh(nxt, na2, nb2);
+            prefetch(nxt, na2, nb2);
+        }
+        // descriptors of the items after the next (all reads of the old ones are done)
+        if (u + 2 < ub && u + 2 >= base + DESC)
+            fill(u + 2);
+        __syncthreads();
+        nn.ok = false;
+        if (u + 2 < ub)
+            decode(u + 2, nn);
+
+        // ---- this wave's 32 rows against the key tiles they reach
+        const int w0 = cur.i0 + 32 * wv;
+        if (cur.ok && w0 < cur.len) {
+            const int len = cur.len;
+            const int qi = w0 + n;
+            int lo = 0, hi = len;
+            if (window > 0) {
+                if (w0 + 1 > window)
+                    lo = (w0 + 1 - window) / BC * BC;
+                if ((int64_t)w0 + 32 + window - 1 < len)
+                    hi = w0 + 32 + window - 1;
+            }
+            // this row's visible keys: jlo <= j < jhi
+            const int jlo = window > 0 ? max(qi - window + 1, 0) : 0;
+            const int jhi = window > 0 ? min(len, qi + window) : len;
+            const int nt = (hi - lo + BC - 1) / BC;
+            float m_ref = -__builtin_inff();
+            float l_run = 0.f;
+            f32x16 o0 = {}, o1 = {};
+            for (int tt = 0; tt < nt; ++tt) {
+                const int j0 = lo + tt * BC;
+                const uint8_t *kt = ring + ((j0 / BC) & (RING - 1)) * BLK;
+                f32x16 s0 = {}, s1 = {};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    s0 = E::mfma(*(const u32x4 *)(kt + cof[c]), qop[c], s0);
+                    s1 = E::mfma(*(const u32x4 *)(kt + 4096 + cof[c]), qop[c], s1);
+                }
+                if ((j0 + BC > len) ||
+                    (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window)))
+                    mask_band(s0, s1, jlo, jhi, j0, g);
+                const float mx = row_max(s0, s1);
+                const bool raise = mx > m_ref + TAU;
+                const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * LOG2E) : 1.0f;
+                m_ref = raise ? mx : m_ref;
+                l_run *= alpha;
+                if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        o0[i] *= alpha;
+                        o1[i] *= alpha;
+                    }
+                }
+                const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], LOG2E, -mb));
+                    s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], LOG2E, -mb));
+                }
+                u32x4 pk[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    pk[0][k] = E::pack(s0[2 * k], s0[2 * k + 1]);
+                    pk[1][k] = E::pack(s0[8 + 2 * k], s0[8 + 2 * k + 1]);
+                    pk[2][k] = E::pack(s1[2 * k], s1[2 * k + 1]);
+                    pk[3][k] = E::pack(s1[8 + 2 * k], s1[8 + 2 * k + 1]);
+                }
+                const uint8_t *vt = kt + IMG;
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    o0 = E::mfma(*(const u32x4 *)(vt + cof[kc]), pk[kc], o0);
+                    o1 = E::mfma(*(const u32x4 *)(vt + 4096 + cof[kc]), pk[kc], o1);
+                }
+                float rs = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    rs += s0[i] + s1[i];
+                l_run += rs;
+            }
+            const float l_tot = pair_sum(l_run);
+            if (qi < len) {
+                uint16_t *orow = out + (int64_t)(cur.start + qi) * hd + cur.h * D;
+                store_out<E>(o0, o1, l_tot, orow, g);
+                if (g == 0)
+                    lse[(int64_t)cur.h * T + cur.start + qi] = m_ref + logf(l_tot);
+            }
+        }
+        cur = nxt;
+        nxt = nn;
+        na = na2;
+        nb = nb2;
+    }
+}
+
 template <class E, int NW, bool FIXED>
 int launch_typed(const AttendArgs &a) {
     const int64_t blocks = (int64_t)a.num_tiles * a.H;
@@ -1508,6 +1909,36 @@ int launch_typed(const AttendArgs &a) {
 }
 
 template <class E>
+int launch_slide(const AttendArgs &a) {
+    const int64_t items = (int64_t)a.num_tiles * a.H;
+    if (items > INT32_MAX)
+        return fail(VLF_EINVAL, "%lld items exceed the grid limit", (long long)items);
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus < 1)
+        return fail(VLF_EHIP, "device query failed: %s", hipGetErrorString(e));
+    // one workgroup per CU (the 128 KB ring admits no second one)
+    const int64_t grid = items < cus ? items : cus;
+    const uint16_t *qkv = (const uint16_t *)a.qkv;
+    const uint16_t *cs = (const uint16_t *)a.cos;
+    const uint16_t *sn = (const uint16_t *)a.sin;
+    uint16_t *out = (uint16_t *)a.out;
+    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows, W = a.window;
+    float scale = a.scale;
+    void *args[] = {(void *)&qkv, (void *)&cs,        (void *)&sn, (void *)&a.cu,
+                    (void *)&a.tiles, (void *)&out,   (void *)&a.lse, (void *)&num_tiles,
+                    (void *)&T,   (void *)&S,         (void *)&H,  (void *)&P,
+                    (void *)&W,   (void *)&scale};
+    e = hipLaunchKernel((const void *)attend_slide<E>, dim3((unsigned)grid), dim3(512), args, 0,
+                        (hipStream_t)a.stream);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "attend launch failed: %s", hipGetErrorString(e));
+    return VLF_OK;
+}
+
+template <class E>
 int launch_pre_br(const AttendArgs &a) {
     switch (a.br) {  // the host side admits 64, 128 and 256 only
     case 64: return launch_pre<E, 2>(a);
@@ -1529,6 +1960,16 @@ int launch_br(const AttendArgs &a) {
 
 }  // namespace
 
+// attend_slide serves 256-row tiles whose window reaches at most eight key tiles: keys from
+// i0 - 64 ceil((W - 1) / 64) (i0 a multiple of 64) to i0 + 256 + W - 2.
+static bool slide_fits(int32_t window) {
+    if (window < 1)
+        return false;
+    const int64_t back = ((int64_t)window - 1 + BC - 1) / BC * BC;
+    const int64_t span = back + 256 + window - 1;
+    return (span + BC - 1) / BC <= 8;
+}
+
 int launch_attend(const AttendArgs &a, Launch what) {
     const bool bf = a.dtype == VLF_BF16;
     if (what == Launch::kRotate || what == Launch::kBoth) {
@@ -1538,6 +1979,8 @@ int launch_attend(const AttendArgs &a, Launch what) {
     }
     if (what != Launch::kDirect)
         return bf ? launch_pre_br<BF16>(a) : launch_pre_br<F16>(a);
+    if (a.br == 256 && slide_fits(a.window))
+        return bf ? launch_slide<BF16>(a) : launch_slide<F16>(a);
     // Whole-sequence descriptors need every row of the longest sequence (at most min(P, T)
     // rows) plus a tile past it to be reachable with a 31-bit byte offset.
     const int64_t rows = (int64_t)(a.table_rows < a.T ? a.table_rows : a.T) + 2 * BC;
