@@ -1523,35 +1523,62 @@ struct SlideVals {
     u32x4 va, vb;
 };
 
-// Where the current item's key and value rows come from.
+// Where the current item's key and value rows come from. With FIXED (every sequence, and the
+// tables, within 2^31 bytes of their first row), one descriptor per item covers its sequence
+// and a tile's byte offset is added to the lane offsets; otherwise descriptors are rebased on
+// each tile. Either way they end at the sequence (table) end, so rows past it read as zero.
+template <bool FIXED>
 struct SlideSrc {
     const uint16_t *kbase, *vbase, *cos_t, *sin_t;
     int64_t ld;
     int len, P, row_bytes;
-    int koff, toff, voff;  // this thread's byte offsets inside a tile
+    int koff, toff, voff;                   // this thread's byte offsets inside a tile
+    __amdgpu_buffer_rsrc_t kr, vr, cr, sr;  // FIXED only
+
+    __device__ void set(const uint16_t *k, const uint16_t *v, int len_) {
+        kbase = k, vbase = v, len = len_;
+        if (FIXED) {
+            kr = rsrc(kbase, (int64_t)len * row_bytes);
+            vr = rsrc(vbase, (int64_t)len * row_bytes);
+        }
+    }
 };
 
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// Loads of the key tile at j0 (< len). Descriptors are rebased on the tile and end at the
-// sequence (table) end, so rows past it read as zero.
-__device__ __forceinline__ void slide_load_keys(SlideKeys &r, const SlideSrc &q, int j0) {
-    const __amdgpu_buffer_rsrc_t kr =
-        rsrc(q.kbase + (int64_t)j0 * q.ld, (int64_t)(q.len - j0) * q.row_bytes);
-    const __amdgpu_buffer_rsrc_t cr = rsrc(q.cos_t + (int64_t)j0 * 32, (int64_t)(q.P - j0) * 64);
-    const __amdgpu_buffer_rsrc_t sr = rsrc(q.sin_t + (int64_t)j0 * 32, (int64_t)(q.P - j0) * 64);
-    r.x1 = load16(kr, q.koff);
-    r.x2 = load16(kr, q.koff + 64);
-    r.c = load16(cr, q.toff);
-    r.s = load16(sr, q.toff);
+// Loads of the key tile at j0 (< len).
+template <bool FIXED>
+__device__ __forceinline__ void slide_load_keys(SlideKeys &r, const SlideSrc<FIXED> &q, int j0) {
+    __amdgpu_buffer_rsrc_t kr, cr, sr;
+    int kd = 0, td = 0;
+    if (FIXED) {
+        kr = q.kr, cr = q.cr, sr = q.sr;
+        kd = j0 * q.row_bytes;
+        td = j0 * 64;
+    } else {
+        kr = rsrc(q.kbase + (int64_t)j0 * q.ld, (int64_t)(q.len - j0) * q.row_bytes);
+        cr = rsrc(q.cos_t + (int64_t)j0 * 32, (int64_t)(q.P - j0) * 64);
+        sr = rsrc(q.sin_t + (int64_t)j0 * 32, (int64_t)(q.P - j0) * 64);
+    }
+    r.x1 = load16(kr, q.koff + kd);
+    r.x2 = load16(kr, q.koff + kd + 64);
+    r.c = load16(cr, q.toff + td);
+    r.s = load16(sr, q.toff + td);
 }
-__device__ __forceinline__ void slide_load_vals(SlideVals &r, const SlideSrc &q, int j0) {
-    const __amdgpu_buffer_rsrc_t vr =
-        rsrc(q.vbase + (int64_t)j0 * q.ld, (int64_t)(q.len - j0) * q.row_bytes);
-    r.va = load16(vr, q.voff);
-    r.vb = load16(vr, q.voff + q.row_bytes);
+template <bool FIXED>
+__device__ __forceinline__ void slide_load_vals(SlideVals &r, const SlideSrc<FIXED> &q, int j0) {
+    __amdgpu_buffer_rsrc_t vr;
+    int vd = 0;
+    if (FIXED) {
+        vr = q.vr;
+        vd = j0 * q.row_bytes;
+    } else {
+        vr = rsrc(q.vbase + (int64_t)j0 * q.ld, (int64_t)(q.len - j0) * q.row_bytes);
+    }
+    r.va = load16(vr, q.voff + vd);
+    r.vb = load16(vr, q.voff + vd + q.row_bytes);
 }
 
 // Rotates and rounds the keys into the block image at blk (the layout prep_tiles writes).
@@ -1602,7 +1629,7 @@ struct SlideItem {
     bool ok;
 };
 
-template <class E>
+template <class E, bool FIXED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
              const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
@@ -1708,19 +1735,22 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
         rh = it.h;
     };
 
-    SlideSrc src;
+    SlideSrc<FIXED> src;
     src.cos_t = cos_t;
     src.sin_t = sin_t;
     src.ld = ld;
     src.P = P;
     src.row_bytes = (int)(ld * 2);
+    if (FIXED) {
+        src.cr = rsrc(cos_t, (int64_t)P * 64);
+        src.sr = rsrc(sin_t, (int64_t)P * 64);
+    }
     src.koff = (t >> 2) * src.row_bytes + 16 * (t & 3);
     src.toff = (t >> 2) * 64 + 16 * (t & 3);
     src.voff = 2 * (t >> 3) * src.row_bytes + 16 * (t & 7);
     auto set_src = [&](const SlideItem &it) {
-        src.kbase = qkv + (int64_t)it.start * ld + hd + it.h * D;
-        src.vbase = src.kbase + hd;
-        src.len = it.len;
+        const uint16_t *k = qkv + (int64_t)it.start * ld + hd + it.h * D;
+        src.set(k, k + hd, it.len);
     };
 
     // New tiles travel in pairs (x, x + 1): waves 0-3 take the keys of x and the values of
@@ -1908,7 +1938,7 @@ int launch_typed(const AttendArgs &a) {
     return VLF_OK;
 }
 
-template <class E>
+template <class E, bool FIXED>
 int launch_slide(const AttendArgs &a) {
     const int64_t items = (int64_t)a.num_tiles * a.H;
     if (items > INT32_MAX)
@@ -1931,8 +1961,8 @@ int launch_slide(const AttendArgs &a) {
                     (void *)&a.tiles, (void *)&out,   (void *)&a.lse, (void *)&num_tiles,
                     (void *)&T,   (void *)&S,         (void *)&H,  (void *)&P,
                     (void *)&W,   (void *)&scale};
-    e = hipLaunchKernel((const void *)attend_slide<E>, dim3((unsigned)grid), dim3(512), args, 0,
-                        (hipStream_t)a.stream);
+    e = hipLaunchKernel((const void *)attend_slide<E, FIXED>, dim3((unsigned)grid), dim3(512),
+                        args, 0, (hipStream_t)a.stream);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "attend launch failed: %s", hipGetErrorString(e));
     return VLF_OK;
@@ -1979,12 +2009,15 @@ int launch_attend(const AttendArgs &a, Launch what) {
     }
     if (what != Launch::kDirect)
         return bf ? launch_pre_br<BF16>(a) : launch_pre_br<F16>(a);
-    if (a.br == 256 && slide_fits(a.window))
-        return bf ? launch_slide<BF16>(a) : launch_slide<F16>(a);
     // Whole-sequence descriptors need every row of the longest sequence (at most min(P, T)
     // rows) plus a tile past it to be reachable with a 31-bit byte offset.
     const int64_t rows = (int64_t)(a.table_rows < a.T ? a.table_rows : a.T) + 2 * BC;
     const bool fixed = rows * 3 * a.H * D * 2 < ((int64_t)1 << 31);
+    if (a.br == 256 && slide_fits(a.window)) {
+        if (bf)
+            return fixed ? launch_slide<BF16, true>(a) : launch_slide<BF16, false>(a);
+        return fixed ? launch_slide<F16, true>(a) : launch_slide<F16, false>(a);
+    }
     if (bf)
         return fixed ? launch_br<BF16, true>(a) : launch_br<BF16, false>(a);
     return fixed ? launch_br<F16, true>(a) : launch_br<F16, false>(a);
