@@ -1772,16 +1772,19 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
         if (tv < nb)
             slide_store_vals(v, ring + (tv & (RING - 1)) * BLK, t);
     };
-    // issue the loads of an item's first four new key tiles and of its query rows
-    auto prefetch = [&](const SlideItem &it, int na, int nb) {
-        if (it.ok) {
-            set_src(it);
-            load_pair(kk[0], vv[0], na, nb);
-            load_pair(kk[1], vv[1], na + 2, nb);
+    // the loads of an item's first four new key tiles and of its query rows, in three parts
+    // (the key-tile pairs, then the query rows): the vector memory path moves about 64 bytes per
+    // clock per CU, so the item's 160 KB are issued a part per key tile of the computation
+    // rather than at once
+    auto prefetch = [&](int part, const SlideItem &it, int na, int nb) {
+        if (part < 2) {
+            if (it.ok)
+                load_pair(kk[part], vv[part], na + 2 * part, nb);
+        } else {
+            // (an item that reads nothing loads zero rows)
+            query_load(qr, qkv, cos_t, sin_t, ld, it.start, it.ok ? it.i0 + 32 * wv + n : 0,
+                       it.ok ? it.len : 0, it.h, g);
         }
-        // (an item that reads nothing loads zero rows)
-        query_load(qr, qkv, cos_t, sin_t, ld, it.start, it.ok ? it.i0 + 32 * wv + n : 0,
-                   it.ok ? it.len : 0, it.h, g);
     };
 
     fill(ua);
@@ -1793,7 +1796,11 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
     if (ua + 1 < ub)
         decode(ua + 1, nxt);
     fresh(cur, na, nb);
-    prefetch(cur, na, nb);
+    if (cur.ok)
+        set_src(cur);
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+        prefetch(part, cur, na, nb);
 
     for (int u = ua; u < ub; ++u) {
         // ---- stage the item's new key tiles (every wave is done with the previous item)
@@ -1812,12 +1819,20 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
         advance(cur);
         u32x4 qop[4];
         query_make<E>(qr, scale, qop);
-        // the next item's loads (into the registers just consumed) fly while this one computes
+        // the next item's loads (into the registers just consumed) are issued during this
+        // item's key loop, one part per key tile
         int na2 = 0, nb2 = 0;
-        if (u + 1 < ub) {
+        const bool more = u + 1 < ub;
+        if (more) {
             fresh(nxt, na2, nb2);
-            prefetch(nxt, na2, nb2);
+            if (nxt.ok)
+                set_src(nxt);
         }
+        auto issue = [&](int part) __attribute__((always_inline)) {
+            if (more)
+                prefetch(part, nxt, na2, nb2);
+        };
+        int issued = 0;
         // descriptors of the items after the next (all reads of the old ones are done)
         if (u + 2 < ub && u + 2 >= base + DESC)
             fill(u + 2);
@@ -1842,10 +1857,11 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
             const int jlo = window > 0 ? max(qi - window + 1, 0) : 0;
             const int jhi = window > 0 ? min(len, qi + window) : len;
             const int nt = (hi - lo + BC - 1) / BC;
+            issued = min(nt, 3);
             float m_ref = -__builtin_inff();
             float l_run = 0.f;
             f32x16 o0 = {}, o1 = {};
-            for (int tt = 0; tt < nt; ++tt) {
+            auto step = [&](int tt) __attribute__((always_inline)) {
                 const int j0 = lo + tt * BC;
                 const uint8_t *kt = ring + ((j0 / BC) & (RING - 1)) * BLK;
                 f32x16 s0 = {}, s1 = {};
@@ -1894,7 +1910,22 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
                 for (int i = 0; i < 16; ++i)
                     rs += s0[i] + s1[i];
                 l_run += rs;
+            };
+            // the first three key tiles, each after issuing a part of the next item's loads
+            if (nt > 0) {
+                issue(0);
+                step(0);
             }
+            if (nt > 1) {
+                issue(1);
+                step(1);
+            }
+            if (nt > 2) {
+                issue(2);
+                step(2);
+            }
+            for (int tt = 3; tt < nt; ++tt)
+                step(tt);
             const float l_tot = pair_sum(l_run);
             if (qi < len) {
                 uint16_t *orow = out + (int64_t)(cur.start + qi) * hd + cur.h * D;
@@ -1903,6 +1934,13 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
                     lse[(int64_t)cur.h * T + cur.start + qi] = m_ref + logf(l_tot);
             }
         }
+        // (waves that swept fewer than three key tiles)
+        if (issued < 1)
+            issue(0);
+        if (issued < 2)
+            issue(1);
+        if (issued < 3)
+            issue(2);
         cur = nxt;
         nxt = nn;
         na = na2;
