@@ -401,20 +401,28 @@ __device__ __forceinline__ void scores(const uint16_t *kt, const u32x4 (&qop)[4]
     }
 }
 
-// Masks the scores of the 64-key tile at j0 for query qi (keys past the sequence and outside
-// the window weigh nothing).
-__device__ __forceinline__ void mask_scores(f32x16 &s0, f32x16 &s1, int j0, int len, int window,
-                                            int qi, int g) {
+// Masks the scores of the key tile at j0 to the keys lo <= j < hi: register i of block b holds
+// key j0 + 32b + 8(i/4) + 4g + i%4 (one subtraction, one comparison and one select each).
+__device__ __forceinline__ void mask_band(f32x16 &s0, f32x16 &s1, int lo, int hi, int j0,
+                                          int g) {
+    const int a = lo - j0 - 4 * g;
+    const uint32_t span = (uint32_t)max(hi - lo, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int ja = j0 + 8 * (i >> 2) + 4 * g + (i & 3), jb = ja + 32;
-        const int da = qi > ja ? qi - ja : ja - qi;
-        const int db = qi > jb ? qi - jb : jb - qi;
-        const bool va = ja < len && (window == 0 || da < window);
-        const bool vb = jb < len && (window == 0 || db < window);
-        s0[i] = va ? s0[i] : -__builtin_inff();
-        s1[i] = vb ? s1[i] : -__builtin_inff();
+        const int o = 8 * (i >> 2) + (i & 3);
+        s0[i] = (uint32_t)(o - a) < span ? s0[i] : -__builtin_inff();
+        s1[i] = (uint32_t)(o + 32 - a) < span ? s1[i] : -__builtin_inff();
     }
+}
+
+// Masks the scores of the 64-key tile at j0 for query qi (keys past the sequence and outside
+// the window weigh nothing): the visible keys of row qi are max(qi - W + 1, 0) <= j <
+// min(len, qi + W), or 0 <= j < len for the full window.
+__device__ __forceinline__ void mask_scores(f32x16 &s0, f32x16 &s1, int j0, int len, int window,
+                                            int qi, int g) {
+    const int lo = window > 0 ? max(qi - window + 1, 0) : 0;
+    const int hi = (window > 0 && window < len - qi) ? qi + window : len;
+    mask_band(s0, s1, lo, hi, j0, g);
 }
 
 // Maximum over the 64 lanes of a wave.
@@ -1462,8 +1470,22 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         // sequences) only stages and waits
         if (__builtin_amdgcn_readfirstlane(w0) >= len)
             continue;
+        // keys j0 + 32 .. j0 + 63 all past the sequence (a sequence of at most 32 tokens): that
+        // half's products, probabilities and sums are skipped, its scores are -inf
+        const bool h1 = j0 + 32 < len;
         f32x16 s0, s1;
-        scores<E>(ks, qop, n, g, s0, s1);
+        if (h1) {
+            scores<E>(ks, qop, n, g, s0, s1);
+        } else {
+            const uint16_t *k0 = ks + n * KS + 8 * g;
+            s0 = f32x16{};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                s0 = E::mfma(*(const u32x4 *)(k0 + 16 * c), qop[c], s0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                s1[i] = -__builtin_inff();
+        }
         if ((j0 + BC > len) ||
             (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window)))
             mask_scores(s0, s1, j0, len, window, qi, g);
@@ -1480,30 +1502,46 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
             }
         }
         const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], LOG2E, -mb));
-            s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], LOG2E, -mb));
-        }
         u32x4 pk[4];
+        const uint16_t *v0 = vt + n * VS + 8 * g;
+        const uint16_t *v1 = vt + (32 + n) * VS + 8 * g;
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], LOG2E, -mb));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             pk[0][k] = E::pack(s0[2 * k], s0[2 * k + 1]);
             pk[1][k] = E::pack(s0[8 + 2 * k], s0[8 + 2 * k + 1]);
-            pk[2][k] = E::pack(s1[2 * k], s1[2 * k + 1]);
-            pk[3][k] = E::pack(s1[8 + 2 * k], s1[8 + 2 * k + 1]);
         }
-        const uint16_t *v0 = vt + n * VS + 8 * g;
-        const uint16_t *v1 = vt + (32 + n) * VS + 8 * g;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
+        for (int kc = 0; kc < 2; ++kc) {
             o0 = E::mfma(*(const u32x4 *)(v0 + 16 * kc), pk[kc], o0);
             o1 = E::mfma(*(const u32x4 *)(v1 + 16 * kc), pk[kc], o1);
         }
-        float rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            rs += s0[i] + s1[i];
+            rs += s0[i];
+        if (h1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], LOG2E, -mb));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                pk[2][k] = E::pack(s1[2 * k], s1[2 * k + 1]);
+                pk[3][k] = E::pack(s1[8 + 2 * k], s1[8 + 2 * k + 1]);
+            }
+#pragma unroll
+            for (int kc = 2; kc < 4; ++kc) {
+                o0 = E::mfma(*(const u32x4 *)(v0 + 16 * kc), pk[kc], o0);
+                o1 = E::mfma(*(const u32x4 *)(v1 + 16 * kc), pk[kc], o1);
+            }
+            float r1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                r1 += s1[i];
+            rs += r1;
+        }
         l_run += rs;
     }
 
@@ -1623,19 +1661,6 @@ __device__ __forceinline__ void slide_store_vals(const SlideVals &r, uint8_t *bl
     }
 }
 
-// Masks the scores of the key tile at j0 to the keys lo <= j < hi: register i of block b holds
-// key j0 + 32b + 8(i/4) + 4g + i%4 (one subtraction, one comparison and one select each).
-__device__ __forceinline__ void mask_band(f32x16 &s0, f32x16 &s1, int lo, int hi, int j0,
-                                          int g) {
-    const int a = lo - j0 - 4 * g;
-    const uint32_t span = (uint32_t)max(hi - lo, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int o = 8 * (i >> 2) + (i & 3);
-        s0[i] = (uint32_t)(o - a) < span ? s0[i] : -__builtin_inff();
-        s1[i] = (uint32_t)(o + 32 - a) < span ? s1[i] : -__builtin_inff();
-    }
-}
 
 // One (head, query tile) item of attend_slide, with the key tiles [ta, tb) its window reaches.
 struct SlideItem {
@@ -1869,7 +1894,7 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
             }
             // this row's visible keys: jlo <= j < jhi
             const int jlo = window > 0 ? max(qi - window + 1, 0) : 0;
-            const int jhi = window > 0 ? min(len, qi + window) : len;
+            const int jhi = (window > 0 && window < len - qi) ? qi + window : len;
             const int nt = (hi - lo + BC - 1) / BC;
             issued = min(nt, 3);
             float m_ref = -__builtin_inff();
