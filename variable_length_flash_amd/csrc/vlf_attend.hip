@@ -298,9 +298,10 @@ __device__ __forceinline__ void stage_load(TileRegs<NTHR> &r, const Staging<NTHR
     }
 }
 
+// Rotates and rounds this thread's keys into K~ and transposes its values into V^T.
 template <class E, int NTHR>
-__device__ __forceinline__ void stage_store(const TileRegs<NTHR> &r, const Staging<NTHR> &sg,
-                                            uint16_t *ks, uint16_t *vt) {
+__device__ __forceinline__ void stage_keys(const TileRegs<NTHR> &r, const Staging<NTHR> &sg,
+                                           uint16_t *ks) {
     using S = Staging<NTHR>;
     uint32_t y1[S::KW], y2[S::KW];
     rotate<E, S::KW>(r.x1, r.x2, r.c, r.s, 1.0f, y1, y2);
@@ -309,6 +310,12 @@ __device__ __forceinline__ void stage_store(const TileRegs<NTHR> &r, const Stagi
         *(u32x2 *)(ks + sg.kk * KS + sg.pp + 2 * w) = u32x2{y1[w], y1[w + 1]};
         *(u32x2 *)(ks + sg.kk * KS + 32 + sg.pp + 2 * w) = u32x2{y2[w], y2[w + 1]};
     }
+}
+
+template <int NTHR>
+__device__ __forceinline__ void stage_values(const TileRegs<NTHR> &r, const Staging<NTHR> &sg,
+                                             uint16_t *vt) {
+    using S = Staging<NTHR>;
     const int slot = vt_slot(2 * sg.kp);
 #pragma unroll
     for (int q = 0; q < S::VC; ++q) {
@@ -320,6 +327,15 @@ __device__ __forceinline__ void stage_store(const TileRegs<NTHR> &r, const Stagi
             *(uint32_t *)(vt + (4 * sg.vchunk[q] + e) * VS + slot) = a | b;
         }
     }
+}
+
+// keys false: this thread's key rows are never read, so they are not staged
+template <class E, int NTHR>
+__device__ __forceinline__ void stage_store(const TileRegs<NTHR> &r, const Staging<NTHR> &sg,
+                                            uint16_t *ks, uint16_t *vt, bool keys = true) {
+    if (keys)
+        stage_keys<E, NTHR>(r, sg, ks);
+    stage_values<NTHR>(r, sg, vt);
 }
 
 // Raw inputs of one lane's query operand: dims 8g .. 8g+7, 16+8g .., 32+8g .., 48+8g .. of the
@@ -1452,8 +1468,12 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
              cos_t, sin_t, len, P, ld);
     TileRegs<NTHR> r;
     stage_load(r, sg, src, lo);
+    // a wave whose rows all lie past the sequence (half the waves of a batch of short
+    // sequences) only stages and waits
+    const bool idle = __builtin_amdgcn_readfirstlane(w0) >= len;
     u32x4 qop[4];
-    query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
+    if (!idle)
+        query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
 
     float m_ref = -__builtin_inff();
     float l_run = 0.f;
@@ -1464,11 +1484,11 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
             stage_load(r, sg, src, j0);
             __syncthreads();  // every wave is done with the previous tile
         }
-        stage_store<E, NTHR>(r, sg, ks, vt);
+        // wave v stages key rows 32v .. 32v+31 of the tile; past the sequence they are never
+        // read (the second half of such a tile is skipped below)
+        stage_store<E, NTHR>(r, sg, ks, vt, __builtin_amdgcn_readfirstlane(j0 + 32 * wv) < len);
         __syncthreads();
-        // a wave whose rows all lie past the sequence (half the waves of a batch of short
-        // sequences) only stages and waits
-        if (__builtin_amdgcn_readfirstlane(w0) >= len)
+        if (idle)
             continue;
         // keys j0 + 32 .. j0 + 63 all past the sequence (a sequence of at most 32 tokens): that
         // half's products, probabilities and sums are skipped, its scores are -inf
