@@ -378,8 +378,11 @@ def _wide_inputs():
     return w, qkv, cos, sin
 
 
-@pytest.mark.parametrize("window", [0, 300])
+@pytest.mark.parametrize("window", [0, 128, 300])
 def test_offsets_past_2gib(window):
+    """Rows past 2^31 bytes from the first: per-tile descriptors on the direct path (W = 128 at
+    256 rows is the key ring's, with about 88 items per workgroup, so its item descriptors are
+    refilled mid-run), 64-bit offsets on the workspace path."""
     w, qkv, cos, sin = _wide_inputs()
     assert qkv.numel() * 2 > 2 ** 31
     w_rows = sample_rows(w, 128, 1200, seed=9)
@@ -423,6 +426,21 @@ def test_window_runs_keep_keys(dtype, window):
     _say(f"case window runs {dtype} W={window}")
     out, lse = run_gpu(w, qkv, cos, sin, br=256, prerotate=False)
     compare(f"window runs {dtype} W={window}", w, out, lse, qkv, cos, sin)
+
+
+@pytest.mark.parametrize("window", [1, 65])
+def test_window_runs_past_the_descriptor_cache(window):
+    """20000 one-token sequences among longer ones, 2 heads: about 160 items per workgroup of
+    the key ring, so each run refills its LDS item descriptors (64 at a time) two or three
+    times, and most items start a new sequence on a cold ring."""
+    lens = [1] * 20000
+    for k, L in ((3, 700), (5000, 300), (12000, 257), (19999, 1000)):
+        lens[k] = L
+    w = workloads.custom(lens, 2, dtype="bf16", window=window, table_rows=1000, seed=53)
+    qkv, cos, sin = inputs(w)
+    _say(f"case window runs past the descriptor cache W={window}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=256, prerotate=False)
+    compare(f"20000 one-token sequences W={window}", w, out, lse, qkv, cos, sin)
 
 
 @pytest.mark.parametrize("order", ["shuffled", "reversed", "doubled"])
