@@ -124,6 +124,10 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
  *   tiles_dev  device, [num_tiles, 2] uint32 (sequence, first row) pairs built for the same cu
  *              and `br` (vlf_tile_table, or any permutation of it: the order is the launch
  *              order). Tiles naming a sequence >= S or a row beyond the sequence are skipped.
+ *              Without a workspace, at br = 256 and 1 <= window <= 129, each CU walks a run
+ *              of consecutive entries and keeps the keys that one entry shares with the
+ *              next of the same sequence in LDS: any order gives the same results, and the
+ *              canonical one is the fastest.
  *   br         64, 128 or 256: rows per tile, as the table was built.
  *   T, S, H    tokens, sequences, heads (1 <= H <= 65536; T = 0 or num_tiles = 0 launches
  *              nothing).

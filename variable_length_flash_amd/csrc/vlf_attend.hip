@@ -1681,7 +1681,6 @@ __device__ __forceinline__ void slide_store_vals(const SlideVals &r, uint8_t *bl
     }
 }
 
-
 // One (head, query tile) item of attend_slide, with the key tiles [ta, tb) its window reaches.
 struct SlideItem {
     int h, seq, i0, start, len, ta, tb;
@@ -1697,8 +1696,8 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
              int32_t P, int32_t window, float scale) {
     constexpr int NW = 8;
     constexpr int BR = 32 * NW;
-    constexpr int RING = 8;  // key tiles held in LDS
-    constexpr int DESC = 64; // items described in LDS at a time
+    constexpr int RING = 8;   // key tiles held in LDS
+    constexpr int DESC = 64;  // items described in LDS at a time
     __shared__ __attribute__((aligned(1024))) uint8_t ring[RING * BLK];
     __shared__ int32_t desc[DESC][8];  // seq (-1: skip), i0, start, len, h, ta, tb
 
