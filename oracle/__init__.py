@@ -14,6 +14,9 @@ Everything here follows hanzo-kernel 0.2.42, ``src/packed.rs``:
 * ``attend`` — the f64 composite ``attend_ref`` (mode "A") and the same with the matrix
   operands rounded as ``attend``'s query- and key-tile loads round them (mode "B"); the C
   source ``vlf_oracle.c`` states both definitions.
+* ``attend_backward`` — the f64 gradient of ``sum(out * dout)`` with respect to qkv
+  (``attend_back_ref``), in the same two modes; ``operands`` gives the score operands it is
+  taken through.
 
 Parity pins for every function live in ``tests/test_oracle.py``.
 """
@@ -47,6 +50,11 @@ def _open(path):
     lib.vlf_oracle_round.restype = ctypes.c_int
     lib.vlf_oracle_threads.argtypes = [ctypes.c_int32]
     lib.vlf_oracle_threads.restype = ctypes.c_int32
+    lib.vlf_oracle_operands.argtypes = [
+        p, p, p, ctypes.c_int64, p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+        ctypes.c_double, ctypes.c_int32, ctypes.c_int32, p, p,
+    ]
+    lib.vlf_oracle_operands.restype = ctypes.c_int
     return lib
 
 
@@ -119,6 +127,88 @@ def attend(qkv, cos, sin, cu, heads: int, window: int, scale: float, *, mode: st
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (rc={rc})")
     return out, np.ascontiguousarray(lse.T)
+
+
+def operands(qkv, cos, sin, cu, heads: int, scale: float, *, mode: str = "B",
+             dtype: str = "bf16", library=None):
+    """The score operands (q~ [T, heads*64], k~ [T, heads*64], float64) of every token: the
+    query rows rotated to their positions and scaled, the key rows rotated; in mode B rounded as
+    ``attend``'s mode B rounds them. The scores are ``<q~_i, k~_j>``."""
+    qkv = np.ascontiguousarray(qkv, dtype=np.float32)
+    cos = np.ascontiguousarray(cos, dtype=np.float32)
+    sin = np.ascontiguousarray(sin, dtype=np.float32)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    T, S = int(cu[-1]), int(cu.shape[0] - 1)
+    if qkv.shape != (T, 3 * heads * 64):
+        raise ValueError(f"qkv shape {qkv.shape} != {(T, 3 * heads * 64)}")
+    q = np.zeros((T, heads * 64), dtype=np.float64)
+    k = np.zeros((T, heads * 64), dtype=np.float64)
+    rc = _load(library).vlf_oracle_operands(
+        _ptr(qkv), _ptr(cos), _ptr(sin), cos.shape[0], _ptr(cu), S, T, heads, float(scale),
+        MODES[mode], DTYPES[dtype], _ptr(q), _ptr(k))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (rc={rc})")
+    return q, k
+
+
+def attend_backward(qkv, cos, sin, cu, heads: int, window: int, scale: float, dout, *,
+                    mode: str = "B", dtype: str = "bf16", library=None) -> np.ndarray:
+    """Gradient of ``sum(out * dout)`` with respect to qkv, in float64 (hanzo-kernel 0.2.42
+    src/packed.rs, ``attend_back_ref``, the f64 composite's gradient; ``attend_back`` computes
+    the same quantities tile by tile).
+
+    Per sequence and head, with the score operands q~ (rotated, scaled) and k~ (rotated) of
+    ``operands``: s_ij = <q~_i, k~_j> over the visible keys, p = softmax_j(s), dp_ij =
+    <dout_i, v_j>, ds_ij = p_ij (dp_ij - sum_j p_ij dp_ij). Then dv_j = sum_i p_ij dout_i, the
+    operand gradients dq~_i = sum_j ds_ij k~_j and dk~_j = sum_i ds_ij q~_i, taken back through
+    the rotation (its transpose, [c s; -s c] per dimension pair at the row's position) and, for
+    the query, the scale. Mode B differs from mode A only in the rounded operands.
+
+    dout: [T, heads*64]. Returns dqkv [T, 3*heads*64] float64. Dense per (sequence, head):
+    meant for test-sized batches.
+    """
+    cos64 = np.asarray(cos, dtype=np.float64)
+    sin64 = np.asarray(sin, dtype=np.float64)
+    x = np.asarray(qkv, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    cu = np.asarray(cu, dtype=np.int64)
+    T = int(cu[-1])
+    hd = heads * 64
+    qt, kt = operands(qkv, cos, sin, cu, heads, scale, mode=mode, dtype=dtype, library=library)
+    g = np.zeros((T, 3 * hd), dtype=np.float64)
+
+    def back(y, c, s):
+        # transpose of the half-split rotation at each row's position
+        y1, y2 = y[:, :32], y[:, 32:]
+        return np.concatenate([y1 * c + y2 * s, y2 * c - y1 * s], axis=1)
+
+    for si in range(len(cu) - 1):
+        a, b = int(cu[si]), int(cu[si + 1])
+        L = b - a
+        if L == 0:
+            continue
+        c, s = cos64[:L], sin64[:L]
+        pos = np.arange(L)
+        gap = np.abs(pos[:, None] - pos[None, :])
+        visible = np.ones((L, L), dtype=bool) if window <= 0 else gap < window
+        for h in range(heads):
+            cols = slice(h * 64, (h + 1) * 64)
+            q, k = qt[a:b, cols], kt[a:b, cols]
+            v = x[a:b, 2 * hd + h * 64:2 * hd + (h + 1) * 64]
+            o = do[a:b, cols]
+            sc = np.where(visible, q @ k.T, -np.inf)
+            m = sc.max(axis=1, keepdims=True)
+            e = np.exp(sc - m)
+            p = e / e.sum(axis=1, keepdims=True)
+            dp = o @ v.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq = ds @ k
+            dk = ds.T @ q
+            dv = p.T @ o
+            g[a:b, h * 64:(h + 1) * 64] = back(dq, c, s) * scale
+            g[a:b, hd + h * 64:hd + (h + 1) * 64] = back(dk, c, s)
+            g[a:b, 2 * hd + h * 64:2 * hd + (h + 1) * 64] = dv
+    return g
 
 
 def tile_table(cu, br: int) -> np.ndarray:

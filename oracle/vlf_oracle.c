@@ -128,6 +128,47 @@ static void rotate_row(const float *x, const float *c, const float *s, int mode,
     }
 }
 
+/*
+ * The score operands of every token and head, as the scores above use them: q_out [T, H*64] the
+ * query rows rotated to their positions and scaled (mode A: scale * rot(q) in float64; mode B: the
+ * rounded operand of rotate_row), k_out [T, H*64] the key rows rotated (mode B: rounded). The
+ * gradient (oracle/__init__.py, attend_backward) is taken with respect to these. Returns 0, or -1
+ * on malformed arguments.
+ */
+int vlf_oracle_operands(const float *qkv, const float *cos_t, const float *sin_t, int64_t P,
+                        const int32_t *cu, int32_t S, int64_t T, int32_t H, double scale,
+                        int32_t mode, int32_t dtype, double *q_out, double *k_out)
+{
+    if (S < 0 || T < 0 || H < 1 || P < 0)
+        return -1;
+    if (mode != ORACLE_MODE_A && mode != ORACLE_MODE_B)
+        return -1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16)
+        return -1;
+    if (cu[0] != 0 || cu[S] != T)
+        return -1;
+    for (int32_t s = 0; s < S; ++s)
+        if (cu[s + 1] < cu[s] || cu[s + 1] - cu[s] > P)
+            return -1;
+    const int64_t hd = (int64_t)H * HD, ld = 3 * hd;
+    for (int32_t s = 0; s < S; ++s) {
+        for (int64_t i = 0; i < cu[s + 1] - cu[s]; ++i) {
+            int64_t t = cu[s] + i;
+            for (int32_t h = 0; h < H; ++h) {
+                double *q = q_out + t * hd + (int64_t)h * HD;
+                rotate_row(qkv + t * ld + (int64_t)h * HD, cos_t + i * HALF, sin_t + i * HALF,
+                           mode, dtype, mode == ORACLE_MODE_B ? (float)scale : 1.0f, q);
+                if (mode == ORACLE_MODE_A)
+                    for (int m = 0; m < HD; ++m)
+                        q[m] *= scale;
+                rotate_row(qkv + t * ld + hd + (int64_t)h * HD, cos_t + i * HALF,
+                           sin_t + i * HALF, mode, dtype, 1.0f, k_out + t * hd + (int64_t)h * HD);
+            }
+        }
+    }
+    return 0;
+}
+
 /* The sequence holding token t: the s with cu[s] <= t < cu[s+1] (zero-length sequences skipped). */
 static int32_t sequence_of(const int32_t *cu, int32_t S, int64_t t)
 {
