@@ -285,3 +285,46 @@ def test_tile_count_and_table_at_int32_extremes():
         table = vlf.tile_table(cu, br)
         assert table.shape == (want, 2)
         assert table[:, 1].tolist() == [i * br for i in range(want)]
+
+
+def test_backward_workspace_bytes():
+    assert vlf.backward_workspace_bytes(0, 4) == 0
+    assert vlf.backward_workspace_bytes(1000, 12) == 1000 * 12 * 65 * 4
+    lib = vlf.load_library()
+    n = ctypes.c_int64(0)
+    assert lib.vlf_backward_workspace_bytes(-1, 2, ctypes.byref(n)) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, 70000, ctypes.byref(n)) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, 2, None) == binding.VLF_EINVAL
+
+
+def _backward_status(**kw):
+    lib = vlf.load_library()
+    cu = np.array([0, 100, 256], dtype=np.int32)
+    a = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=256, cu=cu.ctypes.data, tiles=0x4000,
+             num_tiles=5, T=256, S=2, H=2, W=0, scale=0.125, dtype=binding.VLF_BF16, out=0x5000,
+             dout=0x6000, lse=0x7000, ws=0x8000, ws_bytes=256 * 2 * 65 * 4, dqkv=0x9000)
+    a.update(kw)
+    rc = lib.vlf_attend_backward(a["qkv"], a["cos"], a["sin"], a["P"], a["cu"], a["tiles"],
+                                 a["num_tiles"], a["T"], a["S"], a["H"], a["W"], a["scale"],
+                                 a["dtype"], a["out"], a["dout"], a["lse"], a["ws"],
+                                 a["ws_bytes"], a["dqkv"], None)
+    return rc, lib.vlf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(dtype=7), binding.VLF_EUNSUPPORTED, "dtype"),
+    (dict(W=-1), binding.VLF_EINVAL, "window"),
+    (dict(H=0), binding.VLF_EINVAL, "H = 0"),
+    (dict(ws_bytes=100), binding.VLF_EINVAL, "workspace"),
+    (dict(ws=None), binding.VLF_EINVAL, "workspace"),
+    (dict(dout=None), binding.VLF_EINVAL, "null device pointer"),
+    (dict(dqkv=None), binding.VLF_EINVAL, "null device pointer"),
+    (dict(scale=float("nan")), binding.VLF_EINVAL, "scale"),
+])
+def test_backward_rejects_bad_arguments_before_launching(kw, status, text):
+    rc, msg = _backward_status(**kw)
+    assert rc == status and text in msg, (rc, msg)
+
+
+def test_backward_with_no_tiles_is_a_no_op():
+    assert _backward_status(num_tiles=0, ws=None, ws_bytes=0)[0] == binding.VLF_OK

@@ -1,0 +1,117 @@
+"""GPU parity of the backward (vlf_attend_backward through the C ABI) against the oracle's
+float64 gradient (mode B: the same rounded score operands). The forward that feeds it (out, lse)
+is the library's own, as in a training step.
+
+The measure is the page's: the largest absolute error over dqkv divided by the largest
+magnitude of the oracle's dqkv. The page's backward test bounds it by 3e-2 for bf16 inputs; the
+kernel rounds P and dS to the storage type where they enter the matrix products (relative
+2^-9 for bf16, 2^-12 for fp16), so fp16 is held to 1e-2."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import variable_length_flash_amd as vlf
+from variable_length_flash_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = {"bf16": 3e-2, "fp16": 1e-2}
+GUARD = 4096
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dout(w, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((w.tokens, w.heads * 64)).astype(np.float32)
+    return torch.from_numpy(oracle.round_to(x, w.dtype).astype(np.float32)).to(
+        torch.bfloat16 if w.dtype == "bf16" else torch.float16)
+
+
+def run_backward(w, window=None, seed=0):
+    """Forward then backward on cuda:0, dqkv in a NaN-filled buffer with a guard region."""
+    window = w.window if window is None else window
+    qkv = workloads.draw_qkv(w)
+    cos, sin = workloads.rope_tables(w)
+    dout = _dout(w, seed)
+    dev = torch.device("cuda:0")
+    q, c, s, do = qkv.to(dev), cos.to(dev), sin.to(dev), dout.to(dev)
+    out, lse = vlf.attend(q, c, s, w.cu, w.heads, window, w.scale)
+    batch = vlf.prepare(w.cu, dev, 64, False, window)
+    T, H = w.tokens, w.heads
+    buf = torch.full((T * 3 * H * 64 + GUARD,), float("nan"), dtype=q.dtype, device=dev)
+    dqkv = buf[:T * 3 * H * 64].view(T, 3 * H * 64)
+    vlf.attend_backward_into(batch, q, c, s, H, window, w.scale, out, lse, do, dqkv)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[T * 3 * H * 64:]).all(), "guard region written"
+    return qkv, cos, sin, dout, dqkv.float().cpu().numpy()
+
+
+def compare(name, w, qkv, cos, sin, dout, got, window=None):
+    window = w.window if window is None else window
+    want = oracle.attend_backward(qkv.float().numpy(), cos.float().numpy(), sin.float().numpy(),
+                                  w.cu, w.heads, window, w.scale, dout.float().numpy(),
+                                  mode="B", dtype=w.dtype)
+    assert np.isfinite(got).all(), "unwritten or non-finite dqkv"
+    top = float(np.abs(want).max())
+    err = float(np.abs(got - want).max())
+    hd = w.heads * 64
+    parts = {k: float(np.abs(got[:, sl] - want[:, sl]).max()) / top
+             for k, sl in (("dq", slice(0, hd)), ("dk", slice(hd, 2 * hd)),
+                           ("dv", slice(2 * hd, 3 * hd)))}
+    _say(f"[backward] {name}: rel {err / top:.2e} (tol {REL_TOL[w.dtype]:.0e}); "
+         + ", ".join(f"{k} {v:.2e}" for k, v in parts.items()))
+    assert err <= REL_TOL[w.dtype] * top, (name, err / top)
+
+
+LENS = [5, 40, 1, 33, 70]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("window", [0, 9, 65])
+def test_backward_page_fixture(dtype, window):
+    w = workloads.custom(LENS, 2, dtype=dtype, window=window, table_rows=128, seed=7)
+    _say(f"case backward page fixture {dtype} W={window}")
+    qkv, cos, sin, dout, got = run_backward(w, seed=1)
+    compare(f"lens {LENS} {dtype} W={window}", w, qkv, cos, sin, dout, got)
+
+
+RAGGED = [1, 63, 64, 65, 127, 128, 129, 300, 0, 257, 31, 32, 33, 2]
+
+
+@pytest.mark.parametrize("window", [0, 1, 33, 128])
+def test_backward_ragged(window):
+    w = workloads.custom(RAGGED, 3, dtype="bf16", window=window, base=1e4, table_rows=512,
+                         seed=11)
+    _say(f"case backward ragged W={window}")
+    qkv, cos, sin, dout, got = run_backward(w, seed=2)
+    compare(f"ragged W={window}", w, qkv, cos, sin, dout, got)
+
+
+@pytest.mark.parametrize("dtype,window", [("bf16", 0), ("bf16", 300), ("fp16", 0)])
+def test_backward_longer_sequences(dtype, window):
+    """Many key tiles per sequence: dQ of each query row summed by atomics from up to 21 key
+    tiles."""
+    w = workloads.custom([700, 1300, 64], 2, dtype=dtype, window=window, base=1.6e5,
+                         table_rows=1300, seed=19)
+    _say(f"case backward longer {dtype} W={window}")
+    qkv, cos, sin, dout, got = run_backward(w, seed=3)
+    compare(f"[700, 1300, 64] {dtype} W={window}", w, qkv, cos, sin, dout, got)
+
+
+def test_backward_single_key_rows():
+    """W = 1: each row sees only itself, so dv = dout and dq, dk are zero up to the rounding of
+    dP - delta (one key's dO.v against the same product summed by the delta kernel)."""
+    w = workloads.custom([1, 7, 130, 64, 300], 2, dtype="bf16", window=1, table_rows=512, seed=5)
+    _say("case backward single-key rows")
+    qkv, cos, sin, dout, got = run_backward(w, seed=4)
+    hd = w.heads * 64
+    d = dout.float().numpy()
+    assert np.abs(got[:, 2 * hd:] - d).max() <= 2 ** -8 * np.abs(d).max()
+    assert np.abs(got[:, :2 * hd]).max() <= 1e-2

@@ -1,11 +1,12 @@
-"""MI355X-native packed variable-length attention forward (RoPE in the kernel, optional
-symmetric window), built around the C-ABI library ``libvlf.so`` of hand-written gfx950 HIP.
+"""MI355X-native packed variable-length attention, forward and backward (RoPE in the kernel,
+optional symmetric window), built around the C-ABI library ``libvlf.so`` of hand-written gfx950 HIP.
 
 The binding (``variable_length_flash_amd.binding``) loads the library on first use and fails
 loudly when it is missing: there is no fallback path.
 """
 from .binding import (  # noqa: F401
-    Batch, VlfError, attend, attend_into, attend_rotated_into, choose_br, choose_prerotate,
-    library_path, load_library, new_workspace, prepare, rotate_keys, tile_count, tile_table,
-    typical_length, visible_pairs, workspace_bytes,
+    Batch, VlfError, attend, attend_backward, attend_backward_into, attend_into,
+    attend_rotated_into, backward_workspace_bytes, choose_br, choose_prerotate, library_path,
+    load_library, new_workspace, prepare, rotate_keys, tile_count, tile_table, typical_length,
+    visible_pairs, workspace_bytes,
 )

@@ -22,7 +22,7 @@ HEAD_DIM = 64
 # every function include/vlf.h declares
 EXPORTS = ("vlf_version", "vlf_last_error", "vlf_tile_count", "vlf_tile_table",
            "vlf_visible_pairs", "vlf_workspace_bytes", "vlf_attend", "vlf_rotate_keys",
-           "vlf_attend_rotated")
+           "vlf_attend_rotated", "vlf_backward_workspace_bytes", "vlf_attend_backward")
 
 
 class VlfError(RuntimeError):
@@ -67,6 +67,11 @@ def load_library():
     lib.vlf_attend_rotated.restype = ctypes.c_int
     lib.vlf_rotate_keys.argtypes = [p, p, p, i32, p, i32, i32, i32, i32, p, i64, p]
     lib.vlf_rotate_keys.restype = ctypes.c_int
+    lib.vlf_backward_workspace_bytes.argtypes = [i32, i32, p]
+    lib.vlf_backward_workspace_bytes.restype = ctypes.c_int
+    lib.vlf_attend_backward.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+                                        ctypes.c_float, i32, p, p, p, p, i64, p, p]
+    lib.vlf_attend_backward.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -353,6 +358,59 @@ def attend_rotated_into(batch: Batch, qkv, cos, sin, heads: int, window: int, sc
         batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
         int(window), float(scale), code, ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
         _stream(stream, dev)))
+
+
+def backward_workspace_bytes(tokens: int, heads: int) -> int:
+    """Bytes of the backward's workspace (float32 dQ accumulators and delta)."""
+    n = ctypes.c_int64(0)
+    _check(load_library().vlf_backward_workspace_bytes(int(tokens), int(heads),
+                                                       ctypes.byref(n)))
+    return int(n.value)
+
+
+def attend_backward_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: float,
+                         out, lse, dout, dqkv, stream=None, workspace=None):
+    """Queue the backward (include/vlf.h, vlf_attend_backward): dqkv = d sum(out * dout) / d qkv
+    for the forward with the same arguments, whose ``out`` and ``lse`` are passed in.
+
+    ``batch`` must be prepared with ``br=64`` (64-key tiles). dout and dqkv have the shapes
+    and dtype of out and qkv. ``workspace``: a contiguous uint8 device tensor of at least
+    ``backward_workspace_bytes`` (allocated on the launch stream when None).
+    """
+    import torch
+    if batch.br != 64:
+        raise VlfError(VLF_EINVAL, f"the backward runs on 64-row tiles; batch has br={batch.br}")
+    code = _check_inputs(batch, qkv, cos, sin, heads, out, lse)
+    T = batch.tokens
+    for name, t, shape in (("dout", dout, (T, heads * HEAD_DIM)),
+                           ("dqkv", dqkv, (T, 3 * heads * HEAD_DIM))):
+        if tuple(t.shape) != shape or t.dtype != qkv.dtype or not t.is_contiguous() or \
+                t.device != qkv.device:
+            raise VlfError(VLF_EINVAL, f"{name}: {tuple(t.shape)} {t.dtype} on {t.device}, "
+                                       f"expected {shape} {qkv.dtype} contiguous on {qkv.device}")
+    dev = qkv.device
+    launch = _torch_stream(stream, dev)
+    if workspace is None:
+        with torch.cuda.stream(launch):
+            workspace = torch.empty(backward_workspace_bytes(T, heads), dtype=torch.uint8,
+                                    device=dev)
+    ws_ptr, ws_bytes = _workspace_args(workspace, dev)
+    _check(load_library().vlf_attend_backward(
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        batch.tiles.data_ptr(), batch.num_tiles, T, batch.sequences, heads, int(window),
+        float(scale), code, out.data_ptr(), dout.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
+        dqkv.data_ptr(), launch.cuda_stream))
+
+
+def attend_backward(qkv, cos, sin, cu, heads: int, out, lse, dout, window: int = 0,
+                    scale: float = 0.125):
+    """The backward of ``attend``: returns dqkv [T, 3*heads*64] (zero rows where no sequence
+    reaches)."""
+    import torch
+    batch = cu if isinstance(cu, Batch) else prepare(cu, qkv.device, 64, False, window)
+    dqkv = torch.zeros_like(qkv)
+    attend_backward_into(batch, qkv, cos, sin, heads, window, scale, out, lse, dout, dqkv)
+    return dqkv
 
 
 def attend(qkv, cos, sin, cu, heads: int, window: int = 0, scale: float = 0.125,

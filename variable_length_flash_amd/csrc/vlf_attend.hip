@@ -62,6 +62,7 @@ constexpr int RSRC_WORD3 = 0x00020000;  // buffer descriptor word 3: 32-bit data
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -2084,6 +2085,393 @@ int launch_br(const AttendArgs &a) {
     }
 }
 
+
+// ---- backward: the gradient of sum(out * dout) with respect to qkv ---------------------------
+// hanzo-kernel 0.2.42 src/packed.rs, `delta`, `attend_back` and `rotate_back`: P is recomputed
+// from the forward's lse, dS = P (dP - delta) with delta = rowsum(dO * O), dK and dV are summed
+// per key tile and written rotated back, dQ is added into float32 with atomics and rotated back
+// (and scaled) by a last pass. Every kernel runs on the tile table for 64-row tiles.
+
+constexpr int BQ = 32;  // query rows per step of attend_back
+
+// XCD-aware work index of the block (block b runs on XCD b % 8).
+__device__ __forceinline__ int xcd_work() {
+    const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+    const int xcd = b % XCDS, slot = b / XCDS;
+    const int per = nb / XCDS, extra = nb % XCDS;
+    return xcd * per + min(xcd, extra) + slot;
+}
+
+// The (sequence, first row) of a table entry, or false for an entry that names no tile.
+__device__ __forceinline__ bool back_tile(const uint32_t *tiles, const int32_t *cu, int tile,
+                                          int32_t S, int32_t T, int32_t P, int &start, int &len,
+                                          int &i0) {
+    const uint32_t seq = tiles[2 * tile];
+    i0 = (int)tiles[2 * tile + 1];
+    if (seq >= (uint32_t)S)
+        return false;
+    start = cu[seq];
+    len = cu[seq + 1] - start;
+    return !(i0 < 0 || i0 >= len || len > P || start < 0 || (int64_t)start + len > T);
+}
+
+// delta[h, t] = sum_d dO[t, h, d] O[t, h, d] in float32 for the 64 rows of one tile and head,
+// and the rows' dQ accumulators cleared. Four lanes per row, 16 dims each.
+template <class E>
+__global__ void __launch_bounds__(256)
+back_delta(const uint16_t *__restrict__ out, const uint16_t *__restrict__ dout,
+           const int32_t *__restrict__ cu, const uint32_t *__restrict__ tiles,
+           float *__restrict__ dq, float *__restrict__ delta, int32_t num_tiles, int32_t T,
+           int32_t S, int32_t H, int32_t P) {
+    const int work = xcd_work();
+    const int h = work / num_tiles;
+    int start, len, i0;
+    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, i0))
+        return;
+    const int tid = (int)threadIdx.x;
+    const int r = tid >> 2, q = tid & 3;
+    const int i = i0 + r;
+    const int hd = H * D;
+    float acc = 0.f;
+    if (i < len) {
+        const int64_t at = (int64_t)(start + i) * hd + h * D + 16 * q;
+        const u32x4 oa = *(const u32x4 *)(out + at), ob = *(const u32x4 *)(out + at + 8);
+        const u32x4 da = *(const u32x4 *)(dout + at), db = *(const u32x4 *)(dout + at + 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc = __builtin_fmaf(E::lo(oa[k]), E::lo(da[k]), acc);
+            acc = __builtin_fmaf(E::hi(oa[k]), E::hi(da[k]), acc);
+            acc = __builtin_fmaf(E::lo(ob[k]), E::lo(db[k]), acc);
+            acc = __builtin_fmaf(E::hi(ob[k]), E::hi(db[k]), acc);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            *(f32x4 *)(dq + at + 4 * k) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (i < len && q == 0)
+        delta[(int64_t)h * T + start + i] = acc;
+}
+
+// dQ of the 64 rows of one tile and head rotated back to the rows' positions (the transpose of
+// the half-split rotation) and scaled, into the query part of dqkv. Pairs m = 8q .. 8q+7.
+template <class E>
+__global__ void __launch_bounds__(256)
+back_rotate(const float *__restrict__ dq, const uint16_t *__restrict__ cos_t,
+            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+            const uint32_t *__restrict__ tiles, uint16_t *__restrict__ dqkv, int32_t num_tiles,
+            int32_t T, int32_t S, int32_t H, int32_t P, float scale) {
+    const int work = xcd_work();
+    const int h = work / num_tiles;
+    int start, len, i0;
+    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, i0))
+        return;
+    const int tid = (int)threadIdx.x;
+    const int r = tid >> 2, q = tid & 3;
+    const int i = i0 + r;
+    if (i >= len)
+        return;
+    const int hd = H * D;
+    const float *x = dq + (int64_t)(start + i) * hd + h * D;
+    const u32x4 c = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * q);
+    const u32x4 s = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * q);
+    uint32_t a[4], b[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float y1[2], y2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int m = 8 * q + 2 * k + e;
+            const float x1 = x[m], x2 = x[m + 32];
+            const float cm = e ? E::hi(c[k]) : E::lo(c[k]);
+            const float sm = e ? E::hi(s[k]) : E::lo(s[k]);
+            y1[e] = scale * (x1 * cm + x2 * sm);
+            y2[e] = scale * (x2 * cm - x1 * sm);
+        }
+        asm volatile("" : "+v"(y1[0]), "+v"(y1[1]), "+v"(y2[0]), "+v"(y2[1]));
+        a[k] = E::pack(y1[0], y1[1]);
+        b[k] = E::pack(y2[0], y2[1]);
+    }
+    uint16_t *o = dqkv + (int64_t)(start + i) * 3 * hd + h * D;
+    *(u32x4 *)(o + 8 * q) = u32x4{a[0], a[1], a[2], a[3]};
+    *(u32x4 *)(o + 32 + 8 * q) = u32x4{b[0], b[1], b[2], b[3]};
+}
+
+// One key tile (64 keys) of one head against every query row its window reaches, 32 rows at a
+// time (FlashAttention-2's backward). Wave w owns keys 32w .. 32w+31 of the tile and keeps their
+// rotated keys K~ and values V in registers as the B operands of S = Q~ K~^T and dP = dO V^T,
+// whose accumulators hold one key per lane and 16 query rows. Per step the query rows are
+// staged in LDS as Q~ and dO images and as their transposes with the query slots permuted the
+// way vt_slot permutes keys, so P and dS go straight from the accumulators into the B operands
+// of dV^T += dO^T P and dK^T += Q~^T dS. dS also goes to LDS once, for dQ = dS K~ over the
+// tile's 64 keys (wave w: dims 32w .. 32w+31), which is added into the float32 dQ buffer. LDS
+// images have 128-byte rows with 16-byte chunk c of row r at chunk c ^ swz(r).
+template <class E>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
+attend_back(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+            const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
+            const float *__restrict__ lse, const float *__restrict__ delta,
+            float *__restrict__ dq, uint16_t *__restrict__ dqkv, int32_t num_tiles, int32_t T,
+            int32_t S, int32_t H, int32_t P, int32_t window, float scale) {
+    __shared__ __attribute__((aligned(16))) uint8_t qs[BQ * 128];  // Q~ [query][dim]
+    __shared__ __attribute__((aligned(16))) uint8_t os[BQ * 128];  // dO [query][dim]
+    __shared__ __attribute__((aligned(16))) uint8_t qt[D * 128];   // Q~^T [dim][query slot]
+    __shared__ __attribute__((aligned(16))) uint8_t ot[D * 128];   // dO^T [dim][query slot]
+    __shared__ __attribute__((aligned(16))) uint8_t kt[D * 128];   // K~^T [dim][key]
+    __shared__ __attribute__((aligned(16))) uint8_t dss[BQ * 128]; // dS [query][key]
+    __shared__ __attribute__((aligned(16))) float lb[BQ];          // lse * log2(e) per row
+    __shared__ __attribute__((aligned(16))) float dl[BQ];          // delta per row
+
+    const int work = xcd_work();
+    const int h = work / num_tiles;
+    int start, len, j0;
+    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, j0))
+        return;
+    const int64_t ld = 3LL * H * D;
+    const int hd = H * D;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int kk = 32 * wv + n;  // this lane's key within the tile
+    const int kj = j0 + kk;
+
+    // the lane's key (rotated and rounded as the forward rounds it) and value, dims 16c + 8g ..
+    u32x4 kop[4], vop[4];
+    {
+        QueryRaw r;
+        query_load(r, qkv + hd, cos_t, sin_t, ld, start, kj, len, h, g);
+        query_make<E>(r, 1.0f, kop);
+        const u32x4 z = {0, 0, 0, 0};
+        u32x4 v0 = z, v1 = z, v2 = z, v3 = z;
+        if (kj < len) {
+            const uint16_t *vr = qkv + (int64_t)(start + kj) * ld + 2 * hd + h * D + 8 * g;
+            v0 = *(const u32x4 *)vr;
+            v1 = *(const u32x4 *)(vr + 16);
+            v2 = *(const u32x4 *)(vr + 32);
+            v3 = *(const u32x4 *)(vr + 48);
+        }
+        vop[0] = v0, vop[1] = v1, vop[2] = v2, vop[3] = v3;
+    }
+    // K~^T for dQ: element (dim d, key kk)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int d = 16 * c + 8 * g + 2 * w + e;
+                const uint32_t word = kop[c][w];
+                *(uint16_t *)(kt + d * 128 + 16 * ((kk >> 3) ^ swz(d)) + 2 * (kk & 7)) =
+                    (uint16_t)(e ? word >> 16 : word & 0xffffu);
+            }
+
+    // query rows some key of the tile sees: [qa, qb), qa a multiple of BQ
+    int qa = 0, qb = len;
+    if (window > 0) {
+        if (j0 + 1 > window)
+            qa = (j0 + 1 - window) / BQ * BQ;
+        if ((int64_t)j0 + BC - 1 + window < len)
+            qb = j0 + BC - 1 + window;
+    }
+    // query rows key kj sees: [vlo, vhi) (empty past the sequence)
+    int vlo = 0, vhi = 0;
+    if (kj < len) {
+        vlo = window > 0 ? max(kj - window + 1, 0) : 0;
+        vhi = (window > 0 && window < len - kj) ? kj + window : len;
+    }
+    f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
+    const int row = tid >> 2, q4 = tid & 3;  // staging: query row, dims 8q4 .. and 32 + 8q4 ..
+    const int slot = vt_slot(row);          // the row's slot in the transposed images
+    for (int it = qa; it < qb; it += BQ) {
+        __syncthreads();  // the previous step's reads are done
+        {
+            const int i = it + row;
+            const u32x4 z = {0, 0, 0, 0};
+            u32x4 x1 = z, x2 = z, c = z, s = z, o1 = z, o2 = z;
+            if (i < len) {
+                const uint16_t *qr = qkv + (int64_t)(start + i) * ld + h * D;
+                x1 = *(const u32x4 *)(qr + 8 * q4);
+                x2 = *(const u32x4 *)(qr + 32 + 8 * q4);
+                c = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * q4);
+                s = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * q4);
+                const uint16_t *orow = dout + (int64_t)(start + i) * hd + h * D;
+                o1 = *(const u32x4 *)(orow + 8 * q4);
+                o2 = *(const u32x4 *)(orow + 32 + 8 * q4);
+            }
+            const uint32_t a_[4] = {x1[0], x1[1], x1[2], x1[3]}, b_[4] = {x2[0], x2[1], x2[2], x2[3]};
+            const uint32_t c_[4] = {c[0], c[1], c[2], c[3]}, s_[4] = {s[0], s[1], s[2], s[3]};
+            uint32_t y1[4], y2[4];
+            rotate<E, 4>(a_, b_, c_, s_, scale, y1, y2);
+            *(u32x4 *)(qs + row * 128 + 16 * (q4 ^ swz(row))) = u32x4{y1[0], y1[1], y1[2], y1[3]};
+            *(u32x4 *)(qs + row * 128 + 16 * ((4 + q4) ^ swz(row))) =
+                u32x4{y2[0], y2[1], y2[2], y2[3]};
+            *(u32x4 *)(os + row * 128 + 16 * (q4 ^ swz(row))) = o1;
+            *(u32x4 *)(os + row * 128 + 16 * ((4 + q4) ^ swz(row))) = o2;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int d1 = 8 * q4 + 2 * w + e, d2 = d1 + 32;
+                    const int sh = e ? 16 : 0;
+                    const int p1 = d1 * 128 + 16 * ((slot >> 3) ^ swz(d1)) + 2 * (slot & 7);
+                    const int p2 = d2 * 128 + 16 * ((slot >> 3) ^ swz(d2)) + 2 * (slot & 7);
+                    *(uint16_t *)(qt + p1) = (uint16_t)(y1[w] >> sh);
+                    *(uint16_t *)(qt + p2) = (uint16_t)(y2[w] >> sh);
+                    *(uint16_t *)(ot + p1) = (uint16_t)(o1[w] >> sh);
+                    *(uint16_t *)(ot + p2) = (uint16_t)(o2[w] >> sh);
+                }
+            if (q4 == 0) {
+                lb[row] = i < len ? lse[(int64_t)h * T + start + i] * LOG2E : 0.f;
+                dl[row] = i < len ? delta[(int64_t)h * T + start + i] : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // S = Q~ K~^T and dP = dO V^T for the wave's 32 keys: register i holds query row
+        // it + 8(i/4) + 4g + i%4 of key kj
+        f32x16 sc = {}, dp = {};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int off = n * 128 + 16 * ((2 * c + g) ^ swz(n));
+            sc = E::mfma(*(const u32x4 *)(qs + off), kop[c], sc);
+            dp = E::mfma(*(const u32x4 *)(os + off), vop[c], dp);
+        }
+        // P = exp(S - lse) over the rows key kj sees (0 elsewhere), dS = P (dP - delta)
+        {
+            const int a = vlo - it - 4 * g;
+            const uint32_t span = (uint32_t)max(vhi - vlo, 0);
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const f32x4 lv = *(const f32x4 *)(lb + 8 * gi + 4 * g);
+                const f32x4 dv = *(const f32x4 *)(dl + 8 * gi + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * gi + e;
+                    const bool vis = (uint32_t)(8 * gi + e - a) < span;
+                    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], LOG2E, -lv[e]))
+                                        : 0.f;
+                    sc[i] = p;
+                    dp[i] = p * (dp[i] - dv[e]);
+                }
+            }
+        }
+        u32x4 pp[2], pd[2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                pp[kc][k] = E::pack(sc[8 * kc + 2 * k], sc[8 * kc + 2 * k + 1]);
+                pd[kc][k] = E::pack(dp[8 * kc + 2 * k], dp[8 * kc + 2 * k + 1]);
+            }
+        // dV^T += dO^T P and dK^T += Q~^T dS (dims 0..31 and 32..63 by the wave's keys)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const int r0 = n, r1 = 32 + n;
+            const int f0 = r0 * 128 + 16 * ((2 * kc + g) ^ swz(r0));
+            const int f1 = r1 * 128 + 16 * ((2 * kc + g) ^ swz(r1));
+            dv0 = E::mfma(*(const u32x4 *)(ot + f0), pp[kc], dv0);
+            dv1 = E::mfma(*(const u32x4 *)(ot + f1), pp[kc], dv1);
+            dk0 = E::mfma(*(const u32x4 *)(qt + f0), pd[kc], dk0);
+            dk1 = E::mfma(*(const u32x4 *)(qt + f1), pd[kc], dk1);
+        }
+        // dS, rounded as it entered the products, into [query][key] for dQ
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int q = 8 * (i >> 2) + 4 * g + (i & 3);
+            const uint32_t word = pd[i >> 3][(i & 7) >> 1];
+            *(uint16_t *)(dss + q * 128 + 16 * ((kk >> 3) ^ swz(q)) + 2 * (kk & 7)) =
+                (uint16_t)((i & 1) ? word >> 16 : word & 0xffffu);
+        }
+        __syncthreads();
+        // dQ = dS K~ over the tile's keys, dims 32 wv + n; register i: row it + 8(i/4) + 4g + i%4
+        f32x16 dqa = {};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int rk = 32 * wv + n;
+            const u32x4 a = *(const u32x4 *)(dss + n * 128 + 16 * ((2 * c + g) ^ swz(n)));
+            const u32x4 bb = *(const u32x4 *)(kt + rk * 128 + 16 * ((2 * c + g) ^ swz(rk)));
+            dqa = E::mfma(a, bb, dqa);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int q = it + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (q < len)
+                unsafeAtomicAdd(dq + (int64_t)(start + q) * hd + h * D + 32 * wv + n, dqa[i]);
+        }
+    }
+
+    // dK rotated back to the key's position, and dV; register i of block b holds dim
+    // 32b + 8(i/4) + 4g + i%4 of key kj
+    if (kj < len) {
+        const uint16_t *cr = cos_t + (int64_t)kj * 32, *sr = sin_t + (int64_t)kj * 32;
+        uint16_t *o = dqkv + (int64_t)(start + kj) * ld + h * D;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const int m0 = 8 * gi + 4 * g;
+            const u32x2 cw = *(const u32x2 *)(cr + m0), sw = *(const u32x2 *)(sr + m0);
+            float a[4], b[4], v0[4], v1[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float cm = (e & 1) ? E::hi(cw[e >> 1]) : E::lo(cw[e >> 1]);
+                const float sm = (e & 1) ? E::hi(sw[e >> 1]) : E::lo(sw[e >> 1]);
+                const float x1 = dk0[4 * gi + e], x2 = dk1[4 * gi + e];
+                a[e] = x1 * cm + x2 * sm;
+                b[e] = x2 * cm - x1 * sm;
+                v0[e] = dv0[4 * gi + e];
+                v1[e] = dv1[4 * gi + e];
+            }
+            asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+            asm volatile("" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+            *(u32x2 *)(o + hd + m0) = u32x2{E::pack(a[0], a[1]), E::pack(a[2], a[3])};
+            *(u32x2 *)(o + hd + 32 + m0) = u32x2{E::pack(b[0], b[1]), E::pack(b[2], b[3])};
+            *(u32x2 *)(o + 2 * hd + m0) = u32x2{E::pack(v0[0], v0[1]), E::pack(v0[2], v0[3])};
+            *(u32x2 *)(o + 2 * hd + 32 + m0) = u32x2{E::pack(v1[0], v1[1]), E::pack(v1[2], v1[3])};
+        }
+    }
+}
+
+template <class E>
+int launch_backward_typed(const BackArgs &a) {
+    const int64_t blocks = (int64_t)a.num_tiles * a.H;
+    if (blocks > INT32_MAX)
+        return fail(VLF_EINVAL, "%lld workgroups exceed the grid limit", (long long)blocks);
+    const uint16_t *qkv = (const uint16_t *)a.qkv, *cs = (const uint16_t *)a.cos;
+    const uint16_t *sn = (const uint16_t *)a.sin, *out = (const uint16_t *)a.out;
+    const uint16_t *dout = (const uint16_t *)a.dout;
+    uint16_t *dqkv = (uint16_t *)a.dqkv;
+    float *dq = (float *)a.workspace;
+    float *delta = dq + (int64_t)a.T * a.H * D;
+    const float *lse = a.lse;
+    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows, W = a.window;
+    float scale = a.scale;
+    hipStream_t st = (hipStream_t)a.stream;
+    void *args1[] = {(void *)&out, (void *)&dout, (void *)&a.cu, (void *)&a.tiles, (void *)&dq,
+                     (void *)&delta, (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H,
+                     (void *)&P};
+    hipError_t e = hipLaunchKernel((const void *)back_delta<E>, dim3((unsigned)blocks), dim3(256),
+                                   args1, 0, st);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "delta launch failed: %s", hipGetErrorString(e));
+    void *args2[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
+                     (void *)&dout, (void *)&lse, (void *)&delta, (void *)&dq, (void *)&dqkv,
+                     (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H, (void *)&P,
+                     (void *)&W, (void *)&scale};
+    e = hipLaunchKernel((const void *)attend_back<E>, dim3((unsigned)blocks), dim3(128), args2, 0,
+                        st);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+    const float *dqc = dq;
+    void *args3[] = {(void *)&dqc, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
+                     (void *)&dqkv, (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H,
+                     (void *)&P, (void *)&scale};
+    e = hipLaunchKernel((const void *)back_rotate<E>, dim3((unsigned)blocks), dim3(256), args3, 0,
+                        st);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "dQ rotation launch failed: %s", hipGetErrorString(e));
+    return VLF_OK;
+}
 }  // namespace
 
 // attend_slide serves 256-row tiles whose window reaches at most eight key tiles: keys from
@@ -2094,6 +2482,14 @@ static bool slide_fits(int32_t window) {
     const int64_t back = ((int64_t)window - 1 + BC - 1) / BC * BC;
     const int64_t span = back + 256 + window - 1;
     return (span + BC - 1) / BC <= 8;
+}
+
+int64_t backward_workspace_bytes(int32_t T, int32_t H) {
+    return (int64_t)T * H * (D + 1) * 4;
+}
+
+int launch_backward(const BackArgs &a) {
+    return a.dtype == VLF_BF16 ? launch_backward_typed<BF16>(a) : launch_backward_typed<F16>(a);
 }
 
 int launch_attend(const AttendArgs &a, Launch what) {

@@ -231,6 +231,50 @@ int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_
                          Launch::kRotated);
 }
 
+int vlf_backward_workspace_bytes(int32_t T, int32_t H, int64_t *bytes) {
+    if (!bytes)
+        return fail(VLF_EINVAL, "null bytes");
+    if (T < 0 || H < 0 || H > 65536)
+        return fail(VLF_EINVAL, "T = %d, H = %d", T, H);
+    *bytes = backward_workspace_bytes(T, H);
+    return VLF_OK;
+}
+
+int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                        const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
+                        int32_t T, int32_t S, int32_t H, int32_t window, float scale,
+                        int32_t dtype, const void *out, const void *dout, const float *lse,
+                        void *workspace, int64_t workspace_bytes_, void *dqkv, void *stream) {
+    if (dtype != VLF_BF16 && dtype != VLF_F16)
+        return fail(VLF_EUNSUPPORTED, "dtype = %d; supported: VLF_F16 (0), VLF_BF16 (1)", dtype);
+    if (window < 0)
+        return fail(VLF_EINVAL, "window = %d < 0", window);
+    if (num_tiles < 0)
+        return fail(VLF_EINVAL, "negative size: num_tiles=%d", num_tiles);
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(VLF_EINVAL, "scale is not finite");
+    const bool work = T > 0 && num_tiles > 0;
+    // the forward's checks, without its workspace (this call's workspace is checked below)
+    int rc = check_launch(qkv, cos, sin, table_rows, cu_dev, T, S, H, dtype, nullptr, 0, work,
+                          false);
+    if (rc)
+        return rc;
+    if (workspace_bytes_ < 0)
+        return fail(VLF_EINVAL, "workspace_bytes = %lld < 0", (long long)workspace_bytes_);
+    if (!work)
+        return VLF_OK;
+    if (!workspace || workspace_bytes_ < backward_workspace_bytes(T, H))
+        return fail(VLF_EINVAL, "workspace of %lld bytes; T=%d H=%d need %lld",
+                    (long long)(workspace ? workspace_bytes_ : 0), T, H,
+                    (long long)backward_workspace_bytes(T, H));
+    if (!tiles_dev || !out || !dout || !lse || !dqkv)
+        return fail(VLF_EINVAL, "null device pointer (tiles=%p out=%p dout=%p lse=%p dqkv=%p)",
+                    (const void *)tiles_dev, out, dout, (const void *)lse, dqkv);
+    BackArgs a{qkv, cos,   sin,   table_rows, cu_dev, tiles_dev, num_tiles, T,  S,    H,
+               window, scale, dtype, out,      dout,   lse,       workspace, dqkv, stream};
+    return launch_backward(a);
+}
+
 int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
                     const int32_t *cu_dev, int32_t T, int32_t S, int32_t H, int32_t dtype,
                     void *workspace, int64_t workspace_bytes_, void *stream) {

@@ -40,6 +40,33 @@ enum class Launch {
 // Queue the forward kernels; returns a vlf_status.
 int launch_attend(const AttendArgs &a, Launch what);
 
+// The backward's arguments after validation; tiles are the 64-row tile table.
+struct BackArgs {
+    const void *qkv;
+    const void *cos;
+    const void *sin;
+    int32_t table_rows;
+    const int32_t *cu;
+    const uint32_t *tiles;
+    int32_t num_tiles;
+    int32_t T, S, H;
+    int32_t window;
+    float scale;
+    int32_t dtype;
+    const void *out;
+    const void *dout;
+    const float *lse;
+    void *workspace;  // dQ accumulators (float32 [T, H*64]) then delta (float32 [H, T])
+    void *dqkv;
+    void *stream;
+};
+
+// Bytes of the backward's workspace.
+int64_t backward_workspace_bytes(int32_t T, int32_t H);
+
+// Queue the backward kernels (delta, attend_back, rotate_back); returns a vlf_status.
+int launch_backward(const BackArgs &a);
+
 // Record the calling thread's error message (printf-style) and return `status`.
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 
