@@ -43,7 +43,7 @@ PEAK_BF16_TFLOPS = 2516.6     # dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0         # HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flash_amd", "csrc", "vlf_attend.hip")
 KERNEL_NAMES = ("attend_pre_ph", "attend_pre", "attend_fwd", "attend_one", "attend_slide",
-                "prep_tiles")
+                "prep_tiles", "attend_back")
 
 
 def forward_kernel(prerotate: bool, br: int, window: int) -> str:
@@ -191,6 +191,9 @@ def run(args):
         if ev is not None:
             ev[2].record(stream)
 
+    if args.backward:
+        return run_backward(args, w, q, c, s, out, lse, stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -251,6 +254,77 @@ def run(args):
     }
     if not args.profile_run and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, qkv, cos, sin, args.cpu_seconds, pairs)
+    print(json.dumps(line), flush=True)
+
+
+def run_backward(args, w, q, c, s, out, lse, stream):
+    """``--backward``: the library's forward once (out, lse), then K timed backward calls
+    (include/vlf.h, vlf_attend_backward: delta, back_kv, back_q) on a seeded dout.
+    Effective FLOP = 640 per visible pair and head: the five 64-deep products S, dP, dV, dK and
+    dQ, against the forward's two."""
+    import numpy as np
+    import torch
+
+    import variable_length_flash_amd as vlf
+    dev = q.device
+    vlf.attend_into(vlf.prepare(w.cu, dev, None, None, w.window), q, c, s, w.heads, w.window,
+                    w.scale, out, lse)
+    rng = np.random.default_rng(17)
+    dout = torch.from_numpy(rng.standard_normal((w.tokens, w.heads * 64), dtype=np.float32)).to(
+        dev, q.dtype)
+    br = args.br or vlf.choose_backward_br(vlf.typical_length(w.cu))
+    batch = vlf.prepare(w.cu, dev, br, False, w.window)
+    dqkv = torch.empty_like(q)
+    ws = torch.empty(vlf.backward_workspace_bytes(w.tokens, w.heads), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        vlf.attend_backward_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse, dout,
+                                 dqkv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    pairs = vlf.visible_pairs(w.cu, w.window)
+    flops = 640 * pairs * w.heads
+    # qkv, out and dout read once, dqkv written once, lse read once
+    alg_bytes = (3 + 1 + 1 + 3) * w.tokens * w.heads * 64 * 2 + 4 * w.heads * w.tokens
+    value = flops / (wall_ms / 1e3) / 1e12
+    line = {
+        "metric": "effective backward TFLOP/s (visible pairs, 5 products) + % of bf16 MFMA peak, "
+                  "1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {w.note}", "tokens": w.tokens,
+            "sequences": w.sequences, "heads": w.heads, "head_dim": 64, "window": w.window,
+            "br": br, "path": "backward",
+            "kernel_ms": {"backward (3 kernels)": round(kernel_ms, 4)},
+            "visible_pairs_per_head": pairs, "effective_flop": flops,
+            "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": roofline("back_kv + back_q", flops, alg_bytes, kernel_ms, None),
+        "cpu_baseline": None,
+    }
     print(json.dumps(line), flush=True)
 
 
@@ -331,6 +405,8 @@ def main():
     ap.add_argument("--kernel", default="attend_pre_ph", choices=KERNEL_NAMES,
                     help="kernel whose counters --summarize reads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (vlf_attend_backward) instead of the forward")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", nargs="+")

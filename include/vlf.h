@@ -185,8 +185,8 @@ int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_
                        float *lse, void *stream);
 
 /*
- * Device workspace vlf_attend_backward needs for T tokens and H heads: the float32 dQ
- * accumulators [T, H*64] followed by float32 delta [H, T], T * H * 65 * 4 bytes in all.
+ * Device workspace vlf_attend_backward needs for T tokens and H heads: float32 delta [H, T],
+ * T * H * 4 bytes.
  *   bytes  out: the size (0 when T or H is 0).
  * Errors: VLF_EINVAL (negative size, H > 65536, null bytes).
  */
@@ -203,12 +203,16 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t H, int64_t *bytes);
  *     dv_j    = sum_i p_ij dout_i;
  *     dk_j    = the transposed rotation at position j of sum_i ds_ij q~_i;
  *     dq_i    = scale times the transposed rotation at position i of sum_j ds_ij k~_j.
- *   p and ds are rounded to the storage type where they enter matrix products; dq is summed in
- *   float32 in the workspace.
+ *   p and ds are rounded to the storage type where they enter matrix products; every sum is
+ *   float32 in registers and every element of dqkv is written once (no atomics: the same
+ *   inputs give the same bits). dq has a pass of its own that recomputes p and ds; the page
+ *   adds dq into float32 with atomics instead.
  *
  *   qkv, cos, sin, table_rows, cu_dev, T, S, H, window, scale, dtype  as in vlf_attend.
- *   tiles_dev, num_tiles  the tile table for 64-row tiles (vlf_tile_table with br = 64, or any
- *              permutation of it); each entry is a 64-key tile of one sequence.
+ *   tiles_dev, num_tiles  the tile table for br-row tiles (vlf_tile_table with this br, or any
+ *              permutation of it): each entry is a key tile of the dK/dV pass and a query tile
+ *              of the dQ pass.
+ *   br         64 or 128.
  *   out        device, [T, H*64] of `dtype`: the forward's output for these inputs.
  *   dout       device, [T, H*64] of `dtype`: the gradient of the loss with respect to out.
  *   lse        device, [H, T] float32: the forward's log-sum-exp for these inputs.
@@ -217,13 +221,13 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t H, int64_t *bytes);
  *   stream     hipStream_t (NULL = the null stream). Three kernels; asynchronous; allocates
  *              nothing. Calls that may overlap in time need separate workspaces.
  *
- * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, negative sizes,
- * T or S inconsistent, a workspace smaller than vlf_backward_workspace_bytes), VLF_EUNSUPPORTED
- * (dtype), VLF_EHIP (launch failure).
+ * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, br not 64 or
+ * 128, negative sizes, T or S inconsistent, a workspace smaller than
+ * vlf_backward_workspace_bytes), VLF_EUNSUPPORTED (dtype), VLF_EHIP (launch failure).
  */
 int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
                         const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                        int32_t T, int32_t S, int32_t H, int32_t window, float scale,
+                        int32_t br, int32_t T, int32_t S, int32_t H, int32_t window, float scale,
                         int32_t dtype, const void *out, const void *dout, const float *lse,
                         void *workspace, int64_t workspace_bytes, void *dqkv, void *stream);
 

@@ -159,6 +159,8 @@ def test_attend_with_no_work_is_a_no_op():
     # no tiles or no tokens: returns OK without touching the (fake) pointers or the device
     assert _attend_status(nt=0)[0] == binding.VLF_OK
     assert _attend_status(T=0, S=0, nt=0, qkv=None, out=None)[0] == binding.VLF_OK
+    for br in (64, 128, 256):  # every tile height the forward serves passes validation
+        assert _attend_status(nt=0, br=br)[0] == binding.VLF_OK
 
 
 @pytest.mark.parametrize("T,S,H", [(0, 0, 1), (1, 1, 1), (63, 1, 1), (64, 1, 1), (100, 2, 2),
@@ -289,7 +291,7 @@ def test_tile_count_and_table_at_int32_extremes():
 
 def test_backward_workspace_bytes():
     assert vlf.backward_workspace_bytes(0, 4) == 0
-    assert vlf.backward_workspace_bytes(1000, 12) == 1000 * 12 * 65 * 4
+    assert vlf.backward_workspace_bytes(1000, 12) == 1000 * 12 * 4
     lib = vlf.load_library()
     n = ctypes.c_int64(0)
     assert lib.vlf_backward_workspace_bytes(-1, 2, ctypes.byref(n)) == binding.VLF_EINVAL
@@ -301,11 +303,12 @@ def _backward_status(**kw):
     lib = vlf.load_library()
     cu = np.array([0, 100, 256], dtype=np.int32)
     a = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=256, cu=cu.ctypes.data, tiles=0x4000,
-             num_tiles=5, T=256, S=2, H=2, W=0, scale=0.125, dtype=binding.VLF_BF16, out=0x5000,
-             dout=0x6000, lse=0x7000, ws=0x8000, ws_bytes=256 * 2 * 65 * 4, dqkv=0x9000)
+             num_tiles=5, br=64, T=256, S=2, H=2, W=0, scale=0.125, dtype=binding.VLF_BF16,
+             out=0x5000, dout=0x6000, lse=0x7000, ws=0x8000, ws_bytes=256 * 2 * 4, dqkv=0x9000)
     a.update(kw)
     rc = lib.vlf_attend_backward(a["qkv"], a["cos"], a["sin"], a["P"], a["cu"], a["tiles"],
-                                 a["num_tiles"], a["T"], a["S"], a["H"], a["W"], a["scale"],
+                                 a["num_tiles"], a["br"], a["T"], a["S"], a["H"], a["W"],
+                                 a["scale"],
                                  a["dtype"], a["out"], a["dout"], a["lse"], a["ws"],
                                  a["ws_bytes"], a["dqkv"], None)
     return rc, lib.vlf_last_error().decode()
@@ -314,6 +317,8 @@ def _backward_status(**kw):
 @pytest.mark.parametrize("kw,status,text", [
     (dict(dtype=7), binding.VLF_EUNSUPPORTED, "dtype"),
     (dict(W=-1), binding.VLF_EINVAL, "window"),
+    (dict(br=256), binding.VLF_EINVAL, "br = 256"),
+    (dict(br=32), binding.VLF_EINVAL, "br = 32"),
     (dict(H=0), binding.VLF_EINVAL, "H = 0"),
     (dict(ws_bytes=100), binding.VLF_EINVAL, "workspace"),
     (dict(ws=None), binding.VLF_EINVAL, "workspace"),
@@ -324,6 +329,13 @@ def _backward_status(**kw):
 def test_backward_rejects_bad_arguments_before_launching(kw, status, text):
     rc, msg = _backward_status(**kw)
     assert rc == status and text in msg, (rc, msg)
+
+
+def test_choose_backward_br():
+    assert binding.choose_backward_br(0.0) == 64
+    assert binding.choose_backward_br(127.9) == 64
+    assert binding.choose_backward_br(128.0) == 128
+    assert binding.choose_backward_br(8192.0) == 128
 
 
 def test_backward_with_no_tiles_is_a_no_op():

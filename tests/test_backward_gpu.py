@@ -34,8 +34,9 @@ def _dout(w, seed):
         torch.bfloat16 if w.dtype == "bf16" else torch.float16)
 
 
-def run_backward(w, window=None, seed=0):
-    """Forward then backward on cuda:0, dqkv in a NaN-filled buffer with a guard region."""
+def run_backward(w, window=None, seed=0, br=64):
+    """Forward then backward on cuda:0 on br-row tiles, dqkv in a NaN-filled buffer with a guard
+    region."""
     window = w.window if window is None else window
     qkv = workloads.draw_qkv(w)
     cos, sin = workloads.rope_tables(w)
@@ -43,7 +44,7 @@ def run_backward(w, window=None, seed=0):
     dev = torch.device("cuda:0")
     q, c, s, do = qkv.to(dev), cos.to(dev), sin.to(dev), dout.to(dev)
     out, lse = vlf.attend(q, c, s, w.cu, w.heads, window, w.scale)
-    batch = vlf.prepare(w.cu, dev, 64, False, window)
+    batch = vlf.prepare(w.cu, dev, br, False, window)
     T, H = w.tokens, w.heads
     buf = torch.full((T * 3 * H * 64 + GUARD,), float("nan"), dtype=q.dtype, device=dev)
     dqkv = buf[:T * 3 * H * 64].view(T, 3 * H * 64)
@@ -73,44 +74,59 @@ def compare(name, w, qkv, cos, sin, dout, got, window=None):
 LENS = [5, 40, 1, 33, 70]
 
 
+@pytest.mark.parametrize("br", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("window", [0, 9, 65])
-def test_backward_page_fixture(dtype, window):
+def test_backward_page_fixture(dtype, window, br):
     w = workloads.custom(LENS, 2, dtype=dtype, window=window, table_rows=128, seed=7)
-    _say(f"case backward page fixture {dtype} W={window}")
-    qkv, cos, sin, dout, got = run_backward(w, seed=1)
-    compare(f"lens {LENS} {dtype} W={window}", w, qkv, cos, sin, dout, got)
+    _say(f"case backward page fixture {dtype} W={window} br={br}")
+    qkv, cos, sin, dout, got = run_backward(w, seed=1, br=br)
+    compare(f"lens {LENS} {dtype} W={window} br={br}", w, qkv, cos, sin, dout, got)
 
 
 RAGGED = [1, 63, 64, 65, 127, 128, 129, 300, 0, 257, 31, 32, 33, 2]
 
 
+@pytest.mark.parametrize("br", [64, 128])
 @pytest.mark.parametrize("window", [0, 1, 33, 128])
-def test_backward_ragged(window):
+def test_backward_ragged(window, br):
     w = workloads.custom(RAGGED, 3, dtype="bf16", window=window, base=1e4, table_rows=512,
                          seed=11)
-    _say(f"case backward ragged W={window}")
-    qkv, cos, sin, dout, got = run_backward(w, seed=2)
-    compare(f"ragged W={window}", w, qkv, cos, sin, dout, got)
+    _say(f"case backward ragged W={window} br={br}")
+    qkv, cos, sin, dout, got = run_backward(w, seed=2, br=br)
+    compare(f"ragged W={window} br={br}", w, qkv, cos, sin, dout, got)
 
 
-@pytest.mark.parametrize("dtype,window", [("bf16", 0), ("bf16", 300), ("fp16", 0)])
-def test_backward_longer_sequences(dtype, window):
-    """Many key tiles per sequence: dQ of each query row summed by atomics from up to 21 key
-    tiles."""
+@pytest.mark.parametrize("dtype,window,br", [("bf16", 0, 64), ("bf16", 0, 128),
+                                             ("bf16", 300, 128), ("fp16", 0, 128)])
+def test_backward_longer_sequences(dtype, window, br):
+    """Many steps per tile: each key tile's dK, dV and each query tile's dQ summed over up to
+    41 staged steps, through both LDS buffers many times."""
     w = workloads.custom([700, 1300, 64], 2, dtype=dtype, window=window, base=1.6e5,
                          table_rows=1300, seed=19)
-    _say(f"case backward longer {dtype} W={window}")
-    qkv, cos, sin, dout, got = run_backward(w, seed=3)
-    compare(f"[700, 1300, 64] {dtype} W={window}", w, qkv, cos, sin, dout, got)
+    _say(f"case backward longer {dtype} W={window} br={br}")
+    qkv, cos, sin, dout, got = run_backward(w, seed=3, br=br)
+    compare(f"[700, 1300, 64] {dtype} W={window} br={br}", w, qkv, cos, sin, dout, got)
 
 
-def test_backward_single_key_rows():
+def test_backward_is_deterministic():
+    """Every element of dqkv is written once from sums in registers: two runs agree bit for
+    bit."""
+    w = workloads.custom([700, 1300, 64], 2, dtype="bf16", window=0, base=1.6e5,
+                         table_rows=1300, seed=19)
+    _say("case backward determinism")
+    a = run_backward(w, seed=3, br=128)[4]
+    b = run_backward(w, seed=3, br=128)[4]
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("br", [64, 128])
+def test_backward_single_key_rows(br):
     """W = 1: each row sees only itself, so dv = dout and dq, dk are zero up to the rounding of
     dP - delta (one key's dO.v against the same product summed by the delta kernel)."""
     w = workloads.custom([1, 7, 130, 64, 300], 2, dtype="bf16", window=1, table_rows=512, seed=5)
-    _say("case backward single-key rows")
-    qkv, cos, sin, dout, got = run_backward(w, seed=4)
+    _say(f"case backward single-key rows br={br}")
+    qkv, cos, sin, dout, got = run_backward(w, seed=4, br=br)
     hd = w.heads * 64
     d = dout.float().numpy()
     assert np.abs(got[:, 2 * hd:] - d).max() <= 2 ** -8 * np.abs(d).max()

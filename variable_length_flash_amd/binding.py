@@ -69,7 +69,7 @@ def load_library():
     lib.vlf_rotate_keys.restype = ctypes.c_int
     lib.vlf_backward_workspace_bytes.argtypes = [i32, i32, p]
     lib.vlf_backward_workspace_bytes.restype = ctypes.c_int
-    lib.vlf_attend_backward.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+    lib.vlf_attend_backward.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, p, p, p, p, i64, p, p]
     lib.vlf_attend_backward.restype = ctypes.c_int
     _lib = lib
@@ -143,6 +143,15 @@ def typical_length(cu) -> float:
     lens = np.diff(_host_cu(cu).astype(np.int64))
     total = int(lens.sum())
     return float((lens * lens).sum()) / total if total > 0 else 0.0
+
+
+def choose_backward_br(typical: float) -> int:
+    """Tile height of the backward for a batch of typical length ``typical``: 128-row tiles
+    (four waves sharing each staged step) once the typical sequence fills them, else 64."""
+    return 128 if typical >= BACKWARD_TALL else 64
+
+
+BACKWARD_TALL = 128
 
 
 def choose_prerotate(length: float, br: int, window: int = 0) -> bool:
@@ -361,7 +370,7 @@ def attend_rotated_into(batch: Batch, qkv, cos, sin, heads: int, window: int, sc
 
 
 def backward_workspace_bytes(tokens: int, heads: int) -> int:
-    """Bytes of the backward's workspace (float32 dQ accumulators and delta)."""
+    """Bytes of the backward's workspace (float32 delta)."""
     n = ctypes.c_int64(0)
     _check(load_library().vlf_backward_workspace_bytes(int(tokens), int(heads),
                                                        ctypes.byref(n)))
@@ -373,13 +382,14 @@ def attend_backward_into(batch: Batch, qkv, cos, sin, heads: int, window: int, s
     """Queue the backward (include/vlf.h, vlf_attend_backward): dqkv = d sum(out * dout) / d qkv
     for the forward with the same arguments, whose ``out`` and ``lse`` are passed in.
 
-    ``batch`` must be prepared with ``br=64`` (64-key tiles). dout and dqkv have the shapes
-    and dtype of out and qkv. ``workspace``: a contiguous uint8 device tensor of at least
-    ``backward_workspace_bytes`` (allocated on the launch stream when None).
+    ``batch`` must be prepared with ``br`` 64 or 128 (``choose_backward_br``). dout and dqkv
+    have the shapes and dtype of out and qkv. ``workspace``: a contiguous uint8 device tensor of
+    at least ``backward_workspace_bytes`` (allocated on the launch stream when None).
     """
     import torch
-    if batch.br != 64:
-        raise VlfError(VLF_EINVAL, f"the backward runs on 64-row tiles; batch has br={batch.br}")
+    if batch.br not in (64, 128):
+        raise VlfError(VLF_EINVAL, f"the backward runs on 64- or 128-row tiles; batch has "
+                                   f"br={batch.br}")
     code = _check_inputs(batch, qkv, cos, sin, heads, out, lse)
     T = batch.tokens
     for name, t, shape in (("dout", dout, (T, heads * HEAD_DIM)),
@@ -397,9 +407,9 @@ def attend_backward_into(batch: Batch, qkv, cos, sin, heads: int, window: int, s
     ws_ptr, ws_bytes = _workspace_args(workspace, dev)
     _check(load_library().vlf_attend_backward(
         qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
-        batch.tiles.data_ptr(), batch.num_tiles, T, batch.sequences, heads, int(window),
-        float(scale), code, out.data_ptr(), dout.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
-        dqkv.data_ptr(), launch.cuda_stream))
+        batch.tiles.data_ptr(), batch.num_tiles, batch.br, T, batch.sequences, heads,
+        int(window), float(scale), code, out.data_ptr(), dout.data_ptr(), lse.data_ptr(), ws_ptr,
+        ws_bytes, dqkv.data_ptr(), launch.cuda_stream))
 
 
 def attend_backward(qkv, cos, sin, cu, heads: int, out, lse, dout, window: int = 0,
@@ -407,7 +417,9 @@ def attend_backward(qkv, cos, sin, cu, heads: int, out, lse, dout, window: int =
     """The backward of ``attend``: returns dqkv [T, 3*heads*64] (zero rows where no sequence
     reaches)."""
     import torch
-    batch = cu if isinstance(cu, Batch) else prepare(cu, qkv.device, 64, False, window)
+    batch = cu if isinstance(cu, Batch) else prepare(cu, qkv.device,
+                                                     choose_backward_br(typical_length(cu)),
+                                                     False, window)
     dqkv = torch.zeros_like(qkv)
     attend_backward_into(batch, qkv, cos, sin, heads, window, scale, out, lse, dout, dqkv)
     return dqkv

@@ -2088,11 +2088,11 @@ int launch_br(const AttendArgs &a) {
 
 // ---- backward: the gradient of sum(out * dout) with respect to qkv ---------------------------
 // hanzo-kernel 0.2.42 src/packed.rs, `delta`, `attend_back` and `rotate_back`: P is recomputed
-// from the forward's lse, dS = P (dP - delta) with delta = rowsum(dO * O), dK and dV are summed
-// per key tile and written rotated back, dQ is added into float32 with atomics and rotated back
-// (and scaled) by a last pass. Every kernel runs on the tile table for 64-row tiles.
-
-constexpr int BQ = 32;  // query rows per step of attend_back
+// from the forward's lse and dS = P (dP - delta) with delta = rowsum(dO * O). The page sums dK
+// and dV per key tile and adds dQ into float32 with atomics; here dQ has a pass of its own, over
+// query tiles, that recomputes S and dP (two more products) and writes dQ once, rotated back and
+// scaled: no atomics, and the same dqkv bits on every run. Every kernel walks the tile table of
+// the call's tile height (64 or 128 rows): a key tile for back_kv, a query tile for back_q.
 
 // XCD-aware work index of the block (block b runs on XCD b % 8).
 __device__ __forceinline__ int xcd_work() {
@@ -2115,114 +2115,181 @@ __device__ __forceinline__ bool back_tile(const uint32_t *tiles, const int32_t *
     return !(i0 < 0 || i0 >= len || len > P || start < 0 || (int64_t)start + len > T);
 }
 
-// delta[h, t] = sum_d dO[t, h, d] O[t, h, d] in float32 for the 64 rows of one tile and head,
-// and the rows' dQ accumulators cleared. Four lanes per row, 16 dims each.
-template <class E>
+// delta[h, t] = sum_d dO[t, h, d] O[t, h, d] in float32 for the R rows of one tile and head;
+// 256 / R lanes per row.
+template <class E, int R>
 __global__ void __launch_bounds__(256)
 back_delta(const uint16_t *__restrict__ out, const uint16_t *__restrict__ dout,
            const int32_t *__restrict__ cu, const uint32_t *__restrict__ tiles,
-           float *__restrict__ dq, float *__restrict__ delta, int32_t num_tiles, int32_t T,
-           int32_t S, int32_t H, int32_t P) {
+           float *__restrict__ delta, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
+           int32_t P) {
+    constexpr int L = 256 / R, DL = D / L;  // lanes per row, dims per lane
     const int work = xcd_work();
     const int h = work / num_tiles;
     int start, len, i0;
     if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, i0))
         return;
     const int tid = (int)threadIdx.x;
-    const int r = tid >> 2, q = tid & 3;
+    const int r = tid / L, q = tid % L;
     const int i = i0 + r;
     const int hd = H * D;
     float acc = 0.f;
     if (i < len) {
-        const int64_t at = (int64_t)(start + i) * hd + h * D + 16 * q;
-        const u32x4 oa = *(const u32x4 *)(out + at), ob = *(const u32x4 *)(out + at + 8);
-        const u32x4 da = *(const u32x4 *)(dout + at), db = *(const u32x4 *)(dout + at + 8);
+        const int64_t at = (int64_t)(start + i) * hd + h * D + DL * q;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            acc = __builtin_fmaf(E::lo(oa[k]), E::lo(da[k]), acc);
-            acc = __builtin_fmaf(E::hi(oa[k]), E::hi(da[k]), acc);
-            acc = __builtin_fmaf(E::lo(ob[k]), E::lo(db[k]), acc);
-            acc = __builtin_fmaf(E::hi(ob[k]), E::hi(db[k]), acc);
+        for (int c = 0; c < DL / 8; ++c) {
+            const u32x4 o = *(const u32x4 *)(out + at + 8 * c);
+            const u32x4 d = *(const u32x4 *)(dout + at + 8 * c);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc = __builtin_fmaf(E::lo(o[k]), E::lo(d[k]), acc);
+                acc = __builtin_fmaf(E::hi(o[k]), E::hi(d[k]), acc);
+            }
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            *(f32x4 *)(dq + at + 4 * k) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
+#pragma unroll
+    for (int m = 1; m < L; m <<= 1)
+        acc += __shfl_xor(acc, m);
     if (i < len && q == 0)
         delta[(int64_t)h * T + start + i] = acc;
 }
 
-// dQ of the 64 rows of one tile and head rotated back to the rows' positions (the transpose of
-// the half-split rotation) and scaled, into the query part of dqkv. Pairs m = 8q .. 8q+7.
-template <class E>
-__global__ void __launch_bounds__(256)
-back_rotate(const float *__restrict__ dq, const uint16_t *__restrict__ cos_t,
-            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
-            const uint32_t *__restrict__ tiles, uint16_t *__restrict__ dqkv, int32_t num_tiles,
-            int32_t T, int32_t S, int32_t H, int32_t P, float scale) {
-    const int work = xcd_work();
-    const int h = work / num_tiles;
-    int start, len, i0;
-    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, i0))
-        return;
-    const int tid = (int)threadIdx.x;
-    const int r = tid >> 2, q = tid & 3;
-    const int i = i0 + r;
-    if (i >= len)
-        return;
-    const int hd = H * D;
-    const float *x = dq + (int64_t)(start + i) * hd + h * D;
-    const u32x4 c = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * q);
-    const u32x4 s = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * q);
-    uint32_t a[4], b[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float y1[2], y2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int m = 8 * q + 2 * k + e;
-            const float x1 = x[m], x2 = x[m + 32];
-            const float cm = e ? E::hi(c[k]) : E::lo(c[k]);
-            const float sm = e ? E::hi(s[k]) : E::lo(s[k]);
-            y1[e] = scale * (x1 * cm + x2 * sm);
-            y2[e] = scale * (x2 * cm - x1 * sm);
+// One streamed row of a backward step as loaded from HBM: dims 8c .. 8c+7 and 32+8c .. of the
+// rotated tensor x (queries for back_kv, keys for back_q) with the row's cos and sin, the same
+// dims of the second tensor y (dO, or V), and two per-row floats (lse and delta).
+struct BackRaw {
+    u32x4 x1, x2, c, s, y1, y2;
+    float f0, f1;
+};
+
+// Row i of the sequence (zeros past its end). Locals first, then one assignment: an aggregate
+// written under a branch goes to scratch.
+template <bool FLOATS>
+__device__ __forceinline__ void back_load(BackRaw &r, const uint16_t *xb, int64_t xld,
+                                          const uint16_t *yb, int64_t yld,
+                                          const uint16_t *cos_t, const uint16_t *sin_t,
+                                          const float *fa, const float *fb, int start, int i,
+                                          int len, int c4) {
+    const u32x4 z = {0, 0, 0, 0};
+    u32x4 x1 = z, x2 = z, c = z, s = z, y1 = z, y2 = z;
+    float f0 = 0.f, f1 = 0.f;
+    if (i < len) {
+        const uint16_t *xr = xb + (int64_t)(start + i) * xld + 8 * c4;
+        x1 = *(const u32x4 *)xr;
+        x2 = *(const u32x4 *)(xr + 32);
+        c = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * c4);
+        s = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * c4);
+        const uint16_t *yr = yb + (int64_t)(start + i) * yld + 8 * c4;
+        y1 = *(const u32x4 *)yr;
+        y2 = *(const u32x4 *)(yr + 32);
+        if (FLOATS) {
+            f0 = fa[start + i];
+            f1 = fb[start + i];
         }
-        asm volatile("" : "+v"(y1[0]), "+v"(y1[1]), "+v"(y2[0]), "+v"(y2[1]));
-        a[k] = E::pack(y1[0], y1[1]);
-        b[k] = E::pack(y2[0], y2[1]);
     }
-    uint16_t *o = dqkv + (int64_t)(start + i) * 3 * hd + h * D;
-    *(u32x4 *)(o + 8 * q) = u32x4{a[0], a[1], a[2], a[3]};
-    *(u32x4 *)(o + 32 + 8 * q) = u32x4{b[0], b[1], b[2], b[3]};
+    r.x1 = x1, r.x2 = x2, r.c = c, r.s = s, r.y1 = y1, r.y2 = y2, r.f0 = f0, r.f1 = f1;
 }
 
-// One key tile (64 keys) of one head against every query row its window reaches, 32 rows at a
-// time (FlashAttention-2's backward). Wave w owns keys 32w .. 32w+31 of the tile and keeps their
-// rotated keys K~ and values V in registers as the B operands of S = Q~ K~^T and dP = dO V^T,
-// whose accumulators hold one key per lane and 16 query rows. Per step the query rows are
-// staged in LDS as Q~ and dO images and as their transposes with the query slots permuted the
-// way vt_slot permutes keys, so P and dS go straight from the accumulators into the B operands
-// of dV^T += dO^T P and dK^T += Q~^T dS. dS also goes to LDS once, for dQ = dS K~ over the
-// tile's 64 keys (wave w: dims 32w .. 32w+31), which is added into the float32 dQ buffer. LDS
-// images have 128-byte rows with 16-byte chunk c of row r at chunk c ^ swz(r).
-template <class E>
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
-attend_back(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
-            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
-            const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
-            const float *__restrict__ lse, const float *__restrict__ delta,
-            float *__restrict__ dq, uint16_t *__restrict__ dqkv, int32_t num_tiles, int32_t T,
-            int32_t S, int32_t H, int32_t P, int32_t window, float scale) {
-    __shared__ __attribute__((aligned(16))) uint8_t qs[BQ * 128];  // Q~ [query][dim]
-    __shared__ __attribute__((aligned(16))) uint8_t os[BQ * 128];  // dO [query][dim]
-    __shared__ __attribute__((aligned(16))) uint8_t qt[D * 128];   // Q~^T [dim][query slot]
-    __shared__ __attribute__((aligned(16))) uint8_t ot[D * 128];   // dO^T [dim][query slot]
-    __shared__ __attribute__((aligned(16))) uint8_t kt[D * 128];   // K~^T [dim][key]
-    __shared__ __attribute__((aligned(16))) uint8_t dss[BQ * 128]; // dS [query][key]
-    __shared__ __attribute__((aligned(16))) float lb[BQ];          // lse * log2(e) per row
-    __shared__ __attribute__((aligned(16))) float dl[BQ];          // delta per row
+// Element (d, slot) of a transposed image: 128-byte rows, 16-byte chunk c at c ^ swz(d).
+__device__ __forceinline__ int tr_at(int d, int slot) {
+    return d * 128 + 16 * ((slot >> 3) ^ swz(d)) + 2 * (slot & 7);
+}
+
+// Row `row` of a step into the LDS images: x rotated (times `scale`, rounded to E) into its row
+// image xs and its transposed image xt; y into ys and, when YT, into yt. Transposed images hold
+// row r at slot vt_slot(r), the order in which a score accumulator holds its 16-row groups.
+template <class E, bool YT>
+__device__ __forceinline__ void back_stage(const BackRaw &r, float scale, uint8_t *xs,
+                                           uint8_t *xt, uint8_t *ys, uint8_t *yt, int row,
+                                           int c4) {
+    const uint32_t a_[4] = {r.x1[0], r.x1[1], r.x1[2], r.x1[3]};
+    const uint32_t b_[4] = {r.x2[0], r.x2[1], r.x2[2], r.x2[3]};
+    const uint32_t c_[4] = {r.c[0], r.c[1], r.c[2], r.c[3]};
+    const uint32_t s_[4] = {r.s[0], r.s[1], r.s[2], r.s[3]};
+    uint32_t p1[4], p2[4];
+    rotate<E, 4>(a_, b_, c_, s_, scale, p1, p2);
+    const int sw = swz(row);
+    *(u32x4 *)(xs + row * 128 + 16 * (c4 ^ sw)) = u32x4{p1[0], p1[1], p1[2], p1[3]};
+    *(u32x4 *)(xs + row * 128 + 16 * ((4 + c4) ^ sw)) = u32x4{p2[0], p2[1], p2[2], p2[3]};
+    *(u32x4 *)(ys + row * 128 + 16 * (c4 ^ sw)) = r.y1;
+    *(u32x4 *)(ys + row * 128 + 16 * ((4 + c4) ^ sw)) = r.y2;
+    const int slot = vt_slot(row);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int d1 = 8 * c4 + 2 * w + e, d2 = d1 + 32;
+            const int sh = e ? 16 : 0;
+            const int t1 = tr_at(d1, slot), t2 = tr_at(d2, slot);
+            *(uint16_t *)(xt + t1) = (uint16_t)(p1[w] >> sh);
+            *(uint16_t *)(xt + t2) = (uint16_t)(p2[w] >> sh);
+            if (YT) {
+                *(uint16_t *)(yt + t1) = (uint16_t)(r.y1[w] >> sh);
+                *(uint16_t *)(yt + t2) = (uint16_t)(r.y2[w] >> sh);
+            }
+        }
+}
+
+// dims 16c + 8g .. 16c+8g+7 of row i of a tensor (zeros past the sequence)
+__device__ __forceinline__ void back_row_operand(const uint16_t *base, int64_t ld, int start,
+                                                 int i, int len, int g, u32x4 (&op)[4]) {
+    const u32x4 z = {0, 0, 0, 0};
+    u32x4 v0 = z, v1 = z, v2 = z, v3 = z;
+    if (i < len) {
+        const uint16_t *r = base + (int64_t)(start + i) * ld + 8 * g;
+        v0 = *(const u32x4 *)r;
+        v1 = *(const u32x4 *)(r + 16);
+        v2 = *(const u32x4 *)(r + 32);
+        v3 = *(const u32x4 *)(r + 48);
+    }
+    op[0] = v0, op[1] = v1, op[2] = v2, op[3] = v3;
+}
+
+// The rows [lo, hi) of a sequence of `len` rows that row x sees through the window (empty for x
+// past the sequence).
+__device__ __forceinline__ void back_visible(int x, int len, int window, int &lo, int &hi) {
+    lo = 0, hi = 0;
+    if (x < len) {
+        lo = window > 0 ? max(x - window + 1, 0) : 0;
+        hi = (window > 0 && window < len - x) ? x + window : len;
+    }
+}
+
+// The streamed rows of a tile [t0, t0 + rows) reaches: [a, b), a a multiple of `step`.
+__device__ __forceinline__ void back_span(int t0, int rows, int len, int window, int step,
+                                          int &a, int &b) {
+    a = 0, b = len;
+    if (window > 0) {
+        if (t0 + 1 > window)
+            a = (t0 + 1 - window) / step * step;
+        if ((int64_t)t0 + rows - 1 + window < len)
+            b = t0 + rows - 1 + window;
+    }
+}
+
+// dK and dV of one key tile (32 NW keys) of one head over every query row its window reaches,
+// 16 NW rows a step (FlashAttention-2's backward without dQ). Wave w owns keys 32w .. 32w+31 of
+// the tile and keeps their rotated keys K~ and values V in registers as the B operands of
+// S = Q~ K~^T and dP = dO V^T, whose accumulators hold one key per lane and 16 query rows per
+// 32-row block. A step's query rows sit in LDS as Q~ and dO images and as their transposes, so
+// P and dS go straight from the accumulators into the B operands of dV^T += dO^T P and
+// dK^T += Q~^T dS. The images are double-buffered and the next step's rows are loaded into
+// registers before this step's products: one barrier a step.
+template <class E, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+        const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+        const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
+        const float *__restrict__ lse, const float *__restrict__ delta,
+        uint16_t *__restrict__ dqkv, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
+        int32_t P, int32_t window, float scale) {
+    constexpr int BS = 16 * NW;  // query rows per step
+    __shared__ __attribute__((aligned(16))) uint8_t qs[2][BS * 128];  // Q~ [query][dim]
+    __shared__ __attribute__((aligned(16))) uint8_t os[2][BS * 128];  // dO [query][dim]
+    __shared__ __attribute__((aligned(16))) uint8_t qt[2][D * 128];   // Q~^T [dim][slot]
+    __shared__ __attribute__((aligned(16))) uint8_t ot[2][D * 128];   // dO^T [dim][slot]
+    __shared__ __attribute__((aligned(16))) float lb[2][BS];          // lse * log2(e)
+    __shared__ __attribute__((aligned(16))) float dl[2][BS];          // delta
 
     const int work = xcd_work();
     const int h = work / num_tiles;
@@ -2234,8 +2301,9 @@ attend_back(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, g = lane >> 5;
-    const int kk = 32 * wv + n;  // this lane's key within the tile
-    const int kj = j0 + kk;
+    const int kj = j0 + 32 * wv + n;  // this lane's key
+    // waves whose 32 keys all lie past the sequence only stage
+    const bool idle = __builtin_amdgcn_readfirstlane(j0 + 32 * wv) >= len;
 
     // the lane's key (rotated and rounded as the forward rounds it) and value, dims 16c + 8g ..
     u32x4 kop[4], vop[4];
@@ -2243,163 +2311,87 @@ attend_back(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t
         QueryRaw r;
         query_load(r, qkv + hd, cos_t, sin_t, ld, start, kj, len, h, g);
         query_make<E>(r, 1.0f, kop);
-        const u32x4 z = {0, 0, 0, 0};
-        u32x4 v0 = z, v1 = z, v2 = z, v3 = z;
-        if (kj < len) {
-            const uint16_t *vr = qkv + (int64_t)(start + kj) * ld + 2 * hd + h * D + 8 * g;
-            v0 = *(const u32x4 *)vr;
-            v1 = *(const u32x4 *)(vr + 16);
-            v2 = *(const u32x4 *)(vr + 32);
-            v3 = *(const u32x4 *)(vr + 48);
-        }
-        vop[0] = v0, vop[1] = v1, vop[2] = v2, vop[3] = v3;
     }
-    // K~^T for dQ: element (dim d, key kk)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int d = 16 * c + 8 * g + 2 * w + e;
-                const uint32_t word = kop[c][w];
-                *(uint16_t *)(kt + d * 128 + 16 * ((kk >> 3) ^ swz(d)) + 2 * (kk & 7)) =
-                    (uint16_t)(e ? word >> 16 : word & 0xffffu);
-            }
+    back_row_operand(qkv + 2 * hd + h * D, ld, start, kj, len, g, vop);
 
-    // query rows some key of the tile sees: [qa, qb), qa a multiple of BQ
-    int qa = 0, qb = len;
-    if (window > 0) {
-        if (j0 + 1 > window)
-            qa = (j0 + 1 - window) / BQ * BQ;
-        if ((int64_t)j0 + BC - 1 + window < len)
-            qb = j0 + BC - 1 + window;
-    }
-    // query rows key kj sees: [vlo, vhi) (empty past the sequence)
-    int vlo = 0, vhi = 0;
-    if (kj < len) {
-        vlo = window > 0 ? max(kj - window + 1, 0) : 0;
-        vhi = (window > 0 && window < len - kj) ? kj + window : len;
-    }
+    int qa, qb, vlo, vhi;
+    back_span(j0, 32 * NW, len, window, BS, qa, qb);
+    back_visible(kj, len, window, vlo, vhi);
+    const uint32_t span = (uint32_t)(vhi - vlo);
+
+    const int row = tid >> 2, c4 = tid & 3;  // staging: query row, dims 8c4 .. and 32 + 8c4 ..
+    const uint16_t *qb_ = qkv + h * D, *ob_ = dout + h * D;
+    const float *lse_h = lse + (int64_t)h * T, *dl_h = delta + (int64_t)h * T;
+    BackRaw raw;
+    back_load<true>(raw, qb_, ld, ob_, hd, cos_t, sin_t, lse_h, dl_h, start, qa + row, len, c4);
+    back_stage<E, true>(raw, scale, qs[0], qt[0], os[0], ot[0], row, c4);
+    if (c4 == 0)
+        lb[0][row] = raw.f0 * LOG2E, dl[0][row] = raw.f1;
+    __syncthreads();
+
     f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
-    const int row = tid >> 2, q4 = tid & 3;  // staging: query row, dims 8q4 .. and 32 + 8q4 ..
-    const int slot = vt_slot(row);          // the row's slot in the transposed images
-    for (int it = qa; it < qb; it += BQ) {
-        __syncthreads();  // the previous step's reads are done
-        {
-            const int i = it + row;
-            const u32x4 z = {0, 0, 0, 0};
-            u32x4 x1 = z, x2 = z, c = z, s = z, o1 = z, o2 = z;
-            if (i < len) {
-                const uint16_t *qr = qkv + (int64_t)(start + i) * ld + h * D;
-                x1 = *(const u32x4 *)(qr + 8 * q4);
-                x2 = *(const u32x4 *)(qr + 32 + 8 * q4);
-                c = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * q4);
-                s = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * q4);
-                const uint16_t *orow = dout + (int64_t)(start + i) * hd + h * D;
-                o1 = *(const u32x4 *)(orow + 8 * q4);
-                o2 = *(const u32x4 *)(orow + 32 + 8 * q4);
-            }
-            const uint32_t a_[4] = {x1[0], x1[1], x1[2], x1[3]}, b_[4] = {x2[0], x2[1], x2[2], x2[3]};
-            const uint32_t c_[4] = {c[0], c[1], c[2], c[3]}, s_[4] = {s[0], s[1], s[2], s[3]};
-            uint32_t y1[4], y2[4];
-            rotate<E, 4>(a_, b_, c_, s_, scale, y1, y2);
-            *(u32x4 *)(qs + row * 128 + 16 * (q4 ^ swz(row))) = u32x4{y1[0], y1[1], y1[2], y1[3]};
-            *(u32x4 *)(qs + row * 128 + 16 * ((4 + q4) ^ swz(row))) =
-                u32x4{y2[0], y2[1], y2[2], y2[3]};
-            *(u32x4 *)(os + row * 128 + 16 * (q4 ^ swz(row))) = o1;
-            *(u32x4 *)(os + row * 128 + 16 * ((4 + q4) ^ swz(row))) = o2;
+    int b = 0;
+    for (int it = qa; it < qb; it += BS) {
+        const bool more = it + BS < qb;
+        if (more)
+            back_load<true>(raw, qb_, ld, ob_, hd, cos_t, sin_t, lse_h, dl_h, start,
+                            it + BS + row, len, c4);
+        if (!idle) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
+            for (int rb = 0; rb < BS / 32; ++rb) {
+                // S and dP of query rows it + 32rb + 8(i/4) + 4g + i%4 (register i)
+                f32x16 sc = {}, dp = {};
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int d1 = 8 * q4 + 2 * w + e, d2 = d1 + 32;
-                    const int sh = e ? 16 : 0;
-                    const int p1 = d1 * 128 + 16 * ((slot >> 3) ^ swz(d1)) + 2 * (slot & 7);
-                    const int p2 = d2 * 128 + 16 * ((slot >> 3) ^ swz(d2)) + 2 * (slot & 7);
-                    *(uint16_t *)(qt + p1) = (uint16_t)(y1[w] >> sh);
-                    *(uint16_t *)(qt + p2) = (uint16_t)(y2[w] >> sh);
-                    *(uint16_t *)(ot + p1) = (uint16_t)(o1[w] >> sh);
-                    *(uint16_t *)(ot + p2) = (uint16_t)(o2[w] >> sh);
+                for (int c = 0; c < 4; ++c) {
+                    const int off = (32 * rb + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
+                    sc = E::mfma(*(const u32x4 *)(qs[b] + off), kop[c], sc);
+                    dp = E::mfma(*(const u32x4 *)(os[b] + off), vop[c], dp);
                 }
-            if (q4 == 0) {
-                lb[row] = i < len ? lse[(int64_t)h * T + start + i] * LOG2E : 0.f;
-                dl[row] = i < len ? delta[(int64_t)h * T + start + i] : 0.f;
-            }
-        }
-        __syncthreads();
-
-        // S = Q~ K~^T and dP = dO V^T for the wave's 32 keys: register i holds query row
-        // it + 8(i/4) + 4g + i%4 of key kj
-        f32x16 sc = {}, dp = {};
+                // P = exp(S - lse) over the rows key kj sees (0 elsewhere), dS = P (dP - delta)
+                const int a = vlo - it - 32 * rb - 4 * g;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int off = n * 128 + 16 * ((2 * c + g) ^ swz(n));
-            sc = E::mfma(*(const u32x4 *)(qs + off), kop[c], sc);
-            dp = E::mfma(*(const u32x4 *)(os + off), vop[c], dp);
-        }
-        // P = exp(S - lse) over the rows key kj sees (0 elsewhere), dS = P (dP - delta)
-        {
-            const int a = vlo - it - 4 * g;
-            const uint32_t span = (uint32_t)max(vhi - vlo, 0);
+                for (int gi = 0; gi < 4; ++gi) {
+                    const f32x4 lv = *(const f32x4 *)(&lb[b][32 * rb + 8 * gi + 4 * g]);
+                    const f32x4 dv = *(const f32x4 *)(&dl[b][32 * rb + 8 * gi + 4 * g]);
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-                const f32x4 lv = *(const f32x4 *)(lb + 8 * gi + 4 * g);
-                const f32x4 dv = *(const f32x4 *)(dl + 8 * gi + 4 * g);
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * gi + e;
+                        const bool vis = (uint32_t)(8 * gi + e - a) < span;
+                        const float p =
+                            vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], LOG2E, -lv[e]))
+                                : 0.f;
+                        sc[i] = p;
+                        dp[i] = p * (dp[i] - dv[e]);
+                    }
+                }
+                u32x4 pp[2], pd[2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * gi + e;
-                    const bool vis = (uint32_t)(8 * gi + e - a) < span;
-                    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], LOG2E, -lv[e]))
-                                        : 0.f;
-                    sc[i] = p;
-                    dp[i] = p * (dp[i] - dv[e]);
+                for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        pp[kc][k] = E::pack(sc[8 * kc + 2 * k], sc[8 * kc + 2 * k + 1]);
+                        pd[kc][k] = E::pack(dp[8 * kc + 2 * k], dp[8 * kc + 2 * k + 1]);
+                    }
+                // dV^T += dO^T P and dK^T += Q~^T dS (dims 0..31 and 32..63)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const int ch = 4 * rb + 2 * kc + g;
+                    const int f0 = n * 128 + 16 * (ch ^ swz(n));
+                    const int f1 = (32 + n) * 128 + 16 * (ch ^ swz(32 + n));
+                    dv0 = E::mfma(*(const u32x4 *)(ot[b] + f0), pp[kc], dv0);
+                    dv1 = E::mfma(*(const u32x4 *)(ot[b] + f1), pp[kc], dv1);
+                    dk0 = E::mfma(*(const u32x4 *)(qt[b] + f0), pd[kc], dk0);
+                    dk1 = E::mfma(*(const u32x4 *)(qt[b] + f1), pd[kc], dk1);
                 }
             }
         }
-        u32x4 pp[2], pd[2];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                pp[kc][k] = E::pack(sc[8 * kc + 2 * k], sc[8 * kc + 2 * k + 1]);
-                pd[kc][k] = E::pack(dp[8 * kc + 2 * k], dp[8 * kc + 2 * k + 1]);
-            }
-        // dV^T += dO^T P and dK^T += Q~^T dS (dims 0..31 and 32..63 by the wave's keys)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            const int r0 = n, r1 = 32 + n;
-            const int f0 = r0 * 128 + 16 * ((2 * kc + g) ^ swz(r0));
-            const int f1 = r1 * 128 + 16 * ((2 * kc + g) ^ swz(r1));
-            dv0 = E::mfma(*(const u32x4 *)(ot + f0), pp[kc], dv0);
-            dv1 = E::mfma(*(const u32x4 *)(ot + f1), pp[kc], dv1);
-            dk0 = E::mfma(*(const u32x4 *)(qt + f0), pd[kc], dk0);
-            dk1 = E::mfma(*(const u32x4 *)(qt + f1), pd[kc], dk1);
-        }
-        // dS, rounded as it entered the products, into [query][key] for dQ
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int q = 8 * (i >> 2) + 4 * g + (i & 3);
-            const uint32_t word = pd[i >> 3][(i & 7) >> 1];
-            *(uint16_t *)(dss + q * 128 + 16 * ((kk >> 3) ^ swz(q)) + 2 * (kk & 7)) =
-                (uint16_t)((i & 1) ? word >> 16 : word & 0xffffu);
+        if (more) {
+            back_stage<E, true>(raw, scale, qs[b ^ 1], qt[b ^ 1], os[b ^ 1], ot[b ^ 1], row, c4);
+            if (c4 == 0)
+                lb[b ^ 1][row] = raw.f0 * LOG2E, dl[b ^ 1][row] = raw.f1;
         }
         __syncthreads();
-        // dQ = dS K~ over the tile's keys, dims 32 wv + n; register i: row it + 8(i/4) + 4g + i%4
-        f32x16 dqa = {};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int rk = 32 * wv + n;
-            const u32x4 a = *(const u32x4 *)(dss + n * 128 + 16 * ((2 * c + g) ^ swz(n)));
-            const u32x4 bb = *(const u32x4 *)(kt + rk * 128 + 16 * ((2 * c + g) ^ swz(rk)));
-            dqa = E::mfma(a, bb, dqa);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int q = it + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (q < len)
-                unsafeAtomicAdd(dq + (int64_t)(start + q) * hd + h * D + 32 * wv + n, dqa[i]);
-        }
+        b ^= 1;
     }
 
     // dK rotated back to the key's position, and dV; register i of block b holds dim
@@ -2411,29 +2403,164 @@ attend_back(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t
         for (int gi = 0; gi < 4; ++gi) {
             const int m0 = 8 * gi + 4 * g;
             const u32x2 cw = *(const u32x2 *)(cr + m0), sw = *(const u32x2 *)(sr + m0);
-            float a[4], b[4], v0[4], v1[4];
+            float a[4], bb[4], v0[4], v1[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float cm = (e & 1) ? E::hi(cw[e >> 1]) : E::lo(cw[e >> 1]);
                 const float sm = (e & 1) ? E::hi(sw[e >> 1]) : E::lo(sw[e >> 1]);
                 const float x1 = dk0[4 * gi + e], x2 = dk1[4 * gi + e];
                 a[e] = x1 * cm + x2 * sm;
-                b[e] = x2 * cm - x1 * sm;
+                bb[e] = x2 * cm - x1 * sm;
                 v0[e] = dv0[4 * gi + e];
                 v1[e] = dv1[4 * gi + e];
             }
             asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
-            asm volatile("" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+            asm volatile("" : "+v"(bb[0]), "+v"(bb[1]), "+v"(bb[2]), "+v"(bb[3]));
             *(u32x2 *)(o + hd + m0) = u32x2{E::pack(a[0], a[1]), E::pack(a[2], a[3])};
-            *(u32x2 *)(o + hd + 32 + m0) = u32x2{E::pack(b[0], b[1]), E::pack(b[2], b[3])};
+            *(u32x2 *)(o + hd + 32 + m0) = u32x2{E::pack(bb[0], bb[1]), E::pack(bb[2], bb[3])};
             *(u32x2 *)(o + 2 * hd + m0) = u32x2{E::pack(v0[0], v0[1]), E::pack(v0[2], v0[3])};
-            *(u32x2 *)(o + 2 * hd + 32 + m0) = u32x2{E::pack(v1[0], v1[1]), E::pack(v1[2], v1[3])};
+            *(u32x2 *)(o + 2 * hd + 32 + m0) =
+                u32x2{E::pack(v1[0], v1[1]), E::pack(v1[2], v1[3])};
         }
     }
 }
 
-template <class E>
-int launch_backward_typed(const BackArgs &a) {
+// dQ of one query tile (32 NW rows) of one head over every key its window reaches, 16 NW keys a
+// step. Wave w owns query rows 32w .. 32w+31 and keeps Q~ and dO in registers as the B operands
+// of S^T = K~ Q~^T and dP^T = V dO^T, whose accumulators hold one query per lane (so lse and
+// delta are one value per lane) and 16 keys per 32-key block. A step's keys sit in LDS as K~
+// and V images and a K~^T image, so dS^T goes straight from the accumulators into the B operand
+// of dQ^T += K~^T dS^T. dQ is rotated back to the row's position, scaled and written once.
+template <class E, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+       const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+       const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
+       const float *__restrict__ lse, const float *__restrict__ delta,
+       uint16_t *__restrict__ dqkv, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
+       int32_t P, int32_t window, float scale) {
+    constexpr int BS = 16 * NW;  // keys per step
+    __shared__ __attribute__((aligned(16))) uint8_t ks[2][BS * 128];  // K~ [key][dim]
+    __shared__ __attribute__((aligned(16))) uint8_t vs[2][BS * 128];  // V [key][dim]
+    __shared__ __attribute__((aligned(16))) uint8_t kt[2][D * 128];   // K~^T [dim][slot]
+
+    const int work = xcd_work();
+    const int h = work / num_tiles;
+    int start, len, i0;
+    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, i0))
+        return;
+    const int64_t ld = 3LL * H * D;
+    const int hd = H * D;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int qi = i0 + 32 * wv + n;  // this lane's query row
+    const bool idle = __builtin_amdgcn_readfirstlane(i0 + 32 * wv) >= len;
+
+    // the lane's rotated, scaled query (as the forward rounds it) and its dO, dims 16c + 8g ..
+    u32x4 qop[4], oop[4];
+    {
+        QueryRaw r;
+        query_load(r, qkv, cos_t, sin_t, ld, start, qi, len, h, g);
+        query_make<E>(r, scale, qop);
+    }
+    back_row_operand(dout + h * D, hd, start, qi, len, g, oop);
+    float lq = 0.f, dq_ = 0.f;  // lse * log2(e) and delta of the lane's row
+    if (qi < len) {
+        lq = lse[(int64_t)h * T + start + qi] * LOG2E;
+        dq_ = delta[(int64_t)h * T + start + qi];
+    }
+
+    int ka, kb, klo, khi;
+    back_span(i0, 32 * NW, len, window, BS, ka, kb);
+    back_visible(qi, len, window, klo, khi);
+    const uint32_t span = (uint32_t)(khi - klo);
+
+    const int row = tid >> 2, c4 = tid & 3;  // staging: key row, dims 8c4 .. and 32 + 8c4 ..
+    const uint16_t *kb_ = qkv + hd + h * D, *vb_ = qkv + 2 * hd + h * D;
+    BackRaw raw;
+    back_load<false>(raw, kb_, ld, vb_, ld, cos_t, sin_t, nullptr, nullptr, start, ka + row, len,
+                     c4);
+    back_stage<E, false>(raw, 1.0f, ks[0], kt[0], vs[0], nullptr, row, c4);
+    __syncthreads();
+
+    f32x16 dq0 = {}, dq1 = {};
+    int b = 0;
+    for (int jt = ka; jt < kb; jt += BS) {
+        const bool more = jt + BS < kb;
+        if (more)
+            back_load<false>(raw, kb_, ld, vb_, ld, cos_t, sin_t, nullptr, nullptr, start,
+                             jt + BS + row, len, c4);
+        if (!idle) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < BS / 32; ++kb2) {
+                // S^T and dP^T of keys jt + 32kb2 + 8(i/4) + 4g + i%4 (register i)
+                f32x16 st = {}, dp = {};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int off = (32 * kb2 + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
+                    st = E::mfma(*(const u32x4 *)(ks[b] + off), qop[c], st);
+                    dp = E::mfma(*(const u32x4 *)(vs[b] + off), oop[c], dp);
+                }
+                const int a = klo - jt - 32 * kb2 - 4 * g;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const bool vis = (uint32_t)(8 * (i >> 2) + (i & 3) - a) < span;
+                    const float p =
+                        vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], LOG2E, -lq)) : 0.f;
+                    dp[i] = p * (dp[i] - dq_);
+                }
+                u32x4 pd[2];
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        pd[kc][k] = E::pack(dp[8 * kc + 2 * k], dp[8 * kc + 2 * k + 1]);
+                // dQ^T += K~^T dS^T (dims 0..31 and 32..63)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const int ch = 4 * kb2 + 2 * kc + g;
+                    const int f0 = n * 128 + 16 * (ch ^ swz(n));
+                    const int f1 = (32 + n) * 128 + 16 * (ch ^ swz(32 + n));
+                    dq0 = E::mfma(*(const u32x4 *)(kt[b] + f0), pd[kc], dq0);
+                    dq1 = E::mfma(*(const u32x4 *)(kt[b] + f1), pd[kc], dq1);
+                }
+            }
+        }
+        if (more)
+            back_stage<E, false>(raw, 1.0f, ks[b ^ 1], kt[b ^ 1], vs[b ^ 1], nullptr, row, c4);
+        __syncthreads();
+        b ^= 1;
+    }
+
+    // dQ rotated back to the row's position (the transpose of the half-split rotation) and
+    // scaled; register i of block b holds dim 32b + 8(i/4) + 4g + i%4 of row qi
+    if (qi < len) {
+        const uint16_t *cr = cos_t + (int64_t)qi * 32, *sr = sin_t + (int64_t)qi * 32;
+        uint16_t *o = dqkv + (int64_t)(start + qi) * ld + h * D;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const int m0 = 8 * gi + 4 * g;
+            const u32x2 cw = *(const u32x2 *)(cr + m0), sw = *(const u32x2 *)(sr + m0);
+            float a[4], bb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float cm = (e & 1) ? E::hi(cw[e >> 1]) : E::lo(cw[e >> 1]);
+                const float sm = (e & 1) ? E::hi(sw[e >> 1]) : E::lo(sw[e >> 1]);
+                const float x1 = dq0[4 * gi + e], x2 = dq1[4 * gi + e];
+                a[e] = scale * (x1 * cm + x2 * sm);
+                bb[e] = scale * (x2 * cm - x1 * sm);
+            }
+            asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+            asm volatile("" : "+v"(bb[0]), "+v"(bb[1]), "+v"(bb[2]), "+v"(bb[3]));
+            *(u32x2 *)(o + m0) = u32x2{E::pack(a[0], a[1]), E::pack(a[2], a[3])};
+            *(u32x2 *)(o + 32 + m0) = u32x2{E::pack(bb[0], bb[1]), E::pack(bb[2], bb[3])};
+        }
+    }
+}
+
+template <class E, int NW>
+int launch_backward_tiles(const BackArgs &a) {
     const int64_t blocks = (int64_t)a.num_tiles * a.H;
     if (blocks > INT32_MAX)
         return fail(VLF_EINVAL, "%lld workgroups exceed the grid limit", (long long)blocks);
@@ -2441,36 +2568,36 @@ int launch_backward_typed(const BackArgs &a) {
     const uint16_t *sn = (const uint16_t *)a.sin, *out = (const uint16_t *)a.out;
     const uint16_t *dout = (const uint16_t *)a.dout;
     uint16_t *dqkv = (uint16_t *)a.dqkv;
-    float *dq = (float *)a.workspace;
-    float *delta = dq + (int64_t)a.T * a.H * D;
-    const float *lse = a.lse;
+    float *delta = (float *)a.workspace;
+    const float *dlc = delta, *lse = a.lse;
     int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows, W = a.window;
     float scale = a.scale;
     hipStream_t st = (hipStream_t)a.stream;
-    void *args1[] = {(void *)&out, (void *)&dout, (void *)&a.cu, (void *)&a.tiles, (void *)&dq,
+    void *args1[] = {(void *)&out, (void *)&dout, (void *)&a.cu, (void *)&a.tiles,
                      (void *)&delta, (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H,
                      (void *)&P};
-    hipError_t e = hipLaunchKernel((const void *)back_delta<E>, dim3((unsigned)blocks), dim3(256),
-                                   args1, 0, st);
+    hipError_t e = hipLaunchKernel((const void *)back_delta<E, 32 * NW>,
+                                   dim3((unsigned)blocks), dim3(256), args1, 0, st);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "delta launch failed: %s", hipGetErrorString(e));
     void *args2[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
-                     (void *)&dout, (void *)&lse, (void *)&delta, (void *)&dq, (void *)&dqkv,
+                     (void *)&dout, (void *)&lse, (void *)&dlc, (void *)&dqkv,
                      (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H, (void *)&P,
                      (void *)&W, (void *)&scale};
-    e = hipLaunchKernel((const void *)attend_back<E>, dim3((unsigned)blocks), dim3(128), args2, 0,
-                        st);
+    e = hipLaunchKernel((const void *)back_kv<E, NW>, dim3((unsigned)blocks), dim3(64 * NW),
+                        args2, 0, st);
     if (e != hipSuccess)
-        return fail(VLF_EHIP, "backward launch failed: %s", hipGetErrorString(e));
-    const float *dqc = dq;
-    void *args3[] = {(void *)&dqc, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
-                     (void *)&dqkv, (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H,
-                     (void *)&P, (void *)&scale};
-    e = hipLaunchKernel((const void *)back_rotate<E>, dim3((unsigned)blocks), dim3(256), args3, 0,
-                        st);
+        return fail(VLF_EHIP, "dK/dV launch failed: %s", hipGetErrorString(e));
+    e = hipLaunchKernel((const void *)back_q<E, NW>, dim3((unsigned)blocks), dim3(64 * NW),
+                        args2, 0, st);
     if (e != hipSuccess)
-        return fail(VLF_EHIP, "dQ rotation launch failed: %s", hipGetErrorString(e));
+        return fail(VLF_EHIP, "dQ launch failed: %s", hipGetErrorString(e));
     return VLF_OK;
+}
+
+template <class E>
+int launch_backward_typed(const BackArgs &a) {
+    return a.br == 128 ? launch_backward_tiles<E, 4>(a) : launch_backward_tiles<E, 2>(a);
 }
 }  // namespace
 
@@ -2484,9 +2611,7 @@ static bool slide_fits(int32_t window) {
     return (span + BC - 1) / BC <= 8;
 }
 
-int64_t backward_workspace_bytes(int32_t T, int32_t H) {
-    return (int64_t)T * H * (D + 1) * 4;
-}
+int64_t backward_workspace_bytes(int32_t T, int32_t H) { return (int64_t)T * H * 4; }
 
 int launch_backward(const BackArgs &a) {
     return a.dtype == VLF_BF16 ? launch_backward_typed<BF16>(a) : launch_backward_typed<F16>(a);

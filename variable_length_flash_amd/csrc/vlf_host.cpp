@@ -242,7 +242,7 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t H, int64_t *bytes) {
 
 int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
                         const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                        int32_t T, int32_t S, int32_t H, int32_t window, float scale,
+                        int32_t br, int32_t T, int32_t S, int32_t H, int32_t window, float scale,
                         int32_t dtype, const void *out, const void *dout, const float *lse,
                         void *workspace, int64_t workspace_bytes_, void *dqkv, void *stream) {
     if (dtype != VLF_BF16 && dtype != VLF_F16)
@@ -251,6 +251,8 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
         return fail(VLF_EINVAL, "window = %d < 0", window);
     if (num_tiles < 0)
         return fail(VLF_EINVAL, "negative size: num_tiles=%d", num_tiles);
+    if (br != 64 && br != 128)
+        return fail(VLF_EINVAL, "br = %d; the backward runs on 64- or 128-row tiles", br);
     if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
         return fail(VLF_EINVAL, "scale is not finite");
     const bool work = T > 0 && num_tiles > 0;
@@ -270,8 +272,9 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
     if (!tiles_dev || !out || !dout || !lse || !dqkv)
         return fail(VLF_EINVAL, "null device pointer (tiles=%p out=%p dout=%p lse=%p dqkv=%p)",
                     (const void *)tiles_dev, out, dout, (const void *)lse, dqkv);
-    BackArgs a{qkv, cos,   sin,   table_rows, cu_dev, tiles_dev, num_tiles, T,  S,    H,
-               window, scale, dtype, out,      dout,   lse,       workspace, dqkv, stream};
+    BackArgs a{qkv,    cos,   sin,   table_rows, cu_dev, tiles_dev, num_tiles, br, T,
+               S,      H,     window, scale,     dtype,  out,       dout,      lse, workspace,
+               dqkv,   stream};
     return launch_backward(a);
 }
 

@@ -40,7 +40,7 @@ enum class Launch {
 // Queue the forward kernels; returns a vlf_status.
 int launch_attend(const AttendArgs &a, Launch what);
 
-// The backward's arguments after validation; tiles are the 64-row tile table.
+// The backward's arguments after validation; tiles are the tile table for br-row tiles.
 struct BackArgs {
     const void *qkv;
     const void *cos;
@@ -49,6 +49,7 @@ struct BackArgs {
     const int32_t *cu;
     const uint32_t *tiles;
     int32_t num_tiles;
+    int32_t br;  // 64 or 128
     int32_t T, S, H;
     int32_t window;
     float scale;
@@ -56,7 +57,7 @@ struct BackArgs {
     const void *out;
     const void *dout;
     const float *lse;
-    void *workspace;  // dQ accumulators (float32 [T, H*64]) then delta (float32 [H, T])
+    void *workspace;  // delta (float32 [H, T])
     void *dqkv;
     void *stream;
 };
@@ -64,7 +65,7 @@ struct BackArgs {
 // Bytes of the backward's workspace.
 int64_t backward_workspace_bytes(int32_t T, int32_t H);
 
-// Queue the backward kernels (delta, attend_back, rotate_back); returns a vlf_status.
+// Queue the backward kernels (delta, dK/dV, dQ); returns a vlf_status.
 int launch_backward(const BackArgs &a);
 
 // Record the calling thread's error message (printf-style) and return `status`.
