@@ -275,8 +275,8 @@ def run_backward(args, w, q, c, s, out, lse, stream):
     br = args.br or vlf.choose_backward_br(vlf.typical_length(w.cu))
     batch = vlf.prepare(w.cu, dev, br, False, w.window)
     dqkv = torch.empty_like(q)
-    ws = torch.empty(vlf.backward_workspace_bytes(w.tokens, w.heads), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(vlf.backward_workspace_bytes(w.tokens, w.sequences, w.heads),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         vlf.attend_backward_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse, dout,

@@ -185,12 +185,14 @@ int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_
                        float *lse, void *stream);
 
 /*
- * Device workspace vlf_attend_backward needs for T tokens and H heads: float32 delta [H, T],
- * T * H * 4 bytes.
- *   bytes  out: the size (0 when T or H is 0).
+ * Device workspace vlf_attend_backward needs for T tokens in S sequences and H heads: float32
+ * delta and lse * log2(e), [H, T] each, padded to a multiple of 256 bytes, then per head
+ * floor(T / 64) + S blocks of 40 KiB (the operand images of one 64-row tile: rotated queries,
+ * their transpose, the transposed output gradient, rotated keys and their transpose).
+ *   bytes  out: the size (0 when T is 0).
  * Errors: VLF_EINVAL (negative size, H > 65536, null bytes).
  */
-int vlf_backward_workspace_bytes(int32_t T, int32_t H, int64_t *bytes);
+int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
 
 /*
  * The backward pass (hanzo-kernel 0.2.42 src/packed.rs: `delta`, `attend_back`, `rotate_back`):
@@ -216,7 +218,8 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t H, int64_t *bytes);
  *   out        device, [T, H*64] of `dtype`: the forward's output for these inputs.
  *   dout       device, [T, H*64] of `dtype`: the gradient of the loss with respect to out.
  *   lse        device, [H, T] float32: the forward's log-sum-exp for these inputs.
- *   workspace  device, at least vlf_backward_workspace_bytes(T, H) bytes; overwritten.
+ *   workspace  device, at least vlf_backward_workspace_bytes(T, S, H) bytes, 16-byte aligned;
+ *              overwritten.
  *   dqkv       device, [T, 3*H*64] of `dtype`: every row of every tiled sequence written.
  *   stream     hipStream_t (NULL = the null stream). Three kernels; asynchronous; allocates
  *              nothing. Calls that may overlap in time need separate workspaces.

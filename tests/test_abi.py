@@ -289,14 +289,22 @@ def test_tile_count_and_table_at_int32_extremes():
         assert table[:, 1].tolist() == [i * br for i in range(want)]
 
 
-def test_backward_workspace_bytes():
-    assert vlf.backward_workspace_bytes(0, 4) == 0
-    assert vlf.backward_workspace_bytes(1000, 12) == 1000 * 12 * 4
+@pytest.mark.parametrize("T,S,H", [(1000, 3, 12), (131072, 16, 16), (1, 1, 1), (63, 63, 2)])
+def test_backward_workspace_bytes(T, S, H):
+    # two float32 [H, T] arrays padded to 256 bytes, then H * (floor(T / 64) + S) blocks of
+    # five 8 KiB images
+    floats = (8 * T * H + 255) // 256 * 256
+    assert vlf.backward_workspace_bytes(T, S, H) == floats + H * (T // 64 + S) * 5 * 8192
+
+
+def test_backward_workspace_bytes_rejects():
+    assert vlf.backward_workspace_bytes(0, 0, 4) == 0
     lib = vlf.load_library()
     n = ctypes.c_int64(0)
-    assert lib.vlf_backward_workspace_bytes(-1, 2, ctypes.byref(n)) == binding.VLF_EINVAL
-    assert lib.vlf_backward_workspace_bytes(5, 70000, ctypes.byref(n)) == binding.VLF_EINVAL
-    assert lib.vlf_backward_workspace_bytes(5, 2, None) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(-1, 1, 2, ctypes.byref(n)) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, -1, 2, ctypes.byref(n)) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, 1, 70000, ctypes.byref(n)) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, 1, 2, None) == binding.VLF_EINVAL
 
 
 def _backward_status(**kw):
@@ -304,7 +312,8 @@ def _backward_status(**kw):
     cu = np.array([0, 100, 256], dtype=np.int32)
     a = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=256, cu=cu.ctypes.data, tiles=0x4000,
              num_tiles=5, br=64, T=256, S=2, H=2, W=0, scale=0.125, dtype=binding.VLF_BF16,
-             out=0x5000, dout=0x6000, lse=0x7000, ws=0x8000, ws_bytes=256 * 2 * 4, dqkv=0x9000)
+             out=0x5000, dout=0x6000, lse=0x7000, ws=0x8000,
+             ws_bytes=8 * 256 * 2 + 2 * (256 // 64 + 2) * 5 * 8192, dqkv=0x9000)
     a.update(kw)
     rc = lib.vlf_attend_backward(a["qkv"], a["cos"], a["sin"], a["P"], a["cu"], a["tiles"],
                                  a["num_tiles"], a["br"], a["T"], a["S"], a["H"], a["W"],

@@ -67,7 +67,7 @@ def load_library():
     lib.vlf_attend_rotated.restype = ctypes.c_int
     lib.vlf_rotate_keys.argtypes = [p, p, p, i32, p, i32, i32, i32, i32, p, i64, p]
     lib.vlf_rotate_keys.restype = ctypes.c_int
-    lib.vlf_backward_workspace_bytes.argtypes = [i32, i32, p]
+    lib.vlf_backward_workspace_bytes.argtypes = [i32, i32, i32, p]
     lib.vlf_backward_workspace_bytes.restype = ctypes.c_int
     lib.vlf_attend_backward.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, p, p, p, p, i64, p, p]
@@ -369,10 +369,11 @@ def attend_rotated_into(batch: Batch, qkv, cos, sin, heads: int, window: int, sc
         _stream(stream, dev)))
 
 
-def backward_workspace_bytes(tokens: int, heads: int) -> int:
-    """Bytes of the backward's workspace (float32 delta)."""
+def backward_workspace_bytes(tokens: int, sequences: int, heads: int) -> int:
+    """Bytes of the backward's workspace (per-row floats and the 64-row tiles' operand
+    images)."""
     n = ctypes.c_int64(0)
-    _check(load_library().vlf_backward_workspace_bytes(int(tokens), int(heads),
+    _check(load_library().vlf_backward_workspace_bytes(int(tokens), int(sequences), int(heads),
                                                        ctypes.byref(n)))
     return int(n.value)
 
@@ -402,8 +403,8 @@ def attend_backward_into(batch: Batch, qkv, cos, sin, heads: int, window: int, s
     launch = _torch_stream(stream, dev)
     if workspace is None:
         with torch.cuda.stream(launch):
-            workspace = torch.empty(backward_workspace_bytes(T, heads), dtype=torch.uint8,
-                                    device=dev)
+            workspace = torch.empty(backward_workspace_bytes(T, batch.sequences, heads),
+                                    dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = _workspace_args(workspace, dev)
     _check(load_library().vlf_attend_backward(
         qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),

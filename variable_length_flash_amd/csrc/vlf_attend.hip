@@ -2091,8 +2091,22 @@ int launch_br(const AttendArgs &a) {
 // from the forward's lse and dS = P (dP - delta) with delta = rowsum(dO * O). The page sums dK
 // and dV per key tile and adds dQ into float32 with atomics; here dQ has a pass of its own, over
 // query tiles, that recomputes S and dP (two more products) and writes dQ once, rotated back and
-// scaled: no atomics, and the same dqkv bits on every run. Every kernel walks the tile table of
-// the call's tile height (64 or 128 rows): a key tile for back_kv, a query tile for back_q.
+// scaled: no atomics, and the same dqkv bits on every run.
+//
+// back_prep writes, once per 64-row tile and head, the operand images both passes stage from:
+// Q~ rows, Q~^T, dO^T, K~ rows and K~^T (rotated, scaled and rounded as the forward rounds them),
+// and per row delta and lse * log2(e). back_kv and back_q then fill LDS with plain 16-byte
+// copies (buffer loads straight into LDS); dO and V rows come from their tensors the same way.
+// Every kernel walks the tile table of the call's tile height (64 or 128 rows).
+
+constexpr int BIMG = 5 * IMG;  // one tile's images: Q~, Q~^T, dO^T (24 KB), K~, K~^T (16 KB)
+constexpr int BS = 64;         // streamed rows per step of back_kv and back_q
+
+// Byte offset of the images in the workspace: delta and lse * log2(e), float32 [H, T] each,
+// then padding to 256 bytes.
+__host__ __device__ __forceinline__ int64_t back_img_offset(int32_t T, int32_t H) {
+    return ((int64_t)8 * T * H + 255) / 256 * 256;
+}
 
 // XCD-aware work index of the block (block b runs on XCD b % 8).
 __device__ __forceinline__ int xcd_work() {
@@ -2104,90 +2118,16 @@ __device__ __forceinline__ int xcd_work() {
 
 // The (sequence, first row) of a table entry, or false for an entry that names no tile.
 __device__ __forceinline__ bool back_tile(const uint32_t *tiles, const int32_t *cu, int tile,
-                                          int32_t S, int32_t T, int32_t P, int &start, int &len,
-                                          int &i0) {
-    const uint32_t seq = tiles[2 * tile];
+                                          int32_t S, int32_t T, int32_t P, int &seq, int &start,
+                                          int &len, int &i0) {
+    const uint32_t s = tiles[2 * tile];
     i0 = (int)tiles[2 * tile + 1];
-    if (seq >= (uint32_t)S)
+    if (s >= (uint32_t)S)
         return false;
-    start = cu[seq];
-    len = cu[seq + 1] - start;
+    seq = (int)s;
+    start = cu[s];
+    len = cu[s + 1] - start;
     return !(i0 < 0 || i0 >= len || len > P || start < 0 || (int64_t)start + len > T);
-}
-
-// delta[h, t] = sum_d dO[t, h, d] O[t, h, d] in float32 for the R rows of one tile and head;
-// 256 / R lanes per row.
-template <class E, int R>
-__global__ void __launch_bounds__(256)
-back_delta(const uint16_t *__restrict__ out, const uint16_t *__restrict__ dout,
-           const int32_t *__restrict__ cu, const uint32_t *__restrict__ tiles,
-           float *__restrict__ delta, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
-           int32_t P) {
-    constexpr int L = 256 / R, DL = D / L;  // lanes per row, dims per lane
-    const int work = xcd_work();
-    const int h = work / num_tiles;
-    int start, len, i0;
-    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, i0))
-        return;
-    const int tid = (int)threadIdx.x;
-    const int r = tid / L, q = tid % L;
-    const int i = i0 + r;
-    const int hd = H * D;
-    float acc = 0.f;
-    if (i < len) {
-        const int64_t at = (int64_t)(start + i) * hd + h * D + DL * q;
-#pragma unroll
-        for (int c = 0; c < DL / 8; ++c) {
-            const u32x4 o = *(const u32x4 *)(out + at + 8 * c);
-            const u32x4 d = *(const u32x4 *)(dout + at + 8 * c);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc = __builtin_fmaf(E::lo(o[k]), E::lo(d[k]), acc);
-                acc = __builtin_fmaf(E::hi(o[k]), E::hi(d[k]), acc);
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 1; m < L; m <<= 1)
-        acc += __shfl_xor(acc, m);
-    if (i < len && q == 0)
-        delta[(int64_t)h * T + start + i] = acc;
-}
-
-// One streamed row of a backward step as loaded from HBM: dims 8c .. 8c+7 and 32+8c .. of the
-// rotated tensor x (queries for back_kv, keys for back_q) with the row's cos and sin, the same
-// dims of the second tensor y (dO, or V), and two per-row floats (lse and delta).
-struct BackRaw {
-    u32x4 x1, x2, c, s, y1, y2;
-    float f0, f1;
-};
-
-// Row i of the sequence (zeros past its end). Locals first, then one assignment: an aggregate
-// written under a branch goes to scratch.
-template <bool FLOATS>
-__device__ __forceinline__ void back_load(BackRaw &r, const uint16_t *xb, int64_t xld,
-                                          const uint16_t *yb, int64_t yld,
-                                          const uint16_t *cos_t, const uint16_t *sin_t,
-                                          const float *fa, const float *fb, int start, int i,
-                                          int len, int c4) {
-    const u32x4 z = {0, 0, 0, 0};
-    u32x4 x1 = z, x2 = z, c = z, s = z, y1 = z, y2 = z;
-    float f0 = 0.f, f1 = 0.f;
-    if (i < len) {
-        const uint16_t *xr = xb + (int64_t)(start + i) * xld + 8 * c4;
-        x1 = *(const u32x4 *)xr;
-        x2 = *(const u32x4 *)(xr + 32);
-        c = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * c4);
-        s = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * c4);
-        const uint16_t *yr = yb + (int64_t)(start + i) * yld + 8 * c4;
-        y1 = *(const u32x4 *)yr;
-        y2 = *(const u32x4 *)(yr + 32);
-        if (FLOATS) {
-            f0 = fa[start + i];
-            f1 = fb[start + i];
-        }
-    }
-    r.x1 = x1, r.x2 = x2, r.c = c, r.s = s, r.y1 = y1, r.y2 = y2, r.f0 = f0, r.f1 = f1;
 }
 
 // Element (d, slot) of a transposed image: 128-byte rows, 16-byte chunk c at c ^ swz(d).
@@ -2195,39 +2135,123 @@ __device__ __forceinline__ int tr_at(int d, int slot) {
     return d * 128 + 16 * ((slot >> 3) ^ swz(d)) + 2 * (slot & 7);
 }
 
-// Row `row` of a step into the LDS images: x rotated (times `scale`, rounded to E) into its row
-// image xs and its transposed image xt; y into ys and, when YT, into yt. Transposed images hold
-// row r at slot vt_slot(r), the order in which a score accumulator holds its 16-row groups.
-template <class E, bool YT>
-__device__ __forceinline__ void back_stage(const BackRaw &r, float scale, uint8_t *xs,
-                                           uint8_t *xt, uint8_t *ys, uint8_t *yt, int row,
-                                           int c4) {
-    const uint32_t a_[4] = {r.x1[0], r.x1[1], r.x1[2], r.x1[3]};
-    const uint32_t b_[4] = {r.x2[0], r.x2[1], r.x2[2], r.x2[3]};
-    const uint32_t c_[4] = {r.c[0], r.c[1], r.c[2], r.c[3]};
-    const uint32_t s_[4] = {r.s[0], r.s[1], r.s[2], r.s[3]};
-    uint32_t p1[4], p2[4];
-    rotate<E, 4>(a_, b_, c_, s_, scale, p1, p2);
-    const int sw = swz(row);
-    *(u32x4 *)(xs + row * 128 + 16 * (c4 ^ sw)) = u32x4{p1[0], p1[1], p1[2], p1[3]};
-    *(u32x4 *)(xs + row * 128 + 16 * ((4 + c4) ^ sw)) = u32x4{p2[0], p2[1], p2[2], p2[3]};
-    *(u32x4 *)(ys + row * 128 + 16 * (c4 ^ sw)) = r.y1;
-    *(u32x4 *)(ys + row * 128 + 16 * ((4 + c4) ^ sw)) = r.y2;
+// Dims 8c4 .. 8c4+7 (w1) and 32+8c4 .. (w2) of row `row` into the transposed image t at slot
+// vt_slot(row): the order in which a score accumulator holds a 16-row group.
+__device__ __forceinline__ void stage_transposed(const uint32_t (&w1)[4], const uint32_t (&w2)[4],
+                                                 uint8_t *t, int row, int c4) {
     const int slot = vt_slot(row);
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int d1 = 8 * c4 + 2 * w + e, d2 = d1 + 32;
+            const int d1 = 8 * c4 + 2 * w + e;
             const int sh = e ? 16 : 0;
-            const int t1 = tr_at(d1, slot), t2 = tr_at(d2, slot);
-            *(uint16_t *)(xt + t1) = (uint16_t)(p1[w] >> sh);
-            *(uint16_t *)(xt + t2) = (uint16_t)(p2[w] >> sh);
-            if (YT) {
-                *(uint16_t *)(yt + t1) = (uint16_t)(r.y1[w] >> sh);
-                *(uint16_t *)(yt + t2) = (uint16_t)(r.y2[w] >> sh);
-            }
+            *(uint16_t *)(t + tr_at(d1, slot)) = (uint16_t)(w1[w] >> sh);
+            *(uint16_t *)(t + tr_at(d1 + 32, slot)) = (uint16_t)(w2[w] >> sh);
         }
+}
+
+// The same dims of row `row`, rotated by (c, s), times `scale`, rounded to E: into the row image
+// xs (chunk c at c ^ swz(row)) and the transposed image xt.
+template <class E>
+__device__ __forceinline__ void stage_rotated(const u32x4 &x1, const u32x4 &x2, const u32x4 &c,
+                                              const u32x4 &s, float scale, uint8_t *xs,
+                                              uint8_t *xt, int row, int c4) {
+    const uint32_t a_[4] = {x1[0], x1[1], x1[2], x1[3]};
+    const uint32_t b_[4] = {x2[0], x2[1], x2[2], x2[3]};
+    const uint32_t c_[4] = {c[0], c[1], c[2], c[3]};
+    const uint32_t s_[4] = {s[0], s[1], s[2], s[3]};
+    uint32_t p1[4], p2[4];
+    rotate<E, 4>(a_, b_, c_, s_, scale, p1, p2);
+    const int sw = swz(row);
+    *(u32x4 *)(xs + row * 128 + 16 * (c4 ^ sw)) = u32x4{p1[0], p1[1], p1[2], p1[3]};
+    *(u32x4 *)(xs + row * 128 + 16 * ((4 + c4) ^ sw)) = u32x4{p2[0], p2[1], p2[2], p2[3]};
+    stage_transposed(p1, p2, xt, row, c4);
+}
+
+// 16-byte chunks of row i of a [*, ld] tensor at column col: dims 8c4 .. and 32 + 8c4 ..
+// (zeros past the sequence).
+__device__ __forceinline__ void load_halves(const uint16_t *base, int64_t ld, int start, int i,
+                                            int len, int c4, u32x4 &a, u32x4 &b) {
+    const u32x4 z = {0, 0, 0, 0};
+    u32x4 x = z, y = z;
+    if (i < len) {
+        const uint16_t *r = base + (int64_t)(start + i) * ld + 8 * c4;
+        x = *(const u32x4 *)r;
+        y = *(const u32x4 *)(r + 32);
+    }
+    a = x, b = y;
+}
+
+// The operand images of the 64-row tiles of one table entry (R rows) and head, with delta and
+// lse * log2(e) of their rows. Built in LDS (four lanes per row, 16 dims each) and copied out
+// in 16-byte pieces. Rows past the sequence are zero in every image.
+template <class E, int R>
+__global__ void __launch_bounds__(256)
+back_prep(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+          const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+          const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ out,
+          const uint16_t *__restrict__ dout, const float *__restrict__ lse,
+          uint8_t *__restrict__ ws, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
+          int32_t P, float scale) {
+    __shared__ __attribute__((aligned(16))) uint8_t im[BIMG];
+    const int work = xcd_work();
+    const int h = work / num_tiles;
+    int seq, start, len, i0;
+    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, seq, start, len, i0))
+        return;
+    const int64_t ld = 3LL * H * D;
+    const int hd = H * D;
+    const int tid = (int)threadIdx.x;
+    const int row = tid >> 2, c4 = tid & 3;
+    float *delta = (float *)ws + (int64_t)h * T, *lse2 = (float *)ws + (int64_t)(H + h) * T;
+    const int64_t nb = T / BC + S;
+    uint8_t *blocks = ws + back_img_offset(T, H) + ((int64_t)h * nb + start / BC + seq) * BIMG;
+#pragma unroll 1
+    for (int t = i0; t < i0 + R && t < len; t += BC) {
+        const int i = t + row;
+        u32x4 q1, q2, k1, k2, o1, o2, y1, y2, c, s;
+        load_halves(qkv + h * D, ld, start, i, len, c4, q1, q2);
+        load_halves(qkv + hd + h * D, ld, start, i, len, c4, k1, k2);
+        load_halves(dout + h * D, hd, start, i, len, c4, y1, y2);
+        load_halves(out + h * D, hd, start, i, len, c4, o1, o2);
+        {
+            const u32x4 z = {0, 0, 0, 0};
+            u32x4 cv = z, sv = z;
+            if (i < len) {
+                cv = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * c4);
+                sv = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * c4);
+            }
+            c = cv, s = sv;
+        }
+        stage_rotated<E>(q1, q2, c, s, scale, im, im + IMG, row, c4);
+        {
+            const uint32_t w1[4] = {y1[0], y1[1], y1[2], y1[3]};
+            const uint32_t w2[4] = {y2[0], y2[1], y2[2], y2[3]};
+            stage_transposed(w1, w2, im + 2 * IMG, row, c4);
+        }
+        stage_rotated<E>(k1, k2, c, s, 1.0f, im + 3 * IMG, im + 4 * IMG, row, c4);
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc = __builtin_fmaf(E::lo(o1[k]), E::lo(y1[k]), acc);
+            acc = __builtin_fmaf(E::hi(o1[k]), E::hi(y1[k]), acc);
+            acc = __builtin_fmaf(E::lo(o2[k]), E::lo(y2[k]), acc);
+            acc = __builtin_fmaf(E::hi(o2[k]), E::hi(y2[k]), acc);
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        if (i < len && c4 == 0) {
+            delta[start + i] = acc;
+            lse2[start + i] = lse[(int64_t)h * T + start + i] * LOG2E;
+        }
+        __syncthreads();
+        uint8_t *blk = blocks + (int64_t)(t / BC) * BIMG;
+#pragma unroll
+        for (int j = 0; j < BIMG / 4096; ++j)
+            *(u32x4 *)(blk + 4096 * j + 16 * tid) = *(const u32x4 *)(im + 4096 * j + 16 * tid);
+        __syncthreads();
+    }
 }
 
 // dims 16c + 8g .. 16c+8g+7 of row i of a tensor (zeros past the sequence)
@@ -2255,55 +2279,147 @@ __device__ __forceinline__ void back_visible(int x, int len, int window, int &lo
     }
 }
 
-// The streamed rows of a tile [t0, t0 + rows) reaches: [a, b), a a multiple of `step`.
-__device__ __forceinline__ void back_span(int t0, int rows, int len, int window, int step,
-                                          int &a, int &b) {
+// The streamed rows a tile [t0, t0 + rows) reaches: [a, b), a a multiple of BS.
+__device__ __forceinline__ void back_span(int t0, int rows, int len, int window, int &a, int &b) {
     a = 0, b = len;
     if (window > 0) {
         if (t0 + 1 > window)
-            a = (t0 + 1 - window) / step * step;
+            a = (t0 + 1 - window) / BS * BS;
         if ((int64_t)t0 + rows - 1 + window < len)
             b = t0 + rows - 1 + window;
     }
 }
 
+// True when every pair of the 32-row blocks [x0, x0+32) and [y0, y0+32) of one sequence is
+// visible: no masking needed.
+__device__ __forceinline__ bool back_full(int x0, int y0, int len, int window) {
+    return x0 + 32 <= len && y0 + 32 <= len &&
+           (window == 0 || (x0 + 31 - y0 < window && y0 + 31 - x0 < window));
+}
+
+// Buffer resource over rows [r0, len) of a [*, ld] tensor from column col: rows past the
+// sequence read as zeros. Offsets stay below 64 rows, so 32 bits hold them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t back_rows(const uint16_t *base, int64_t ld,
+                                                            int start, int r0, int len) {
+    const int64_t bytes = (int64_t)(len - r0 - 1) * ld * 2 + 128;
+    return rsrc(base + (int64_t)(start + r0) * ld, bytes);
+}
+
+// Copies 64 rows of a [*, ld] tensor (128 bytes each from the resource's column) into a row
+// image (chunk c of row r at c ^ swz(r)): piece p = 8 rows = 1 KB, 16 bytes per lane.
+template <int NW>
+__device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t r, int64_t ld, lds_u8 *dst,
+                                          int wvu, int lane) {
+#pragma unroll
+    for (int j = 0; j < 8 / NW; ++j) {
+        const int p = NW * j + wvu;
+        const int row = 8 * p + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 1024 * p), 16,
+                                                 (int)(row * ld * 2 + 16 * chunk), 0, 0, 0);
+    }
+}
+
+// Copies `bytes` (a multiple of 1 KB) of a workspace block into LDS, 1 KB pieces by wave.
+template <int NW, int BYTES>
+__device__ __forceinline__ void copy_block(const uint8_t *src, lds_u8 *dst, int wvu, int lane) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, BYTES, RSRC_WORD3);
+#pragma unroll
+    for (int j = 0; j < BYTES / 1024 / NW; ++j) {
+        const int off = 1024 * (NW * j + wvu);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + off), 16, 16 * lane, off,
+                                                 0, 0);
+    }
+}
+
+// 64 floats of rows [r0, r0 + 64) of a per-row float array into LDS (zeros past the sequence).
+__device__ __forceinline__ void copy_floats(const float *base, int start, int r0, int len,
+                                            lds_u8 *dst, int lane) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(base + start + r0), 0, 4 * (len - r0), RSRC_WORD3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, 4 * lane, 0, 0, 0);
+}
+
+// P = exp2(S log2(e) - lse2) and dS = P (dP - delta) of a 32 x 32 accumulator block whose
+// register i holds row 8(i/4) + 4g + i%4 (lse2 and delta per register), packed to E as the B
+// operands of the next products. With MASK, only rows r with r - a in [0, span) count (a is
+// relative to register 0 of the lane's group).
+template <class E, bool MASK>
+__device__ __forceinline__ void back_pds(f32x16 &sc, f32x16 &dp, const f32x4 (&lv)[4],
+                                         const f32x4 (&dv)[4], int a, uint32_t span,
+                                         u32x4 (&pp)[2], u32x4 (&pd)[2]) {
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * gi + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], LOG2E, -lv[gi][e]));
+            if (MASK)
+                p = (uint32_t)(8 * gi + e - a) < span ? p : 0.f;
+            sc[i] = p;
+            dp[i] = p * (dp[i] - dv[gi][e]);
+        }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            pp[kc][k] = E::pack(sc[8 * kc + 2 * k], sc[8 * kc + 2 * k + 1]);
+            pd[kc][k] = E::pack(dp[8 * kc + 2 * k], dp[8 * kc + 2 * k + 1]);
+        }
+}
+
+// The same for a transposed block (one row per lane: lse2 and delta are the lane's), dS only.
+template <class E, bool MASK>
+__device__ __forceinline__ void back_ds(const f32x16 &st, f32x16 &dp, float lq, float dl,
+                                        int a, uint32_t span, u32x4 (&pd)[2]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], LOG2E, -lq));
+        if (MASK)
+            p = (uint32_t)(8 * (i >> 2) + (i & 3) - a) < span ? p : 0.f;
+        dp[i] = p * (dp[i] - dl);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            pd[kc][k] = E::pack(dp[8 * kc + 2 * k], dp[8 * kc + 2 * k + 1]);
+}
+
 // dK and dV of one key tile (32 NW keys) of one head over every query row its window reaches,
-// 16 NW rows a step (FlashAttention-2's backward without dQ). Wave w owns keys 32w .. 32w+31 of
+// 64 rows a step (FlashAttention-2's backward without dQ). Wave w owns keys 32w .. 32w+31 of
 // the tile and keeps their rotated keys K~ and values V in registers as the B operands of
 // S = Q~ K~^T and dP = dO V^T, whose accumulators hold one key per lane and 16 query rows per
-// 32-row block. A step's query rows sit in LDS as Q~ and dO images and as their transposes, so
-// P and dS go straight from the accumulators into the B operands of dV^T += dO^T P and
-// dK^T += Q~^T dS. The images are double-buffered and the next step's rows are loaded into
-// registers before this step's products: one barrier a step.
+// 32-row block. A step's Q~, Q~^T and dO^T images come from back_prep and its dO rows from dout,
+// straight into one of two LDS slots while the other slot's step is computed; P and dS go from
+// the accumulators into the B operands of dV^T += dO^T P and dK^T += Q~^T dS.
+// Two slots of 65 KB leave room for two workgroups a CU: two waves a SIMD with four waves a
+// workgroup, one with two.
 template <class E, int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)))
 back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
         const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
-        const float *__restrict__ lse, const float *__restrict__ delta,
-        uint16_t *__restrict__ dqkv, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
-        int32_t P, int32_t window, float scale) {
-    constexpr int BS = 16 * NW;  // query rows per step
-    __shared__ __attribute__((aligned(16))) uint8_t qs[2][BS * 128];  // Q~ [query][dim]
-    __shared__ __attribute__((aligned(16))) uint8_t os[2][BS * 128];  // dO [query][dim]
-    __shared__ __attribute__((aligned(16))) uint8_t qt[2][D * 128];   // Q~^T [dim][slot]
-    __shared__ __attribute__((aligned(16))) uint8_t ot[2][D * 128];   // dO^T [dim][slot]
-    __shared__ __attribute__((aligned(16))) float lb[2][BS];          // lse * log2(e)
-    __shared__ __attribute__((aligned(16))) float dl[2][BS];          // delta
+        const uint8_t *__restrict__ ws, uint16_t *__restrict__ dqkv, int32_t num_tiles,
+        int32_t T, int32_t S, int32_t H, int32_t P, int32_t window) {
+    constexpr int SLOT = 4 * IMG + 512;  // Q~, Q~^T, dO^T, dO rows, lse * log2(e), delta
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
 
     const int work = xcd_work();
     const int h = work / num_tiles;
-    int start, len, j0;
-    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, j0))
+    int seq, start, len, j0;
+    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, seq, start, len, j0))
         return;
     const int64_t ld = 3LL * H * D;
     const int hd = H * D;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
     const int n = lane & 31, g = lane >> 5;
-    const int kj = j0 + 32 * wv + n;  // this lane's key
-    // waves whose 32 keys all lie past the sequence only stage
-    const bool idle = __builtin_amdgcn_readfirstlane(j0 + 32 * wv) >= len;
+    const int kw0 = j0 + 32 * wvu;  // the wave's first key
+    const int kj = kw0 + n;         // this lane's key
+    const bool idle = kw0 >= len;   // the wave's keys all lie past the sequence: copies only
 
     // the lane's key (rotated and rounded as the forward rounds it) and value, dims 16c + 8g ..
     u32x4 kop[4], vop[4];
@@ -2315,82 +2431,87 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     back_row_operand(qkv + 2 * hd + h * D, ld, start, kj, len, g, vop);
 
     int qa, qb, vlo, vhi;
-    back_span(j0, 32 * NW, len, window, BS, qa, qb);
+    back_span(j0, 32 * NW, len, window, qa, qb);
     back_visible(kj, len, window, vlo, vhi);
     const uint32_t span = (uint32_t)(vhi - vlo);
 
-    const int row = tid >> 2, c4 = tid & 3;  // staging: query row, dims 8c4 .. and 32 + 8c4 ..
-    const uint16_t *qb_ = qkv + h * D, *ob_ = dout + h * D;
-    const float *lse_h = lse + (int64_t)h * T, *dl_h = delta + (int64_t)h * T;
-    BackRaw raw;
-    back_load<true>(raw, qb_, ld, ob_, hd, cos_t, sin_t, lse_h, dl_h, start, qa + row, len, c4);
-    back_stage<E, true>(raw, scale, qs[0], qt[0], os[0], ot[0], row, c4);
-    if (c4 == 0)
-        lb[0][row] = raw.f0 * LOG2E, dl[0][row] = raw.f1;
-    __syncthreads();
+    const float *lse2 = (const float *)ws + (int64_t)(H + h) * T;
+    const float *delta = (const float *)ws + (int64_t)h * T;
+    const uint8_t *imgs =
+        ws + back_img_offset(T, H) + ((int64_t)h * (T / BC + S) + start / BC + seq) * BIMG;
+    lds_u8 *const base = (lds_u8 *)lds;
+    auto copy = [&](int it, int sl) {
+        lds_u8 *d = base + sl * SLOT;
+        copy_block<NW, 3 * IMG>(imgs + (int64_t)(it / BC) * BIMG, d, wvu, lane);
+        copy_rows<NW>(back_rows(dout + h * D, hd, start, it, len), hd, d + 3 * IMG, wvu, lane);
+        if (wvu == 0)
+            copy_floats(lse2, start, it, len, d + 4 * IMG, lane);
+        if (wvu == 1)
+            copy_floats(delta, start, it, len, d + 4 * IMG + 256, lane);
+    };
+    copy(qa, 0);
+    ring_barrier<0>();
 
     f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
     int b = 0;
     for (int it = qa; it < qb; it += BS) {
-        const bool more = it + BS < qb;
-        if (more)
-            back_load<true>(raw, qb_, ld, ob_, hd, cos_t, sin_t, lse_h, dl_h, start,
-                            it + BS + row, len, c4);
+        if (it + BS < qb)
+            copy(it + BS, b ^ 1);
         if (!idle) {
+            const uint8_t *qs = lds + b * SLOT, *qt = qs + IMG, *ot = qs + 2 * IMG;
+            const uint8_t *os = qs + 3 * IMG;
+            const float *lb = (const float *)(qs + 4 * IMG), *dl = lb + 64;
 #pragma unroll
-            for (int rb = 0; rb < BS / 32; ++rb) {
-                // S and dP of query rows it + 32rb + 8(i/4) + 4g + i%4 (register i)
-                f32x16 sc = {}, dp = {};
+            for (int rb = 0; rb < 2; ++rb) {
+                // every LDS operand of the block first, so that the reads overlap
+                u32x4 qa_[4], oa_[4], ta[8];
+                f32x4 lv[4], dv[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int off = (32 * rb + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
-                    sc = E::mfma(*(const u32x4 *)(qs[b] + off), kop[c], sc);
-                    dp = E::mfma(*(const u32x4 *)(os[b] + off), vop[c], dp);
+                    qa_[c] = *(const u32x4 *)(qs + off);
+                    oa_[c] = *(const u32x4 *)(os + off);
                 }
-                // P = exp(S - lse) over the rows key kj sees (0 elsewhere), dS = P (dP - delta)
-                const int a = vlo - it - 32 * rb - 4 * g;
-#pragma unroll
-                for (int gi = 0; gi < 4; ++gi) {
-                    const f32x4 lv = *(const f32x4 *)(&lb[b][32 * rb + 8 * gi + 4 * g]);
-                    const f32x4 dv = *(const f32x4 *)(&dl[b][32 * rb + 8 * gi + 4 * g]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * gi + e;
-                        const bool vis = (uint32_t)(8 * gi + e - a) < span;
-                        const float p =
-                            vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], LOG2E, -lv[e]))
-                                : 0.f;
-                        sc[i] = p;
-                        dp[i] = p * (dp[i] - dv[e]);
-                    }
-                }
-                u32x4 pp[2], pd[2];
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        pp[kc][k] = E::pack(sc[8 * kc + 2 * k], sc[8 * kc + 2 * k + 1]);
-                        pd[kc][k] = E::pack(dp[8 * kc + 2 * k], dp[8 * kc + 2 * k + 1]);
-                    }
-                // dV^T += dO^T P and dK^T += Q~^T dS (dims 0..31 and 32..63)
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
                     const int ch = 4 * rb + 2 * kc + g;
                     const int f0 = n * 128 + 16 * (ch ^ swz(n));
                     const int f1 = (32 + n) * 128 + 16 * (ch ^ swz(32 + n));
-                    dv0 = E::mfma(*(const u32x4 *)(ot[b] + f0), pp[kc], dv0);
-                    dv1 = E::mfma(*(const u32x4 *)(ot[b] + f1), pp[kc], dv1);
-                    dk0 = E::mfma(*(const u32x4 *)(qt[b] + f0), pd[kc], dk0);
-                    dk1 = E::mfma(*(const u32x4 *)(qt[b] + f1), pd[kc], dk1);
+                    ta[4 * kc] = *(const u32x4 *)(ot + f0);
+                    ta[4 * kc + 1] = *(const u32x4 *)(ot + f1);
+                    ta[4 * kc + 2] = *(const u32x4 *)(qt + f0);
+                    ta[4 * kc + 3] = *(const u32x4 *)(qt + f1);
+                }
+#pragma unroll
+                for (int gi = 0; gi < 4; ++gi) {
+                    lv[gi] = *(const f32x4 *)(lb + 32 * rb + 8 * gi + 4 * g);
+                    dv[gi] = *(const f32x4 *)(dl + 32 * rb + 8 * gi + 4 * g);
+                }
+                // S and dP of query rows it + 32rb + 8(i/4) + 4g + i%4 (register i)
+                f32x16 sc = {}, dp = {};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    sc = E::mfma(qa_[c], kop[c], sc);
+                    dp = E::mfma(oa_[c], vop[c], dp);
+                }
+                // P = exp(S - lse) over the rows key kj sees (0 elsewhere), dS = P (dP - delta);
+                // blocks every pair of which is visible take the branch without the mask
+                u32x4 pp[2], pd[2];
+                if (back_full(it + 32 * rb, kw0, len, window))
+                    back_pds<E, false>(sc, dp, lv, dv, 0, 0, pp, pd);
+                else
+                    back_pds<E, true>(sc, dp, lv, dv, vlo - it - 32 * rb - 4 * g, span, pp, pd);
+                // dV^T += dO^T P and dK^T += Q~^T dS (dims 0..31 and 32..63)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    dv0 = E::mfma(ta[4 * kc], pp[kc], dv0);
+                    dv1 = E::mfma(ta[4 * kc + 1], pp[kc], dv1);
+                    dk0 = E::mfma(ta[4 * kc + 2], pd[kc], dk0);
+                    dk1 = E::mfma(ta[4 * kc + 3], pd[kc], dk1);
                 }
             }
         }
-        if (more) {
-            back_stage<E, true>(raw, scale, qs[b ^ 1], qt[b ^ 1], os[b ^ 1], ot[b ^ 1], row, c4);
-            if (c4 == 0)
-                lb[b ^ 1][row] = raw.f0 * LOG2E, dl[b ^ 1][row] = raw.f1;
-        }
-        __syncthreads();
+        ring_barrier<0>();
         b ^= 1;
     }
 
@@ -2425,37 +2546,37 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     }
 }
 
-// dQ of one query tile (32 NW rows) of one head over every key its window reaches, 16 NW keys a
+// dQ of one query tile (32 NW rows) of one head over every key its window reaches, 64 keys a
 // step. Wave w owns query rows 32w .. 32w+31 and keeps Q~ and dO in registers as the B operands
 // of S^T = K~ Q~^T and dP^T = V dO^T, whose accumulators hold one query per lane (so lse and
-// delta are one value per lane) and 16 keys per 32-key block. A step's keys sit in LDS as K~
-// and V images and a K~^T image, so dS^T goes straight from the accumulators into the B operand
-// of dQ^T += K~^T dS^T. dQ is rotated back to the row's position, scaled and written once.
+// delta are one value per lane) and 16 keys per 32-key block. A step's K~ and K~^T images come
+// from back_prep and its V rows from qkv, straight into one of two LDS slots; dS^T goes from the
+// accumulators into the B operand of dQ^T += K~^T dS^T. dQ is rotated back to the row's
+// position, scaled and written once.
 template <class E, int NW>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
        const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
        const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
-       const float *__restrict__ lse, const float *__restrict__ delta,
-       uint16_t *__restrict__ dqkv, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
-       int32_t P, int32_t window, float scale) {
-    constexpr int BS = 16 * NW;  // keys per step
-    __shared__ __attribute__((aligned(16))) uint8_t ks[2][BS * 128];  // K~ [key][dim]
-    __shared__ __attribute__((aligned(16))) uint8_t vs[2][BS * 128];  // V [key][dim]
-    __shared__ __attribute__((aligned(16))) uint8_t kt[2][D * 128];   // K~^T [dim][slot]
+       const uint8_t *__restrict__ ws, uint16_t *__restrict__ dqkv, int32_t num_tiles,
+       int32_t T, int32_t S, int32_t H, int32_t P, int32_t window, float scale) {
+    constexpr int SLOT = 3 * IMG;  // K~, K~^T, V rows
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
 
     const int work = xcd_work();
     const int h = work / num_tiles;
-    int start, len, i0;
-    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, start, len, i0))
+    int seq, start, len, i0;
+    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, seq, start, len, i0))
         return;
     const int64_t ld = 3LL * H * D;
     const int hd = H * D;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
     const int n = lane & 31, g = lane >> 5;
-    const int qi = i0 + 32 * wv + n;  // this lane's query row
-    const bool idle = __builtin_amdgcn_readfirstlane(i0 + 32 * wv) >= len;
+    const int qw0 = i0 + 32 * wvu;  // the wave's first query row
+    const int qi = qw0 + n;         // this lane's query row
+    const bool idle = qw0 >= len;
 
     // the lane's rotated, scaled query (as the forward rounds it) and its dO, dims 16c + 8g ..
     u32x4 qop[4], oop[4];
@@ -2467,69 +2588,72 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     back_row_operand(dout + h * D, hd, start, qi, len, g, oop);
     float lq = 0.f, dq_ = 0.f;  // lse * log2(e) and delta of the lane's row
     if (qi < len) {
-        lq = lse[(int64_t)h * T + start + qi] * LOG2E;
-        dq_ = delta[(int64_t)h * T + start + qi];
+        lq = ((const float *)ws)[(int64_t)(H + h) * T + start + qi];
+        dq_ = ((const float *)ws)[(int64_t)h * T + start + qi];
     }
 
     int ka, kb, klo, khi;
-    back_span(i0, 32 * NW, len, window, BS, ka, kb);
+    back_span(i0, 32 * NW, len, window, ka, kb);
     back_visible(qi, len, window, klo, khi);
     const uint32_t span = (uint32_t)(khi - klo);
 
-    const int row = tid >> 2, c4 = tid & 3;  // staging: key row, dims 8c4 .. and 32 + 8c4 ..
-    const uint16_t *kb_ = qkv + hd + h * D, *vb_ = qkv + 2 * hd + h * D;
-    BackRaw raw;
-    back_load<false>(raw, kb_, ld, vb_, ld, cos_t, sin_t, nullptr, nullptr, start, ka + row, len,
-                     c4);
-    back_stage<E, false>(raw, 1.0f, ks[0], kt[0], vs[0], nullptr, row, c4);
-    __syncthreads();
+    const uint8_t *imgs = ws + back_img_offset(T, H) +
+                          ((int64_t)h * (T / BC + S) + start / BC + seq) * BIMG + 3 * IMG;
+    lds_u8 *const base = (lds_u8 *)lds;
+    auto copy = [&](int jt, int sl) {
+        lds_u8 *d = base + sl * SLOT;
+        copy_block<NW, 2 * IMG>(imgs + (int64_t)(jt / BC) * BIMG, d, wvu, lane);
+        copy_rows<NW>(back_rows(qkv + 2 * hd + h * D, ld, start, jt, len), ld, d + 2 * IMG, wvu,
+                      lane);
+    };
+    copy(ka, 0);
+    ring_barrier<0>();
 
     f32x16 dq0 = {}, dq1 = {};
     int b = 0;
     for (int jt = ka; jt < kb; jt += BS) {
-        const bool more = jt + BS < kb;
-        if (more)
-            back_load<false>(raw, kb_, ld, vb_, ld, cos_t, sin_t, nullptr, nullptr, start,
-                             jt + BS + row, len, c4);
+        if (jt + BS < kb)
+            copy(jt + BS, b ^ 1);
         if (!idle) {
+            const uint8_t *ks = lds + b * SLOT, *kt = ks + IMG, *vs = ks + 2 * IMG;
 #pragma unroll
-            for (int kb2 = 0; kb2 < BS / 32; ++kb2) {
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                // every LDS operand of the block first, so that the reads overlap
+                u32x4 ka_[4], va_[4], ta[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int off = (32 * kb2 + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
+                    ka_[c] = *(const u32x4 *)(ks + off);
+                    va_[c] = *(const u32x4 *)(vs + off);
+                }
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const int ch = 4 * kb2 + 2 * kc + g;
+                    ta[2 * kc] = *(const u32x4 *)(kt + n * 128 + 16 * (ch ^ swz(n)));
+                    ta[2 * kc + 1] =
+                        *(const u32x4 *)(kt + (32 + n) * 128 + 16 * (ch ^ swz(32 + n)));
+                }
                 // S^T and dP^T of keys jt + 32kb2 + 8(i/4) + 4g + i%4 (register i)
                 f32x16 st = {}, dp = {};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const int off = (32 * kb2 + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
-                    st = E::mfma(*(const u32x4 *)(ks[b] + off), qop[c], st);
-                    dp = E::mfma(*(const u32x4 *)(vs[b] + off), oop[c], dp);
-                }
-                const int a = klo - jt - 32 * kb2 - 4 * g;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const bool vis = (uint32_t)(8 * (i >> 2) + (i & 3) - a) < span;
-                    const float p =
-                        vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], LOG2E, -lq)) : 0.f;
-                    dp[i] = p * (dp[i] - dq_);
+                    st = E::mfma(ka_[c], qop[c], st);
+                    dp = E::mfma(va_[c], oop[c], dp);
                 }
                 u32x4 pd[2];
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        pd[kc][k] = E::pack(dp[8 * kc + 2 * k], dp[8 * kc + 2 * k + 1]);
+                if (back_full(jt + 32 * kb2, qw0, len, window))
+                    back_ds<E, false>(st, dp, lq, dq_, 0, 0, pd);
+                else
+                    back_ds<E, true>(st, dp, lq, dq_, klo - jt - 32 * kb2 - 4 * g, span, pd);
                 // dQ^T += K~^T dS^T (dims 0..31 and 32..63)
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
-                    const int ch = 4 * kb2 + 2 * kc + g;
-                    const int f0 = n * 128 + 16 * (ch ^ swz(n));
-                    const int f1 = (32 + n) * 128 + 16 * (ch ^ swz(32 + n));
-                    dq0 = E::mfma(*(const u32x4 *)(kt[b] + f0), pd[kc], dq0);
-                    dq1 = E::mfma(*(const u32x4 *)(kt[b] + f1), pd[kc], dq1);
+                    dq0 = E::mfma(ta[2 * kc], pd[kc], dq0);
+                    dq1 = E::mfma(ta[2 * kc + 1], pd[kc], dq1);
                 }
             }
         }
-        if (more)
-            back_stage<E, false>(raw, 1.0f, ks[b ^ 1], kt[b ^ 1], vs[b ^ 1], nullptr, row, c4);
-        __syncthreads();
+        ring_barrier<0>();
         b ^= 1;
     }
 
@@ -2568,28 +2692,33 @@ int launch_backward_tiles(const BackArgs &a) {
     const uint16_t *sn = (const uint16_t *)a.sin, *out = (const uint16_t *)a.out;
     const uint16_t *dout = (const uint16_t *)a.dout;
     uint16_t *dqkv = (uint16_t *)a.dqkv;
-    float *delta = (float *)a.workspace;
-    const float *dlc = delta, *lse = a.lse;
+    uint8_t *ws = (uint8_t *)a.workspace;
+    const uint8_t *wsc = ws;
+    const float *lse = a.lse;
     int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows, W = a.window;
     float scale = a.scale;
     hipStream_t st = (hipStream_t)a.stream;
-    void *args1[] = {(void *)&out, (void *)&dout, (void *)&a.cu, (void *)&a.tiles,
-                     (void *)&delta, (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H,
-                     (void *)&P};
-    hipError_t e = hipLaunchKernel((const void *)back_delta<E, 32 * NW>,
-                                   dim3((unsigned)blocks), dim3(256), args1, 0, st);
+    void *args1[] = {(void *)&qkv, (void *)&cs,   (void *)&sn,        (void *)&a.cu,
+                     (void *)&a.tiles, (void *)&out, (void *)&dout, (void *)&lse,
+                     (void *)&ws,  (void *)&num_tiles, (void *)&T, (void *)&S,
+                     (void *)&H,   (void *)&P,    (void *)&scale};
+    hipError_t e = hipLaunchKernel((const void *)back_prep<E, 32 * NW>, dim3((unsigned)blocks),
+                                   dim3(256), args1, 0, st);
     if (e != hipSuccess)
-        return fail(VLF_EHIP, "delta launch failed: %s", hipGetErrorString(e));
+        return fail(VLF_EHIP, "backward prep launch failed: %s", hipGetErrorString(e));
     void *args2[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
-                     (void *)&dout, (void *)&lse, (void *)&dlc, (void *)&dqkv,
-                     (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H, (void *)&P,
-                     (void *)&W, (void *)&scale};
+                     (void *)&dout, (void *)&wsc, (void *)&dqkv, (void *)&num_tiles,
+                     (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&W};
     e = hipLaunchKernel((const void *)back_kv<E, NW>, dim3((unsigned)blocks), dim3(64 * NW),
                         args2, 0, st);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "dK/dV launch failed: %s", hipGetErrorString(e));
+    void *args3[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
+                     (void *)&dout, (void *)&wsc, (void *)&dqkv, (void *)&num_tiles,
+                     (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&W,
+                     (void *)&scale};
     e = hipLaunchKernel((const void *)back_q<E, NW>, dim3((unsigned)blocks), dim3(64 * NW),
-                        args2, 0, st);
+                        args3, 0, st);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "dQ launch failed: %s", hipGetErrorString(e));
     return VLF_OK;
@@ -2611,7 +2740,9 @@ static bool slide_fits(int32_t window) {
     return (span + BC - 1) / BC <= 8;
 }
 
-int64_t backward_workspace_bytes(int32_t T, int32_t H) { return (int64_t)T * H * 4; }
+int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H) {
+    return T == 0 ? 0 : back_img_offset(T, H) + (int64_t)H * (T / BC + S) * BIMG;
+}
 
 int launch_backward(const BackArgs &a) {
     return a.dtype == VLF_BF16 ? launch_backward_typed<BF16>(a) : launch_backward_typed<F16>(a);

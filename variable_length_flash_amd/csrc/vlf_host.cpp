@@ -231,12 +231,12 @@ int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_
                          Launch::kRotated);
 }
 
-int vlf_backward_workspace_bytes(int32_t T, int32_t H, int64_t *bytes) {
+int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes) {
     if (!bytes)
         return fail(VLF_EINVAL, "null bytes");
-    if (T < 0 || H < 0 || H > 65536)
-        return fail(VLF_EINVAL, "T = %d, H = %d", T, H);
-    *bytes = backward_workspace_bytes(T, H);
+    if (T < 0 || S < 0 || H < 0 || H > 65536)
+        return fail(VLF_EINVAL, "T = %d, S = %d, H = %d", T, S, H);
+    *bytes = backward_workspace_bytes(T, S, H);
     return VLF_OK;
 }
 
@@ -265,10 +265,10 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
         return fail(VLF_EINVAL, "workspace_bytes = %lld < 0", (long long)workspace_bytes_);
     if (!work)
         return VLF_OK;
-    if (!workspace || workspace_bytes_ < backward_workspace_bytes(T, H))
-        return fail(VLF_EINVAL, "workspace of %lld bytes; T=%d H=%d need %lld",
-                    (long long)(workspace ? workspace_bytes_ : 0), T, H,
-                    (long long)backward_workspace_bytes(T, H));
+    if (!workspace || workspace_bytes_ < backward_workspace_bytes(T, S, H))
+        return fail(VLF_EINVAL, "workspace of %lld bytes; T=%d S=%d H=%d need %lld",
+                    (long long)(workspace ? workspace_bytes_ : 0), T, S, H,
+                    (long long)backward_workspace_bytes(T, S, H));
     if (!tiles_dev || !out || !dout || !lse || !dqkv)
         return fail(VLF_EINVAL, "null device pointer (tiles=%p out=%p dout=%p lse=%p dqkv=%p)",
                     (const void *)tiles_dev, out, dout, (const void *)lse, dqkv);

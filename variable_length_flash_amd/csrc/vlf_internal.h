@@ -57,15 +57,15 @@ struct BackArgs {
     const void *out;
     const void *dout;
     const float *lse;
-    void *workspace;  // delta (float32 [H, T])
+    void *workspace;  // delta and lse * log2(e) (float32 [H, T] each), then the tile images
     void *dqkv;
     void *stream;
 };
 
 // Bytes of the backward's workspace.
-int64_t backward_workspace_bytes(int32_t T, int32_t H);
+int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H);
 
-// Queue the backward kernels (delta, dK/dV, dQ); returns a vlf_status.
+// Queue the backward kernels (prep, dK/dV, dQ); returns a vlf_status.
 int launch_backward(const BackArgs &a);
 
 // Record the calling thread's error message (printf-style) and return `status`.
