@@ -214,7 +214,7 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes
  *   tiles_dev, num_tiles  the tile table for br-row tiles (vlf_tile_table with this br, or any
  *              permutation of it): each entry is a key tile of the dK/dV pass and a query tile
  *              of the dQ pass.
- *   br         64 or 128.
+ *   br         64, 128 or 256: the rows of a tile, 32 per wave of the two passes.
  *   out        device, [T, H*64] of `dtype`: the forward's output for these inputs.
  *   dout       device, [T, H*64] of `dtype`: the gradient of the loss with respect to out.
  *   lse        device, [H, T] float32: the forward's log-sum-exp for these inputs.
@@ -224,8 +224,8 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes
  *   stream     hipStream_t (NULL = the null stream). Three kernels; asynchronous; allocates
  *              nothing. Calls that may overlap in time need separate workspaces.
  *
- * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, br not 64 or
- * 128, negative sizes, T or S inconsistent, a workspace smaller than
+ * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, br not 64, 128
+ * or 256, negative sizes, T or S inconsistent, a workspace smaller than
  * vlf_backward_workspace_bytes), VLF_EUNSUPPORTED (dtype), VLF_EHIP (launch failure).
  */
 int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32_t table_rows,

@@ -326,7 +326,7 @@ def _backward_status(**kw):
 @pytest.mark.parametrize("kw,status,text", [
     (dict(dtype=7), binding.VLF_EUNSUPPORTED, "dtype"),
     (dict(W=-1), binding.VLF_EINVAL, "window"),
-    (dict(br=256), binding.VLF_EINVAL, "br = 256"),
+    (dict(br=512), binding.VLF_EINVAL, "br = 512"),
     (dict(br=32), binding.VLF_EINVAL, "br = 32"),
     (dict(H=0), binding.VLF_EINVAL, "H = 0"),
     (dict(ws_bytes=100), binding.VLF_EINVAL, "workspace"),

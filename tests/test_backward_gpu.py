@@ -74,7 +74,7 @@ def compare(name, w, qkv, cos, sin, dout, got, window=None):
 LENS = [5, 40, 1, 33, 70]
 
 
-@pytest.mark.parametrize("br", [64, 128])
+@pytest.mark.parametrize("br", [64, 128, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("window", [0, 9, 65])
 def test_backward_page_fixture(dtype, window, br):
@@ -87,7 +87,7 @@ def test_backward_page_fixture(dtype, window, br):
 RAGGED = [1, 63, 64, 65, 127, 128, 129, 300, 0, 257, 31, 32, 33, 2]
 
 
-@pytest.mark.parametrize("br", [64, 128])
+@pytest.mark.parametrize("br", [64, 128, 256])
 @pytest.mark.parametrize("window", [0, 1, 33, 128])
 def test_backward_ragged(window, br):
     w = workloads.custom(RAGGED, 3, dtype="bf16", window=window, base=1e4, table_rows=512,
@@ -98,7 +98,9 @@ def test_backward_ragged(window, br):
 
 
 @pytest.mark.parametrize("dtype,window,br", [("bf16", 0, 64), ("bf16", 0, 128),
-                                             ("bf16", 300, 128), ("fp16", 0, 128)])
+                                             ("bf16", 300, 128), ("fp16", 0, 128),
+                                             ("bf16", 0, 256), ("bf16", 300, 256),
+                                             ("fp16", 0, 256)])
 def test_backward_longer_sequences(dtype, window, br):
     """Many steps per tile: each key tile's dK, dV and each query tile's dQ summed over up to
     41 staged steps, through both LDS buffers many times."""
@@ -115,12 +117,12 @@ def test_backward_is_deterministic():
     w = workloads.custom([700, 1300, 64], 2, dtype="bf16", window=0, base=1.6e5,
                          table_rows=1300, seed=19)
     _say("case backward determinism")
-    a = run_backward(w, seed=3, br=128)[4]
-    b = run_backward(w, seed=3, br=128)[4]
+    a = run_backward(w, seed=3, br=256)[4]
+    b = run_backward(w, seed=3, br=256)[4]
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("br", [64, 128])
+@pytest.mark.parametrize("br", [64, 128, 256])
 def test_backward_single_key_rows(br):
     """W = 1: each row sees only itself, so dv = dout and dq, dk are zero up to the rounding of
     dP - delta (one key's dO.v against the same product summed by the delta kernel)."""

@@ -383,13 +383,13 @@ def attend_backward_into(batch: Batch, qkv, cos, sin, heads: int, window: int, s
     """Queue the backward (include/vlf.h, vlf_attend_backward): dqkv = d sum(out * dout) / d qkv
     for the forward with the same arguments, whose ``out`` and ``lse`` are passed in.
 
-    ``batch`` must be prepared with ``br`` 64 or 128 (``choose_backward_br``). dout and dqkv
+    ``batch`` must be prepared with ``br`` 64, 128 or 256 (``choose_backward_br``). dout and dqkv
     have the shapes and dtype of out and qkv. ``workspace``: a contiguous uint8 device tensor of
     at least ``backward_workspace_bytes`` (allocated on the launch stream when None).
     """
     import torch
-    if batch.br not in (64, 128):
-        raise VlfError(VLF_EINVAL, f"the backward runs on 64- or 128-row tiles; batch has "
+    if batch.br not in (64, 128, 256):
+        raise VlfError(VLF_EINVAL, f"the backward runs on 64-, 128- or 256-row tiles; batch has "
                                    f"br={batch.br}")
     code = _check_inputs(batch, qkv, cos, sin, heads, out, lse)
     T = batch.tokens

@@ -2102,8 +2102,8 @@ int launch_br(const AttendArgs &a) {
 constexpr int BIMG = 5 * IMG;  // one tile's images: Q~, Q~^T, dO^T (24 KB), K~, K~^T (16 KB)
 constexpr int BS = 64;         // streamed rows per step of back_kv and back_q
 
-// Byte offset of the images in the workspace: delta and lse * log2(e), float32 [H, T] each,
-// then padding to 256 bytes.
+// Byte offset of the images in the workspace: -delta and -lse, float32 [H, T] each, then
+// padding to 256 bytes.
 __host__ __device__ __forceinline__ int64_t back_img_offset(int32_t T, int32_t H) {
     return ((int64_t)8 * T * H + 255) / 256 * 256;
 }
@@ -2183,8 +2183,8 @@ __device__ __forceinline__ void load_halves(const uint16_t *base, int64_t ld, in
     a = x, b = y;
 }
 
-// The operand images of the 64-row tiles of one table entry (R rows) and head, with delta and
-// lse * log2(e) of their rows. Built in LDS (four lanes per row, 16 dims each) and copied out
+// The operand images of the 64-row tiles of one table entry (R rows) and head, with -delta and
+// -lse of their rows. Built in LDS (four lanes per row, 16 dims each) and copied out
 // in 16-byte pieces. Rows past the sequence are zero in every image.
 template <class E, int R>
 __global__ void __launch_bounds__(256)
@@ -2204,7 +2204,7 @@ back_prep(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int hd = H * D;
     const int tid = (int)threadIdx.x;
     const int row = tid >> 2, c4 = tid & 3;
-    float *delta = (float *)ws + (int64_t)h * T, *lse2 = (float *)ws + (int64_t)(H + h) * T;
+    float *ndelta = (float *)ws + (int64_t)h * T, *nlse = (float *)ws + (int64_t)(H + h) * T;
     const int64_t nb = T / BC + S;
     uint8_t *blocks = ws + back_img_offset(T, H) + ((int64_t)h * nb + start / BC + seq) * BIMG;
 #pragma unroll 1
@@ -2242,8 +2242,8 @@ back_prep(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
         if (i < len && c4 == 0) {
-            delta[start + i] = acc;
-            lse2[start + i] = lse[(int64_t)h * T + start + i] * LOG2E;
+            ndelta[start + i] = -acc;
+            nlse[start + i] = -lse[(int64_t)h * T + start + i];
         }
         __syncthreads();
         uint8_t *blk = blocks + (int64_t)(t / BC) * BIMG;
@@ -2341,25 +2341,27 @@ __device__ __forceinline__ void copy_floats(const float *base, int start, int r0
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, 4 * lane, 0, 0, 0);
 }
 
-// P = exp2(S log2(e) - lse2) and dS = P (dP - delta) of a 32 x 32 accumulator block whose
-// register i holds row 8(i/4) + 4g + i%4 (lse2 and delta per register), packed to E as the B
-// operands of the next products. With MASK, only rows r with r - a in [0, span) count (a is
-// relative to register 0 of the lane's group).
+// Compile-time choice of the masked or the unmasked step.
+template <bool B>
+struct Masked {
+    static constexpr bool value = B;
+};
+
+// P = exp(S - lse) and dS = P (dP - delta) of a 32 x 32 accumulator block whose register i holds
+// row 8(i/4) + 4g + i%4 (sc holds S - lse and dp holds dP - delta: the products started from
+// -lse and -delta), packed to E as the B operands of the next products. With MASK, only rows r
+// with r - a in [0, span) count (a is relative to register 0 of the lane's group).
 template <class E, bool MASK>
-__device__ __forceinline__ void back_pds(f32x16 &sc, f32x16 &dp, const f32x4 (&lv)[4],
-                                         const f32x4 (&dv)[4], int a, uint32_t span,
+__device__ __forceinline__ void back_pds(f32x16 &sc, f32x16 &dp, int a, uint32_t span,
                                          u32x4 (&pp)[2], u32x4 (&pd)[2]) {
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 4 * gi + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], LOG2E, -lv[gi][e]));
-            if (MASK)
-                p = (uint32_t)(8 * gi + e - a) < span ? p : 0.f;
-            sc[i] = p;
-            dp[i] = p * (dp[i] - dv[gi][e]);
-        }
+    for (int i = 0; i < 16; ++i) {
+        float p = __builtin_amdgcn_exp2f(sc[i] * LOG2E);
+        if (MASK)
+            p = (uint32_t)(8 * (i >> 2) + (i & 3) - a) < span ? p : 0.f;
+        sc[i] = p;
+        dp[i] = p * dp[i];
+    }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -2369,16 +2371,16 @@ __device__ __forceinline__ void back_pds(f32x16 &sc, f32x16 &dp, const f32x4 (&l
         }
 }
 
-// The same for a transposed block (one row per lane: lse2 and delta are the lane's), dS only.
+// The same for a transposed block (one row per lane), dS only.
 template <class E, bool MASK>
-__device__ __forceinline__ void back_ds(const f32x16 &st, f32x16 &dp, float lq, float dl,
-                                        int a, uint32_t span, u32x4 (&pd)[2]) {
+__device__ __forceinline__ void back_ds(const f32x16 &st, f32x16 &dp, int a, uint32_t span,
+                                        u32x4 (&pd)[2]) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], LOG2E, -lq));
+        float p = __builtin_amdgcn_exp2f(st[i] * LOG2E);
         if (MASK)
             p = (uint32_t)(8 * (i >> 2) + (i & 3) - a) < span ? p : 0.f;
-        dp[i] = p * (dp[i] - dl);
+        dp[i] = p * dp[i];
     }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
@@ -2394,17 +2396,19 @@ __device__ __forceinline__ void back_ds(const f32x16 &st, f32x16 &dp, float lq, 
 // 32-row block. A step's Q~, Q~^T and dO^T images come from back_prep and its dO rows from dout,
 // straight into one of two LDS slots while the other slot's step is computed; P and dS go from
 // the accumulators into the B operands of dV^T += dO^T P and dK^T += Q~^T dS.
-// Two slots of 65 KB leave room for two workgroups a CU: two waves a SIMD with four waves a
-// workgroup, one with two.
-template <class E, int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)))
+// SL slots of 33 KB: copies run SL - 1 steps ahead. Eight waves take two a SIMD and the CU's
+// LDS for four slots; four take two a SIMD with two workgroups of two slots a CU; two take one.
+template <class E, int NW, int SL>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 1 : 2)))
 back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
         const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
         const uint8_t *__restrict__ ws, uint16_t *__restrict__ dqkv, int32_t num_tiles,
         int32_t T, int32_t S, int32_t H, int32_t P, int32_t window) {
-    constexpr int SLOT = 4 * IMG + 512;  // Q~, Q~^T, dO^T, dO rows, lse * log2(e), delta
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
+    constexpr int SLOT = 4 * IMG + 512;  // Q~, Q~^T, dO^T, dO rows, -lse, -delta
+    // buffer loads a wave issues per copy (waves 0 and 1 issue one more)
+    constexpr int PIECES = 3 * IMG / 1024 / NW + 8 / NW;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SL * SLOT];
 
     const int work = xcd_work();
     const int h = work / num_tiles;
@@ -2435,8 +2439,8 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     back_visible(kj, len, window, vlo, vhi);
     const uint32_t span = (uint32_t)(vhi - vlo);
 
-    const float *lse2 = (const float *)ws + (int64_t)(H + h) * T;
-    const float *delta = (const float *)ws + (int64_t)h * T;
+    const float *nlse = (const float *)ws + (int64_t)(H + h) * T;
+    const float *ndelta = (const float *)ws + (int64_t)h * T;
     const uint8_t *imgs =
         ws + back_img_offset(T, H) + ((int64_t)h * (T / BC + S) + start / BC + seq) * BIMG;
     lds_u8 *const base = (lds_u8 *)lds;
@@ -2445,74 +2449,79 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         copy_block<NW, 3 * IMG>(imgs + (int64_t)(it / BC) * BIMG, d, wvu, lane);
         copy_rows<NW>(back_rows(dout + h * D, hd, start, it, len), hd, d + 3 * IMG, wvu, lane);
         if (wvu == 0)
-            copy_floats(lse2, start, it, len, d + 4 * IMG, lane);
+            copy_floats(nlse, start, it, len, d + 4 * IMG, lane);
         if (wvu == 1)
-            copy_floats(delta, start, it, len, d + 4 * IMG + 256, lane);
+            copy_floats(ndelta, start, it, len, d + 4 * IMG + 256, lane);
     };
-    copy(qa, 0);
-    ring_barrier<0>();
+    const int steps = (qb - qa + BS - 1) / BS;
+    for (int k = 0; k < SL - 1 && k < steps; ++k)
+        copy(qa + k * BS, k);
+    if (steps >= SL - 1)
+        ring_barrier<PIECES * (SL - 2)>();
+    else
+        ring_barrier<0>();
 
     f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
-    int b = 0;
-    for (int it = qa; it < qb; it += BS) {
-        if (it + BS < qb)
-            copy(it + BS, b ^ 1);
+    for (int st = 0; st < steps; ++st) {
+        const int it = qa + st * BS;
+        const bool more = st + SL - 1 < steps;
+        if (more)
+            copy(it + (SL - 1) * BS, (st + SL - 1) % SL);
         if (!idle) {
-            const uint8_t *qs = lds + b * SLOT, *qt = qs + IMG, *ot = qs + 2 * IMG;
+            const uint8_t *qs = lds + (st % SL) * SLOT, *qt = qs + IMG, *ot = qs + 2 * IMG;
             const uint8_t *os = qs + 3 * IMG;
-            const float *lb = (const float *)(qs + 4 * IMG), *dl = lb + 64;
+            const float *nl = (const float *)(qs + 4 * IMG), *nd = nl + 64;
+            // both 32-row blocks in one stretch, so that the softmax of one overlaps the
+            // products of the other; steps every pair of which is visible skip the mask
+            auto body = [&](auto masked) {
+                constexpr bool MASK = decltype(masked)::value;
+                f32x16 sc[2], dp[2];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                // every LDS operand of the block first, so that the reads overlap
-                u32x4 qa_[4], oa_[4], ta[8];
-                f32x4 lv[4], dv[4];
+                for (int rb = 0; rb < 2; ++rb) {
+                    // S - lse and dP - delta of query rows it + 32rb + 8(i/4) + 4g + i%4
+                    // (register i): the accumulators start at -lse and -delta
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int off = (32 * rb + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
-                    qa_[c] = *(const u32x4 *)(qs + off);
-                    oa_[c] = *(const u32x4 *)(os + off);
+                    for (int gi = 0; gi < 4; ++gi) {
+                        const f32x4 x = *(const f32x4 *)(nl + 32 * rb + 8 * gi + 4 * g);
+                        const f32x4 y = *(const f32x4 *)(nd + 32 * rb + 8 * gi + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sc[rb][4 * gi + e] = x[e], dp[rb][4 * gi + e] = y[e];
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int off = (32 * rb + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
+                        sc[rb] = E::mfma(*(const u32x4 *)(qs + off), kop[c], sc[rb]);
+                        dp[rb] = E::mfma(*(const u32x4 *)(os + off), vop[c], dp[rb]);
+                    }
                 }
 #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    const int ch = 4 * rb + 2 * kc + g;
-                    const int f0 = n * 128 + 16 * (ch ^ swz(n));
-                    const int f1 = (32 + n) * 128 + 16 * (ch ^ swz(32 + n));
-                    ta[4 * kc] = *(const u32x4 *)(ot + f0);
-                    ta[4 * kc + 1] = *(const u32x4 *)(ot + f1);
-                    ta[4 * kc + 2] = *(const u32x4 *)(qt + f0);
-                    ta[4 * kc + 3] = *(const u32x4 *)(qt + f1);
-                }
+                for (int rb = 0; rb < 2; ++rb) {
+                    u32x4 pp[2], pd[2];
+                    back_pds<E, MASK>(sc[rb], dp[rb], vlo - it - 32 * rb - 4 * g, span, pp, pd);
+                    // dV^T += dO^T P and dK^T += Q~^T dS (dims 0..31 and 32..63)
 #pragma unroll
-                for (int gi = 0; gi < 4; ++gi) {
-                    lv[gi] = *(const f32x4 *)(lb + 32 * rb + 8 * gi + 4 * g);
-                    dv[gi] = *(const f32x4 *)(dl + 32 * rb + 8 * gi + 4 * g);
+                    for (int kc = 0; kc < 2; ++kc) {
+                        const int ch = 4 * rb + 2 * kc + g;
+                        const int f0 = n * 128 + 16 * (ch ^ swz(n));
+                        const int f1 = (32 + n) * 128 + 16 * (ch ^ swz(32 + n));
+                        dv0 = E::mfma(*(const u32x4 *)(ot + f0), pp[kc], dv0);
+                        dv1 = E::mfma(*(const u32x4 *)(ot + f1), pp[kc], dv1);
+                        dk0 = E::mfma(*(const u32x4 *)(qt + f0), pd[kc], dk0);
+                        dk1 = E::mfma(*(const u32x4 *)(qt + f1), pd[kc], dk1);
+                    }
                 }
-                // S and dP of query rows it + 32rb + 8(i/4) + 4g + i%4 (register i)
-                f32x16 sc = {}, dp = {};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    sc = E::mfma(qa_[c], kop[c], sc);
-                    dp = E::mfma(oa_[c], vop[c], dp);
-                }
-                // P = exp(S - lse) over the rows key kj sees (0 elsewhere), dS = P (dP - delta);
-                // blocks every pair of which is visible take the branch without the mask
-                u32x4 pp[2], pd[2];
-                if (back_full(it + 32 * rb, kw0, len, window))
-                    back_pds<E, false>(sc, dp, lv, dv, 0, 0, pp, pd);
-                else
-                    back_pds<E, true>(sc, dp, lv, dv, vlo - it - 32 * rb - 4 * g, span, pp, pd);
-                // dV^T += dO^T P and dK^T += Q~^T dS (dims 0..31 and 32..63)
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    dv0 = E::mfma(ta[4 * kc], pp[kc], dv0);
-                    dv1 = E::mfma(ta[4 * kc + 1], pp[kc], dv1);
-                    dk0 = E::mfma(ta[4 * kc + 2], pd[kc], dk0);
-                    dk1 = E::mfma(ta[4 * kc + 3], pd[kc], dk1);
-                }
-            }
+            };
+            if (back_full(it, kw0, len, window) && back_full(it + 32, kw0, len, window))
+                body(Masked<false>{});
+            else
+                body(Masked<true>{});
         }
-        ring_barrier<0>();
-        b ^= 1;
+        // the next step's copies have landed (later steps' may still be in flight)
+        if (more)
+            ring_barrier<PIECES * (SL - 2)>();
+        else
+            ring_barrier<0>();
     }
 
     // dK rotated back to the key's position, and dV; register i of block b holds dim
@@ -2553,7 +2562,7 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 // from back_prep and its V rows from qkv, straight into one of two LDS slots; dS^T goes from the
 // accumulators into the B operand of dQ^T += K~^T dS^T. dQ is rotated back to the row's
 // position, scaled and written once.
-template <class E, int NW>
+template <class E, int NW, int SL>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
        const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
@@ -2561,7 +2570,8 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
        const uint8_t *__restrict__ ws, uint16_t *__restrict__ dqkv, int32_t num_tiles,
        int32_t T, int32_t S, int32_t H, int32_t P, int32_t window, float scale) {
     constexpr int SLOT = 3 * IMG;  // K~, K~^T, V rows
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
+    constexpr int PIECES = 2 * IMG / 1024 / NW + 8 / NW;  // buffer loads a wave issues per copy
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SL * SLOT];
 
     const int work = xcd_work();
     const int h = work / num_tiles;
@@ -2586,11 +2596,15 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         query_make<E>(r, scale, qop);
     }
     back_row_operand(dout + h * D, hd, start, qi, len, g, oop);
-    float lq = 0.f, dq_ = 0.f;  // lse * log2(e) and delta of the lane's row
+    float nl = 0.f, nd = 0.f;  // -lse and -delta of the lane's row
     if (qi < len) {
-        lq = ((const float *)ws)[(int64_t)(H + h) * T + start + qi];
-        dq_ = ((const float *)ws)[(int64_t)h * T + start + qi];
+        nl = ((const float *)ws)[(int64_t)(H + h) * T + start + qi];
+        nd = ((const float *)ws)[(int64_t)h * T + start + qi];
     }
+    f32x16 nlv, ndv;  // where the S^T and dP^T blocks start: -lse and -delta in every register
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        nlv[i] = nl, ndv[i] = nd;
 
     int ka, kb, klo, khi;
     back_span(i0, 32 * NW, len, window, ka, kb);
@@ -2606,55 +2620,61 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         copy_rows<NW>(back_rows(qkv + 2 * hd + h * D, ld, start, jt, len), ld, d + 2 * IMG, wvu,
                       lane);
     };
-    copy(ka, 0);
-    ring_barrier<0>();
+    const int steps = (kb - ka + BS - 1) / BS;
+    for (int k = 0; k < SL - 1 && k < steps; ++k)
+        copy(ka + k * BS, k);
+    if (steps >= SL - 1)
+        ring_barrier<PIECES * (SL - 2)>();
+    else
+        ring_barrier<0>();
 
     f32x16 dq0 = {}, dq1 = {};
-    int b = 0;
-    for (int jt = ka; jt < kb; jt += BS) {
-        if (jt + BS < kb)
-            copy(jt + BS, b ^ 1);
+    for (int st = 0; st < steps; ++st) {
+        const int jt = ka + st * BS;
+        const bool more = st + SL - 1 < steps;
+        if (more)
+            copy(jt + (SL - 1) * BS, (st + SL - 1) % SL);
         if (!idle) {
-            const uint8_t *ks = lds + b * SLOT, *kt = ks + IMG, *vs = ks + 2 * IMG;
+            const uint8_t *ks = lds + (st % SL) * SLOT, *kt = ks + IMG, *vs = ks + 2 * IMG;
+            auto body = [&](auto masked) {
+                constexpr bool MASK = decltype(masked)::value;
+                f32x16 st[2], dp[2];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                // every LDS operand of the block first, so that the reads overlap
-                u32x4 ka_[4], va_[4], ta[4];
+                for (int kb2 = 0; kb2 < 2; ++kb2) {
+                    // S^T - lse and dP^T - delta of keys jt + 32kb2 + 8(i/4) + 4g + i%4
+                    st[kb2] = nlv, dp[kb2] = ndv;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int off = (32 * kb2 + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
-                    ka_[c] = *(const u32x4 *)(ks + off);
-                    va_[c] = *(const u32x4 *)(vs + off);
+                    for (int c = 0; c < 4; ++c) {
+                        const int off = (32 * kb2 + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
+                        st[kb2] = E::mfma(*(const u32x4 *)(ks + off), qop[c], st[kb2]);
+                        dp[kb2] = E::mfma(*(const u32x4 *)(vs + off), oop[c], dp[kb2]);
+                    }
                 }
 #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    const int ch = 4 * kb2 + 2 * kc + g;
-                    ta[2 * kc] = *(const u32x4 *)(kt + n * 128 + 16 * (ch ^ swz(n)));
-                    ta[2 * kc + 1] =
-                        *(const u32x4 *)(kt + (32 + n) * 128 + 16 * (ch ^ swz(32 + n)));
-                }
-                // S^T and dP^T of keys jt + 32kb2 + 8(i/4) + 4g + i%4 (register i)
-                f32x16 st = {}, dp = {};
+                for (int kb2 = 0; kb2 < 2; ++kb2) {
+                    u32x4 pd[2];
+                    back_ds<E, MASK>(st[kb2], dp[kb2], klo - jt - 32 * kb2 - 4 * g, span, pd);
+                    // dQ^T += K~^T dS^T (dims 0..31 and 32..63)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    st = E::mfma(ka_[c], qop[c], st);
-                    dp = E::mfma(va_[c], oop[c], dp);
+                    for (int kc = 0; kc < 2; ++kc) {
+                        const int ch = 4 * kb2 + 2 * kc + g;
+                        dq0 = E::mfma(*(const u32x4 *)(kt + n * 128 + 16 * (ch ^ swz(n))), pd[kc],
+                                      dq0);
+                        dq1 = E::mfma(
+                            *(const u32x4 *)(kt + (32 + n) * 128 + 16 * (ch ^ swz(32 + n))),
+                            pd[kc], dq1);
+                    }
                 }
-                u32x4 pd[2];
-                if (back_full(jt + 32 * kb2, qw0, len, window))
-                    back_ds<E, false>(st, dp, lq, dq_, 0, 0, pd);
-                else
-                    back_ds<E, true>(st, dp, lq, dq_, klo - jt - 32 * kb2 - 4 * g, span, pd);
-                // dQ^T += K~^T dS^T (dims 0..31 and 32..63)
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    dq0 = E::mfma(ta[2 * kc], pd[kc], dq0);
-                    dq1 = E::mfma(ta[2 * kc + 1], pd[kc], dq1);
-                }
-            }
+            };
+            if (back_full(jt, qw0, len, window) && back_full(jt + 32, qw0, len, window))
+                body(Masked<false>{});
+            else
+                body(Masked<true>{});
         }
-        ring_barrier<0>();
-        b ^= 1;
+        if (more)
+            ring_barrier<PIECES * (SL - 2)>();
+        else
+            ring_barrier<0>();
     }
 
     // dQ rotated back to the row's position (the transpose of the half-split rotation) and
@@ -2709,7 +2729,8 @@ int launch_backward_tiles(const BackArgs &a) {
     void *args2[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
                      (void *)&dout, (void *)&wsc, (void *)&dqkv, (void *)&num_tiles,
                      (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&W};
-    e = hipLaunchKernel((const void *)back_kv<E, NW>, dim3((unsigned)blocks), dim3(64 * NW),
+    constexpr int SL = NW == 8 ? 4 : 2;
+    e = hipLaunchKernel((const void *)back_kv<E, NW, SL>, dim3((unsigned)blocks), dim3(64 * NW),
                         args2, 0, st);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "dK/dV launch failed: %s", hipGetErrorString(e));
@@ -2717,7 +2738,7 @@ int launch_backward_tiles(const BackArgs &a) {
                      (void *)&dout, (void *)&wsc, (void *)&dqkv, (void *)&num_tiles,
                      (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&W,
                      (void *)&scale};
-    e = hipLaunchKernel((const void *)back_q<E, NW>, dim3((unsigned)blocks), dim3(64 * NW),
+    e = hipLaunchKernel((const void *)back_q<E, NW, SL>, dim3((unsigned)blocks), dim3(64 * NW),
                         args3, 0, st);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "dQ launch failed: %s", hipGetErrorString(e));
@@ -2726,6 +2747,8 @@ int launch_backward_tiles(const BackArgs &a) {
 
 template <class E>
 int launch_backward_typed(const BackArgs &a) {
+    if (a.br == 256)
+        return launch_backward_tiles<E, 8>(a);
     return a.br == 128 ? launch_backward_tiles<E, 4>(a) : launch_backward_tiles<E, 2>(a);
 }
 }  // namespace

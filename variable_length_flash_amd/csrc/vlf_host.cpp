@@ -251,8 +251,8 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
         return fail(VLF_EINVAL, "window = %d < 0", window);
     if (num_tiles < 0)
         return fail(VLF_EINVAL, "negative size: num_tiles=%d", num_tiles);
-    if (br != 64 && br != 128)
-        return fail(VLF_EINVAL, "br = %d; the backward runs on 64- or 128-row tiles", br);
+    if (br != 64 && br != 128 && br != 256)
+        return fail(VLF_EINVAL, "br = %d; the backward runs on 64-, 128- or 256-row tiles", br);
     if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
         return fail(VLF_EINVAL, "scale is not finite");
     const bool work = T > 0 && num_tiles > 0;
