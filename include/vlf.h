@@ -48,7 +48,7 @@ enum vlf_dtype {
     VLF_BF16 = 1, /* bfloat16 */
 };
 
-/* Library ABI version (this header: 2). */
+/* Library ABI version (this header: 3). */
 int32_t vlf_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). The pointer

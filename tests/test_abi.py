@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     lib = vlf.load_library()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.vlf_version() == 2
+    assert lib.vlf_version() == 3
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

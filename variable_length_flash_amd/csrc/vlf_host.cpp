@@ -63,7 +63,7 @@ using namespace vlf;
 
 extern "C" {
 
-int32_t vlf_version(void) { return 2; }
+int32_t vlf_version(void) { return 3; }
 
 const char *vlf_last_error(void) { return g_error.c_str(); }
 
