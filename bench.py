@@ -43,7 +43,7 @@ PEAK_BF16_TFLOPS = 2516.6     # dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0         # HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flash_amd", "csrc", "vlf_attend.hip")
 KERNEL_NAMES = ("attend_pre_ph", "attend_pre", "attend_fwd", "attend_one", "attend_slide",
-                "prep_tiles", "attend_back")
+                "prep_tiles", "back_prep", "back_kv", "back_q")
 
 
 def forward_kernel(prerotate: bool, br: int, window: int) -> str:

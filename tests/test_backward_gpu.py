@@ -133,3 +133,41 @@ def test_backward_single_key_rows(br):
     d = dout.float().numpy()
     assert np.abs(got[:, 2 * hd:] - d).max() <= 2 ** -8 * np.abs(d).max()
     assert np.abs(got[:, :2 * hd]).max() <= 1e-2
+
+
+def test_backward_offsets_past_2gib():
+    """qkv of 2.2 GB (88 sequences of 1024 tokens, 64 heads, bf16): byte offsets into qkv, dout
+    and dqkv pass 2^31, the prep pass's block offsets pass 2^32, and both passes build their
+    per-step buffer descriptors from 64-bit row offsets. Inputs drawn on the GPU from a seeded
+    generator; the first and the last two sequences (all rows, every head) against the
+    oracle."""
+    lens, H = [1024] * 88, 64
+    w = workloads.custom(lens, H, dtype="bf16", window=0, base=1.6e5, table_rows=1024, seed=23)
+    T = w.tokens
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(23)
+    q = torch.randn((T, 3 * H * 64), generator=gen, device=dev).to(torch.bfloat16)
+    do = torch.randn((T, H * 64), generator=gen, device=dev).to(torch.bfloat16)
+    assert q.numel() * 2 > 2 ** 31
+    cos, sin = workloads.rope_tables(w)
+    c, s = cos.to(dev), sin.to(dev)
+    out, lse = vlf.attend(q, c, s, w.cu, H, 0, w.scale)
+    _say("case backward offsets past 2 GiB")
+    batch = vlf.prepare(w.cu, dev, 128, False, 0)
+    ws_bytes = vlf.backward_workspace_bytes(T, len(lens), H)
+    assert ws_bytes > 2 ** 31
+    dqkv = torch.full_like(q, float("nan"))
+    vlf.attend_backward_into(batch, q, c, s, H, 0, w.scale, out, lse, do, dqkv)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dqkv).any()
+    cu1 = np.array([0, 1024], dtype=np.int32)
+    for si in (0, 86, 87):
+        a, b = 1024 * si, 1024 * (si + 1)
+        want = oracle.attend_backward(q[a:b].float().cpu().numpy(), cos.float().numpy(),
+                                      sin.float().numpy(), cu1, H, 0, w.scale,
+                                      do[a:b].float().cpu().numpy(), mode="B", dtype="bf16")
+        got = dqkv[a:b].float().cpu().numpy()
+        rel = float(np.abs(got - want).max() / np.abs(want).max())
+        _say(f"[backward] 2.2 GB qkv, sequence {si}: rel {rel:.2e}")
+        assert rel <= REL_TOL["bf16"], (si, rel)
