@@ -11,3 +11,4 @@ from .binding import (  # noqa: F401
     load_library, new_workspace, prepare, rotate_keys, tile_count, tile_table, typical_length,
     visible_pairs, workspace_bytes,
 )
+from . import tune  # noqa: F401
