@@ -193,6 +193,8 @@ def run(args):
 
     if args.backward:
         return run_backward(args, w, q, c, s, out, lse, stream)
+    if args.unfused:
+        return run_unfused(args, w, q, c, s, out, lse, stream, batch, ws)
 
     for _ in range(args.warmup):
         step()
@@ -328,6 +330,47 @@ def run_backward(args, w, q, c, s, out, lse, stream):
     print(json.dumps(line), flush=True)
 
 
+def run_unfused(args, w, q, c, s, out, lse, stream, batch, ws):
+    """``--unfused``: what fusing the rotation into the forward saves. Times, on the launch
+    stream, the fused forward (the default schedule), the rotation pass alone (vlf_rotate_qkv)
+    and the forward over its output with identity tables and scale 1 on the same schedule; both
+    forwards multiply the same rounded operands."""
+    import torch
+
+    import variable_length_flash_amd as vlf
+    dst = torch.empty_like(q)
+    one, zero = torch.ones_like(c), torch.zeros_like(s)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    fused = timed(lambda: vlf.attend_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse,
+                                          workspace=ws))
+    rot = timed(lambda: vlf.rotate_qkv_into(batch, q, c, s, w.heads, w.scale, dst))
+    plain = timed(lambda: vlf.attend_into(batch, dst, one, zero, w.heads, w.window, 1.0, out,
+                                          lse, workspace=ws))
+    line = {
+        "metric": "fused forward time against rotation pass + forward (unfused baseline)",
+        "value": round(fused, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {w.note}", "br": batch.br,
+                   "path": "prerotate" if batch.prerotate else "direct"},
+        "fused_ms": round(fused, 4), "rotation_pass_ms": round(rot, 4),
+        "forward_on_rotated_ms": round(plain, 4), "unfused_ms": round(rot + plain, 4),
+        "fusion_saving_pct": round(100 * (rot + plain - fused) / (rot + plain), 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def roofline(kernel: str, flops: float, alg_bytes: int, kernel_ms: float, traffic):
     """The forward kernel against its bound: the matrix unit when the workload's arithmetic
     intensity (effective FLOP per algorithmic byte) is above the ridge of the bf16 peak and HBM,
@@ -407,6 +450,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (vlf_attend_backward) instead of the forward")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the fused forward against the rotation pass plus the forward")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", nargs="+")

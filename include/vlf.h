@@ -234,6 +234,29 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
                         int32_t dtype, const void *out, const void *dout, const float *lse,
                         void *workspace, int64_t workspace_bytes, void *dqkv, void *stream);
 
+/*
+ * The unfused baseline's rotation pass: the forward's rotation as a kernel of its own (the page
+ * applies it inside `attend`; this pass exists to measure what that fusion saves). For every
+ * row i of every tiled sequence and every head it writes
+ *     qkv_out q part = RNE_dtype(RN_f32(rot(q, i)) * scale),
+ *     qkv_out k part = RNE_dtype(RN_f32(rot(k, i))),
+ *     qkv_out v part = v,
+ * the operands exactly as vlf_attend rounds them, so vlf_attend over qkv_out with identity
+ * tables (cos 1, sin 0) and scale 1 gives the bits vlf_attend gives over qkv.
+ *
+ *   qkv, cos, sin, table_rows, cu_dev, T, S, H, scale, dtype  as in vlf_attend.
+ *   tiles_dev, num_tiles, br  a tile table (vlf_tile_table) for br = 64, 128 or 256.
+ *   qkv_out    device, [T, 3*H*64] of `dtype`, not qkv; rows no tile covers are not written.
+ *   stream     hipStream_t (NULL = the null stream). One kernel; asynchronous.
+ *
+ * Errors: VLF_EINVAL (null pointer with work to do, qkv_out == qkv, H out of range, br, negative
+ * sizes, T or S inconsistent), VLF_EUNSUPPORTED (dtype), VLF_EHIP (launch failure).
+ */
+int vlf_rotate_qkv(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                   const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
+                   int32_t br, int32_t T, int32_t S, int32_t H, float scale, int32_t dtype,
+                   void *qkv_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -349,3 +349,35 @@ def test_choose_backward_br():
 
 def test_backward_with_no_tiles_is_a_no_op():
     assert _backward_status(num_tiles=0, ws=None, ws_bytes=0)[0] == binding.VLF_OK
+
+
+def _rotate_qkv_status(**kw):
+    lib = vlf.load_library()
+    cu = np.array([0, 100, 256], dtype=np.int32)
+    a = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=256, cu=cu.ctypes.data, tiles=0x4000,
+             num_tiles=5, br=64, T=256, S=2, H=2, scale=0.125, dtype=binding.VLF_BF16,
+             dst=0x9000)
+    a.update(kw)
+    rc = lib.vlf_rotate_qkv(a["qkv"], a["cos"], a["sin"], a["P"], a["cu"], a["tiles"],
+                            a["num_tiles"], a["br"], a["T"], a["S"], a["H"], a["scale"],
+                            a["dtype"], a["dst"], None)
+    return rc, lib.vlf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(dtype=7), binding.VLF_EUNSUPPORTED, "dtype"),
+    (dict(br=32), binding.VLF_EINVAL, "br = 32"),
+    (dict(H=0), binding.VLF_EINVAL, "H = 0"),
+    (dict(num_tiles=-1), binding.VLF_EINVAL, "negative"),
+    (dict(dst=None), binding.VLF_EINVAL, "null device pointer"),
+    (dict(tiles=None), binding.VLF_EINVAL, "null device pointer"),
+    (dict(dst=0x1000), binding.VLF_EINVAL, "must not be qkv"),
+    (dict(scale=float("inf")), binding.VLF_EINVAL, "scale"),
+])
+def test_rotate_qkv_rejects_bad_arguments_before_launching(kw, status, text):
+    rc, msg = _rotate_qkv_status(**kw)
+    assert rc == status and text in msg, (rc, msg)
+
+
+def test_rotate_qkv_with_no_tiles_is_a_no_op():
+    assert _rotate_qkv_status(num_tiles=0, dst=None)[0] == binding.VLF_OK

@@ -8,7 +8,8 @@ from .binding import (  # noqa: F401
     Batch, VlfError, attend, attend_backward, attend_backward_into, attend_into,
     attend_rotated_into, backward_workspace_bytes, choose_backward_br, choose_br, choose_prerotate,
     library_path,
-    load_library, new_workspace, prepare, rotate_keys, tile_count, tile_table, typical_length,
+    load_library, new_workspace, prepare, rotate_keys, rotate_qkv_into, tile_count, tile_table,
+    typical_length,
     visible_pairs, workspace_bytes,
 )
 from . import tune  # noqa: F401

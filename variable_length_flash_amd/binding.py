@@ -22,7 +22,8 @@ HEAD_DIM = 64
 # every function include/vlf.h declares
 EXPORTS = ("vlf_version", "vlf_last_error", "vlf_tile_count", "vlf_tile_table",
            "vlf_visible_pairs", "vlf_workspace_bytes", "vlf_attend", "vlf_rotate_keys",
-           "vlf_attend_rotated", "vlf_backward_workspace_bytes", "vlf_attend_backward")
+           "vlf_attend_rotated", "vlf_backward_workspace_bytes", "vlf_attend_backward",
+           "vlf_rotate_qkv")
 
 
 class VlfError(RuntimeError):
@@ -72,6 +73,9 @@ def load_library():
     lib.vlf_attend_backward.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, p, p, p, p, i64, p, p]
     lib.vlf_attend_backward.restype = ctypes.c_int
+    lib.vlf_rotate_qkv.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, ctypes.c_float,
+                                   i32, p, p]
+    lib.vlf_rotate_qkv.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -367,6 +371,23 @@ def attend_rotated_into(batch: Batch, qkv, cos, sin, heads: int, window: int, sc
         batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
         int(window), float(scale), code, ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
         _stream(stream, dev)))
+
+
+def rotate_qkv_into(batch: Batch, qkv, cos, sin, heads: int, scale: float, qkv_out,
+                    stream=None):
+    """Queue the unfused baseline's rotation pass (include/vlf.h, vlf_rotate_qkv): qkv_out gets
+    the rotated, scaled queries, the rotated keys and the values, rounded as the forward rounds
+    its operands."""
+    code = _check_inputs(batch, qkv, cos, sin, heads)
+    if tuple(qkv_out.shape) != tuple(qkv.shape) or qkv_out.dtype != qkv.dtype or \
+            not qkv_out.is_contiguous() or qkv_out.device != qkv.device:
+        raise VlfError(VLF_EINVAL, f"qkv_out: {tuple(qkv_out.shape)} {qkv_out.dtype}, expected "
+                                   f"{tuple(qkv.shape)} {qkv.dtype} contiguous on {qkv.device}")
+    dev = qkv.device
+    _check(load_library().vlf_rotate_qkv(
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
+        float(scale), code, qkv_out.data_ptr(), _stream(stream, dev)))
 
 
 def backward_workspace_bytes(tokens: int, sequences: int, heads: int) -> int:

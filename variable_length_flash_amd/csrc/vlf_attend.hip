@@ -2751,6 +2751,76 @@ int launch_backward_typed(const BackArgs &a) {
         return launch_backward_tiles<E, 8>(a);
     return a.br == 128 ? launch_backward_tiles<E, 4>(a) : launch_backward_tiles<E, 2>(a);
 }
+
+// ---- the unfused baseline's rotation pass ------------------------------------------------------
+// The forward's rotation as a pass of its own, writing qkv' with q' = the query rotated at its
+// position and times `scale`, k' = the key rotated, v' = v, each rounded exactly as the fused
+// kernels round their operands. The forward over qkv' with identity tables (cos 1, sin 0) and
+// scale 1 then multiplies the same rounded operands as the fused forward over qkv. R rows of one
+// table entry and one head per workgroup, four lanes a row.
+template <class E, int R>
+__global__ void __launch_bounds__(256)
+rotate_qkv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
+           const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
+           const uint32_t *__restrict__ tiles, uint16_t *__restrict__ dst, int32_t num_tiles,
+           int32_t T, int32_t S, int32_t H, int32_t P, float scale) {
+    const int work = xcd_work();
+    const int h = work / num_tiles;
+    int seq, start, len, i0;
+    if (!back_tile(tiles, cu, work - h * num_tiles, S, T, P, seq, start, len, i0))
+        return;
+    const int64_t ld = 3LL * H * D;
+    const int hd = H * D;
+    const int tid = (int)threadIdx.x;
+    const int row = tid >> 2, c4 = tid & 3;
+#pragma unroll 1
+    for (int t = i0; t < i0 + R && t < len; t += BC) {
+        const int i = t + row;
+        if (i >= len)
+            continue;
+        const uint16_t *src = qkv + (int64_t)(start + i) * ld + h * D + 8 * c4;
+        uint16_t *o = dst + (int64_t)(start + i) * ld + h * D + 8 * c4;
+        const u32x4 c = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * c4);
+        const u32x4 sn = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * c4);
+        const uint32_t c_[4] = {c[0], c[1], c[2], c[3]}, s_[4] = {sn[0], sn[1], sn[2], sn[3]};
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {  // the query, then the key
+            const u32x4 x1 = *(const u32x4 *)(src + part * hd);
+            const u32x4 x2 = *(const u32x4 *)(src + part * hd + 32);
+            const uint32_t a_[4] = {x1[0], x1[1], x1[2], x1[3]};
+            const uint32_t b_[4] = {x2[0], x2[1], x2[2], x2[3]};
+            uint32_t y1[4], y2[4];
+            rotate<E, 4>(a_, b_, c_, s_, part == 0 ? scale : 1.0f, y1, y2);
+            *(u32x4 *)(o + part * hd) = u32x4{y1[0], y1[1], y1[2], y1[3]};
+            *(u32x4 *)(o + part * hd + 32) = u32x4{y2[0], y2[1], y2[2], y2[3]};
+        }
+        *(u32x4 *)(o + 2 * hd) = *(const u32x4 *)(src + 2 * hd);
+        *(u32x4 *)(o + 2 * hd + 32) = *(const u32x4 *)(src + 2 * hd + 32);
+    }
+}
+
+template <class E>
+int launch_rotate_qkv_typed(const RotateArgs &a) {
+    const int64_t blocks = (int64_t)a.num_tiles * a.H;
+    if (blocks > INT32_MAX)
+        return fail(VLF_EINVAL, "%lld workgroups exceed the grid limit", (long long)blocks);
+    const uint16_t *qkv = (const uint16_t *)a.qkv, *cs = (const uint16_t *)a.cos;
+    const uint16_t *sn = (const uint16_t *)a.sin;
+    uint16_t *dst = (uint16_t *)a.dst;
+    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows;
+    float scale = a.scale;
+    void *args[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
+                    (void *)&dst, (void *)&num_tiles, (void *)&T, (void *)&S, (void *)&H,
+                    (void *)&P, (void *)&scale};
+    const void *k = a.br == 256   ? (const void *)rotate_qkv<E, 256>
+                    : a.br == 128 ? (const void *)rotate_qkv<E, 128>
+                                  : (const void *)rotate_qkv<E, 64>;
+    const hipError_t e =
+        hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)a.stream);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "rotation pass launch failed: %s", hipGetErrorString(e));
+    return VLF_OK;
+}
 }  // namespace
 
 // attend_slide serves 256-row tiles whose window reaches at most eight key tiles: keys from
@@ -2769,6 +2839,11 @@ int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H) {
 
 int launch_backward(const BackArgs &a) {
     return a.dtype == VLF_BF16 ? launch_backward_typed<BF16>(a) : launch_backward_typed<F16>(a);
+}
+
+int launch_rotate_qkv(const RotateArgs &a) {
+    return a.dtype == VLF_BF16 ? launch_rotate_qkv_typed<BF16>(a)
+                               : launch_rotate_qkv_typed<F16>(a);
 }
 
 int launch_attend(const AttendArgs &a, Launch what) {

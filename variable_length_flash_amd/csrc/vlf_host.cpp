@@ -278,6 +278,31 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
     return launch_backward(a);
 }
 
+int vlf_rotate_qkv(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                   const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
+                   int32_t br, int32_t T, int32_t S, int32_t H, float scale, int32_t dtype,
+                   void *qkv_out, void *stream) {
+    if (num_tiles < 0)
+        return fail(VLF_EINVAL, "negative size: num_tiles=%d", num_tiles);
+    if (br != 64 && br != 128 && br != 256)
+        return fail(VLF_EINVAL, "br = %d; tiles of 64, 128 or 256 rows", br);
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(VLF_EINVAL, "scale is not finite");
+    const bool work = T > 0 && num_tiles > 0;
+    int rc = check_launch(qkv, cos, sin, table_rows, cu_dev, T, S, H, dtype, nullptr, 0, work,
+                          false);
+    if (rc || !work)
+        return rc;
+    if (!tiles_dev || !qkv_out)
+        return fail(VLF_EINVAL, "null device pointer (tiles=%p qkv_out=%p)",
+                    (const void *)tiles_dev, qkv_out);
+    if (qkv_out == qkv)
+        return fail(VLF_EINVAL, "qkv_out must not be qkv");
+    RotateArgs a{qkv, cos, sin, table_rows, cu_dev, tiles_dev, num_tiles, br, T,
+                 S,   H,   scale, dtype,    qkv_out, stream};
+    return launch_rotate_qkv(a);
+}
+
 int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
                     const int32_t *cu_dev, int32_t T, int32_t S, int32_t H, int32_t dtype,
                     void *workspace, int64_t workspace_bytes_, void *stream) {

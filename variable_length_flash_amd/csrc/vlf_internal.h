@@ -68,6 +68,26 @@ int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H);
 // Queue the backward kernels (prep, dK/dV, dQ); returns a vlf_status.
 int launch_backward(const BackArgs &a);
 
+// The unfused baseline's rotation pass after validation.
+struct RotateArgs {
+    const void *qkv;
+    const void *cos;
+    const void *sin;
+    int32_t table_rows;
+    const int32_t *cu;
+    const uint32_t *tiles;
+    int32_t num_tiles;
+    int32_t br;  // 64, 128 or 256
+    int32_t T, S, H;
+    float scale;
+    int32_t dtype;
+    void *dst;
+    void *stream;
+};
+
+// Queue the rotation pass; returns a vlf_status.
+int launch_rotate_qkv(const RotateArgs &a);
+
 // Record the calling thread's error message (printf-style) and return `status`.
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 
