@@ -115,10 +115,10 @@ def cpu_baseline(w, qkv, cos, sin, target_s: float, pairs_per_head_total: int):
             s = int(np.searchsorted(cu, t, side="right") - 1)
             L = int(cu[s + 1] - cu[s])
             i = int(t - cu[s])
-            if w.window == 0:
-                total += L
-            else:
-                total += min(L, i + w.window) - max(0, i - w.window + 1)
+            wv, causal = w.window & ~oracle.CAUSAL, w.window & oracle.CAUSAL
+            lo = max(0, i - wv + 1) if wv else 0
+            hi = i + 1 if causal else (min(L, i + wv) if wv else L)
+            total += hi - lo
         return total * w.heads
 
     # calibrate on a few rows, then size the sample to the target time
@@ -160,6 +160,9 @@ def run(args):
         sys.exit(2)
     dev = torch.device("cuda:0")
     w, qkv, cos, sin = make_inputs(args.workload)
+    if args.causal:  # the same batch under the causal window (keys i - W < j <= i)
+        w.window |= vlf.CAUSAL
+        w.note += ", causal"
     prerotate = None if args.path == "auto" else args.path == "prerotate"
     batch = vlf.prepare(w.cu, dev, args.br, prerotate, w.window)
     path = "prerotate" if batch.prerotate else "direct"
@@ -220,7 +223,8 @@ def run(args):
 
     value = flops / (wall_ms / 1e3) / 1e12
     achieved = flops / (kernel_ms / 1e3) / 1e12
-    traffic = read_traffic(kernel, args.workload)
+    # the committed counters are for the workloads' own windows
+    traffic = None if args.causal else read_traffic(kernel, args.workload)
     # the key-tile kernel reads every key and value row once and writes each used block once
     key_tiles = sum(-(-int(L) // 64) for L in w.lens)
     rotate_bytes = (2 * w.tokens * w.heads * 64 * 2 + 2 * sum(w.lens) * 32 * 2
@@ -450,6 +454,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (vlf_attend_backward) instead of the forward")
+    ap.add_argument("--causal", action="store_true",
+                    help="run the workload under the causal window (window | CAUSAL)")
     ap.add_argument("--unfused", action="store_true",
                     help="time the fused forward against the rotation pass plus the forward")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)

@@ -13,7 +13,10 @@
  *   - cu [S+1] int32: cu[0] = 0, non-decreasing, cu[S] = T. Sequence s owns tokens
  *     cu[s] .. cu[s+1]-1. Zero-length sequences are allowed.
  *   - window: 0 = every key of the query's own sequence; W >= 1 = keys j with |i - j| < W
- *     (i, j positions within the sequence).
+ *     (i, j positions within the sequence). ORed with VLF_CAUSAL it is the causal sliding
+ *     window instead: keys j with i - W < j <= i (W >= 1), or j <= i (W = 0). The causal mode
+ *     is not on the page's `attend`, which takes the symmetric one; the convention is that of
+ *     the array library page's sliding-window mask.
  *   - Status codes are returned; nothing aborts or throws across this boundary. After a
  *     non-zero status, vlf_last_error() returns a message (per calling thread).
  *   - Pointers marked "host" are read by the CPU during the call only. Pointers marked
@@ -48,6 +51,9 @@ enum vlf_dtype {
     VLF_BF16 = 1, /* bfloat16 */
 };
 
+/* Flag ORed into `window` for the causal sliding window (see the conventions above). */
+#define VLF_CAUSAL 0x40000000
+
 /* Library ABI version (this header: 3). */
 int32_t vlf_version(void);
 
@@ -80,9 +86,9 @@ int vlf_tile_table(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, uin
 
 /*
  * The number of (query, key) pairs one head computes: for each row i of each sequence, the
- * keys j of the same sequence with window == 0 or |i - j| < window (the masking of
- * hanzo-kernel 0.2.42 src/packed.rs `attend`). Effective FLOPs of one call are
- * 4 * 64 * pairs * H.
+ * keys j of the same sequence the window admits (the masking of hanzo-kernel 0.2.42
+ * src/packed.rs `attend`, or the causal window with VLF_CAUSAL). Effective FLOPs of one call
+ * are 4 * 64 * pairs * H.
  *   cu_host  host, [S+1]. pairs  out.
  * Errors: VLF_EINVAL (bad cu, window < 0).
  */
@@ -124,14 +130,15 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
  *   tiles_dev  device, [num_tiles, 2] uint32 (sequence, first row) pairs built for the same cu
  *              and `br` (vlf_tile_table, or any permutation of it: the order is the launch
  *              order). Tiles naming a sequence >= S or a row beyond the sequence are skipped.
- *              Without a workspace, at br = 256 and 1 <= window <= 129, each CU walks a run
+ *              Without a workspace, at br = 256 and a window that reaches at most eight key
+ *              tiles (1 <= W <= 129, or causal 1 <= W <= 257), each CU walks a run
  *              of consecutive entries and keeps the keys that one entry shares with the
  *              next of the same sequence in LDS: any order gives the same results, and the
  *              canonical one is the fastest.
  *   br         64, 128 or 256: rows per tile, as the table was built.
  *   T, S, H    tokens, sequences, heads (1 <= H <= 65536; T = 0 or num_tiles = 0 launches
  *              nothing).
- *   window     0 or W >= 1 as above.
+ *   window     0 or W >= 1, optionally | VLF_CAUSAL, as above.
  *   scale      multiplies the rotated query before rounding (1/8 for head dimension 64).
  *   dtype      VLF_BF16 or VLF_F16: storage type of qkv, cos, sin and out.
  *   workspace  device or NULL. With workspace_bytes >= vlf_workspace_bytes(T, S, H), the call

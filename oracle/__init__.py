@@ -188,9 +188,7 @@ def attend_backward(qkv, cos, sin, cu, heads: int, window: int, scale: float, do
         if L == 0:
             continue
         c, s = cos64[:L], sin64[:L]
-        pos = np.arange(L)
-        gap = np.abs(pos[:, None] - pos[None, :])
-        visible = np.ones((L, L), dtype=bool) if window <= 0 else gap < window
+        visible = visible_mask(L, window)
         for h in range(heads):
             cols = slice(h * 64, (h + 1) * 64)
             q, k = qt[a:b, cols], kt[a:b, cols]
@@ -221,9 +219,26 @@ def tile_table(cu, br: int) -> np.ndarray:
     return np.array(tiles, dtype=np.uint32).reshape(-1, 2)
 
 
+CAUSAL = 0x40000000  # ORed into a window value: the causal sliding window
+
+
+def visible_mask(L: int, window: int) -> np.ndarray:
+    """[L, L] bool: key j visible to row i of one sequence. window: 0 = every key, W >= 1 =
+    |i - j| < W (hanzo-kernel 0.2.42 src/packed.rs, `attend`'s window); with CAUSAL set, j <= i
+    and, for W >= 1, i - j < W (the array library page's sliding-window mask)."""
+    w = int(window) & ~CAUSAL
+    pos = np.arange(L)
+    diff = pos[:, None] - pos[None, :]  # i - j
+    visible = np.ones((L, L), dtype=bool) if w <= 0 else np.abs(diff) < w
+    if int(window) & CAUSAL:
+        visible &= diff >= 0
+    return visible
+
+
 def visible_pairs(cu, window: int) -> int:
-    """(query, key) pairs one head computes: per row i of each sequence, keys j of the same
-    sequence with window == 0 or |i - j| < window, counted row by row."""
+    """(query, key) pairs one head computes: per row i of each sequence, the keys j of the same
+    sequence the window admits, counted row by row."""
+    w, causal = int(window) & ~CAUSAL, bool(int(window) & CAUSAL)
     total = 0
     cu = [int(x) for x in cu]
     for s in range(len(cu) - 1):
@@ -231,10 +246,10 @@ def visible_pairs(cu, window: int) -> int:
         if L == 0:
             continue
         i = np.arange(L, dtype=np.int64)
-        if window == 0:
-            total += L * L
+        lo = np.maximum(0, i - w + 1) if w > 0 else np.zeros(L, dtype=np.int64)
+        if causal:
+            hi = i + 1
         else:
-            lo = np.maximum(0, i - window + 1)
-            hi = np.minimum(L, i + window)  # exclusive
-            total += int((hi - lo).sum())
+            hi = np.minimum(L, i + w) if w > 0 else np.full(L, L, dtype=np.int64)  # exclusive
+        total += int((hi - lo).sum())
     return int(total)

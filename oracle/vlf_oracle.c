@@ -23,7 +23,8 @@
  *
  * W is the window value the kernel receives: 0 means every key of the sequence, W >= 1 means
  * |i - j| < W (the page passes its window option w as w + 1; its composite's |i-j| <= w is the
- * same set).
+ * same set). With the flag CAUSAL_FLAG set in the window value, key j is visible to row i when
+ * j <= i and, for W >= 1, i - j < W: the causal sliding window of the array library page.
  *
  * Two modes:
  *   mode A (0): the definition above, exactly, in float64.
@@ -50,6 +51,7 @@
 
 enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
 enum { ORACLE_MODE_A = 0, ORACLE_MODE_B = 1 };
+#define CAUSAL_FLAG 0x40000000 /* set in the window value: the causal sliding window */
 
 /*
  * Round a finite double to the nearest value with `p` significand bits and minimum normal
@@ -200,6 +202,8 @@ int vlf_oracle_attend(const float *qkv, const float *cos_t, const float *sin_t, 
         return -1;
     if (cu[0] != 0 || cu[S] != T)
         return -1;
+    const int causal = (window & CAUSAL_FLAG) != 0;
+    const int32_t w = window & ~CAUSAL_FLAG;
     int64_t max_len = 0;
     for (int32_t s = 0; s < S; ++s) {
         if (cu[s + 1] < cu[s])
@@ -267,7 +271,7 @@ int vlf_oracle_attend(const float *qkv, const float *cos_t, const float *sin_t, 
             double m = -INFINITY;
             for (int64_t j = 0; j < L; ++j) {
                 int64_t gap = i > j ? i - j : j - i;
-                if (window > 0 && gap >= window) {
+                if ((w > 0 && gap >= w) || (causal && j > i)) {
                     sc[j] = -INFINITY;
                     continue;
                 }

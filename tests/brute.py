@@ -49,9 +49,7 @@ def attend(qkv, cos, sin, lens, heads, window, scale, mode="A", dtype="bf16"):
     for L in lens:
         if L == 0:
             continue
-        pos = np.arange(L)
-        gap = np.abs(pos[:, None] - pos[None, :])
-        mask = np.ones((L, L), dtype=bool) if window == 0 else gap < window
+        mask = _mask(L, window)
         for h in range(heads):
             rows = qkv[start:start + L]
             q = rotate_block(rows[:, h * 64:(h + 1) * 64], cos[:L], sin[:L], mode, dtype,
@@ -80,7 +78,7 @@ def scores(qkv, cos, sin, lens, heads, window, scale, mode="A", dtype="bf16"):
     start = 0
     for L in lens:
         pos = np.arange(L)
-        mask = np.ones((L, L), bool) if window == 0 else np.abs(pos[:, None] - pos[None, :]) < window
+        mask = _mask(L, window)
         per_head = []
         for h in range(heads):
             rows = qkv[start:start + L]
@@ -106,12 +104,27 @@ def tile_table(lens, br):
     return np.array(out, dtype=np.uint32).reshape(-1, 2)
 
 
+CAUSAL = 1 << 30  # the causal flag of a window value
+
+
+def _visible(i, j, window):
+    """Key j visible to row i: |i - j| < W (W = 0: always), and j <= i under the causal flag."""
+    w = window & ~CAUSAL
+    ok = w == 0 or abs(i - j) < w
+    return ok and (j <= i if window & CAUSAL else True)
+
+
+def _mask(L, window):
+    return np.array([[_visible(i, j, window) for j in range(L)] for i in range(L)],
+                    dtype=bool).reshape(L, L)
+
+
 def pair_count(lens, window):
     """Visible (query, key) pairs per head by a double loop."""
     n = 0
     for L in lens:
         for i in range(L):
             for j in range(L):
-                if window == 0 or abs(i - j) < window:
+                if _visible(i, j, window):
                     n += 1
     return n

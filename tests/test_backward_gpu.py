@@ -171,3 +171,15 @@ def test_backward_offsets_past_2gib():
         rel = float(np.abs(got - want).max() / np.abs(want).max())
         _say(f"[backward] 2.2 GB qkv, sequence {si}: rel {rel:.2e}")
         assert rel <= REL_TOL["bf16"], (si, rel)
+
+
+@pytest.mark.parametrize("br", [64, 128, 256])
+@pytest.mark.parametrize("window", [0, 1, 33, 200])
+def test_backward_causal_window(window, br):
+    """The causal mask (keys i - W < j <= i): the key pass sees only queries at or after its
+    keys, the query pass only keys at or before its rows."""
+    w = workloads.custom(RAGGED + [700], 2, dtype="bf16", window=window | vlf.CAUSAL,
+                         base=1.6e5, table_rows=700, seed=13)
+    _say(f"case backward causal W={window} br={br}")
+    qkv, cos, sin, dout, got = run_backward(w, seed=5, br=br)
+    compare(f"causal W={window} br={br}", w, qkv, cos, sin, dout, got)

@@ -14,6 +14,7 @@ import torch
 
 import brute
 import oracle
+import variable_length_flash_amd as vlf
 from variable_length_flash_amd import workloads
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +71,38 @@ def test_matches_brute_force(window, mode, dtype):
     np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("window", [0, 1, 2, 9, 65])
+@pytest.mark.parametrize("mode", ["A", "B"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_causal_matches_brute_force(window, mode, dtype):
+    """The causal window (j <= i, and i - j < W for W >= 1) against the explicit-mask brute
+    force."""
+    w, qkv, cos, sin = _inputs(LENS, HEADS, dtype=dtype)
+    win = window | oracle.CAUSAL
+    out, lse = oracle.attend(qkv, cos, sin, w.cu, HEADS, win, SCALE, mode=mode, dtype=dtype)
+    bout, blse = brute.attend(qkv, cos, sin, LENS, HEADS, win, SCALE, mode=mode, dtype=dtype)
+    np.testing.assert_allclose(out, bout, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+
+
+def test_causal_first_rows_see_only_themselves():
+    """Row 0 of every sequence has one visible key under the causal mask: out = v_0 exactly and
+    lse = its own score (mode A: scale * <rot q, rot k>)."""
+    w, qkv, cos, sin = _inputs(LENS, HEADS)
+    out, lse = oracle.attend(qkv, cos, sin, w.cu, HEADS, oracle.CAUSAL, SCALE, mode="A")
+    hd = HEADS * 64
+    for s, L in enumerate(LENS):
+        if L == 0:
+            continue
+        a = int(w.cu[s])
+        np.testing.assert_array_equal(out[a], qkv[a, 2 * hd:].astype(np.float64))
+        qt, kt = oracle.operands(qkv[a:a + 1], cos, sin, np.array([0, 1]), HEADS, SCALE,
+                                 mode="A")
+        for h in range(HEADS):
+            own = float(qt[0, h * 64:(h + 1) * 64] @ kt[0, h * 64:(h + 1) * 64])
+            assert abs(lse[h, a] - own) <= 1e-12 * max(1.0, abs(own))
+
+
 def test_row_subset_equals_full():
     w, qkv, cos, sin = _inputs(LENS, HEADS)
     out, lse = oracle.attend(qkv, cos, sin, w.cu, HEADS, 9, SCALE)
@@ -110,6 +143,35 @@ def test_identity_rotation_is_plain_attention(window):
         sc = sc.masked_fill(~mask, float("-inf"))
         ref_lse = torch.logsumexp(sc, dim=-1)
         torch.testing.assert_close(torch.from_numpy(lse[:, a:a + L]), ref_lse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [0, 3])
+def test_identity_rotation_causal_is_plain_attention(window):
+    """cos = 1, sin = 0 under the causal mask: PyTorch's scaled_dot_product_attention with
+    is_causal=True (W = 0), or with the boolean mask 0 <= i - j < W."""
+    lens = [7, 30, 1, 12]
+    heads = 2
+    w, qkv, _, _ = _inputs(lens, heads)
+    cos = np.ones((64, 32), np.float32)
+    sin = np.zeros((64, 32), np.float32)
+    out, _ = oracle.attend(qkv, cos, sin, w.cu, heads, window | oracle.CAUSAL, SCALE, mode="A")
+    x = torch.from_numpy(qkv).double()
+    hd = heads * 64
+    for s, L in enumerate(lens):
+        a = int(w.cu[s])
+        q = x[a:a + L, :hd].reshape(L, heads, 64).transpose(0, 1)
+        k = x[a:a + L, hd:2 * hd].reshape(L, heads, 64).transpose(0, 1)
+        v = x[a:a + L, 2 * hd:].reshape(L, heads, 64).transpose(0, 1)
+        if window == 0:
+            ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True,
+                                                                   scale=SCALE)
+        else:
+            pos = torch.arange(L)
+            d = pos[:, None] - pos[None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q, k, v, attn_mask=(d >= 0) & (d < window), scale=SCALE)
+        got = torch.from_numpy(out[a:a + L]).reshape(L, heads, 64).transpose(0, 1)
+        torch.testing.assert_close(got, ref, rtol=0, atol=1e-12)
 
 
 # ---------------------------------------------------------------- closed forms
@@ -290,6 +352,22 @@ def test_pair_count_golden():
             cu = np.concatenate([[0], np.cumsum(lens)])
             assert oracle.visible_pairs(cu, int(window)) == int(want)
             assert brute.pair_count(lens, int(window)) == int(want)
+
+
+@pytest.mark.parametrize("lens,window", [([5, 40, 1, 33, 70], 0), ([5, 40, 1, 33, 70], 9),
+                                         ([300, 0, 64, 65], 64), ([1, 2, 3], 1)])
+def test_causal_pair_count_brute(lens, window):
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    win = window | oracle.CAUSAL
+    assert oracle.visible_pairs(cu, win) == brute.pair_count(lens, win)
+    assert vlf.visible_pairs(cu, win) == brute.pair_count(lens, win)
+
+
+@pytest.mark.parametrize("L,W", [(8192, 0), (8192, 128), (100, 128), (128, 128), (5000, 1)])
+def test_causal_pair_count_closed_form(L, W):
+    """Row i sees min(i + 1, W) keys (W = 0: i + 1)."""
+    want = L * (L + 1) // 2 if W == 0 or L <= W else W * (W + 1) // 2 + (L - W) * W
+    assert oracle.visible_pairs([0, L], W | oracle.CAUSAL) == want
 
 
 @pytest.mark.parametrize("L,W", [(8192, 128), (600, 128), (128, 128), (5000, 1), (1000, 999)])

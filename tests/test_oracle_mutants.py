@@ -26,7 +26,10 @@ MUTANTS = {
     "cos/sin swapped": ("y[m + HALF] = x1 * sm + x2 * cm;", "y[m + HALF] = x1 * cm + x2 * sm;"),
     "mode B sign": ("float a = fmaf(x[m], c[m], -(x[m + HALF] * s[m]));",
                     "float a = fmaf(x[m], c[m], (x[m + HALF] * s[m]));"),
-    "window bound": ("if (window > 0 && gap >= window) {", "if (window > 0 && gap > window) {"),
+    "window bound": ("if ((w > 0 && gap >= w) || (causal && j > i)) {",
+                     "if ((w > 0 && gap > w) || (causal && j > i)) {"),
+    "causal bound": ("if ((w > 0 && gap >= w) || (causal && j > i)) {",
+                     "if ((w > 0 && gap >= w) || (causal && j >= i)) {"),
     "key position global": ("cos_t + j * HALF, sin_t + j * HALF,", "cos_t + t * HALF, sin_t + t * HALF,"),
     "query position global": ("cos_t + i * HALF, sin_t + i * HALF, mode,",
                               "cos_t + t * HALF, sin_t + t * HALF, mode,"),
@@ -84,7 +87,7 @@ def _pins_pass(lib) -> bool:
     for dtype in ("bf16", "fp16"):
         w, qkv, cos, sin = _inputs(dtype)
         for mode in ("A", "B"):
-            for window in (0, 9):
+            for window in (0, 9, brute.CAUSAL | 9):
                 out, lse = oracle.attend(qkv, cos, sin, w.cu, HEADS, window, SCALE, mode=mode,
                                          dtype=dtype, library=lib)
                 bout, blse = brute.attend(qkv, cos, sin, LENS, HEADS, window, SCALE, mode=mode,

@@ -510,3 +510,38 @@ def test_tile_order_and_foreign_entries(br, prerotate):
     assert torch.isnan(out_buf[T * H * 64:]).all() and torch.isnan(lse_buf[H * T:]).all()
     compare(f"shuffled table with foreign entries br={br} pre={int(prerotate)}", w,
             out.float().cpu().numpy(), lse.cpu().numpy(), qkv, cos, sin)
+
+
+# ---- the causal sliding window (window | CAUSAL): keys i - W < j <= i, or j <= i for W = 0
+
+CAUSAL_LENS = [5, 40, 1, 33, 70, 0, 300, 257, 64, 65, 1000]
+
+
+@pytest.mark.parametrize("prerotate", PATHS)
+@pytest.mark.parametrize("br", [64, 128, 256])
+@pytest.mark.parametrize("window", [0, 1, 9, 65, 200])
+def test_causal_window(window, br, prerotate):
+    """Every kernel of both paths under the causal mask, bf16, on ragged sequences up to 1000
+    tokens (several key tiles behind each query tile, none ahead); every output row."""
+    w = workloads.custom(CAUSAL_LENS, 2, dtype="bf16", window=window | vlf.CAUSAL, base=1.6e5,
+                         table_rows=1000, seed=37)
+    qkv, cos, sin = inputs(w)
+    _say(f"case causal W={window} br={br} prerotate={prerotate}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=prerotate)
+    compare(f"causal W={window} br={br} pre={int(prerotate)}", w, out, lse, qkv, cos, sin)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("window", [1, 64, 129, 200, 257])
+def test_causal_window_runs_keep_keys(dtype, window):
+    """The key ring (attend_slide) under causal windows: nothing ahead of a query tile, so
+    windows up to 257 keys fit its eight tiles. Runs of items across sequences and heads."""
+    assert vlf.binding.window_fits_ring(window | vlf.CAUSAL)
+    w = workloads.custom(RUN_LENS, 16, dtype=dtype, window=window | vlf.CAUSAL, base=1.6e5,
+                         table_rows=9000, seed=43)
+    qkv, cos, sin = inputs(w)
+    _say(f"case causal window runs {dtype} W={window}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=256, prerotate=False)
+    rows = sample_rows(w, 256, 1500, seed=5)
+    compare(f"causal ring {dtype} W={window} ({len(rows)} rows)", w, out, lse, qkv, cos, sin,
+            rows=rows)

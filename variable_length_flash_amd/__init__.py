@@ -5,7 +5,7 @@ The binding (``variable_length_flash_amd.binding``) loads the library on first u
 loudly when it is missing: there is no fallback path.
 """
 from .binding import (  # noqa: F401
-    Batch, VlfError, attend, attend_backward, attend_backward_into, attend_into,
+    CAUSAL, Batch, VlfError, attend, attend_backward, attend_backward_into, attend_into,
     attend_rotated_into, backward_workspace_bytes, choose_backward_br, choose_br, choose_prerotate,
     library_path,
     load_library, new_workspace, prepare, rotate_keys, rotate_qkv_into, tile_count, tile_table,

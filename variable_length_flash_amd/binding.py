@@ -167,7 +167,8 @@ def choose_prerotate(length: float, br: int, window: int = 0) -> bool:
     of 256-4096-token sequences, the encoder and the sliding-window workloads)."""
     if br == 256 and window_fits_ring(window):
         return False  # the direct path keeps such a window's keys in LDS (attend_slide)
-    span = length if window <= 0 else min(length, br + 2 * window - 1)
+    back, ahead = window_reaches(window)
+    span = length if back is None or ahead is None else min(length, br + back + ahead + 1)
     return span >= (3 * br if br < 256 else 7 * br // 4)
 
 
@@ -184,19 +185,32 @@ def choose_br(max_len: int, window: int = 0, typical: float | None = None) -> in
         return 64
     if window_fits_ring(window) and typical >= 256:
         return 256
-    if 0 < window <= 512:
+    if 0 < (int(window) & ~CAUSAL) <= 512:
         return 128
     return 256 if typical >= 448 else 128
 
 
+CAUSAL = 0x40000000  # ORed into a window: the causal sliding window (include/vlf.h, VLF_CAUSAL)
+
+
+def window_reaches(window: int):
+    """(back, ahead) of a window value: row x sees keys x - back .. x + ahead of its sequence;
+    None reaches every key on that side."""
+    w = int(window) & ~CAUSAL
+    back = w - 1 if w > 0 else None
+    return back, (0 if int(window) & CAUSAL else back)
+
+
 def window_fits_ring(window: int) -> bool:
     """Whether the direct path runs 256-row tiles under ``window`` on its LDS-resident key
-    ring (attend_slide): a tile's keys, from i0 - 64 ceil((W - 1) / 64) to i0 + 256 + W - 2,
-    must span at most eight 64-key tiles, which holds for 1 <= W <= 129."""
-    if window < 1:
+    ring (attend_slide): a tile's keys, from i0 - 64 ceil(back / 64) to i0 + 255 + ahead,
+    must span at most eight 64-key tiles, which holds for 1 <= W <= 129, or causal
+    1 <= W <= 257."""
+    back, ahead = window_reaches(window)
+    if back is None or ahead is None:
         return False
-    back = -(-(window - 1) // 64) * 64
-    return -(-(back + 256 + window - 1) // 64) <= 8
+    behind = -(-back // 64) * 64
+    return -(-(behind + 256 + ahead) // 64) <= 8
 
 
 @dataclass

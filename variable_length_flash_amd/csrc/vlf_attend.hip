@@ -432,13 +432,37 @@ __device__ __forceinline__ void mask_band(f32x16 &s0, f32x16 &s1, int lo, int hi
     }
 }
 
+// The window as two reaches: row x sees keys x - back <= j <= x + ahead of its sequence. The
+// symmetric window W >= 1 is back = ahead = W - 1, the causal window W >= 1 is back = W - 1 and
+// ahead = 0, and REACH_ALL (on both sides, or behind for the causal full window) reaches every
+// key. The host turns the caller's window into the two.
+constexpr int32_t REACH_ALL = 0x7fffffff;
+
+// The visible keys [lo, hi) of row x of a sequence of `len` rows.
+__device__ __forceinline__ void row_keys(int x, int len, int back, int ahead, int &lo, int &hi) {
+    lo = x > back ? x - back : 0;
+    hi = (int)min((int64_t)x + ahead + 1, (int64_t)len);
+}
+
+// The whole 64-key tiles [lo, hi) that rows [r0, r0 + rows) reach (hi clipped to the sequence).
+__device__ __forceinline__ void key_span(int r0, int rows, int len, int back, int ahead, int &lo,
+                                         int &hi) {
+    lo = r0 > back ? (r0 - back) / BC * BC : 0;
+    hi = (int64_t)r0 + rows + ahead < len ? r0 + rows + ahead : len;
+}
+
+// Whether some pair of rows [w0, w0 + 32) and keys [j0, j0 + 64) lies outside the window or the
+// sequence: the tile then needs masks.
+__device__ __forceinline__ bool tile_edge(int w0, int j0, int len, int back, int ahead) {
+    return j0 + BC > len || w0 + 31 - j0 > back || j0 + BC - 1 - w0 > ahead;
+}
+
 // Masks the scores of the 64-key tile at j0 for query qi (keys past the sequence and outside
-// the window weigh nothing): the visible keys of row qi are max(qi - W + 1, 0) <= j <
-// min(len, qi + W), or 0 <= j < len for the full window.
-__device__ __forceinline__ void mask_scores(f32x16 &s0, f32x16 &s1, int j0, int len, int window,
-                                            int qi, int g) {
-    const int lo = window > 0 ? max(qi - window + 1, 0) : 0;
-    const int hi = (window > 0 && window < len - qi) ? qi + window : len;
+// the window weigh nothing).
+__device__ __forceinline__ void mask_scores(f32x16 &s0, f32x16 &s1, int j0, int len, int back,
+                                            int ahead, int qi, int g) {
+    int lo, hi;
+    row_keys(qi, len, back, ahead, lo, hi);
     mask_band(s0, s1, lo, hi, j0, g);
 }
 
@@ -549,7 +573,7 @@ __device__ __forceinline__ float exact_row_max(const uint8_t *wblock,
                                                          const u32x4 (&qop)[4],
                                                          const int (&cof)[4], int ntiles,
                                                          KeyF key, EdgeF edge, int len,
-                                                         int window, int qi, int g) {
+                                                         int back, int ahead, int qi, int g) {
     float mx = -__builtin_inff();
     for (int u = 0; u < ntiles; ++u) {
         const int ju = key(u);
@@ -561,7 +585,7 @@ __device__ __forceinline__ float exact_row_max(const uint8_t *wblock,
             a1 = E::mfma(*(const u32x4 *)(kg + 4096 + cof[c]), qop[c], a1);
         }
         if (edge(ju))
-            mask_scores(a0, a1, ju, len, window, qi, g);
+            mask_scores(a0, a1, ju, len, back, ahead, qi, g);
         mx = __builtin_fmaxf(mx, row_max(a0, a1));
     }
     return mx;
@@ -672,7 +696,7 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            const uint32_t *__restrict__ tiles, uint16_t *__restrict__ out,
            float *__restrict__ lse, int32_t num_tiles, int32_t T, int32_t S, int32_t H, int32_t P,
-           int32_t window, float scale) {
+           int32_t back, int32_t ahead, float scale) {
     constexpr int BR = 32 * NW;
     constexpr int NTHR = 64 * NW;
     constexpr int RING = 3;  // key/value tiles in LDS: t (values), t+1 (keys), t+2 (being staged)
@@ -706,19 +730,16 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int qi = w0 + n;        // this lane's query position
 
     // ---- the key span this tile's window reaches (whole key tiles of BC)
-    int lo = 0, hi = len;
-    if (window > 0) {
-        if (i0 + 1 > window)
-            lo = (i0 + 1 - window) / BC * BC;
-        if ((int64_t)i0 + BR + window - 1 < len)
-            hi = i0 + BR + window - 1;
-    }
+    int lo, hi;
+    key_span(i0, BR, len, back, ahead, lo, hi);
     const int ntiles = (hi - lo + BC - 1) / BC;
     // Over the full window every query tile of a sequence reads every key tile: start each at
     // a different key tile (and wrap around) so the workgroups of one (sequence, head), which
     // run side by side on one XCD, do not all miss L2 on the same tile at the same time. The
     // online softmax does not depend on the order of the keys.
-    const int offset = window > 0 ? 0 : (int)((int64_t)(i0 / BR) * ntiles / ((len + BR - 1) / BR));
+    const int offset = (back < REACH_ALL || ahead < REACH_ALL)
+                           ? 0
+                           : (int)((int64_t)(i0 / BR) * ntiles / ((len + BR - 1) / BR));
     // first key of the t-th tile in this workgroup's order (t <= ntiles)
     auto key = [&](int t) {
         int u = t + offset;
@@ -754,8 +775,7 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     // A tile needs masks when it reaches past the sequence or some pair of this wave's rows
     // and its keys lies outside the window.
     auto edge = [&](int j0) {
-        return (j0 + BC > len) ||
-               (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window));
+        return tile_edge(w0, j0, len, back, ahead);
     };
 
     float m_ref = -__builtin_inff();  // reference maximum, natural-log units
@@ -765,7 +785,7 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 
     scores<E>(ks[0], qop, n, g, sa0, sa1);
     if (edge(key(0)))
-        mask_scores(sa0, sa1, key(0), len, window, qi, g);
+        mask_scores(sa0, sa1, key(0), len, back, ahead, qi, g);
     float mx = row_max(sa0, sa1);
 
     // One key tile t: c0/c1 hold its masked scores and mx their row maximum; n0/n1 receive the
@@ -842,7 +862,7 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 
         // ---- masks (edge tiles only) and row maximum of tile t+1
         if (edge(j1))
-            mask_scores(n0, n1, j1, len, window, qi, g);
+            mask_scores(n0, n1, j1, len, back, ahead, qi, g);
         mx = row_max(n0, n1);
         __syncthreads();
     };
@@ -895,7 +915,8 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            const uint32_t *__restrict__ tiles, const uint8_t *__restrict__ ws,
            uint16_t *__restrict__ out, float *__restrict__ lse, int32_t num_tiles, int32_t T,
-           int32_t S, int32_t H, int32_t P, int32_t NB, int32_t window, float scale) {
+           int32_t S, int32_t H, int32_t P, int32_t NB, int32_t back, int32_t ahead,
+           float scale) {
     constexpr int BR = 32 * NW;
     constexpr int RING = 4;
     constexpr int PIECES = 16 / NW;  // 16-byte copies per thread per tile
@@ -926,15 +947,12 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int w0 = i0 + 32 * wv;
     const int qi = w0 + n;
 
-    int lo = 0, hi = len;
-    if (window > 0) {
-        if (i0 + 1 > window)
-            lo = (i0 + 1 - window) / BC * BC;
-        if ((int64_t)i0 + BR + window - 1 < len)
-            hi = i0 + BR + window - 1;
-    }
+    int lo, hi;
+    key_span(i0, BR, len, back, ahead, lo, hi);
     const int ntiles = (hi - lo + BC - 1) / BC;
-    const int offset = window > 0 ? 0 : (int)((int64_t)(i0 / BR) * ntiles / ((len + BR - 1) / BR));
+    const int offset = (back < REACH_ALL || ahead < REACH_ALL)
+                           ? 0
+                           : (int)((int64_t)(i0 / BR) * ntiles / ((len + BR - 1) / BR));
     auto key = [&](int t) {
         int u = t + offset;
         if (u >= ntiles)
@@ -999,8 +1017,7 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         cof[kc] = n * 128 + 16 * ((2 * kc + g) ^ swz(n));
 
     auto edge = [&](int j0) {
-        return (j0 + BC > len) ||
-               (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window));
+        return tile_edge(w0, j0, len, back, ahead);
     };
     auto kscores = [&](int sl, f32x16 &s0, f32x16 &s1) {
         const uint8_t *kt = ring + sl * BLK;
@@ -1024,12 +1041,12 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     f32x16 sa0, sa1, sb0, sb1;
     kscores(0, sa0, sa1);
     if (edge(key(0)))
-        mask_scores(sa0, sa1, key(0), len, window, qi, g);
+        mask_scores(sa0, sa1, key(0), len, back, ahead, qi, g);
     const float m_ref =
         fixed_reference<E>(row_max(sa0, sa1), own_score<E>(wblock, qop, qi, len, g), bq,
                            qi < len, [&] {
                                return exact_row_max<E>(wblock, qop, cof, ntiles, key, edge, len,
-                                                       window, qi, g);
+                                                       back, ahead, qi, g);
                            });
     const float mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
 
@@ -1077,7 +1094,7 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         asm volatile("" : "+v"(l_run));
         // past the last tile the scores of "tile t+1" come from a stale slot: never used
         if (t + 1 < ntiles && edge(j1))
-            mask_scores(n0, n1, j1, len, window, qi, g);
+            mask_scores(n0, n1, j1, len, back, ahead, qi, g);
         if (more)
             ring_barrier<PIECES>();
         else
@@ -1141,7 +1158,8 @@ attend_pre_ph(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
               const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
               const uint32_t *__restrict__ tiles, const uint8_t *__restrict__ ws,
               uint16_t *__restrict__ out, float *__restrict__ lse, int32_t num_tiles, int32_t T,
-              int32_t S, int32_t H, int32_t P, int32_t NB, int32_t window, float scale) {
+              int32_t S, int32_t H, int32_t P, int32_t NB, int32_t back, int32_t ahead,
+              float scale) {
     constexpr int NW = 8;
     constexpr int BR = 32 * NW;
     constexpr int RING = 4;
@@ -1170,13 +1188,8 @@ attend_pre_ph(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
     const int n = lane & 31, g = lane >> 5;
     const int w0 = i0 + 32 * wv;
     const int qi = w0 + n;
-    int lo = 0, hi = len;
-    if (window > 0) {
-        if (i0 + 1 > window)
-            lo = (i0 + 1 - window) / BC * BC;
-        if ((int64_t)i0 + BR + window - 1 < len)
-            hi = i0 + BR + window - 1;
-    }
+    int lo, hi;
+    key_span(i0, BR, len, back, ahead, lo, hi);
     const int ntiles = (hi - lo + BC - 1) / BC;
     // every query tile sweeps its keys in order: the tiles of one (sequence, head) then read
     // the same blocks at about the same time, which keeps two such pairs per XCD within its L2
@@ -1239,8 +1252,7 @@ attend_pre_ph(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
     for (int kc = 0; kc < 4; ++kc)
         cof[kc] = n * 128 + 16 * ((2 * kc + g) ^ swz(n));
     auto edge = [&](int j0) {
-        return (j0 + BC > len) ||
-               (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window));
+        return tile_edge(w0, j0, len, back, ahead);
     };
     // the two groups: waves 0-3 and 4-7 (one of each on every SIMD)
     const bool late = __builtin_amdgcn_readfirstlane(wv) >= 4;
@@ -1269,9 +1281,9 @@ attend_pre_ph(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
     auto first = [&]() __attribute__((always_inline)) {
         scores(0);
         if (edge(key(0)))
-            mask_scores(s0, s1, key(0), len, window, qi, g);
+            mask_scores(s0, s1, key(0), len, back, ahead, qi, g);
         m_ref = fixed_reference<E>(row_max(s0, s1), s_own, bq, qi < len, [&] {
-            return exact_row_max<E>(wblock, qop, cof, ntiles, key, edge, len, window, qi, g);
+            return exact_row_max<E>(wblock, qop, cof, ntiles, key, edge, len, back, ahead, qi, g);
         });
         mb = m_ref == -__builtin_inff() ? 0.f : m_ref * LOG2E;
     };
@@ -1279,7 +1291,7 @@ attend_pre_ph(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
     auto softmax = [&](int t) __attribute__((always_inline)) {
         const int j0 = key(t);
         if (t > 0 && edge(j0))
-            mask_scores(s0, s1, j0, len, window, qi, g);
+            mask_scores(s0, s1, j0, len, back, ahead, qi, g);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], LOG2E, -mb));
@@ -1393,12 +1405,12 @@ int launch_pre(const AttendArgs &a) {
     const uint8_t *ws = (const uint8_t *)a.workspace;
     uint16_t *out = (uint16_t *)a.out;
     int32_t nb32 = (int32_t)tile_blocks(a), num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H;
-    int32_t P = a.table_rows, W = a.window;
+    int32_t P = a.table_rows, Bk = a.back, Ah = a.ahead;
     float scale = a.scale;
     void *args[] = {(void *)&qkv, (void *)&cs,  (void *)&sn,    (void *)&a.cu,
                     (void *)&a.tiles, (void *)&ws, (void *)&out, (void *)&a.lse,
                     (void *)&num_tiles, (void *)&T, (void *)&S,   (void *)&H,
-                    (void *)&P,   (void *)&nb32, (void *)&W,   (void *)&scale};
+                    (void *)&P,   (void *)&nb32, (void *)&Bk,  (void *)&Ah, (void *)&scale};
     const void *fn;
     if constexpr (NW == 8)
         fn = (const void *)attend_pre_ph<E>;
@@ -1422,7 +1434,7 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            const uint32_t *__restrict__ tiles, uint16_t *__restrict__ out,
            float *__restrict__ lse, int32_t num_tiles, int32_t T, int32_t S, int32_t H, int32_t P,
-           int32_t window, float scale) {
+           int32_t back, int32_t ahead, float scale) {
     constexpr int BR = 64;
     constexpr int NTHR = 128;
     __shared__ __attribute__((aligned(16))) uint16_t ks[BC * KS];
@@ -1453,13 +1465,8 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int w0 = i0 + 32 * wv;
     const int qi = w0 + n;
 
-    int lo = 0, hi = len;
-    if (window > 0) {
-        if (i0 + 1 > window)
-            lo = (i0 + 1 - window) / BC * BC;
-        if ((int64_t)i0 + BR + window - 1 < len)
-            hi = i0 + BR + window - 1;
-    }
+    int lo, hi;
+    key_span(i0, BR, len, back, ahead, lo, hi);
     const int ntiles = (hi - lo + BC - 1) / BC;
 
     Staging<NTHR> sg;
@@ -1507,9 +1514,8 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
             for (int i = 0; i < 16; ++i)
                 s1[i] = -__builtin_inff();
         }
-        if ((j0 + BC > len) ||
-            (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window)))
-            mask_scores(s0, s1, j0, len, window, qi, g);
+        if (tile_edge(w0, j0, len, back, ahead))
+            mask_scores(s0, s1, j0, len, back, ahead, qi, g);
         const float mx = row_max(s0, s1);
         const bool raise = mx > m_ref + TAU;
         const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * LOG2E) : 1.0f;
@@ -1694,7 +1700,7 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
              const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
              const uint32_t *__restrict__ tiles, uint16_t *__restrict__ out,
              float *__restrict__ lse, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
-             int32_t P, int32_t window, float scale) {
+             int32_t P, int32_t back, int32_t ahead, float scale) {
     constexpr int NW = 8;
     constexpr int BR = 32 * NW;
     constexpr int RING = 8;   // key tiles held in LDS
@@ -1735,13 +1741,8 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
                 if (seq < (uint32_t)S) {
                     const int start = cu[seq];
                     const int len = cu[seq + 1] - start;
-                    int lo = 0, hi = len;
-                    if (window > 0) {
-                        if (i0 + 1 > window)
-                            lo = (i0 + 1 - window) / BC * BC;
-                        if ((int64_t)i0 + BR + window - 1 < len)
-                            hi = i0 + BR + window - 1;
-                    }
+                    int lo, hi;
+                    key_span(i0, BR, len, back, ahead, lo, hi);
                     // a tile that does not match cu, or reaches more key tiles than the ring
                     // holds (the host admits no such window), reads and writes nothing
                     if (i0 >= 0 && i0 < len && len <= P && start >= 0 &&
@@ -1905,16 +1906,11 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
         if (cur.ok && w0 < cur.len) {
             const int len = cur.len;
             const int qi = w0 + n;
-            int lo = 0, hi = len;
-            if (window > 0) {
-                if (w0 + 1 > window)
-                    lo = (w0 + 1 - window) / BC * BC;
-                if ((int64_t)w0 + 32 + window - 1 < len)
-                    hi = w0 + 32 + window - 1;
-            }
+            int lo, hi;
+            key_span(w0, 32, len, back, ahead, lo, hi);
             // this row's visible keys: jlo <= j < jhi
-            const int jlo = window > 0 ? max(qi - window + 1, 0) : 0;
-            const int jhi = (window > 0 && window < len - qi) ? qi + window : len;
+            int jlo, jhi;
+            row_keys(qi, len, back, ahead, jlo, jhi);
             const int nt = (hi - lo + BC - 1) / BC;
             issued = min(nt, 3);
             float m_ref = -__builtin_inff();
@@ -1929,8 +1925,7 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
                     s0 = E::mfma(*(const u32x4 *)(kt + cof[c]), qop[c], s0);
                     s1 = E::mfma(*(const u32x4 *)(kt + 4096 + cof[c]), qop[c], s1);
                 }
-                if ((j0 + BC > len) ||
-                    (window > 0 && (w0 + 31 - j0 >= window || j0 + BC - 1 - w0 >= window)))
+                if (tile_edge(w0, j0, len, back, ahead))
                     mask_band(s0, s1, jlo, jhi, j0, g);
                 const float mx = row_max(s0, s1);
                 const bool raise = mx > m_ref + TAU;
@@ -2016,12 +2011,13 @@ int launch_typed(const AttendArgs &a) {
     const uint16_t *cs = (const uint16_t *)a.cos;
     const uint16_t *sn = (const uint16_t *)a.sin;
     uint16_t *out = (uint16_t *)a.out;
-    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows, W = a.window;
+    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows;
+    int32_t Bk = a.back, Ah = a.ahead;
     float scale = a.scale;
     void *args[] = {(void *)&qkv, (void *)&cs,        (void *)&sn, (void *)&a.cu,
                     (void *)&a.tiles, (void *)&out,   (void *)&a.lse, (void *)&num_tiles,
                     (void *)&T,   (void *)&S,         (void *)&H,  (void *)&P,
-                    (void *)&W,   (void *)&scale};
+                    (void *)&Bk,  (void *)&Ah, (void *)&scale};
     // 64-row tiles take the unpipelined kernel (short sequences), taller ones the pipeline
     const void *fn;
     if constexpr (NW == 2)
@@ -2052,12 +2048,13 @@ int launch_slide(const AttendArgs &a) {
     const uint16_t *cs = (const uint16_t *)a.cos;
     const uint16_t *sn = (const uint16_t *)a.sin;
     uint16_t *out = (uint16_t *)a.out;
-    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows, W = a.window;
+    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows;
+    int32_t Bk = a.back, Ah = a.ahead;
     float scale = a.scale;
     void *args[] = {(void *)&qkv, (void *)&cs,        (void *)&sn, (void *)&a.cu,
                     (void *)&a.tiles, (void *)&out,   (void *)&a.lse, (void *)&num_tiles,
                     (void *)&T,   (void *)&S,         (void *)&H,  (void *)&P,
-                    (void *)&W,   (void *)&scale};
+                    (void *)&Bk,  (void *)&Ah, (void *)&scale};
     e = hipLaunchKernel((const void *)attend_slide<E, FIXED>, dim3((unsigned)grid), dim3(512),
                         args, 0, (hipStream_t)a.stream);
     if (e != hipSuccess)
@@ -2269,32 +2266,28 @@ __device__ __forceinline__ void back_row_operand(const uint16_t *base, int64_t l
     op[0] = v0, op[1] = v1, op[2] = v2, op[3] = v3;
 }
 
-// The rows [lo, hi) of a sequence of `len` rows that row x sees through the window (empty for x
-// past the sequence).
-__device__ __forceinline__ void back_visible(int x, int len, int window, int &lo, int &hi) {
+// The rows a row sees through the window (empty for a row past the sequence): the keys
+// [lo, hi) of query x (x - back <= j <= x + ahead), or the queries [lo, hi) that see key x
+// (x - ahead <= i <= x + back: pass the reaches swapped).
+__device__ __forceinline__ void back_visible(int x, int len, int back, int ahead, int &lo,
+                                             int &hi) {
     lo = 0, hi = 0;
-    if (x < len) {
-        lo = window > 0 ? max(x - window + 1, 0) : 0;
-        hi = (window > 0 && window < len - x) ? x + window : len;
-    }
+    if (x < len)
+        row_keys(x, len, back, ahead, lo, hi);
 }
 
-// The streamed rows a tile [t0, t0 + rows) reaches: [a, b), a a multiple of BS.
-__device__ __forceinline__ void back_span(int t0, int rows, int len, int window, int &a, int &b) {
-    a = 0, b = len;
-    if (window > 0) {
-        if (t0 + 1 > window)
-            a = (t0 + 1 - window) / BS * BS;
-        if ((int64_t)t0 + rows - 1 + window < len)
-            b = t0 + rows - 1 + window;
-    }
+// The streamed rows a tile [t0, t0 + rows) reaches: [a, b), a a multiple of BS. For a key tile
+// (the queries that see it) pass the reaches swapped.
+__device__ __forceinline__ void back_span(int t0, int rows, int len, int back, int ahead, int &a,
+                                          int &b) {
+    a = t0 > back ? (t0 - back) / BS * BS : 0;
+    b = (int64_t)t0 + rows + ahead < len ? t0 + rows + ahead : len;
 }
 
-// True when every pair of the 32-row blocks [x0, x0+32) and [y0, y0+32) of one sequence is
-// visible: no masking needed.
-__device__ __forceinline__ bool back_full(int x0, int y0, int len, int window) {
-    return x0 + 32 <= len && y0 + 32 <= len &&
-           (window == 0 || (x0 + 31 - y0 < window && y0 + 31 - x0 < window));
+// True when every pair of the 32-row query block [q0, q0+32) and key block [k0, k0+32) of one
+// sequence is visible: no masking needed.
+__device__ __forceinline__ bool back_full(int q0, int k0, int len, int back, int ahead) {
+    return q0 + 32 <= len && k0 + 32 <= len && q0 + 31 - k0 <= back && k0 + 31 - q0 <= ahead;
 }
 
 // Buffer resource over rows [r0, len) of a [*, ld] tensor from column col: rows past the
@@ -2404,7 +2397,7 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
         const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
         const uint8_t *__restrict__ ws, uint16_t *__restrict__ dqkv, int32_t num_tiles,
-        int32_t T, int32_t S, int32_t H, int32_t P, int32_t window) {
+        int32_t T, int32_t S, int32_t H, int32_t P, int32_t back, int32_t ahead) {
     constexpr int SLOT = 4 * IMG + 512;  // Q~, Q~^T, dO^T, dO rows, -lse, -delta
     // buffer loads a wave issues per copy (waves 0 and 1 issue one more)
     constexpr int PIECES = 3 * IMG / 1024 / NW + 8 / NW;
@@ -2435,8 +2428,8 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     back_row_operand(qkv + 2 * hd + h * D, ld, start, kj, len, g, vop);
 
     int qa, qb, vlo, vhi;
-    back_span(j0, 32 * NW, len, window, qa, qb);
-    back_visible(kj, len, window, vlo, vhi);
+    back_span(j0, 32 * NW, len, ahead, back, qa, qb);  // the queries that see the tile's keys
+    back_visible(kj, len, ahead, back, vlo, vhi);
     const uint32_t span = (uint32_t)(vhi - vlo);
 
     const float *nlse = (const float *)ws + (int64_t)(H + h) * T;
@@ -2512,7 +2505,7 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
                     }
                 }
             };
-            if (back_full(it, kw0, len, window) && back_full(it + 32, kw0, len, window))
+            if (back_full(it, kw0, len, back, ahead) && back_full(it + 32, kw0, len, back, ahead))
                 body(Masked<false>{});
             else
                 body(Masked<true>{});
@@ -2568,7 +2561,7 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
        const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
        const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
        const uint8_t *__restrict__ ws, uint16_t *__restrict__ dqkv, int32_t num_tiles,
-       int32_t T, int32_t S, int32_t H, int32_t P, int32_t window, float scale) {
+       int32_t T, int32_t S, int32_t H, int32_t P, int32_t back, int32_t ahead, float scale) {
     constexpr int SLOT = 3 * IMG;  // K~, K~^T, V rows
     constexpr int PIECES = 2 * IMG / 1024 / NW + 8 / NW;  // buffer loads a wave issues per copy
     __shared__ __attribute__((aligned(16))) uint8_t lds[SL * SLOT];
@@ -2607,8 +2600,8 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         nlv[i] = nl, ndv[i] = nd;
 
     int ka, kb, klo, khi;
-    back_span(i0, 32 * NW, len, window, ka, kb);
-    back_visible(qi, len, window, klo, khi);
+    back_span(i0, 32 * NW, len, back, ahead, ka, kb);
+    back_visible(qi, len, back, ahead, klo, khi);
     const uint32_t span = (uint32_t)(khi - klo);
 
     const uint8_t *imgs = ws + back_img_offset(T, H) +
@@ -2666,7 +2659,7 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
                     }
                 }
             };
-            if (back_full(jt, qw0, len, window) && back_full(jt + 32, qw0, len, window))
+            if (back_full(qw0, jt, len, back, ahead) && back_full(qw0, jt + 32, len, back, ahead))
                 body(Masked<false>{});
             else
                 body(Masked<true>{});
@@ -2715,7 +2708,8 @@ int launch_backward_tiles(const BackArgs &a) {
     uint8_t *ws = (uint8_t *)a.workspace;
     const uint8_t *wsc = ws;
     const float *lse = a.lse;
-    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows, W = a.window;
+    int32_t num_tiles = a.num_tiles, T = a.T, S = a.S, H = a.H, P = a.table_rows;
+    int32_t Bk = a.back, Ah = a.ahead;
     float scale = a.scale;
     hipStream_t st = (hipStream_t)a.stream;
     void *args1[] = {(void *)&qkv, (void *)&cs,   (void *)&sn,        (void *)&a.cu,
@@ -2728,7 +2722,7 @@ int launch_backward_tiles(const BackArgs &a) {
         return fail(VLF_EHIP, "backward prep launch failed: %s", hipGetErrorString(e));
     void *args2[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
                      (void *)&dout, (void *)&wsc, (void *)&dqkv, (void *)&num_tiles,
-                     (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&W};
+                     (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&Bk, (void *)&Ah};
     constexpr int SL = NW == 8 ? 4 : 2;
     e = hipLaunchKernel((const void *)back_kv<E, NW, SL>, dim3((unsigned)blocks), dim3(64 * NW),
                         args2, 0, st);
@@ -2736,7 +2730,7 @@ int launch_backward_tiles(const BackArgs &a) {
         return fail(VLF_EHIP, "dK/dV launch failed: %s", hipGetErrorString(e));
     void *args3[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
                      (void *)&dout, (void *)&wsc, (void *)&dqkv, (void *)&num_tiles,
-                     (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&W,
+                     (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&Bk, (void *)&Ah,
                      (void *)&scale};
     e = hipLaunchKernel((const void *)back_q<E, NW, SL>, dim3((unsigned)blocks), dim3(64 * NW),
                         args3, 0, st);
@@ -2824,12 +2818,12 @@ int launch_rotate_qkv_typed(const RotateArgs &a) {
 }  // namespace
 
 // attend_slide serves 256-row tiles whose window reaches at most eight key tiles: keys from
-// i0 - 64 ceil((W - 1) / 64) (i0 a multiple of 64) to i0 + 256 + W - 2.
-static bool slide_fits(int32_t window) {
-    if (window < 1)
+// i0 - 64 ceil(back / 64) (i0 a multiple of 64) to i0 + 255 + ahead.
+static bool slide_fits(int32_t back, int32_t ahead) {
+    if (back == REACH_ALL || ahead == REACH_ALL)
         return false;
-    const int64_t back = ((int64_t)window - 1 + BC - 1) / BC * BC;
-    const int64_t span = back + 256 + window - 1;
+    const int64_t behind = ((int64_t)back + BC - 1) / BC * BC;
+    const int64_t span = behind + 256 + ahead;
     return (span + BC - 1) / BC <= 8;
 }
 
@@ -2859,7 +2853,7 @@ int launch_attend(const AttendArgs &a, Launch what) {
     // rows) plus a tile past it to be reachable with a 31-bit byte offset.
     const int64_t rows = (int64_t)(a.table_rows < a.T ? a.table_rows : a.T) + 2 * BC;
     const bool fixed = rows * 3 * a.H * D * 2 < ((int64_t)1 << 31);
-    if (a.br == 256 && slide_fits(a.window)) {
+    if (a.br == 256 && slide_fits(a.back, a.ahead)) {
         if (bf)
             return fixed ? launch_slide<BF16, true>(a) : launch_slide<BF16, false>(a);
         return fixed ? launch_slide<F16, true>(a) : launch_slide<F16, false>(a);

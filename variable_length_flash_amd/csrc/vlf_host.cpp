@@ -57,6 +57,12 @@ int64_t workspace_bytes(int32_t T, int32_t S, int32_t H) {
     return (int64_t)H * ((int64_t)(T / 64) + S) * (16384 + 4);
 }
 
+void window_reaches(int32_t window, int32_t &back, int32_t &ahead) {
+    const int32_t W = window & ~VLF_CAUSAL;
+    back = W > 0 ? W - 1 : 0x7fffffff;
+    ahead = (window & VLF_CAUSAL) ? 0 : back;
+}
+
 }  // namespace vlf
 
 using namespace vlf;
@@ -113,6 +119,8 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
                       uint64_t *pairs) {
     if (window < 0)
         return fail(VLF_EINVAL, "window = %d < 0", window);
+    const bool causal = (window & VLF_CAUSAL) != 0;
+    window &= ~VLF_CAUSAL;
     if (!pairs)
         return fail(VLF_EINVAL, "pairs is NULL");
     int rc = check_cu(cu_host, S, T, nullptr);
@@ -121,7 +129,11 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
     uint64_t total = 0;
     for (int32_t s = 0; s < S; ++s) {
         const uint64_t L = (uint64_t)(cu_host[s + 1] - cu_host[s]);
-        if (window == 0 || L <= (uint64_t)window) {
+        if (causal) {
+            // row i sees min(i + 1, W) keys: L(L + 1)/2 while L <= W, then W per row
+            const uint64_t W = window == 0 ? L : (uint64_t)window;
+            total += L <= W ? L * (L + 1) / 2 : W * (W + 1) / 2 + (L - W) * W;
+        } else if (window == 0 || L <= (uint64_t)window) {
             total += L * L;  // every key of the sequence
         } else {
             // rows see min(L, i + W) - max(0, i - W + 1) keys; summed over i this is
@@ -206,9 +218,11 @@ static int attend_common(const void *qkv, const void *cos, const void *sin, int3
     if (!tiles_dev || !out || !lse)
         return fail(VLF_EINVAL, "null device pointer (tiles=%p out=%p lse=%p)",
                     (const void *)tiles_dev, out, (void *)lse);
+    int32_t back, ahead;
+    window_reaches(window, back, ahead);
     AttendArgs a{qkv,    cos,   sin,   table_rows, cu_dev, tiles_dev, num_tiles,
-                 br,     T,     S,     H,          window, scale,     dtype,
-                 const_cast<void *>(workspace), out, lse, stream};
+                 br,     T,     S,     H,          back,   ahead,     scale,
+                 dtype,  const_cast<void *>(workspace), out, lse, stream};
     return launch_attend(a, what);
 }
 
@@ -272,9 +286,11 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
     if (!tiles_dev || !out || !dout || !lse || !dqkv)
         return fail(VLF_EINVAL, "null device pointer (tiles=%p out=%p dout=%p lse=%p dqkv=%p)",
                     (const void *)tiles_dev, out, dout, (const void *)lse, dqkv);
-    BackArgs a{qkv,    cos,   sin,   table_rows, cu_dev, tiles_dev, num_tiles, br, T,
-               S,      H,     window, scale,     dtype,  out,       dout,      lse, workspace,
-               dqkv,   stream};
+    int32_t back, ahead;
+    window_reaches(window, back, ahead);
+    BackArgs a{qkv,  cos,   sin,   table_rows, cu_dev, tiles_dev, num_tiles, br,  T,
+               S,    H,     back,  ahead,      scale,  dtype,     out,       dout, lse,
+               workspace, dqkv, stream};
     return launch_backward(a);
 }
 
@@ -310,8 +326,8 @@ int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t t
                           workspace_bytes_, T > 0, true);
     if (rc || T == 0)
         return rc;
-    AttendArgs a{qkv, cos, sin, table_rows, cu_dev, nullptr, 0,       0,       T,     S,
-                 H,   0,   1.f, dtype,      workspace, nullptr, nullptr, stream};
+    AttendArgs a{qkv, cos, sin, table_rows, cu_dev, nullptr,   0,       0,       T, S,
+                 H,   0,   0,   1.f,        dtype,  workspace, nullptr, nullptr, stream};
     return launch_attend(a, Launch::kRotate);
 }
 

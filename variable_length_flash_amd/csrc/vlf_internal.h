@@ -17,7 +17,7 @@ struct AttendArgs {
     int32_t num_tiles;
     int32_t br;
     int32_t T, S, H;
-    int32_t window;
+    int32_t back, ahead;  // row x sees keys x - back .. x + ahead (window_reaches)
     float scale;
     int32_t dtype;
     void *workspace;  // NULL: every workgroup rotates the key tiles it reads
@@ -25,6 +25,10 @@ struct AttendArgs {
     float *lse;
     void *stream;
 };
+
+// The window of the ABI (W, or W | VLF_CAUSAL) as the reaches the kernels take: row x sees the
+// keys x - back .. x + ahead of its sequence, 0x7fffffff reaching every key on that side.
+void window_reaches(int32_t window, int32_t &back, int32_t &ahead);
 
 // Bytes of the key-tile workspace for T tokens, S sequences and H heads.
 int64_t workspace_bytes(int32_t T, int32_t S, int32_t H);
@@ -49,9 +53,9 @@ struct BackArgs {
     const int32_t *cu;
     const uint32_t *tiles;
     int32_t num_tiles;
-    int32_t br;  // 64 or 128
+    int32_t br;  // 64, 128 or 256
     int32_t T, S, H;
-    int32_t window;
+    int32_t back, ahead;
     float scale;
     int32_t dtype;
     const void *out;
