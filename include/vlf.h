@@ -1,11 +1,13 @@
 /*
- * vlf.h — C ABI of libvlf.so: the forward pass of packed variable-length attention with rotary
- * position embeddings applied inside the kernel and an optional symmetric window, for AMD
- * Instinct MI355X (gfx950).
+ * vlf.h — C ABI of libvlf.so: packed variable-length attention with rotary position embeddings
+ * applied inside the kernel and an optional symmetric (or causal) window, forward and backward,
+ * for AMD Instinct MI355X (gfx950).
  *
  * The operation is the one hanzo-kernel 0.2.42 `src/packed.rs` defines: its module contract
  * (layouts of qkv, cu, tiles, cos/sin and the window value), the host `layout` function (the tile
- * table) and the `attend` kernel (rotation, masking, online softmax, outputs and log-sum-exp).
+ * table), the `attend` kernel (rotation, masking, online softmax, outputs and log-sum-exp) and
+ * its backward (`delta`, `attend_back`, `rotate_back`). vlf_rotate_qkv is the rotation as a pass
+ * of its own, the baseline that measures what its fusion saves.
  *
  * Conventions for every call:
  *   - Head dimension is 64. H heads; a token's row of qkv holds 3*H*64 elements: the H query

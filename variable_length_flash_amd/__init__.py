@@ -1,5 +1,6 @@
 """MI355X-native packed variable-length attention, forward and backward (RoPE in the kernel,
-optional symmetric window), built around the C-ABI library ``libvlf.so`` of hand-written gfx950 HIP.
+optional symmetric or causal window), built around the C-ABI library ``libvlf.so`` of
+hand-written gfx950 HIP; ``tune`` picks the schedule per shape by measurement.
 
 The binding (``variable_length_flash_amd.binding``) loads the library on first use and fails
 loudly when it is missing: there is no fallback path.
