@@ -143,7 +143,8 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
  *   window     0 or W >= 1, optionally | VLF_CAUSAL, as above.
  *   scale      multiplies the rotated query before rounding (1/8 for head dimension 64).
  *   dtype      VLF_BF16 or VLF_F16: storage type of qkv, cos, sin and out.
- *   workspace  device or NULL. With workspace_bytes >= vlf_workspace_bytes(T, S, H), the call
+ *   workspace  device (16-byte aligned) or NULL. With workspace_bytes >=
+ *              vlf_workspace_bytes(T, S, H), the call
  *              first rotates every key tile once into it (vlf_rotate_keys, then
  *              vlf_attend_rotated: two kernels on `stream`); its
  *              previous contents are ignored and overwritten, so calls that may overlap in
@@ -157,7 +158,8 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
  *              it never synchronises, never allocates, and returns once the launch is queued.
  *
  * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, negative sizes, T or
- * S inconsistent with each other, num_tiles < 0, a workspace smaller than vlf_workspace_bytes or
+ * S inconsistent with each other, num_tiles < 0, a workspace not 16-byte aligned or smaller than
+ * vlf_workspace_bytes or
  * a size without a pointer), VLF_EUNSUPPORTED (dtype, br),
  * VLF_EHIP (launch failure, from hipGetLastError). Device-side contents (cu_dev, tiles_dev)
  * cannot be checked here; the kernel skips tiles that would read out of range.
@@ -235,7 +237,8 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes
  *
  * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, br not 64, 128
  * or 256, negative sizes, T or S inconsistent, a workspace smaller than
- * vlf_backward_workspace_bytes), VLF_EUNSUPPORTED (dtype), VLF_EHIP (launch failure).
+ * vlf_backward_workspace_bytes or not 16-byte aligned), VLF_EUNSUPPORTED (dtype), VLF_EHIP
+ * (launch failure).
  */
 int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
                         const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,

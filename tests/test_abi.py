@@ -148,6 +148,7 @@ def _attend_status(**kw):
     (dict(ws=0x8000, ws_bytes=0), binding.VLF_EINVAL, "workspace of"),
     (dict(ws=None, ws_bytes=4096), binding.VLF_EINVAL, "without a workspace"),
     (dict(ws=0x8000, ws_bytes=-1), binding.VLF_EINVAL, "workspace_bytes"),
+    (dict(ws=0x8004, ws_bytes=6 * 16388), binding.VLF_EINVAL, "16-byte aligned"),
 ])
 def test_attend_rejects_bad_arguments(kw, status, msg):
     rc, text = _attend_status(**kw)
@@ -331,6 +332,7 @@ def _backward_status(**kw):
     (dict(H=0), binding.VLF_EINVAL, "H = 0"),
     (dict(ws_bytes=100), binding.VLF_EINVAL, "workspace"),
     (dict(ws=None), binding.VLF_EINVAL, "workspace"),
+    (dict(ws=0x8008), binding.VLF_EINVAL, "16-byte aligned"),
     (dict(dout=None), binding.VLF_EINVAL, "null device pointer"),
     (dict(dqkv=None), binding.VLF_EINVAL, "null device pointer"),
     (dict(scale=float("nan")), binding.VLF_EINVAL, "scale"),

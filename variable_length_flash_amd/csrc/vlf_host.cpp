@@ -180,6 +180,8 @@ static int check_launch(const void *qkv, const void *cos, const void *sin, int32
                     (long long)ws_bytes);
     if (need_ws && !workspace && work)
         return fail(VLF_EINVAL, "this call needs a workspace");
+    if (((uintptr_t)workspace & 15) != 0)
+        return fail(VLF_EINVAL, "workspace %p is not 16-byte aligned", workspace);
     if (workspace && ws_bytes < workspace_bytes(T, S, H))
         return fail(VLF_EINVAL, "workspace of %lld bytes; T=%d S=%d H=%d need %lld",
                     (long long)ws_bytes, T, S, H, (long long)workspace_bytes(T, S, H));
@@ -279,6 +281,8 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
         return fail(VLF_EINVAL, "workspace_bytes = %lld < 0", (long long)workspace_bytes_);
     if (!work)
         return VLF_OK;
+    if (((uintptr_t)workspace & 15) != 0)
+        return fail(VLF_EINVAL, "workspace %p is not 16-byte aligned", workspace);
     if (!workspace || workspace_bytes_ < backward_workspace_bytes(T, S, H))
         return fail(VLF_EINVAL, "workspace of %lld bytes; T=%d S=%d H=%d need %lld",
                     (long long)(workspace ? workspace_bytes_ : 0), T, S, H,
