@@ -159,8 +159,7 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
  *
  * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, negative sizes, T or
  * S inconsistent with each other, num_tiles < 0, a workspace not 16-byte aligned or smaller than
- * vlf_workspace_bytes or
- * a size without a pointer), VLF_EUNSUPPORTED (dtype, br),
+ * vlf_workspace_bytes or a size without a pointer), VLF_EUNSUPPORTED (dtype, br),
  * VLF_EHIP (launch failure, from hipGetLastError). Device-side contents (cu_dev, tiles_dev)
  * cannot be checked here; the kernel skips tiles that would read out of range.
  */
