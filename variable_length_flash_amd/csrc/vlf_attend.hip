@@ -2180,10 +2180,23 @@ __device__ __forceinline__ void load_halves(const uint16_t *base, int64_t ld, in
     a = x, b = y;
 }
 
+// The rotation table entries of position i for dims 8c4 .. 8c4+7 (zeros past the sequence).
+__device__ __forceinline__ void load_table_row(const uint16_t *cos_t, const uint16_t *sin_t, int i,
+                                               int len, int c4, u32x4 &c, u32x4 &s) {
+    const u32x4 z = {0, 0, 0, 0};
+    u32x4 cv = z, sv = z;
+    if (i < len) {
+        cv = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * c4);
+        sv = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * c4);
+    }
+    c = cv, s = sv;
+}
+
 // The operand images of the 64-row tiles of one table entry (R rows) and head, with -delta and
-// -lse of their rows. Built in LDS (four lanes per row, 16 dims each) and copied out
-// in 16-byte pieces. Rows past the sequence are zero in every image.
-template <class E, int R>
+// -lse of their rows. Built in LDS (four lanes per row, 16 dims each) and copied out in 16-byte
+// pieces. Rows past the sequence are zero in every image. Without IMAGES only the two per-row
+// floats are written (the passes then stage their operands themselves).
+template <class E, int R, bool IMAGES>
 __global__ void __launch_bounds__(256)
 back_prep(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
           const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
@@ -2191,7 +2204,7 @@ back_prep(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
           const uint16_t *__restrict__ dout, const float *__restrict__ lse,
           uint8_t *__restrict__ ws, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
           int32_t P, float scale) {
-    __shared__ __attribute__((aligned(16))) uint8_t im[BIMG];
+    __shared__ __attribute__((aligned(16))) uint8_t im[IMAGES ? BIMG : 16];
     const int work = xcd_work();
     const int h = work / num_tiles;
     int seq, start, len, i0;
@@ -2207,27 +2220,20 @@ back_prep(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 #pragma unroll 1
     for (int t = i0; t < i0 + R && t < len; t += BC) {
         const int i = t + row;
-        u32x4 q1, q2, k1, k2, o1, o2, y1, y2, c, s;
-        load_halves(qkv + h * D, ld, start, i, len, c4, q1, q2);
-        load_halves(qkv + hd + h * D, ld, start, i, len, c4, k1, k2);
+        u32x4 o1, o2, y1, y2;
         load_halves(dout + h * D, hd, start, i, len, c4, y1, y2);
         load_halves(out + h * D, hd, start, i, len, c4, o1, o2);
-        {
-            const u32x4 z = {0, 0, 0, 0};
-            u32x4 cv = z, sv = z;
-            if (i < len) {
-                cv = *(const u32x4 *)(cos_t + (int64_t)i * 32 + 8 * c4);
-                sv = *(const u32x4 *)(sin_t + (int64_t)i * 32 + 8 * c4);
-            }
-            c = cv, s = sv;
-        }
-        stage_rotated<E>(q1, q2, c, s, scale, im, im + IMG, row, c4);
-        {
+        if constexpr (IMAGES) {
+            u32x4 q1, q2, k1, k2, c, s;
+            load_halves(qkv + h * D, ld, start, i, len, c4, q1, q2);
+            load_halves(qkv + hd + h * D, ld, start, i, len, c4, k1, k2);
+            load_table_row(cos_t, sin_t, i, len, c4, c, s);
+            stage_rotated<E>(q1, q2, c, s, scale, im, im + IMG, row, c4);
             const uint32_t w1[4] = {y1[0], y1[1], y1[2], y1[3]};
             const uint32_t w2[4] = {y2[0], y2[1], y2[2], y2[3]};
             stage_transposed(w1, w2, im + 2 * IMG, row, c4);
+            stage_rotated<E>(k1, k2, c, s, 1.0f, im + 3 * IMG, im + 4 * IMG, row, c4);
         }
-        stage_rotated<E>(k1, k2, c, s, 1.0f, im + 3 * IMG, im + 4 * IMG, row, c4);
         float acc = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -2242,12 +2248,15 @@ back_prep(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
             ndelta[start + i] = -acc;
             nlse[start + i] = -lse[(int64_t)h * T + start + i];
         }
-        __syncthreads();
-        uint8_t *blk = blocks + (int64_t)(t / BC) * BIMG;
+        if constexpr (IMAGES) {
+            __syncthreads();
+            uint8_t *blk = blocks + (int64_t)(t / BC) * BIMG;
 #pragma unroll
-        for (int j = 0; j < BIMG / 4096; ++j)
-            *(u32x4 *)(blk + 4096 * j + 16 * tid) = *(const u32x4 *)(im + 4096 * j + 16 * tid);
-        __syncthreads();
+            for (int j = 0; j < BIMG / 4096; ++j)
+                *(u32x4 *)(blk + 4096 * j + 16 * tid) =
+                    *(const u32x4 *)(im + 4096 * j + 16 * tid);
+            __syncthreads();
+        }
     }
 }
 
@@ -2391,13 +2400,13 @@ __device__ __forceinline__ void back_ds(const f32x16 &st, f32x16 &dp, int a, uin
 // the accumulators into the B operands of dV^T += dO^T P and dK^T += Q~^T dS.
 // SL slots of 33 KB: copies run SL - 1 steps ahead. Eight waves take two a SIMD and the CU's
 // LDS for four slots; four take two a SIMD with two workgroups of two slots a CU; two take one.
-template <class E, int NW, int SL>
+template <class E, int NW, int SL, bool DIRECT>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 1 : 2)))
 back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
         const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
         const uint8_t *__restrict__ ws, uint16_t *__restrict__ dqkv, int32_t num_tiles,
-        int32_t T, int32_t S, int32_t H, int32_t P, int32_t back, int32_t ahead) {
+        int32_t T, int32_t S, int32_t H, int32_t P, int32_t back, int32_t ahead, float scale) {
     constexpr int SLOT = 4 * IMG + 512;  // Q~, Q~^T, dO^T, dO rows, -lse, -delta
     // buffer loads a wave issues per copy (waves 0 and 1 issue one more)
     constexpr int PIECES = 3 * IMG / 1024 / NW + 8 / NW;
@@ -2438,6 +2447,29 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         ws + back_img_offset(T, H) + ((int64_t)h * (T / BC + S) + start / BC + seq) * BIMG;
     lds_u8 *const base = (lds_u8 *)lds;
     auto copy = [&](int it, int sl) {
+        if constexpr (DIRECT) {
+            // the step's rows loaded, rotated and stored here: four lanes a row
+            uint8_t *dg = lds + sl * SLOT;
+            const int c4 = tid & 3;
+            for (int r = tid >> 2; r < BS; r += 16 * NW) {
+                const int i = it + r;
+                u32x4 q1, q2, y1, y2, c, s;
+                load_halves(qkv + h * D, ld, start, i, len, c4, q1, q2);
+                load_halves(dout + h * D, hd, start, i, len, c4, y1, y2);
+                load_table_row(cos_t, sin_t, i, len, c4, c, s);
+                stage_rotated<E>(q1, q2, c, s, scale, dg, dg + IMG, r, c4);
+                const uint32_t w1[4] = {y1[0], y1[1], y1[2], y1[3]};
+                const uint32_t w2[4] = {y2[0], y2[1], y2[2], y2[3]};
+                stage_transposed(w1, w2, dg + 2 * IMG, r, c4);
+                *(u32x4 *)(dg + 3 * IMG + r * 128 + 16 * (c4 ^ swz(r))) = y1;
+                *(u32x4 *)(dg + 3 * IMG + r * 128 + 16 * ((4 + c4) ^ swz(r))) = y2;
+                if (c4 == 0) {
+                    ((float *)(dg + 4 * IMG))[r] = i < len ? nlse[start + i] : 0.f;
+                    ((float *)(dg + 4 * IMG + 256))[r] = i < len ? ndelta[start + i] : 0.f;
+                }
+            }
+            return;
+        }
         lds_u8 *d = base + sl * SLOT;
         copy_block<NW, 3 * IMG>(imgs + (int64_t)(it / BC) * BIMG, d, wvu, lane);
         copy_rows<NW>(back_rows(dout + h * D, hd, start, it, len), hd, d + 3 * IMG, wvu, lane);
@@ -2555,7 +2587,7 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 // from back_prep and its V rows from qkv, straight into one of two LDS slots; dS^T goes from the
 // accumulators into the B operand of dQ^T += K~^T dS^T. dQ is rotated back to the row's
 // position, scaled and written once.
-template <class E, int NW, int SL>
+template <class E, int NW, int SL, bool DIRECT>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
        const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
@@ -2608,6 +2640,21 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
                           ((int64_t)h * (T / BC + S) + start / BC + seq) * BIMG + 3 * IMG;
     lds_u8 *const base = (lds_u8 *)lds;
     auto copy = [&](int jt, int sl) {
+        if constexpr (DIRECT) {
+            uint8_t *dg = lds + sl * SLOT;
+            const int c4 = tid & 3;
+            for (int r = tid >> 2; r < BS; r += 16 * NW) {
+                const int i = jt + r;
+                u32x4 k1, k2, v1, v2, c, s;
+                load_halves(qkv + hd + h * D, ld, start, i, len, c4, k1, k2);
+                load_halves(qkv + 2 * hd + h * D, ld, start, i, len, c4, v1, v2);
+                load_table_row(cos_t, sin_t, i, len, c4, c, s);
+                stage_rotated<E>(k1, k2, c, s, 1.0f, dg, dg + IMG, r, c4);
+                *(u32x4 *)(dg + 2 * IMG + r * 128 + 16 * (c4 ^ swz(r))) = v1;
+                *(u32x4 *)(dg + 2 * IMG + r * 128 + 16 * ((4 + c4) ^ swz(r))) = v2;
+            }
+            return;
+        }
         lds_u8 *d = base + sl * SLOT;
         copy_block<NW, 2 * IMG>(imgs + (int64_t)(jt / BC) * BIMG, d, wvu, lane);
         copy_rows<NW>(back_rows(qkv + 2 * hd + h * D, ld, start, jt, len), ld, d + 2 * IMG, wvu,
@@ -2716,24 +2763,24 @@ int launch_backward_tiles(const BackArgs &a) {
                      (void *)&a.tiles, (void *)&out, (void *)&dout, (void *)&lse,
                      (void *)&ws,  (void *)&num_tiles, (void *)&T, (void *)&S,
                      (void *)&H,   (void *)&P,    (void *)&scale};
-    hipError_t e = hipLaunchKernel((const void *)back_prep<E, 32 * NW>, dim3((unsigned)blocks),
-                                   dim3(256), args1, 0, st);
+    // 64-row tiles stage their operands in the passes (sequences of one or two steps gain
+    // nothing from images written once); taller ones stream the images back_prep writes
+    constexpr bool DIRECT = NW == 2;
+    hipError_t e = hipLaunchKernel((const void *)back_prep<E, 32 * NW, !DIRECT>,
+                                   dim3((unsigned)blocks), dim3(256), args1, 0, st);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "backward prep launch failed: %s", hipGetErrorString(e));
-    void *args2[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
-                     (void *)&dout, (void *)&wsc, (void *)&dqkv, (void *)&num_tiles,
-                     (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&Bk, (void *)&Ah};
     constexpr int SL = NW == 8 ? 4 : 2;
-    e = hipLaunchKernel((const void *)back_kv<E, NW, SL>, dim3((unsigned)blocks), dim3(64 * NW),
-                        args2, 0, st);
-    if (e != hipSuccess)
-        return fail(VLF_EHIP, "dK/dV launch failed: %s", hipGetErrorString(e));
     void *args3[] = {(void *)&qkv, (void *)&cs, (void *)&sn, (void *)&a.cu, (void *)&a.tiles,
                      (void *)&dout, (void *)&wsc, (void *)&dqkv, (void *)&num_tiles,
                      (void *)&T, (void *)&S, (void *)&H, (void *)&P, (void *)&Bk, (void *)&Ah,
                      (void *)&scale};
-    e = hipLaunchKernel((const void *)back_q<E, NW, SL>, dim3((unsigned)blocks), dim3(64 * NW),
-                        args3, 0, st);
+    e = hipLaunchKernel((const void *)back_kv<E, NW, SL, DIRECT>, dim3((unsigned)blocks),
+                        dim3(64 * NW), args3, 0, st);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "dK/dV launch failed: %s", hipGetErrorString(e));
+    e = hipLaunchKernel((const void *)back_q<E, NW, SL, DIRECT>, dim3((unsigned)blocks),
+                        dim3(64 * NW), args3, 0, st);
     if (e != hipSuccess)
         return fail(VLF_EHIP, "dQ launch failed: %s", hipGetErrorString(e));
     return VLF_OK;
