@@ -198,7 +198,8 @@ int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_
  * Device workspace vlf_attend_backward needs for T tokens in S sequences and H heads: float32
  * delta and lse * log2(e), [H, T] each, padded to a multiple of 256 bytes, then per head
  * floor(T / 64) + S blocks of 40 KiB (the operand images of one 64-row tile: rotated queries,
- * their transpose, the transposed output gradient, rotated keys and their transpose).
+ * their transpose, the transposed output gradient, rotated keys and their transpose). Calls on
+ * 64-row tiles stage their operands inside the passes and leave the blocks untouched.
  *   bytes  out: the size (0 when T is 0).
  * Errors: VLF_EINVAL (negative size, H > 65536, null bytes).
  */
