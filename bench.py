@@ -23,7 +23,10 @@ Other modes:
   --profile-run        short run for rocprofv3 (no CPU baseline) plus one plain 1 GiB copy that
                        calibrates the byte counters;
   --summarize DIR      read a rocprofv3 counter-collection directory and print the traffic
-                       summary for profiles/.
+                       summary for profiles/;
+  --counters DIR ...   read rocprofv3 --pmc directories (any counters) and print, for one
+                       kernel, each counter's average per dispatch with the derived matrix,
+                       vector and LDS figures.
 """
 from __future__ import annotations
 
@@ -437,6 +440,88 @@ def summarize(directories, workload: str, kernel: str):
     print(f"hbm_bytes_per_launch: {fetch + write:.0f}")
 
 
+def _kernel_rows(directories, kernel: str):
+    """Per-dispatch sums of every counter of ``kernel`` in rocprofv3 --pmc directories."""
+    import re
+    pattern = re.compile(r"::" + re.escape(kernel) + r"<")
+    per = {}
+    for directory in directories:
+        for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                              recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if not pattern.search(r.get("Kernel_Name", "")):
+                        continue
+                    key = (path, r.get("Dispatch_Id", ""))
+                    d = per.setdefault(key, {})
+                    d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(
+                        r["Counter_Value"])
+    return list(per.values())
+
+
+def counters(directories, workload: str, kernel: str):
+    """Averages per dispatch of every counter taken for ``kernel``, over all passes, and the
+    figures derived from them. GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's active
+    cycles are a eighth of it; the SQ counters are totals over the chip (the *_CYCLES ones of
+    the matrix unit in clocks, SQ_ACTIVE_INST_VALU and SQ_WAVE_CYCLES in quad-cycles)."""
+    rows = _kernel_rows(directories, kernel)
+    if not rows:
+        raise SystemExit(f"no dispatch of {kernel} under {directories}")
+    names = sorted({n for r in rows for n in r})
+    avg = {}
+    for n in names:
+        vals = [r[n] for r in rows if n in r]
+        avg[n] = sum(vals) / len(vals)
+    cus, simds = 256, 1024
+    print(f"kernel: {kernel}")
+    print(f"workload: {workload}")
+    print(f"kernel_source_sha256_16: {kernel_hash()}")
+    print(f"dispatches: {len(rows)}")
+    for n in names:
+        print(f"{n}_per_dispatch: {avg[n]:.6e}")
+    grbm = avg.get("GRBM_GUI_ACTIVE")
+    if not grbm:
+        return
+    xcd_cycles = grbm / 8
+    simd_cycles = xcd_cycles * simds
+    derived = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        derived.append(("mfma_busy_pct_of_simd_cycles",
+                        100 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles))
+    if "SQ_INSTS_MFMA" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        derived.append(("mfma_busy_cycles_per_mfma",
+                        avg["SQ_VALU_MFMA_BUSY_CYCLES"] / avg["SQ_INSTS_MFMA"]))
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        derived.append(("valu_coexec_pct_of_mfma_busy",
+                        100 * avg["SQ_VALU_MFMA_COEXEC_CYCLES"] /
+                        avg["SQ_VALU_MFMA_BUSY_CYCLES"]))
+    if "SQ_ACTIVE_INST_VALU" in avg:
+        derived.append(("VALUBusy_pct (100 SQ_ACTIVE_INST_VALU / CUs / XCD cycles)",
+                        100 * avg["SQ_ACTIVE_INST_VALU"] / cus / xcd_cycles))
+    if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg:
+        derived.append(("non_mfma_valu_insts_per_mfma",
+                        (avg["SQ_INSTS_VALU"] - avg["SQ_INSTS_MFMA"]) / avg["SQ_INSTS_MFMA"]))
+    if "SQ_INSTS_VALU_TRANS_F32" in avg and "SQ_INSTS_MFMA" in avg:
+        derived.append(("trans_f32_insts_per_mfma",
+                        avg["SQ_INSTS_VALU_TRANS_F32"] / avg["SQ_INSTS_MFMA"]))
+    if "SQ_LDS_BANK_CONFLICT" in avg:
+        derived.append(("LDSBankConflict_pct (100 SQ_LDS_BANK_CONFLICT / CUs / XCD cycles)",
+                        100 * avg["SQ_LDS_BANK_CONFLICT"] / cus / xcd_cycles))
+        if avg.get("SQ_LDS_IDX_ACTIVE"):
+            derived.append(("lds_bank_conflict_pct_of_lds_active",
+                            100 * avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_LDS_IDX_ACTIVE"]))
+    if "SQ_WAVE_CYCLES" in avg:
+        derived.append(("waves_resident_per_cu", 4 * avg["SQ_WAVE_CYCLES"] / cus / xcd_cycles))
+        for n in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY"):
+            if n in avg:
+                derived.append((f"{n}_pct_of_wave_cycles", 100 * avg[n] / avg["SQ_WAVE_CYCLES"]))
+    if "SQ_INST_LEVEL_VMEM" in avg and avg.get("SQ_INSTS_VMEM_RD"):
+        derived.append(("vmem_instructions_in_flight_per_cu",
+                        avg["SQ_INST_LEVEL_VMEM"] / cus / xcd_cycles))
+    for name, v in derived:
+        print(f"{name}: {v:.3f}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -450,7 +535,7 @@ def main():
                     help="direct: every workgroup rotates its key tiles; prerotate: key-tile "
                          "workspace (default: chosen from the longest sequence)")
     ap.add_argument("--kernel", default="attend_pre_ph", choices=KERNEL_NAMES,
-                    help="kernel whose counters --summarize reads")
+                    help="kernel whose counters --summarize and --counters read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (vlf_attend_backward) instead of the forward")
@@ -461,9 +546,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", nargs="+")
+    ap.add_argument("--counters", metavar="DIR", nargs="+")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.workload, args.kernel)
+        return
+    if args.counters:
+        counters(args.counters, args.workload, args.kernel)
         return
     run(args)
 
