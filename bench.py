@@ -49,15 +49,6 @@ KERNEL_NAMES = ("attend_pre_ph", "attend_pre", "attend_fwd", "attend_one", "atte
                 "prep_tiles", "back_prep", "back_kv", "back_q")
 
 
-def forward_kernel(prerotate: bool, br: int, window: int) -> str:
-    """The library's forward kernel for a path, tile height and window (vlf_attend.hip's
-    launchers)."""
-    from variable_length_flash_amd import binding
-    if prerotate:
-        return "attend_pre_ph" if br == 256 else "attend_pre"
-    if br == 256 and binding.window_fits_ring(window):
-        return "attend_slide"
-    return "attend_one" if br == 64 else "attend_fwd"
 COPY_BYTES = 1 << 30
 
 
@@ -169,7 +160,7 @@ def run(args):
     prerotate = None if args.path == "auto" else args.path == "prerotate"
     batch = vlf.prepare(w.cu, dev, args.br, prerotate, w.window)
     path = "prerotate" if batch.prerotate else "direct"
-    kernel = forward_kernel(batch.prerotate, batch.br, w.window)
+    kernel = vlf.forward_kernel(batch.br, batch.prerotate, w.window)
     q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
     out = torch.empty((w.tokens, w.heads * 64), dtype=q.dtype, device=dev)
     lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
@@ -281,10 +272,10 @@ def run_backward(args, w, q, c, s, out, lse, stream):
     rng = np.random.default_rng(17)
     dout = torch.from_numpy(rng.standard_normal((w.tokens, w.heads * 64), dtype=np.float32)).to(
         dev, q.dtype)
-    br = args.br or vlf.choose_backward_br(vlf.typical_length(w.cu))
+    br = args.br or vlf.choose_backward(w.cu, w.heads, w.window)[0]
     batch = vlf.prepare(w.cu, dev, br, False, w.window)
     dqkv = torch.empty_like(q)
-    ws = torch.empty(vlf.backward_workspace_bytes(w.tokens, w.sequences, w.heads),
+    ws = torch.empty(vlf.backward_workspace_bytes(w.tokens, w.sequences, w.heads, br),
                      dtype=torch.uint8, device=dev)
 
     def step():

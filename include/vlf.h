@@ -56,7 +56,7 @@ enum vlf_dtype {
 /* Flag ORed into `window` for the causal sliding window (see the conventions above). */
 #define VLF_CAUSAL 0x40000000
 
-/* Library ABI version (this header: 3). */
+/* Library ABI version (this header: 4). */
 int32_t vlf_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). The pointer
@@ -111,6 +111,75 @@ int vlf_visible_pairs(const int32_t *cu_host, int32_t S, int32_t T, int32_t wind
 int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
 
 /*
+ * The schedule rule: which tile height and forward path serve a batch best, from two statistics
+ * of its lengths, and which tile height the backward takes. The page picks its launch shape per
+ * batch by measurement (hanzo-kernel 0.2.42 src/packed.rs, `attend_tuned` and
+ * `attend_back_tuned`, with `usable` / `fits` checking capacity); this rule was fitted to such
+ * measurements on MI355X and is what vlf_choose_schedule and vlf_choose_backward apply.
+ *   max_len     the longest sequence (vlf_tile_count).
+ *   typical     the length of the sequence an average token sits in, sum(L^2) / sum(L)
+ *               (vlf_typical_length); work per token grows with it.
+ *   window      as in vlf_attend.
+ *   br_request  0: choose the tile height; 64, 128 or 256: take it and choose only the path.
+ *   br          out: 64 when no sequence is longer than 64 (one key tile per query tile);
+ *               256 under a window the direct path keeps in LDS (vlf_forward_kernel names
+ *               attend_slide) once typical >= 256; 128 under other windows of at most 512;
+ *               for wider or full windows 256 once typical >= 448, else 128.
+ *   prerotate   out: 1 to rotate keys once into a workspace (vlf_attend with a workspace),
+ *               0 for the direct path. 1 when a query tile's key span (typical, or
+ *               br + back + ahead + 1 for a window) reaches three tiles at 64 or 128 rows,
+ *               1.75 tiles at 256 rows; 0 where the direct path runs attend_slide.
+ *   backward_br out (may be NULL): the backward's tile height, 128 once typical >= 128,
+ *               else 64.
+ * Errors: VLF_EINVAL (negative max_len or typical, window < 0, br_request not 0, 64, 128 or
+ * 256, null br or prerotate).
+ */
+int vlf_schedule_rule(int32_t max_len, double typical, int32_t window, int32_t br_request,
+                      int32_t *br, int32_t *prerotate, int32_t *backward_br);
+
+/*
+ * sum(L^2) / sum(L) over the sequences of cu (0 for a batch without tokens).
+ *   cu_host  host, [S+1].   typical  out.
+ * Errors: VLF_EINVAL (bad cu, null typical).
+ */
+int vlf_typical_length(const int32_t *cu_host, int32_t S, int32_t T, double *typical);
+
+/*
+ * The forward's schedule for a batch: vlf_schedule_rule applied to cu's statistics.
+ *   cu_host          host, [S+1], checked as vlf_tile_count checks it.
+ *   H, window        as in vlf_attend.
+ *   br, prerotate    out: as vlf_schedule_rule returns them.
+ *   max_len          out (may be NULL): the longest sequence, vlf_attend's max_len.
+ *   workspace_bytes  out (may be NULL): vlf_workspace_bytes(T, S, H) when prerotate is 1,
+ *                    else 0: what the caller allocates for vlf_attend.
+ * Errors: VLF_EINVAL (bad cu, H out of range, window < 0, null br or prerotate).
+ */
+int vlf_choose_schedule(const int32_t *cu_host, int32_t S, int32_t T, int32_t H, int32_t window,
+                        int32_t *br, int32_t *prerotate, int32_t *max_len,
+                        int64_t *workspace_bytes);
+
+/*
+ * The backward's schedule for a batch: its tile height (vlf_schedule_rule's backward_br) and
+ * the workspace vlf_attend_backward needs at that height.
+ *   cu_host, H, window  as in vlf_choose_schedule.
+ *   br               out: 64 or 128.
+ *   workspace_bytes  out (may be NULL): vlf_backward_workspace_bytes(T, S, H, br).
+ * Errors: VLF_EINVAL (bad cu, H out of range, window < 0, null br).
+ */
+int vlf_choose_backward(const int32_t *cu_host, int32_t S, int32_t T, int32_t H, int32_t window,
+                        int32_t *br, int64_t *workspace_bytes);
+
+/*
+ * Name of the forward kernel vlf_attend launches for a tile height, path and window (the
+ * key-tile kernel prep_tiles runs before it when prerotate is 1): "attend_pre_ph" (workspace,
+ * 256 rows), "attend_pre" (workspace, 64 or 128 rows), "attend_slide" (direct, 256 rows, a window
+ * of at most eight key tiles kept in LDS: 1 <= W <= 129, or causal 1 <= W <= 257), "attend_one"
+ * (direct, 64 rows) or "attend_fwd" (direct, 128 or 256 rows); "" for a tile height the library
+ * does not run or a negative window. A static string.
+ */
+const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window);
+
+/*
  * The forward pass (hanzo-kernel 0.2.42 src/packed.rs, `attend`): for each tile in tiles_dev
  * and each head h, query rows i0 .. i0+br-1 of sequence s against the keys of s the window
  * reaches.
@@ -126,8 +195,11 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
  *
  *   qkv        device, [T, 3*H*64] elements of `dtype`, rows contiguous.
  *   cos, sin   device, [table_rows, 32] elements of `dtype`: entry [p][m] for position p.
- *   table_rows P; the caller guarantees P >= the longest sequence of cu (vlf_tile_count's
- *              max_len). Tiles whose sequence is longer than P are skipped, not read.
+ *   table_rows P, rows of the tables.
+ *   max_len    the longest sequence of cu (vlf_tile_count's max_len). The call fails with
+ *              VLF_EINVAL when P < max_len. Should a tile still name a sequence longer than P
+ *              (a max_len that understates), the kernels skip it rather than read past the
+ *              tables.
  *   cu_dev     device, [S+1] int32, the same values as the cu the tiles were built from.
  *   tiles_dev  device, [num_tiles, 2] uint32 (sequence, first row) pairs built for the same cu
  *              and `br` (vlf_tile_table, or any permutation of it: the order is the launch
@@ -157,16 +229,18 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
  *   stream     hipStream_t to launch on (NULL = the null stream). The call is asynchronous:
  *              it never synchronises, never allocates, and returns once the launch is queued.
  *
- * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, negative sizes, T or
- * S inconsistent with each other, num_tiles < 0, a workspace not 16-byte aligned or smaller than
- * vlf_workspace_bytes or a size without a pointer), VLF_EUNSUPPORTED (dtype, br),
- * VLF_EHIP (launch failure, from hipGetLastError). Device-side contents (cu_dev, tiles_dev)
- * cannot be checked here; the kernel skips tiles that would read out of range.
+ * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, negative sizes,
+ * T or S inconsistent with each other, num_tiles < 0, max_len < 0, table_rows < max_len, a
+ * workspace not 16-byte aligned or smaller than vlf_workspace_bytes or a size without a
+ * pointer), VLF_EUNSUPPORTED (dtype, br), VLF_EHIP (launch failure, from hipGetLastError).
+ * Device-side contents (cu_dev, tiles_dev) cannot be checked here; the kernel skips tiles that
+ * would read out of range.
  */
 int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-               const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles, int32_t br,
-               int32_t T, int32_t S, int32_t H, int32_t window, float scale, int32_t dtype,
-               void *workspace, int64_t workspace_bytes, void *out, float *lse, void *stream);
+               int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+               int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H, int32_t window,
+               float scale, int32_t dtype, void *workspace, int64_t workspace_bytes, void *out,
+               float *lse, void *stream);
 
 /*
  * The first half of vlf_attend with a workspace: rotate every key tile of cu once and write it,
@@ -174,12 +248,12 @@ int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_
  * rounding of k~ in vlf_attend's formula). Arguments as in vlf_attend. One kernel on `stream`;
  * asynchronous; allocates nothing.
  * Errors: VLF_EINVAL (null pointer with work to do, H out of range, negative sizes, T or S
- * inconsistent, workspace missing or smaller than vlf_workspace_bytes), VLF_EUNSUPPORTED
- * (dtype), VLF_EHIP (launch failure).
+ * inconsistent, table_rows < max_len, workspace missing or smaller than vlf_workspace_bytes),
+ * VLF_EUNSUPPORTED (dtype), VLF_EHIP (launch failure).
  */
 int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                    const int32_t *cu_dev, int32_t T, int32_t S, int32_t H, int32_t dtype,
-                    void *workspace, int64_t workspace_bytes, void *stream);
+                    int32_t max_len, const int32_t *cu_dev, int32_t T, int32_t S, int32_t H,
+                    int32_t dtype, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * The second half of vlf_attend with a workspace: the forward over key tiles a previous
@@ -189,21 +263,23 @@ int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t t
  * Errors: as vlf_attend; the workspace is required.
  */
 int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                       const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                       int32_t br, int32_t T, int32_t S, int32_t H, int32_t window, float scale,
-                       int32_t dtype, const void *workspace, int64_t workspace_bytes, void *out,
-                       float *lse, void *stream);
+                       int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                       int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H,
+                       int32_t window, float scale, int32_t dtype, const void *workspace,
+                       int64_t workspace_bytes, void *out, float *lse, void *stream);
 
 /*
- * Device workspace vlf_attend_backward needs for T tokens in S sequences and H heads: float32
- * delta and lse * log2(e), [H, T] each, padded to a multiple of 256 bytes, then per head
- * floor(T / 64) + S blocks of 40 KiB (the operand images of one 64-row tile: rotated queries,
- * their transpose, the transposed output gradient, rotated keys and their transpose). Calls on
- * 64-row tiles stage their operands inside the passes and leave the blocks untouched.
+ * Device workspace vlf_attend_backward needs for T tokens in S sequences and H heads on br-row
+ * tiles: float32 -delta and -lse (natural log), [H, T] each, padded to a multiple of 256 bytes;
+ * then, for br = 128 or 256 only, per head floor(T / 64) + S blocks of 40 KiB (the operand images
+ * of one 64-row tile: rotated queries, their transpose, the transposed output gradient, rotated
+ * keys and their transpose). Calls on 64-row tiles stage their operands inside the passes and
+ * need no blocks.
+ *   br     64, 128 or 256.
  *   bytes  out: the size (0 when T is 0).
- * Errors: VLF_EINVAL (negative size, H > 65536, null bytes).
+ * Errors: VLF_EINVAL (negative size, H > 65536, br, null bytes).
  */
-int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
+int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int32_t br, int64_t *bytes);
 
 /*
  * The backward pass (hanzo-kernel 0.2.42 src/packed.rs: `delta`, `attend_back`, `rotate_back`):
@@ -221,7 +297,8 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes
  *   inputs give the same bits). dq has a pass of its own that recomputes p and ds; the page
  *   adds dq into float32 with atomics instead.
  *
- *   qkv, cos, sin, table_rows, cu_dev, T, S, H, window, scale, dtype  as in vlf_attend.
+ *   qkv, cos, sin, table_rows, max_len, cu_dev, T, S, H, window, scale, dtype  as in
+ *              vlf_attend.
  *   tiles_dev, num_tiles  the tile table for br-row tiles (vlf_tile_table with this br, or any
  *              permutation of it): each entry is a key tile of the dK/dV pass and a query tile
  *              of the dQ pass.
@@ -229,22 +306,23 @@ int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes
  *   out        device, [T, H*64] of `dtype`: the forward's output for these inputs.
  *   dout       device, [T, H*64] of `dtype`: the gradient of the loss with respect to out.
  *   lse        device, [H, T] float32: the forward's log-sum-exp for these inputs.
- *   workspace  device, at least vlf_backward_workspace_bytes(T, S, H) bytes, 16-byte aligned;
- *              overwritten.
+ *   workspace  device, at least vlf_backward_workspace_bytes(T, S, H, br) bytes, 16-byte
+ *              aligned; overwritten.
  *   dqkv       device, [T, 3*H*64] of `dtype`: every row of every tiled sequence written.
  *   stream     hipStream_t (NULL = the null stream). Three kernels; asynchronous; allocates
  *              nothing. Calls that may overlap in time need separate workspaces.
  *
  * Errors: VLF_EINVAL (null pointer with work to do, H out of range, window < 0, br not 64, 128
- * or 256, negative sizes, T or S inconsistent, a workspace smaller than
+ * or 256, negative sizes, T or S inconsistent, table_rows < max_len, a workspace smaller than
  * vlf_backward_workspace_bytes or not 16-byte aligned), VLF_EUNSUPPORTED (dtype), VLF_EHIP
  * (launch failure).
  */
 int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                        const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                        int32_t br, int32_t T, int32_t S, int32_t H, int32_t window, float scale,
-                        int32_t dtype, const void *out, const void *dout, const float *lse,
-                        void *workspace, int64_t workspace_bytes, void *dqkv, void *stream);
+                        int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                        int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H,
+                        int32_t window, float scale, int32_t dtype, const void *out,
+                        const void *dout, const float *lse, void *workspace,
+                        int64_t workspace_bytes, void *dqkv, void *stream);
 
 /*
  * The unfused baseline's rotation pass: the forward's rotation as a kernel of its own (the page
@@ -256,18 +334,19 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
  * the operands exactly as vlf_attend rounds them, so vlf_attend over qkv_out with identity
  * tables (cos 1, sin 0) and scale 1 gives the bits vlf_attend gives over qkv.
  *
- *   qkv, cos, sin, table_rows, cu_dev, T, S, H, scale, dtype  as in vlf_attend.
+ *   qkv, cos, sin, table_rows, max_len, cu_dev, T, S, H, scale, dtype  as in vlf_attend.
  *   tiles_dev, num_tiles, br  a tile table (vlf_tile_table) for br = 64, 128 or 256.
  *   qkv_out    device, [T, 3*H*64] of `dtype`, not qkv; rows no tile covers are not written.
  *   stream     hipStream_t (NULL = the null stream). One kernel; asynchronous.
  *
  * Errors: VLF_EINVAL (null pointer with work to do, qkv_out == qkv, H out of range, br, negative
- * sizes, T or S inconsistent), VLF_EUNSUPPORTED (dtype), VLF_EHIP (launch failure).
+ * sizes, T or S inconsistent, table_rows < max_len), VLF_EUNSUPPORTED (dtype), VLF_EHIP (launch
+ * failure).
  */
 int vlf_rotate_qkv(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                   const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                   int32_t br, int32_t T, int32_t S, int32_t H, float scale, int32_t dtype,
-                   void *qkv_out, void *stream);
+                   int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                   int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H, float scale,
+                   int32_t dtype, void *qkv_out, void *stream);
 
 #ifdef __cplusplus
 }

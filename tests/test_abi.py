@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     lib = vlf.load_library()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.vlf_version() == 3
+    assert lib.vlf_version() == 4
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -116,14 +116,14 @@ def test_tile_table_capacity_is_checked():
 def _attend_status(**kw):
     """Call vlf_attend with fake (never dereferenced) pointers: every case below must be
     rejected on the host before any launch."""
-    args = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=64, cu=0x4000, tiles=0x5000, nt=4,
-                br=64, T=100, S=2, H=2, window=0, scale=0.125, dtype=binding.VLF_BF16,
+    args = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=64, max_len=60, cu=0x4000, tiles=0x5000,
+                nt=4, br=64, T=100, S=2, H=2, window=0, scale=0.125, dtype=binding.VLF_BF16,
                 ws=None, ws_bytes=0, out=0x6000, lse=0x7000, stream=None)
     args.update(kw)
     lib = vlf.load_library()
-    rc = lib.vlf_attend(args["qkv"], args["cos"], args["sin"], args["P"], args["cu"],
-                        args["tiles"], args["nt"], args["br"], args["T"], args["S"], args["H"],
-                        args["window"], args["scale"], args["dtype"], args["ws"],
+    rc = lib.vlf_attend(args["qkv"], args["cos"], args["sin"], args["P"], args["max_len"],
+                        args["cu"], args["tiles"], args["nt"], args["br"], args["T"], args["S"],
+                        args["H"], args["window"], args["scale"], args["dtype"], args["ws"],
                         args["ws_bytes"], args["out"], args["lse"], args["stream"])
     return rc, lib.vlf_last_error().decode()
 
@@ -141,6 +141,9 @@ def _attend_status(**kw):
     (dict(lse=None), binding.VLF_EINVAL, "null"),
     (dict(tiles=None), binding.VLF_EINVAL, "null"),
     (dict(P=0), binding.VLF_EINVAL, "rotary"),
+    (dict(P=59), binding.VLF_EINVAL, "the longest sequence has 60"),
+    (dict(max_len=-1), binding.VLF_EINVAL, "negative"),
+    (dict(max_len=101), binding.VLF_EINVAL, "above T"),
     (dict(scale=float("nan")), binding.VLF_EINVAL, "scale"),
     (dict(scale=float("inf")), binding.VLF_EINVAL, "scale"),
     # T=100, S=2, H=2 need 2 * (1 + 2) blocks of 16 KiB plus 6 norm bounds
@@ -159,7 +162,7 @@ def test_attend_rejects_bad_arguments(kw, status, msg):
 def test_attend_with_no_work_is_a_no_op():
     # no tiles or no tokens: returns OK without touching the (fake) pointers or the device
     assert _attend_status(nt=0)[0] == binding.VLF_OK
-    assert _attend_status(T=0, S=0, nt=0, qkv=None, out=None)[0] == binding.VLF_OK
+    assert _attend_status(T=0, S=0, nt=0, max_len=0, qkv=None, out=None)[0] == binding.VLF_OK
     for br in (64, 128, 256):  # every tile height the forward serves passes validation
         assert _attend_status(nt=0, br=br)[0] == binding.VLF_OK
 
@@ -195,13 +198,13 @@ def test_workspace_bytes_rejects(T, S, H, msg):
 
 
 def _rotate_status(**kw):
-    args = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=64, cu=0x4000, T=100, S=2, H=2,
-                dtype=binding.VLF_BF16, ws=0x8000, ws_bytes=6 * 16388, stream=None)
+    args = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=64, max_len=60, cu=0x4000, T=100, S=2,
+                H=2, dtype=binding.VLF_BF16, ws=0x8000, ws_bytes=6 * 16388, stream=None)
     args.update(kw)
     lib = vlf.load_library()
-    rc = lib.vlf_rotate_keys(args["qkv"], args["cos"], args["sin"], args["P"], args["cu"],
-                             args["T"], args["S"], args["H"], args["dtype"], args["ws"],
-                             args["ws_bytes"], args["stream"])
+    rc = lib.vlf_rotate_keys(args["qkv"], args["cos"], args["sin"], args["P"], args["max_len"],
+                             args["cu"], args["T"], args["S"], args["H"], args["dtype"],
+                             args["ws"], args["ws_bytes"], args["stream"])
     return rc, lib.vlf_last_error().decode()
 
 
@@ -214,6 +217,7 @@ def _rotate_status(**kw):
     (dict(ws_bytes=6 * 16388 - 4), binding.VLF_EINVAL, "workspace of"),
     (dict(cu=None), binding.VLF_EINVAL, "null"),
     (dict(P=0), binding.VLF_EINVAL, "rotary"),
+    (dict(P=59), binding.VLF_EINVAL, "the longest sequence has 60"),
 ])
 def test_rotate_keys_rejects_bad_arguments(kw, status, msg):
     rc, text = _rotate_status(**kw)
@@ -222,13 +226,13 @@ def test_rotate_keys_rejects_bad_arguments(kw, status, msg):
 
 
 def test_rotate_keys_with_no_tokens_is_a_no_op():
-    assert _rotate_status(T=0, S=0, qkv=None, ws=None, ws_bytes=0)[0] == binding.VLF_OK
+    assert _rotate_status(T=0, S=0, max_len=0, qkv=None, ws=None, ws_bytes=0)[0] == binding.VLF_OK
 
 
 def test_attend_rotated_needs_a_workspace():
     lib = vlf.load_library()
-    rc = lib.vlf_attend_rotated(0x1000, 0x2000, 0x3000, 64, 0x4000, 0x5000, 4, 64, 100, 2, 2, 0,
-                                0.125, binding.VLF_BF16, None, 0, 0x6000, 0x7000, None)
+    rc = lib.vlf_attend_rotated(0x1000, 0x2000, 0x3000, 64, 60, 0x4000, 0x5000, 4, 64, 100, 2,
+                                2, 0, 0.125, binding.VLF_BF16, None, 0, 0x6000, 0x7000, None)
     assert rc == binding.VLF_EINVAL and "needs a workspace" in lib.vlf_last_error().decode()
 
 
@@ -278,6 +282,64 @@ def test_typical_length(lens, want):
     assert vlf.typical_length(cu) == pytest.approx(want)
 
 
+@pytest.mark.parametrize("name", ["tiny", "encoder", "sliding", "many_short", "long"])
+def test_choose_schedule_of_the_workloads(name):
+    """The library's whole-batch choice equals its rule on the batch's statistics, and sizes
+    the workspace it asks for; the five workloads get the schedules measured best for them."""
+    from variable_length_flash_amd import workloads
+    w = workloads.WORKLOADS[name]()
+    br, pre, max_len, ws = vlf.choose_schedule(w.cu, w.heads, w.window)
+    assert max_len == max(w.lens)
+    assert (br, pre) == vlf.schedule_rule(max_len, vlf.typical_length(w.cu), w.window)[:2]
+    assert ws == (vlf.workspace_bytes(w.tokens, w.sequences, w.heads) if pre else 0)
+    want = {"tiny": (128, False), "encoder": (128, False), "sliding": (256, False),
+            "many_short": (64, False), "long": (256, True)}[name]
+    assert (br, pre) == want
+    bbr, bws = vlf.choose_backward(w.cu, w.heads, w.window)
+    assert bbr == vlf.choose_backward_br(vlf.typical_length(w.cu))
+    assert bws == vlf.backward_workspace_bytes(w.tokens, w.sequences, w.heads, bbr)
+
+
+@pytest.mark.parametrize("br,pre,window,name", [
+    (256, True, 0, "attend_pre_ph"), (128, True, 0, "attend_pre"), (64, True, 128, "attend_pre"),
+    (256, False, 128, "attend_slide"), (256, False, 129, "attend_slide"),
+    (256, False, 130, "attend_fwd"), (256, False, 0, "attend_fwd"),
+    (256, False, 257 | vlf.CAUSAL, "attend_slide"), (256, False, 258 | vlf.CAUSAL, "attend_fwd"),
+    (128, False, 128, "attend_fwd"), (64, False, 0, "attend_one"), (32, False, 0, ""),
+    (128, False, -1, "")])
+def test_forward_kernel_names(br, pre, window, name):
+    assert vlf.forward_kernel(br, pre, window) == name
+
+
+def test_schedule_calls_reject_bad_arguments():
+    lib = vlf.load_library()
+    b, p, m = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    ws = ctypes.c_int64()
+    bad = np.array([0, 5, 3], dtype=np.int32).ctypes.data_as(ctypes.c_void_p)
+    good_arr = np.array([0, 5, 9], dtype=np.int32)
+    good = good_arr.ctypes.data_as(ctypes.c_void_p)
+    cases = [
+        (lambda: lib.vlf_schedule_rule(-1, 10.0, 0, 0, ctypes.byref(b), ctypes.byref(p), None),
+         "max_len"),
+        (lambda: lib.vlf_schedule_rule(10, -1.0, 0, 0, ctypes.byref(b), ctypes.byref(p), None),
+         "typical"),
+        (lambda: lib.vlf_schedule_rule(10, 10.0, -1, 0, ctypes.byref(b), ctypes.byref(p), None),
+         "window"),
+        (lambda: lib.vlf_schedule_rule(10, 10.0, 0, 96, ctypes.byref(b), ctypes.byref(p), None),
+         "96"),
+        (lambda: lib.vlf_schedule_rule(10, 10.0, 0, 0, None, ctypes.byref(p), None), "null"),
+        (lambda: lib.vlf_choose_schedule(bad, 2, 3, 2, 0, ctypes.byref(b), ctypes.byref(p),
+                                         ctypes.byref(m), ctypes.byref(ws)), "decreases"),
+        (lambda: lib.vlf_choose_schedule(good, 2, 9, 0, 0, ctypes.byref(b), ctypes.byref(p),
+                                         None, None), "H ="),
+        (lambda: lib.vlf_choose_backward(good, 2, 9, 2, -3, ctypes.byref(b), None), "window"),
+        (lambda: lib.vlf_typical_length(good, 2, 9, None), "typical"),
+    ]
+    for call, text in cases:
+        rc = call()
+        assert rc == binding.VLF_EINVAL and text in lib.vlf_last_error().decode(), text
+
+
 def test_tile_count_and_table_at_int32_extremes():
     # one sequence of INT32_MAX - 1 tokens: tile counts for tile heights near INT32_MAX, where
     # the row arithmetic must not wrap in 32 bits
@@ -290,33 +352,38 @@ def test_tile_count_and_table_at_int32_extremes():
         assert table[:, 1].tolist() == [i * br for i in range(want)]
 
 
+@pytest.mark.parametrize("br", [64, 128, 256])
 @pytest.mark.parametrize("T,S,H", [(1000, 3, 12), (131072, 16, 16), (1, 1, 1), (63, 63, 2)])
-def test_backward_workspace_bytes(T, S, H):
-    # two float32 [H, T] arrays padded to 256 bytes, then H * (floor(T / 64) + S) blocks of
-    # five 8 KiB images
+def test_backward_workspace_bytes(T, S, H, br):
+    # two float32 [H, T] arrays padded to 256 bytes; above 64 rows, then H * (floor(T / 64) + S)
+    # blocks of five 8 KiB images
     floats = (8 * T * H + 255) // 256 * 256
-    assert vlf.backward_workspace_bytes(T, S, H) == floats + H * (T // 64 + S) * 5 * 8192
+    blocks = 0 if br == 64 else H * (T // 64 + S) * 5 * 8192
+    assert vlf.backward_workspace_bytes(T, S, H, br) == floats + blocks
 
 
 def test_backward_workspace_bytes_rejects():
-    assert vlf.backward_workspace_bytes(0, 0, 4) == 0
+    assert vlf.backward_workspace_bytes(0, 0, 4, 128) == 0
     lib = vlf.load_library()
     n = ctypes.c_int64(0)
-    assert lib.vlf_backward_workspace_bytes(-1, 1, 2, ctypes.byref(n)) == binding.VLF_EINVAL
-    assert lib.vlf_backward_workspace_bytes(5, -1, 2, ctypes.byref(n)) == binding.VLF_EINVAL
-    assert lib.vlf_backward_workspace_bytes(5, 1, 70000, ctypes.byref(n)) == binding.VLF_EINVAL
-    assert lib.vlf_backward_workspace_bytes(5, 1, 2, None) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(-1, 1, 2, 64, ctypes.byref(n)) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, -1, 2, 64, ctypes.byref(n)) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, 1, 70000, 64,
+                                            ctypes.byref(n)) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, 1, 2, 64, None) == binding.VLF_EINVAL
+    assert lib.vlf_backward_workspace_bytes(5, 1, 2, 32, ctypes.byref(n)) == binding.VLF_EINVAL
 
 
 def _backward_status(**kw):
     lib = vlf.load_library()
     cu = np.array([0, 100, 256], dtype=np.int32)
-    a = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=256, cu=cu.ctypes.data, tiles=0x4000,
-             num_tiles=5, br=64, T=256, S=2, H=2, W=0, scale=0.125, dtype=binding.VLF_BF16,
-             out=0x5000, dout=0x6000, lse=0x7000, ws=0x8000,
+    a = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=256, max_len=156, cu=cu.ctypes.data,
+             tiles=0x4000, num_tiles=5, br=64, T=256, S=2, H=2, W=0, scale=0.125,
+             dtype=binding.VLF_BF16, out=0x5000, dout=0x6000, lse=0x7000, ws=0x8000,
              ws_bytes=8 * 256 * 2 + 2 * (256 // 64 + 2) * 5 * 8192, dqkv=0x9000)
     a.update(kw)
-    rc = lib.vlf_attend_backward(a["qkv"], a["cos"], a["sin"], a["P"], a["cu"], a["tiles"],
+    rc = lib.vlf_attend_backward(a["qkv"], a["cos"], a["sin"], a["P"], a["max_len"], a["cu"],
+                                 a["tiles"],
                                  a["num_tiles"], a["br"], a["T"], a["S"], a["H"], a["W"],
                                  a["scale"],
                                  a["dtype"], a["out"], a["dout"], a["lse"], a["ws"],
@@ -331,7 +398,11 @@ def _backward_status(**kw):
     (dict(br=32), binding.VLF_EINVAL, "br = 32"),
     (dict(H=0), binding.VLF_EINVAL, "H = 0"),
     (dict(ws_bytes=100), binding.VLF_EINVAL, "workspace"),
+    # 64-row tiles need the two float arrays only; taller ones the images as well
+    (dict(ws_bytes=8 * 256 * 2 - 1), binding.VLF_EINVAL, "workspace"),
+    (dict(br=128, ws_bytes=8 * 256 * 2), binding.VLF_EINVAL, "workspace"),
     (dict(ws=None), binding.VLF_EINVAL, "workspace"),
+    (dict(P=155), binding.VLF_EINVAL, "the longest sequence has 156"),
     (dict(ws=0x8008), binding.VLF_EINVAL, "16-byte aligned"),
     (dict(dout=None), binding.VLF_EINVAL, "null device pointer"),
     (dict(dqkv=None), binding.VLF_EINVAL, "null device pointer"),
@@ -353,14 +424,24 @@ def test_backward_with_no_tiles_is_a_no_op():
     assert _backward_status(num_tiles=0, ws=None, ws_bytes=0)[0] == binding.VLF_OK
 
 
+def test_backward_at_64_rows_takes_the_float_arrays_only():
+    # validation passes with exactly the two float arrays; num_tiles = 0 stops before a launch
+    assert _backward_status(ws_bytes=8 * 256 * 2, num_tiles=0)[0] == binding.VLF_OK
+    lib = vlf.load_library()
+    n = ctypes.c_int64(0)
+    assert lib.vlf_backward_workspace_bytes(256, 2, 2, 64, ctypes.byref(n)) == binding.VLF_OK
+    assert n.value == 8 * 256 * 2
+
+
 def _rotate_qkv_status(**kw):
     lib = vlf.load_library()
     cu = np.array([0, 100, 256], dtype=np.int32)
-    a = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=256, cu=cu.ctypes.data, tiles=0x4000,
-             num_tiles=5, br=64, T=256, S=2, H=2, scale=0.125, dtype=binding.VLF_BF16,
-             dst=0x9000)
+    a = dict(qkv=0x1000, cos=0x2000, sin=0x3000, P=256, max_len=156, cu=cu.ctypes.data,
+             tiles=0x4000, num_tiles=5, br=64, T=256, S=2, H=2, scale=0.125,
+             dtype=binding.VLF_BF16, dst=0x9000)
     a.update(kw)
-    rc = lib.vlf_rotate_qkv(a["qkv"], a["cos"], a["sin"], a["P"], a["cu"], a["tiles"],
+    rc = lib.vlf_rotate_qkv(a["qkv"], a["cos"], a["sin"], a["P"], a["max_len"], a["cu"],
+                            a["tiles"],
                             a["num_tiles"], a["br"], a["T"], a["S"], a["H"], a["scale"],
                             a["dtype"], a["dst"], None)
     return rc, lib.vlf_last_error().decode()
@@ -374,6 +455,7 @@ def _rotate_qkv_status(**kw):
     (dict(dst=None), binding.VLF_EINVAL, "null device pointer"),
     (dict(tiles=None), binding.VLF_EINVAL, "null device pointer"),
     (dict(dst=0x1000), binding.VLF_EINVAL, "must not be qkv"),
+    (dict(P=100), binding.VLF_EINVAL, "the longest sequence has 156"),
     (dict(scale=float("inf")), binding.VLF_EINVAL, "scale"),
 ])
 def test_rotate_qkv_rejects_bad_arguments_before_launching(kw, status, text):

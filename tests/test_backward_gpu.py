@@ -97,7 +97,8 @@ def test_backward_ragged(window, br):
     compare(f"ragged W={window} br={br}", w, qkv, cos, sin, dout, got)
 
 
-@pytest.mark.parametrize("dtype,window,br", [("bf16", 0, 64), ("bf16", 0, 128),
+@pytest.mark.parametrize("dtype,window,br", [("bf16", 0, 64), ("fp16", 0, 64),
+                                             ("bf16", 300, 64), ("bf16", 0, 128),
                                              ("bf16", 300, 128), ("fp16", 0, 128),
                                              ("bf16", 0, 256), ("bf16", 300, 256),
                                              ("fp16", 0, 256)])
@@ -135,10 +136,12 @@ def test_backward_single_key_rows(br):
     assert np.abs(got[:, :2 * hd]).max() <= 1e-2
 
 
-def test_backward_offsets_past_2gib():
+@pytest.mark.parametrize("br", [64, 128])
+def test_backward_offsets_past_2gib(br):
     """qkv of 2.2 GB (88 sequences of 1024 tokens, 64 heads, bf16): byte offsets into qkv, dout
-    and dqkv pass 2^31, the prep pass's block offsets pass 2^32, and both passes build their
-    per-step buffer descriptors from 64-bit row offsets. Inputs drawn on the GPU from a seeded
+    and dqkv pass 2^31. At 128 rows the prep pass's block offsets pass 2^32 and both passes
+    build their per-step buffer descriptors from 64-bit row offsets; at 64 rows the passes
+    stage every step from qkv and dout themselves, from their own 64-bit row offsets. Inputs drawn on the GPU from a seeded
     generator; the first and the last two sequences (all rows, every head) against the
     oracle."""
     lens, H = [1024] * 88, 64
@@ -153,10 +156,10 @@ def test_backward_offsets_past_2gib():
     cos, sin = workloads.rope_tables(w)
     c, s = cos.to(dev), sin.to(dev)
     out, lse = vlf.attend(q, c, s, w.cu, H, 0, w.scale)
-    _say("case backward offsets past 2 GiB")
-    batch = vlf.prepare(w.cu, dev, 128, False, 0)
-    ws_bytes = vlf.backward_workspace_bytes(T, len(lens), H)
-    assert ws_bytes > 2 ** 31
+    _say(f"case backward offsets past 2 GiB br={br}")
+    batch = vlf.prepare(w.cu, dev, br, False, 0)
+    ws_bytes = vlf.backward_workspace_bytes(T, len(lens), H, br)
+    assert ws_bytes > 2 ** 31 or br == 64
     dqkv = torch.full_like(q, float("nan"))
     vlf.attend_backward_into(batch, q, c, s, H, 0, w.scale, out, lse, do, dqkv)
     torch.cuda.synchronize()
@@ -169,7 +172,7 @@ def test_backward_offsets_past_2gib():
                                       do[a:b].float().cpu().numpy(), mode="B", dtype="bf16")
         got = dqkv[a:b].float().cpu().numpy()
         rel = float(np.abs(got - want).max() / np.abs(want).max())
-        _say(f"[backward] 2.2 GB qkv, sequence {si}: rel {rel:.2e}")
+        _say(f"[backward] 2.2 GB qkv br={br}, sequence {si}: rel {rel:.2e}")
         assert rel <= REL_TOL["bf16"], (si, rel)
 
 

@@ -21,9 +21,10 @@ HEAD_DIM = 64
 
 # every function include/vlf.h declares
 EXPORTS = ("vlf_version", "vlf_last_error", "vlf_tile_count", "vlf_tile_table",
-           "vlf_visible_pairs", "vlf_workspace_bytes", "vlf_attend", "vlf_rotate_keys",
-           "vlf_attend_rotated", "vlf_backward_workspace_bytes", "vlf_attend_backward",
-           "vlf_rotate_qkv")
+           "vlf_visible_pairs", "vlf_workspace_bytes", "vlf_schedule_rule", "vlf_typical_length",
+           "vlf_choose_schedule", "vlf_choose_backward", "vlf_forward_kernel", "vlf_attend",
+           "vlf_rotate_keys", "vlf_attend_rotated", "vlf_backward_workspace_bytes",
+           "vlf_attend_backward", "vlf_rotate_qkv")
 
 
 class VlfError(RuntimeError):
@@ -61,20 +62,30 @@ def load_library():
     lib.vlf_visible_pairs.restype = ctypes.c_int
     lib.vlf_workspace_bytes.argtypes = [i32, i32, i32, p]
     lib.vlf_workspace_bytes.restype = ctypes.c_int
-    lib.vlf_attend.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32,
+    lib.vlf_schedule_rule.argtypes = [i32, ctypes.c_double, i32, i32, p, p, p]
+    lib.vlf_schedule_rule.restype = ctypes.c_int
+    lib.vlf_typical_length.argtypes = [p, i32, i32, p]
+    lib.vlf_typical_length.restype = ctypes.c_int
+    lib.vlf_choose_schedule.argtypes = [p, i32, i32, i32, i32, p, p, p, p]
+    lib.vlf_choose_schedule.restype = ctypes.c_int
+    lib.vlf_choose_backward.argtypes = [p, i32, i32, i32, i32, p, p]
+    lib.vlf_choose_backward.restype = ctypes.c_int
+    lib.vlf_forward_kernel.argtypes = [i32, i32, i32]
+    lib.vlf_forward_kernel.restype = ctypes.c_char_p
+    lib.vlf_attend.argtypes = [p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32,
                                ctypes.c_float, i32, p, i64, p, p, p]
     lib.vlf_attend.restype = ctypes.c_int
     lib.vlf_attend_rotated.argtypes = lib.vlf_attend.argtypes
     lib.vlf_attend_rotated.restype = ctypes.c_int
-    lib.vlf_rotate_keys.argtypes = [p, p, p, i32, p, i32, i32, i32, i32, p, i64, p]
+    lib.vlf_rotate_keys.argtypes = [p, p, p, i32, i32, p, i32, i32, i32, i32, p, i64, p]
     lib.vlf_rotate_keys.restype = ctypes.c_int
-    lib.vlf_backward_workspace_bytes.argtypes = [i32, i32, i32, p]
+    lib.vlf_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, p]
     lib.vlf_backward_workspace_bytes.restype = ctypes.c_int
-    lib.vlf_attend_backward.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, i32,
+    lib.vlf_attend_backward.argtypes = [p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, p, p, p, p, i64, p, p]
     lib.vlf_attend_backward.restype = ctypes.c_int
-    lib.vlf_rotate_qkv.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, ctypes.c_float,
-                                   i32, p, p]
+    lib.vlf_rotate_qkv.argtypes = [p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32,
+                                   ctypes.c_float, i32, p, p]
     lib.vlf_rotate_qkv.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -142,75 +153,80 @@ def workspace_bytes(tokens: int, sequences: int, heads: int) -> int:
 
 def typical_length(cu) -> float:
     """The sequence length an average token sits in: sum(L^2) / sum(L) over the batch (0 for
-    an empty batch). Work per token grows with its sequence's length, so this, not the longest
-    sequence, is what the tile height and path choices below weigh."""
-    lens = np.diff(_host_cu(cu).astype(np.int64))
-    total = int(lens.sum())
-    return float((lens * lens).sum()) / total if total > 0 else 0.0
+    an empty batch), from the library (vlf_typical_length). Work per token grows with its
+    sequence's length, so this, not the longest sequence, is what the schedule rule weighs."""
+    cu = _host_cu(cu)
+    out = ctypes.c_double()
+    _check(load_library().vlf_typical_length(_ptr(cu), cu.shape[0] - 1, int(cu[-1]),
+                                             ctypes.byref(out)))
+    return float(out.value)
 
 
-def choose_backward_br(typical: float) -> int:
-    """Tile height of the backward for a batch of typical length ``typical``: 128-row tiles
-    (four waves sharing each staged step) once the typical sequence fills them, else 64."""
-    return 128 if typical >= BACKWARD_TALL else 64
-
-
-BACKWARD_TALL = 128
-
-
-def choose_prerotate(length: float, br: int, window: int = 0) -> bool:
-    """Rotate keys once into a workspace when one query tile's key span (``length``, the
-    batch's typical length, or the window's reach br + 2W - 1) is long enough for each key tile
-    to be read by several workgroups per head: three query tiles at 64 and 128 rows, 448 tokens
-    (1.75 tiles) at 256 rows, whose workspace kernel is the most efficient one. Below that,
-    streaming pre-rotated images does not repay the pass that writes them (measured on batches
-    of 256-4096-token sequences, the encoder and the sliding-window workloads)."""
-    if br == 256 and window_fits_ring(window):
-        return False  # the direct path keeps such a window's keys in LDS (attend_slide)
-    back, ahead = window_reaches(window)
-    span = length if back is None or ahead is None else min(length, br + back + ahead + 1)
-    return span >= (3 * br if br < 256 else 7 * br // 4)
+def schedule_rule(max_len: int, typical: float, window: int = 0, br: int = 0):
+    """(br, prerotate, backward_br) from the library's rule (vlf_schedule_rule) for a batch's
+    longest and typical lengths; ``br`` non-zero fixes the tile height and asks for the path."""
+    b, p, bb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().vlf_schedule_rule(int(max_len), float(typical), int(window), int(br),
+                                            ctypes.byref(b), ctypes.byref(p), ctypes.byref(bb)))
+    return b.value, bool(p.value), bb.value
 
 
 def choose_br(max_len: int, window: int = 0, typical: float | None = None) -> int:
-    """Query rows per workgroup: 64 when no sequence is longer than 64 (one key tile per
-    query tile: the unpipelined kernel). Under a window of at most 129 keys, 256 when the
-    typical length (``typical``, default ``max_len``; see ``typical_length``) fills a 256-row
-    tile (the direct path then walks consecutive tiles with the window's keys held in LDS).
-    Otherwise 128 under a window of at most 512 (a query tile's key span is br + 2W - 1, so
-    taller tiles compute more masked pairs), and for full windows 256 when the typical length
-    reaches 448 tokens (fewer, longer key loops on the most efficient kernel), 128 below."""
-    typical = max_len if typical is None else typical
-    if max_len <= 64:
-        return 64
-    if window_fits_ring(window) and typical >= 256:
-        return 256
-    if 0 < (int(window) & ~CAUSAL) <= 512:
-        return 128
-    return 256 if typical >= 448 else 128
+    """Query rows per workgroup the library's rule picks (``typical`` defaults to
+    ``max_len``)."""
+    return schedule_rule(max_len, max_len if typical is None else typical, window)[0]
+
+
+def choose_prerotate(length: float, br: int, window: int = 0) -> bool:
+    """Whether the library's rule takes the key-tile workspace at tile height ``br`` for a batch
+    of typical length ``length``."""
+    return schedule_rule(0, length, window, br)[1]
+
+
+def choose_backward_br(typical: float) -> int:
+    """Tile height of the backward the library's rule picks for a batch of typical length
+    ``typical``."""
+    return schedule_rule(0, typical)[2]
+
+
+def choose_schedule(cu, heads: int, window: int = 0):
+    """(br, prerotate, max_len, workspace_bytes) of the forward for this batch, from the
+    library (vlf_choose_schedule)."""
+    cu = _host_cu(cu)
+    b, p, m, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(load_library().vlf_choose_schedule(_ptr(cu), cu.shape[0] - 1, int(cu[-1]),
+                                              int(heads), int(window), ctypes.byref(b),
+                                              ctypes.byref(p), ctypes.byref(m),
+                                              ctypes.byref(ws)))
+    return b.value, bool(p.value), m.value, int(ws.value)
+
+
+def choose_backward(cu, heads: int, window: int = 0):
+    """(br, workspace_bytes) of the backward for this batch, from the library
+    (vlf_choose_backward)."""
+    cu = _host_cu(cu)
+    b, ws = ctypes.c_int32(), ctypes.c_int64()
+    _check(load_library().vlf_choose_backward(_ptr(cu), cu.shape[0] - 1, int(cu[-1]),
+                                              int(heads), int(window), ctypes.byref(b),
+                                              ctypes.byref(ws)))
+    return b.value, int(ws.value)
+
+
+def forward_kernel(br: int, prerotate: bool, window: int = 0) -> str:
+    """Name of the forward kernel the library launches for this schedule
+    (vlf_forward_kernel)."""
+    return load_library().vlf_forward_kernel(int(br), int(bool(prerotate)), int(window)).decode()
 
 
 CAUSAL = 0x40000000  # ORed into a window: the causal sliding window (include/vlf.h, VLF_CAUSAL)
 
 
-def window_reaches(window: int):
-    """(back, ahead) of a window value: row x sees keys x - back .. x + ahead of its sequence;
-    None reaches every key on that side."""
-    w = int(window) & ~CAUSAL
-    back = w - 1 if w > 0 else None
-    return back, (0 if int(window) & CAUSAL else back)
-
-
 def window_fits_ring(window: int) -> bool:
-    """Whether the direct path runs 256-row tiles under ``window`` on its LDS-resident key
-    ring (attend_slide): a tile's keys, from i0 - 64 ceil(back / 64) to i0 + 255 + ahead,
-    must span at most eight 64-key tiles, which holds for 1 <= W <= 129, or causal
+    """Whether the direct path runs 256-row tiles under ``window`` on its LDS-resident key ring
+    (the library names attend_slide for it): a tile's keys, from i0 - 64 ceil(back / 64) to
+    i0 + 255 + ahead, span at most eight 64-key tiles, which holds for 1 <= W <= 129, or causal
     1 <= W <= 257."""
-    back, ahead = window_reaches(window)
-    if back is None or ahead is None:
-        return False
-    behind = -(-back // 64) * 64
-    return -(-(behind + 256 + ahead) // 64) <= 8
+    return forward_kernel(256, False, window) == "attend_slide"
 
 
 @dataclass
@@ -237,17 +253,17 @@ def prepare(cu, device=None, br: int | None = None, prerotate: bool | None = Non
             window: int = 0) -> Batch:
     """Validate ``cu``, build the tile table on the host and copy both to ``device``.
 
-    ``br`` (query rows per tile) and ``prerotate`` (use a key-tile workspace) default to
-    ``choose_br`` and ``choose_prerotate`` of the longest sequence, the typical length and
-    ``window`` (the window the batch will be run with; it only informs that choice)."""
+    ``br`` (query rows per tile) and ``prerotate`` (use a key-tile workspace) default to the
+    library's schedule rule for the longest sequence, the typical length and ``window`` (the
+    window the batch will be run with; it only informs that choice)."""
     import torch
     cu_host = _host_cu(cu)
     device = torch.device("cuda") if device is None else torch.device(device)
     _, max_len = tile_count(cu_host, 128)
-    typical = typical_length(cu_host)
-    br = choose_br(max_len, window, typical) if br is None else int(br)
-    prerotate = (choose_prerotate(typical, br, window) if prerotate is None
-                 else bool(prerotate))
+    rule_br, rule_pre, _ = schedule_rule(max_len, typical_length(cu_host), window,
+                                         0 if br is None else int(br))
+    br = rule_br
+    prerotate = rule_pre if prerotate is None else bool(prerotate)
     table = tile_table(cu_host, br)
     return Batch(cu_host, torch.from_numpy(cu_host).to(device),
                  torch.from_numpy(table.view(np.int32)).to(device), table.shape[0], max_len, br,
@@ -356,7 +372,8 @@ def attend_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: flo
             workspace = new_workspace(batch, heads, dev)
     ws_ptr, ws_bytes = _workspace_args(workspace, dev)
     _check(load_library().vlf_attend(
-        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.max_len,
+        batch.cu.data_ptr(),
         batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
         int(window), float(scale), code, ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
         launch.cuda_stream))
@@ -369,7 +386,8 @@ def rotate_keys(batch: Batch, qkv, cos, sin, heads: int, workspace, stream=None)
     dev = qkv.device
     ws_ptr, ws_bytes = _workspace_args(workspace, dev)
     _check(load_library().vlf_rotate_keys(
-        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.max_len,
+        batch.cu.data_ptr(),
         batch.tokens, batch.sequences, heads, code, ws_ptr, ws_bytes, _stream(stream, dev)))
 
 
@@ -381,7 +399,8 @@ def attend_rotated_into(batch: Batch, qkv, cos, sin, heads: int, window: int, sc
     dev = qkv.device
     ws_ptr, ws_bytes = _workspace_args(workspace, dev)
     _check(load_library().vlf_attend_rotated(
-        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.max_len,
+        batch.cu.data_ptr(),
         batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
         int(window), float(scale), code, ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
         _stream(stream, dev)))
@@ -399,17 +418,18 @@ def rotate_qkv_into(batch: Batch, qkv, cos, sin, heads: int, scale: float, qkv_o
                                    f"{tuple(qkv.shape)} {qkv.dtype} contiguous on {qkv.device}")
     dev = qkv.device
     _check(load_library().vlf_rotate_qkv(
-        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.max_len,
+        batch.cu.data_ptr(),
         batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
         float(scale), code, qkv_out.data_ptr(), _stream(stream, dev)))
 
 
-def backward_workspace_bytes(tokens: int, sequences: int, heads: int) -> int:
-    """Bytes of the backward's workspace (per-row floats and the 64-row tiles' operand
-    images)."""
+def backward_workspace_bytes(tokens: int, sequences: int, heads: int, br: int) -> int:
+    """Bytes of the backward's workspace on ``br``-row tiles (per-row floats, and above 64 rows
+    the 64-row tiles' operand images)."""
     n = ctypes.c_int64(0)
     _check(load_library().vlf_backward_workspace_bytes(int(tokens), int(sequences), int(heads),
-                                                       ctypes.byref(n)))
+                                                       int(br), ctypes.byref(n)))
     return int(n.value)
 
 
@@ -418,7 +438,7 @@ def attend_backward_into(batch: Batch, qkv, cos, sin, heads: int, window: int, s
     """Queue the backward (include/vlf.h, vlf_attend_backward): dqkv = d sum(out * dout) / d qkv
     for the forward with the same arguments, whose ``out`` and ``lse`` are passed in.
 
-    ``batch`` must be prepared with ``br`` 64, 128 or 256 (``choose_backward_br``). dout and dqkv
+    ``batch`` must be prepared with ``br`` 64, 128 or 256 (``choose_backward``). dout and dqkv
     have the shapes and dtype of out and qkv. ``workspace``: a contiguous uint8 device tensor of
     at least ``backward_workspace_bytes`` (allocated on the launch stream when None).
     """
@@ -438,11 +458,13 @@ def attend_backward_into(batch: Batch, qkv, cos, sin, heads: int, window: int, s
     launch = _torch_stream(stream, dev)
     if workspace is None:
         with torch.cuda.stream(launch):
-            workspace = torch.empty(backward_workspace_bytes(T, batch.sequences, heads),
+            workspace = torch.empty(backward_workspace_bytes(T, batch.sequences, heads,
+                                                             batch.br),
                                     dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = _workspace_args(workspace, dev)
     _check(load_library().vlf_attend_backward(
-        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.cu.data_ptr(),
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.max_len,
+        batch.cu.data_ptr(),
         batch.tiles.data_ptr(), batch.num_tiles, batch.br, T, batch.sequences, heads,
         int(window), float(scale), code, out.data_ptr(), dout.data_ptr(), lse.data_ptr(), ws_ptr,
         ws_bytes, dqkv.data_ptr(), launch.cuda_stream))
@@ -453,9 +475,11 @@ def attend_backward(qkv, cos, sin, cu, heads: int, out, lse, dout, window: int =
     """The backward of ``attend``: returns dqkv [T, 3*heads*64] (zero rows where no sequence
     reaches)."""
     import torch
-    batch = cu if isinstance(cu, Batch) else prepare(cu, qkv.device,
-                                                     choose_backward_br(typical_length(cu)),
-                                                     False, window)
+    if isinstance(cu, Batch):
+        batch = cu
+    else:
+        br, _ = choose_backward(cu, heads, window)
+        batch = prepare(cu, qkv.device, br, False, window)
     dqkv = torch.zeros_like(qkv)
     attend_backward_into(batch, qkv, cos, sin, heads, window, scale, out, lse, dout, dqkv)
     return dqkv

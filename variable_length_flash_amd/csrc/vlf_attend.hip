@@ -2090,11 +2090,14 @@ int launch_br(const AttendArgs &a) {
 // query tiles, that recomputes S and dP (two more products) and writes dQ once, rotated back and
 // scaled: no atomics, and the same dqkv bits on every run.
 //
-// back_prep writes, once per 64-row tile and head, the operand images both passes stage from:
-// Q~ rows, Q~^T, dO^T, K~ rows and K~^T (rotated, scaled and rounded as the forward rounds them),
-// and per row delta and lse * log2(e). back_kv and back_q then fill LDS with plain 16-byte
-// copies (buffer loads straight into LDS); dO and V rows come from their tensors the same way.
-// Every kernel walks the tile table of the call's tile height (64 or 128 rows).
+// back_prep writes, per row and head, -delta and -lse (float32, natural log; the passes apply
+// log2(e) where they form P). On tiles taller than 64 rows (128 or 256) it also writes, once per
+// 64-row tile and head, the operand images both passes stage from: Q~ rows, Q~^T, dO^T, K~ rows
+// and K~^T (rotated, scaled and rounded as the forward rounds them); back_kv and back_q then fill
+// LDS with plain 16-byte copies (buffer loads straight into LDS), dO and V rows coming from their
+// tensors the same way. On 64-row tiles the passes load, rotate and store each step's operands
+// themselves and no image is written. Every kernel walks the tile table of the call's tile
+// height (64, 128 or 256 rows).
 
 constexpr int BIMG = 5 * IMG;  // one tile's images: Q~, Q~^T, dO^T (24 KB), K~, K~^T (16 KB)
 constexpr int BS = 64;         // streamed rows per step of back_kv and back_q
@@ -2864,18 +2867,11 @@ int launch_rotate_qkv_typed(const RotateArgs &a) {
 }
 }  // namespace
 
-// attend_slide serves 256-row tiles whose window reaches at most eight key tiles: keys from
-// i0 - 64 ceil(back / 64) (i0 a multiple of 64) to i0 + 255 + ahead.
-static bool slide_fits(int32_t back, int32_t ahead) {
-    if (back == REACH_ALL || ahead == REACH_ALL)
-        return false;
-    const int64_t behind = ((int64_t)back + BC - 1) / BC * BC;
-    const int64_t span = behind + 256 + ahead;
-    return (span + BC - 1) / BC <= 8;
-}
-
-int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H) {
-    return T == 0 ? 0 : back_img_offset(T, H) + (int64_t)H * (T / BC + S) * BIMG;
+int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int32_t br) {
+    if (T == 0)
+        return 0;
+    const int64_t floats = back_img_offset(T, H);
+    return br == 64 ? floats : floats + (int64_t)H * (T / BC + S) * BIMG;
 }
 
 int launch_backward(const BackArgs &a) {
@@ -2900,7 +2896,7 @@ int launch_attend(const AttendArgs &a, Launch what) {
     // rows) plus a tile past it to be reachable with a 31-bit byte offset.
     const int64_t rows = (int64_t)(a.table_rows < a.T ? a.table_rows : a.T) + 2 * BC;
     const bool fixed = rows * 3 * a.H * D * 2 < ((int64_t)1 << 31);
-    if (a.br == 256 && slide_fits(a.back, a.ahead)) {
+    if (a.br == 256 && ring_fits(a.back, a.ahead)) {
         if (bf)
             return fixed ? launch_slide<BF16, true>(a) : launch_slide<BF16, false>(a);
         return fixed ? launch_slide<F16, true>(a) : launch_slide<F16, false>(a);

@@ -1,4 +1,5 @@
-// Host side of libvlf.so: argument checks, the tile table and the visible-pair count.
+// Host side of libvlf.so: argument checks, the tile table, the visible-pair count and the
+// schedule rule (tile height and path per batch).
 //
 // The tile table is the host-built index of hanzo-kernel 0.2.42 src/packed.rs (`layout`): one
 // (sequence, first row) pair per `br` query rows of every sequence, in sequence order. The pair
@@ -57,10 +58,62 @@ int64_t workspace_bytes(int32_t T, int32_t S, int32_t H) {
     return (int64_t)H * ((int64_t)(T / 64) + S) * (16384 + 4);
 }
 
+constexpr int32_t kReachAll = 0x7fffffff;
+
 void window_reaches(int32_t window, int32_t &back, int32_t &ahead) {
     const int32_t W = window & ~VLF_CAUSAL;
-    back = W > 0 ? W - 1 : 0x7fffffff;
+    back = W > 0 ? W - 1 : kReachAll;
     ahead = (window & VLF_CAUSAL) ? 0 : back;
+}
+
+bool ring_fits(int32_t back, int32_t ahead) {
+    if (back == kReachAll || ahead == kReachAll)
+        return false;
+    const int64_t behind = ((int64_t)back + 63) / 64 * 64;
+    return (behind + 256 + ahead + 63) / 64 <= 8;
+}
+
+// sum(L^2) / sum(L): the length of the sequence an average token sits in.
+static double typical_of(const int32_t *cu, int32_t S) {
+    double sq = 0, total = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        const double L = (double)cu[s + 1] - (double)cu[s];
+        sq += L * L;
+        total += L;
+    }
+    return total > 0 ? sq / total : 0.0;
+}
+
+// The rule vlf_schedule_rule documents; arguments already checked.
+static void rule(int32_t max_len, double typical, int32_t window, int32_t br_request,
+                 int32_t &br, int32_t &prerotate, int32_t &backward_br) {
+    int32_t back, ahead;
+    window_reaches(window, back, ahead);
+    const bool ring = ring_fits(back, ahead);
+    const int32_t W = window & ~VLF_CAUSAL;
+    if (br_request) {
+        br = br_request;
+    } else if (max_len <= 64) {
+        br = 64;  // one key tile per query tile: the unpipelined kernel
+    } else if (ring && typical >= 256) {
+        br = 256;  // the window's keys stay in an LDS ring across consecutive tiles
+    } else if (W > 0 && W <= 512) {
+        br = 128;  // taller tiles would compute more masked pairs (span br + 2W - 1)
+    } else {
+        br = typical >= 448 ? 256 : 128;
+    }
+    if (br == 256 && ring) {
+        prerotate = 0;  // attend_slide keeps the window's keys in LDS already
+    } else {
+        // a query tile's key span: the typical length, or the window's reach
+        double span = typical;
+        if (back != kReachAll && ahead != kReachAll) {
+            const double reach = (double)br + back + ahead + 1;
+            span = reach < span ? reach : span;
+        }
+        prerotate = span >= (br < 256 ? 3.0 * br : 7.0 * br / 4) ? 1 : 0;
+    }
+    backward_br = typical >= 128 ? 128 : 64;
 }
 
 }  // namespace vlf
@@ -69,7 +122,7 @@ using namespace vlf;
 
 extern "C" {
 
-int32_t vlf_version(void) { return 3; }
+int32_t vlf_version(void) { return 4; }
 
 const char *vlf_last_error(void) { return g_error.c_str(); }
 
@@ -157,17 +210,106 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes) {
     return VLF_OK;
 }
 
+int vlf_schedule_rule(int32_t max_len, double typical, int32_t window, int32_t br_request,
+                      int32_t *br, int32_t *prerotate, int32_t *backward_br) {
+    if (!br || !prerotate)
+        return fail(VLF_EINVAL, "null br or prerotate");
+    if (max_len < 0 || !(typical >= 0))
+        return fail(VLF_EINVAL, "max_len = %d, typical = %g", max_len, typical);
+    if (window < 0)
+        return fail(VLF_EINVAL, "window = %d < 0", window);
+    if (br_request != 0 && !supported_br(br_request))
+        return fail(VLF_EINVAL, "br_request = %d; 0, 64, 128 or 256", br_request);
+    int32_t b, p, bb;
+    rule(max_len, typical, window, br_request, b, p, bb);
+    *br = b;
+    *prerotate = p;
+    if (backward_br)
+        *backward_br = bb;
+    return VLF_OK;
+}
+
+int vlf_typical_length(const int32_t *cu_host, int32_t S, int32_t T, double *typical) {
+    if (!typical)
+        return fail(VLF_EINVAL, "typical is NULL");
+    int rc = check_cu(cu_host, S, T, nullptr);
+    if (rc)
+        return rc;
+    *typical = typical_of(cu_host, S);
+    return VLF_OK;
+}
+
+int vlf_choose_schedule(const int32_t *cu_host, int32_t S, int32_t T, int32_t H, int32_t window,
+                        int32_t *br, int32_t *prerotate, int32_t *max_len,
+                        int64_t *workspace_bytes_) {
+    if (!br || !prerotate)
+        return fail(VLF_EINVAL, "null br or prerotate");
+    if (H < 1 || H > 65536)
+        return fail(VLF_EINVAL, "H = %d outside 1 .. 65536", H);
+    if (window < 0)
+        return fail(VLF_EINVAL, "window = %d < 0", window);
+    int32_t longest = 0;
+    int rc = check_cu(cu_host, S, T, &longest);
+    if (rc)
+        return rc;
+    int32_t b, p, bb;
+    rule(longest, typical_of(cu_host, S), window, 0, b, p, bb);
+    *br = b;
+    *prerotate = p;
+    if (max_len)
+        *max_len = longest;
+    if (workspace_bytes_)
+        *workspace_bytes_ = p ? workspace_bytes(T, S, H) : 0;
+    return VLF_OK;
+}
+
+int vlf_choose_backward(const int32_t *cu_host, int32_t S, int32_t T, int32_t H, int32_t window,
+                        int32_t *br, int64_t *workspace_bytes_) {
+    if (!br)
+        return fail(VLF_EINVAL, "br is NULL");
+    if (H < 1 || H > 65536)
+        return fail(VLF_EINVAL, "H = %d outside 1 .. 65536", H);
+    if (window < 0)
+        return fail(VLF_EINVAL, "window = %d < 0", window);
+    int32_t longest = 0;
+    int rc = check_cu(cu_host, S, T, &longest);
+    if (rc)
+        return rc;
+    int32_t b, p, bb;
+    rule(longest, typical_of(cu_host, S), window, 0, b, p, bb);
+    *br = bb;
+    if (workspace_bytes_)
+        *workspace_bytes_ = backward_workspace_bytes(T, S, H, bb);
+    return VLF_OK;
+}
+
+const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window) {
+    if (!supported_br(br) || window < 0)
+        return "";
+    if (prerotate)
+        return br == 256 ? "attend_pre_ph" : "attend_pre";
+    int32_t back, ahead;
+    window_reaches(window, back, ahead);
+    if (br == 256 && ring_fits(back, ahead))
+        return "attend_slide";
+    return br == 64 ? "attend_one" : "attend_fwd";
+}
+
 // Checks shared by the three launching calls. `work`: the call launches something (pointers
 // are checked only then); `need_ws`: the call cannot run without a workspace.
 static int check_launch(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                        const int32_t *cu_dev, int32_t T, int32_t S, int32_t H, int32_t dtype,
-                        const void *workspace, int64_t ws_bytes, bool work, bool need_ws) {
+                        int32_t max_len, const int32_t *cu_dev, int32_t T, int32_t S, int32_t H,
+                        int32_t dtype, const void *workspace, int64_t ws_bytes, bool work,
+                        bool need_ws) {
     if (dtype != VLF_BF16 && dtype != VLF_F16)
         return fail(VLF_EUNSUPPORTED, "dtype = %d; supported: VLF_F16 (0), VLF_BF16 (1)", dtype);
     if (H < 1 || H > 65536)
         return fail(VLF_EINVAL, "H = %d outside 1 .. 65536", H);
-    if (T < 0 || S < 0 || table_rows < 0)
-        return fail(VLF_EINVAL, "negative size: T=%d S=%d table_rows=%d", T, S, table_rows);
+    if (T < 0 || S < 0 || table_rows < 0 || max_len < 0)
+        return fail(VLF_EINVAL, "negative size: T=%d S=%d table_rows=%d max_len=%d", T, S,
+                    table_rows, max_len);
+    if (max_len > T)
+        return fail(VLF_EINVAL, "max_len = %d above T = %d", max_len, T);
     if (T > 0 && S == 0)
         return fail(VLF_EINVAL, "T = %d tokens but no sequence", T);
     if ((int64_t)T * 3 * H * 64 > ((int64_t)1 << 40))
@@ -192,14 +334,17 @@ static int check_launch(const void *qkv, const void *cos, const void *sin, int32
                     sin, (const void *)cu_dev);
     if (table_rows == 0)
         return fail(VLF_EINVAL, "empty rotary tables with %d tokens", T);
+    if (table_rows < max_len)
+        return fail(VLF_EINVAL, "rotary tables have %d rows; the longest sequence has %d",
+                    table_rows, max_len);
     return VLF_OK;
 }
 
 static int attend_common(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                         const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                         int32_t br, int32_t T, int32_t S, int32_t H, int32_t window,
-                         float scale, int32_t dtype, const void *workspace, int64_t ws_bytes,
-                         void *out, float *lse, void *stream, Launch what) {
+                         int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                         int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H,
+                         int32_t window, float scale, int32_t dtype, const void *workspace,
+                         int64_t ws_bytes, void *out, float *lse, void *stream, Launch what) {
     if (dtype != VLF_BF16 && dtype != VLF_F16)
         return fail(VLF_EUNSUPPORTED, "dtype = %d; supported: VLF_F16 (0), VLF_BF16 (1)", dtype);
     if (!supported_br(br))
@@ -211,8 +356,8 @@ static int attend_common(const void *qkv, const void *cos, const void *sin, int3
     if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
         return fail(VLF_EINVAL, "scale is not finite");
     const bool work = T > 0 && num_tiles > 0;
-    int rc = check_launch(qkv, cos, sin, table_rows, cu_dev, T, S, H, dtype, workspace, ws_bytes,
-                          work, what == Launch::kRotated);
+    int rc = check_launch(qkv, cos, sin, table_rows, max_len, cu_dev, T, S, H, dtype, workspace,
+                          ws_bytes, work, what == Launch::kRotated);
     if (rc)
         return rc;
     if (!work)
@@ -229,38 +374,42 @@ static int attend_common(const void *qkv, const void *cos, const void *sin, int3
 }
 
 int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-               const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles, int32_t br,
-               int32_t T, int32_t S, int32_t H, int32_t window, float scale, int32_t dtype,
-               void *workspace, int64_t workspace_bytes_, void *out, float *lse, void *stream) {
-    return attend_common(qkv, cos, sin, table_rows, cu_dev, tiles_dev, num_tiles, br, T, S, H,
-                         window, scale, dtype, workspace, workspace_bytes_, out, lse, stream,
+               int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+               int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H, int32_t window,
+               float scale, int32_t dtype, void *workspace, int64_t workspace_bytes_, void *out,
+               float *lse, void *stream) {
+    return attend_common(qkv, cos, sin, table_rows, max_len, cu_dev, tiles_dev, num_tiles, br, T,
+                         S, H, window, scale, dtype, workspace, workspace_bytes_, out, lse, stream,
                          workspace ? Launch::kBoth : Launch::kDirect);
 }
 
 int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                       const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                       int32_t br, int32_t T, int32_t S, int32_t H, int32_t window, float scale,
-                       int32_t dtype, const void *workspace, int64_t workspace_bytes_, void *out,
-                       float *lse, void *stream) {
-    return attend_common(qkv, cos, sin, table_rows, cu_dev, tiles_dev, num_tiles, br, T, S, H,
-                         window, scale, dtype, workspace, workspace_bytes_, out, lse, stream,
+                       int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                       int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H,
+                       int32_t window, float scale, int32_t dtype, const void *workspace,
+                       int64_t workspace_bytes_, void *out, float *lse, void *stream) {
+    return attend_common(qkv, cos, sin, table_rows, max_len, cu_dev, tiles_dev, num_tiles, br, T,
+                         S, H, window, scale, dtype, workspace, workspace_bytes_, out, lse, stream,
                          Launch::kRotated);
 }
 
-int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes) {
+int vlf_backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int32_t br, int64_t *bytes) {
     if (!bytes)
         return fail(VLF_EINVAL, "null bytes");
     if (T < 0 || S < 0 || H < 0 || H > 65536)
         return fail(VLF_EINVAL, "T = %d, S = %d, H = %d", T, S, H);
-    *bytes = backward_workspace_bytes(T, S, H);
+    if (!supported_br(br))
+        return fail(VLF_EINVAL, "br = %d; the backward runs on 64-, 128- or 256-row tiles", br);
+    *bytes = backward_workspace_bytes(T, S, H, br);
     return VLF_OK;
 }
 
 int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                        const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                        int32_t br, int32_t T, int32_t S, int32_t H, int32_t window, float scale,
-                        int32_t dtype, const void *out, const void *dout, const float *lse,
-                        void *workspace, int64_t workspace_bytes_, void *dqkv, void *stream) {
+                        int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                        int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H,
+                        int32_t window, float scale, int32_t dtype, const void *out,
+                        const void *dout, const float *lse, void *workspace,
+                        int64_t workspace_bytes_, void *dqkv, void *stream) {
     if (dtype != VLF_BF16 && dtype != VLF_F16)
         return fail(VLF_EUNSUPPORTED, "dtype = %d; supported: VLF_F16 (0), VLF_BF16 (1)", dtype);
     if (window < 0)
@@ -273,8 +422,8 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
         return fail(VLF_EINVAL, "scale is not finite");
     const bool work = T > 0 && num_tiles > 0;
     // the forward's checks, without its workspace (this call's workspace is checked below)
-    int rc = check_launch(qkv, cos, sin, table_rows, cu_dev, T, S, H, dtype, nullptr, 0, work,
-                          false);
+    int rc = check_launch(qkv, cos, sin, table_rows, max_len, cu_dev, T, S, H, dtype, nullptr, 0,
+                          work, false);
     if (rc)
         return rc;
     if (workspace_bytes_ < 0)
@@ -283,10 +432,10 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
         return VLF_OK;
     if (((uintptr_t)workspace & 15) != 0)
         return fail(VLF_EINVAL, "workspace %p is not 16-byte aligned", workspace);
-    if (!workspace || workspace_bytes_ < backward_workspace_bytes(T, S, H))
-        return fail(VLF_EINVAL, "workspace of %lld bytes; T=%d S=%d H=%d need %lld",
-                    (long long)(workspace ? workspace_bytes_ : 0), T, S, H,
-                    (long long)backward_workspace_bytes(T, S, H));
+    if (!workspace || workspace_bytes_ < backward_workspace_bytes(T, S, H, br))
+        return fail(VLF_EINVAL, "workspace of %lld bytes; T=%d S=%d H=%d br=%d need %lld",
+                    (long long)(workspace ? workspace_bytes_ : 0), T, S, H, br,
+                    (long long)backward_workspace_bytes(T, S, H, br));
     if (!tiles_dev || !out || !dout || !lse || !dqkv)
         return fail(VLF_EINVAL, "null device pointer (tiles=%p out=%p dout=%p lse=%p dqkv=%p)",
                     (const void *)tiles_dev, out, dout, (const void *)lse, dqkv);
@@ -299,9 +448,9 @@ int vlf_attend_backward(const void *qkv, const void *cos, const void *sin, int32
 }
 
 int vlf_rotate_qkv(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                   const int32_t *cu_dev, const uint32_t *tiles_dev, int32_t num_tiles,
-                   int32_t br, int32_t T, int32_t S, int32_t H, float scale, int32_t dtype,
-                   void *qkv_out, void *stream) {
+                   int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                   int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H, float scale,
+                   int32_t dtype, void *qkv_out, void *stream) {
     if (num_tiles < 0)
         return fail(VLF_EINVAL, "negative size: num_tiles=%d", num_tiles);
     if (br != 64 && br != 128 && br != 256)
@@ -309,8 +458,8 @@ int vlf_rotate_qkv(const void *qkv, const void *cos, const void *sin, int32_t ta
     if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
         return fail(VLF_EINVAL, "scale is not finite");
     const bool work = T > 0 && num_tiles > 0;
-    int rc = check_launch(qkv, cos, sin, table_rows, cu_dev, T, S, H, dtype, nullptr, 0, work,
-                          false);
+    int rc = check_launch(qkv, cos, sin, table_rows, max_len, cu_dev, T, S, H, dtype, nullptr, 0,
+                          work, false);
     if (rc || !work)
         return rc;
     if (!tiles_dev || !qkv_out)
@@ -324,9 +473,9 @@ int vlf_rotate_qkv(const void *qkv, const void *cos, const void *sin, int32_t ta
 }
 
 int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
-                    const int32_t *cu_dev, int32_t T, int32_t S, int32_t H, int32_t dtype,
-                    void *workspace, int64_t workspace_bytes_, void *stream) {
-    int rc = check_launch(qkv, cos, sin, table_rows, cu_dev, T, S, H, dtype, workspace,
+                    int32_t max_len, const int32_t *cu_dev, int32_t T, int32_t S, int32_t H,
+                    int32_t dtype, void *workspace, int64_t workspace_bytes_, void *stream) {
+    int rc = check_launch(qkv, cos, sin, table_rows, max_len, cu_dev, T, S, H, dtype, workspace,
                           workspace_bytes_, T > 0, true);
     if (rc || T == 0)
         return rc;

@@ -33,6 +33,11 @@ void window_reaches(int32_t window, int32_t &back, int32_t &ahead);
 // Bytes of the key-tile workspace for T tokens, S sequences and H heads.
 int64_t workspace_bytes(int32_t T, int32_t S, int32_t H);
 
+// Whether a 256-row query tile's keys under the reaches span at most eight 64-key tiles: from
+// i0 - 64 ceil(back / 64) (i0 a multiple of 64) to i0 + 255 + ahead. The direct path then runs
+// the kernel that keeps them in an LDS ring (attend_slide).
+bool ring_fits(int32_t back, int32_t ahead);
+
 // What launch_attend queues.
 enum class Launch {
     kDirect,   // the forward, every workgroup rotating the key tiles it reads
@@ -61,13 +66,13 @@ struct BackArgs {
     const void *out;
     const void *dout;
     const float *lse;
-    void *workspace;  // delta and lse * log2(e) (float32 [H, T] each), then the tile images
+    void *workspace;  // -delta and -lse (float32 [H, T] each), then, above 64 rows, the images
     void *dqkv;
     void *stream;
 };
 
-// Bytes of the backward's workspace.
-int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H);
+// Bytes of the backward's workspace on br-row tiles (the images only above 64 rows).
+int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int32_t br);
 
 // Queue the backward kernels (prep, dK/dV, dQ); returns a vlf_status.
 int launch_backward(const BackArgs &a);

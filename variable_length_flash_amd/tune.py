@@ -9,7 +9,8 @@ later call with that key. Here the candidates are the library's schedules (64-, 
 them a launch configuration the parity tests cover, and the key adds the device and the storage
 type. Timing uses HIP events on the launch stream around library calls; no computation happens
 here. The heuristic picks of ``binding.choose_br``, ``choose_prerotate`` and
-``choose_backward_br`` remain the default when no tuning is asked for.
+``choose_backward_br`` (the library's schedule rule) remain the default when no tuning is asked
+for.
 """
 from __future__ import annotations
 
@@ -138,8 +139,8 @@ def tune_backward(qkv, cos, sin, cu, heads: int, out, lse, dout, window: int = 0
     cu_host = binding._host_cu(cu)
     T, S = int(cu_host[-1]), int(cu_host.shape[0] - 1)
     dqkv = torch.empty_like(qkv)
-    ws = torch.empty(binding.backward_workspace_bytes(T, S, heads), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(max(binding.backward_workspace_bytes(T, S, heads, br)
+                         for br in BACKWARD_CANDIDATES), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     ms = {}
     for br in BACKWARD_CANDIDATES:
