@@ -17,7 +17,15 @@ sixteen 8192-token sequences, 16 heads, bf16, full window. It prints one JSON li
   by the reading of a plain copy of known size), recorded in profiles/ with the hash of the
   kernel source they were taken on (null when the source has changed since);
 * cpu_baseline: the float64 oracle (test infrastructure) on the host cores over a bounded
-  sample of rows of the same workload, in the same unit.
+  sample of rows of the same workload, in the same unit (mode B, the parity gate; mode A on a
+  quarter of the rows beside it), and its wall seconds over every row of the other workloads;
+* secondary: the other four workloads (tiny, encoder, sliding, many_short), each on its own
+  schedule, against HBM (algorithmic bytes over the step's time, and that over 8 TB/s);
+* roofline.measured_peak: the sustained rate and clock of the matrix probe (libvlf_probe.so),
+  beside the 2516.6 TFLOP/s spec.
+
+Beside wall-clock means, the line carries HIP-event means and medians per step and per kernel,
+and the host time of the tile table.
 
 Other modes:
   --profile-run        short run for rocprofv3 (no CPU baseline) plus one plain 1 GiB copy that
@@ -26,7 +34,8 @@ Other modes:
                        summary for profiles/;
   --counters DIR ...   read rocprofv3 --pmc directories (any counters) and print, for one
                        kernel, each counter's average per dispatch with the derived matrix,
-                       vector and LDS figures.
+                       vector and LDS figures;
+  --mfma-peak          the matrix probe alone.
 """
 from __future__ import annotations
 
@@ -127,8 +136,24 @@ def cpu_baseline(w, qkv, cos, sin, target_s: float, pairs_per_head_total: int):
     oracle.attend(q32, c32, s32, w.cu, w.heads, w.window, w.scale, mode="B", dtype=w.dtype,
                   rows=rows)
     dt = time.perf_counter() - t0
+    # mode A (the unrounded definition) on a quarter of the same rows
+    rows_a = rows[::4]
+    t0 = time.perf_counter()
+    oracle.attend(q32, c32, s32, w.cu, w.heads, w.window, w.scale, mode="A", dtype=w.dtype,
+                  rows=rows_a)
+    dt_a = time.perf_counter() - t0
     pairs = visible(rows)
+    pairs_a = visible(rows_a)
     flops = 4 * 64 * pairs
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -137,7 +162,147 @@ def cpu_baseline(w, qkv, cos, sin, target_s: float, pairs_per_head_total: int):
         "sample": f"{n} of {w.tokens} rows spread evenly over the workload, all {w.heads} heads "
                   f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP effective), oracle mode B "
                   f"(float64), {dt:.1f} s on {cores} threads",
+        "wall_s": round(dt, 2),
+        "cpu_model": cpu,
+        "mode_a": {"value": 4 * 64 * pairs_a / dt_a / 1e12, "rows": len(rows_a),
+                   "wall_s": round(dt_a, 2)},
     }
+
+
+def algorithmic_bytes(w) -> int:
+    """qkv read once, out and lse written once."""
+    return (3 * w.tokens * w.heads * 64 * 2 + w.tokens * w.heads * 64 * 2
+            + 4 * w.heads * w.tokens)
+
+
+class Forward:
+    """One workload's forward on the device, its inputs resident in HBM, as the binding
+    schedules it (or a fixed tile height and path): a step is the key-tile kernel then the
+    forward over the tiles (workspace path) or the one forward kernel (direct path)."""
+
+    def __init__(self, w, qkv, cos, sin, dev, br=None, prerotate=None):
+        import torch
+
+        import variable_length_flash_amd as vlf
+        self.vlf, self.w, self.dev = vlf, w, dev
+        self.batch = vlf.prepare(w.cu, dev, br, prerotate, w.window)
+        self.kernel = vlf.forward_kernel(self.batch.br, self.batch.prerotate, w.window)
+        self.q, self.c, self.s = qkv.to(dev), cos.to(dev), sin.to(dev)
+        self.out = torch.empty((w.tokens, w.heads * 64), dtype=self.q.dtype, device=dev)
+        self.lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
+        self.ws = vlf.new_workspace(self.batch, w.heads, dev)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def step(self, ev=None):
+        # ev: three events recorded before, between and after the step's kernels
+        vlf, w, b = self.vlf, self.w, self.batch
+        if ev is not None:
+            ev[0].record(self.stream)
+        if b.prerotate:
+            vlf.rotate_keys(b, self.q, self.c, self.s, w.heads, self.ws)
+            if ev is not None:
+                ev[1].record(self.stream)
+            vlf.attend_rotated_into(b, self.q, self.c, self.s, w.heads, w.window, w.scale,
+                                    self.out, self.lse, self.ws)
+        else:
+            if ev is not None:
+                ev[1].record(self.stream)
+            vlf.attend_into(b, self.q, self.c, self.s, w.heads, w.window, w.scale, self.out,
+                            self.lse)
+        if ev is not None:
+            ev[2].record(self.stream)
+
+    def time(self, steps: int, warmup: int):
+        """Wall-clock mean over exactly ``steps`` steps (synchronised on both sides), and the
+        per-step HIP-event durations of the whole step, the forward kernel and the key-tile
+        kernel (mean and median)."""
+        import statistics
+
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                  for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            self.step(events[k])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        whole = [e[0].elapsed_time(e[2]) for e in events]
+        fwd = [e[1].elapsed_time(e[2]) for e in events]
+        rot = [e[0].elapsed_time(e[1]) for e in events]
+        return {"wall_ms": wall,
+                "step_ms": statistics.mean(whole), "step_ms_median": statistics.median(whole),
+                "kernel_ms": statistics.mean(fwd), "kernel_ms_median": statistics.median(fwd),
+                "rotate_ms": statistics.mean(rot), "rotate_ms_median": statistics.median(rot)}
+
+
+def tile_table_host_us(cu, br: int, reps: int = 50) -> float:
+    """Median host time of building the tile table through the library (vlf_tile_count, then
+    vlf_tile_table), microseconds."""
+    import statistics
+
+    import variable_length_flash_amd as vlf
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        vlf.tile_table(cu, br)
+        times.append((time.perf_counter() - t0) * 1e6)
+    return statistics.median(times)
+
+
+SECONDARY = ("tiny", "encoder", "sliding", "many_short")
+
+
+def secondary(args, dev):
+    """The other workloads, each timed as the default line times long (its own schedule, HIP
+    events on the launch stream), against HBM: algorithmic bytes over the forward's time."""
+    import torch
+
+    import variable_length_flash_amd as vlf
+    res = {}
+    for name in SECONDARY:
+        w, qkv, cos, sin = make_inputs(name)
+        f = Forward(w, qkv, cos, sin, dev)
+        t = f.time(args.steps, args.warmup)
+        pairs = vlf.visible_pairs(w.cu, w.window)
+        flops = 4 * 64 * pairs * w.heads
+        nbytes = algorithmic_bytes(w)
+        gbs = nbytes / (t["step_ms"] / 1e3) / 1e9
+        res[name] = {
+            "workload": w.note, "dtype": w.dtype, "br": f.batch.br,
+            "path": "prerotate" if f.batch.prerotate else "direct", "kernel": f.kernel,
+            "ms_per_step": round(t["wall_ms"], 4), "step_ms_mean": round(t["step_ms"], 4),
+            "step_ms_median": round(t["step_ms_median"], 4),
+            "tflops": round(flops / (t["step_ms"] / 1e3) / 1e12, 2),
+            "hbm_gbs_algorithmic": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes, "effective_flop": flops,
+            "tile_table_host_us": round(tile_table_host_us(w.cu, f.batch.br), 1),
+        }
+        del f
+        torch.cuda.empty_cache()
+    return res
+
+
+def oracle_per_config(names):
+    """Wall seconds of the oracle (mode B, the gate, and mode A) over every row of each named
+    workload, on the host cores."""
+    import oracle
+    res = {}
+    for name in names:
+        w, qkv, cos, sin = make_inputs(name)
+        q32 = qkv.float().numpy()
+        c32, s32 = cos.float().numpy(), sin.float().numpy()
+        row = {"rows": w.tokens}
+        for mode in ("B", "A"):
+            t0 = time.perf_counter()
+            oracle.attend(q32, c32, s32, w.cu, w.heads, w.window, w.scale, mode=mode,
+                          dtype=w.dtype)
+            row[f"mode_{mode.lower()}_s"] = round(time.perf_counter() - t0, 2)
+        res[name] = row
+    return res
 
 
 def run(args):
@@ -158,55 +323,20 @@ def run(args):
         w.window |= vlf.CAUSAL
         w.note += ", causal"
     prerotate = None if args.path == "auto" else args.path == "prerotate"
-    batch = vlf.prepare(w.cu, dev, args.br, prerotate, w.window)
+    f = Forward(w, qkv, cos, sin, dev, args.br, prerotate)
+    batch, kernel = f.batch, f.kernel
     path = "prerotate" if batch.prerotate else "direct"
-    kernel = vlf.forward_kernel(batch.br, batch.prerotate, w.window)
-    q, c, s = qkv.to(dev), cos.to(dev), sin.to(dev)
-    out = torch.empty((w.tokens, w.heads * 64), dtype=q.dtype, device=dev)
-    lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)
-    ws = vlf.new_workspace(batch, w.heads, dev)
     pairs = vlf.visible_pairs(w.cu, w.window)
     flops = 4 * 64 * pairs * w.heads
-    alg_bytes = (3 * w.tokens * w.heads * 64 * 2      # qkv read once
-                 + w.tokens * w.heads * 64 * 2        # out written once
-                 + 4 * w.heads * w.tokens)            # lse written once
-    stream = torch.cuda.current_stream(dev)
-
-    def step(ev=None):
-        # ev: three events recorded before, between and after the step's kernels
-        if ev is not None:
-            ev[0].record(stream)
-        if batch.prerotate:
-            vlf.rotate_keys(batch, q, c, s, w.heads, ws)
-            if ev is not None:
-                ev[1].record(stream)
-            vlf.attend_rotated_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse, ws)
-        else:
-            if ev is not None:
-                ev[1].record(stream)
-            vlf.attend_into(batch, q, c, s, w.heads, w.window, w.scale, out, lse)
-        if ev is not None:
-            ev[2].record(stream)
+    alg_bytes = algorithmic_bytes(w)
 
     if args.backward:
-        return run_backward(args, w, q, c, s, out, lse, stream)
+        return run_backward(args, w, f.q, f.c, f.s, f.out, f.lse, f.stream)
     if args.unfused:
-        return run_unfused(args, w, q, c, s, out, lse, stream, batch, ws)
+        return run_unfused(args, w, f.q, f.c, f.s, f.out, f.lse, f.stream, batch, f.ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    kernel_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    rotate_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    t = f.time(args.steps, args.warmup)
+    wall_ms, kernel_ms, rotate_ms = t["wall_ms"], t["kernel_ms"], t["rotate_ms"]
 
     if args.profile_run:
         # a plain copy of known size on the same stream: the counter runs scale by it
@@ -216,7 +346,6 @@ def run(args):
         torch.cuda.synchronize()
 
     value = flops / (wall_ms / 1e3) / 1e12
-    achieved = flops / (kernel_ms / 1e3) / 1e12
     # the committed counters are for the workloads' own windows
     traffic = None if args.causal else read_traffic(kernel, args.workload)
     # the key-tile kernel reads every key and value row once and writes each used block once
@@ -241,10 +370,16 @@ def run(args):
             "tokens": w.tokens, "sequences": w.sequences, "heads": w.heads, "head_dim": 64,
             "window": w.window, "rope_base": w.base, "scale": w.scale, "br": batch.br,
             "path": path,
+            "step_ms_events": {"mean": round(t["step_ms"], 4),
+                               "median": round(t["step_ms_median"], 4)},
             "kernel_ms": {kernel: round(kernel_ms, 4),
                           **({"prep_tiles": round(rotate_ms, 4)} if batch.prerotate else {})},
+            "kernel_ms_median": {kernel: round(t["kernel_ms_median"], 4),
+                                 **({"prep_tiles": round(t["rotate_ms_median"], 4)}
+                                    if batch.prerotate else {})},
             **({"rotate_hbm_gbs_algorithmic": round(rotate_bytes / (rotate_ms / 1e3) / 1e9, 1)}
                if batch.prerotate else {}),
+            "tile_table_host_us": round(tile_table_host_us(w.cu, batch.br), 1),
             "visible_pairs_per_head": pairs, "effective_flop": flops,
             "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "achieved_hbm_gbs_algorithmic": round(alg_bytes / (kernel_ms / 1e3) / 1e9, 1),
@@ -252,9 +387,37 @@ def run(args):
         "roofline": roofline(kernel, flops, alg_bytes, kernel_ms, traffic),
         "cpu_baseline": None,
     }
+    del f
+    torch.cuda.empty_cache()
+    if not args.profile_run and not args.no_mfma_peak:
+        from variable_length_flash_amd import probe
+        peak = probe.mfma_peak(dev)
+        line["roofline"]["measured_peak"] = peak
+        if line["roofline"]["unit"] == "TFLOP/s":
+            line["roofline"]["frac_of_measured_peak"] = round(
+                line["roofline"]["achieved"] / peak["tflops"], 4)
+    if not args.profile_run and not args.no_secondary and args.workload == "long" \
+            and not args.causal and args.br is None and args.path == "auto":
+        line["secondary"] = secondary(args, dev)
     if not args.profile_run and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, qkv, cos, sin, args.cpu_seconds, pairs)
+        if "secondary" in line:
+            line["cpu_baseline"]["per_config"] = oracle_per_config(SECONDARY)
     print(json.dumps(line), flush=True)
+
+
+def run_mfma_peak(args):
+    """``--mfma-peak``: the matrix probe alone, one JSON line."""
+    import torch
+
+    from variable_length_flash_amd import probe
+    dev = torch.device("cuda:0")
+    peak = probe.mfma_peak(dev)
+    print(json.dumps({"metric": "sustained bf16 MFMA TFLOP/s (v_mfma_f32_32x32x16_bf16, two "
+                                "waves per SIMD, independent accumulators)",
+                      "value": peak["tflops"], "unit": "TFLOP/s", "spec": PEAK_BF16_TFLOPS,
+                      "frac_of_spec": round(peak["tflops"] / PEAK_BF16_TFLOPS, 4), **peak}),
+          flush=True)
 
 
 def run_backward(args, w, q, c, s, out, lse, stream):
@@ -528,6 +691,12 @@ def main():
     ap.add_argument("--kernel", default="attend_pre_ph", choices=KERNEL_NAMES,
                     help="kernel whose counters --summarize and --counters read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other four workloads in the default line")
+    ap.add_argument("--no-mfma-peak", action="store_true",
+                    help="skip the matrix probe in the default line")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="run only the matrix probe (sustained bf16 MFMA rate and clock)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (vlf_attend_backward) instead of the forward")
     ap.add_argument("--causal", action="store_true",
@@ -544,6 +713,9 @@ def main():
         return
     if args.counters:
         counters(args.counters, args.workload, args.kernel)
+        return
+    if args.mfma_peak:
+        run_mfma_peak(args)
         return
     run(args)
 

@@ -15,14 +15,31 @@ from variable_length_flash_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    text = open(os.path.join(ROOT, "include", "vlf.h")).read()
+def _declared(header="vlf.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(vlf_[a-z_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
     assert _declared() == sorted(binding.EXPORTS)
+
+
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["vlf.h", "vlf_probe.h"]
+
+
+def test_probe_library_exports_its_header():
+    from variable_length_flash_amd import probe
+    assert _declared("vlf_probe.h") == sorted(probe.EXPORTS)
+    lib = probe.load_library()
+    for name in probe.EXPORTS:
+        assert hasattr(lib, name), name
+    # argument errors come back before any launch
+    assert lib.vlf_probe_mfma(0, 512, 0x1000, None) == -1
+    assert "iters" in lib.vlf_probe_last_error().decode()
+    assert lib.vlf_probe_mfma(10, 512, 0x1004, None) == -1
+    assert "aligned" in lib.vlf_probe_last_error().decode()
 
 
 def test_library_exports_every_declared_function():

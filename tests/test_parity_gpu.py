@@ -62,7 +62,10 @@ def inputs(w):
     return qkv, cos, sin
 
 
-def compare(name, w, got_out, got_lse, qkv, cos, sin, rows=None, window=None):
+def compare(name, w, got_out, got_lse, qkv, cos, sin, rows=None, window=None, mode_a=True):
+    """The gate: out and lse against the mode-B oracle; out also against mode A unless
+    ``mode_a`` is False (inputs far from the workloads' N(0, 1) recipe, where rounding the
+    operands alone moves the oracle's own out by more than the tolerance)."""
     window = w.window if window is None else window
     q32 = qkv.float().numpy()
     c32, s32 = cos.float().numpy(), sin.float().numpy()
@@ -81,7 +84,8 @@ def compare(name, w, got_out, got_lse, qkv, cos, sin, rows=None, window=None):
          f"(tol {LSE_TOL:.0e}); vs unrounded definition: out {a_eo:.2e}, lse {a_el:.2e}")
     assert e_out <= OUT_TOL[w.dtype], (name, e_out)
     assert e_lse <= LSE_TOL, (name, e_lse)
-    assert a_eo <= OUT_TOL[w.dtype], (name, "out against mode A", a_eo)
+    if mode_a:
+        assert a_eo <= OUT_TOL[w.dtype], (name, "out against mode A", a_eo)
 
 
 LENS = [5, 40, 1, 33, 70]
@@ -375,7 +379,10 @@ def test_outlying_key_norms(dtype, factor, window):
     tiles' sweeps. With the factor 6 a bfloat16 row's reference on the 256-row workspace path
     can sit some 30 above its largest score (probabilities near e^-30); with 12, and for every
     fp16 row whose bound is loose, the kernel first sweeps the scores for the exact row
-    maximum. Every row must match the oracle on both paths and at every tile height."""
+    maximum. Every row must match the oracle on both paths and at every tile height. Mode A is
+    printed, not gated: with keys scaled by 6 or 12 the oracle's own mode-B out lies 4.8e-2 to
+    9.6e-2 (bf16) and 4.8e-3 to 9.4e-3 (fp16) from mode A, so no kernel that rounds its operands
+    to the storage type can be within the out tolerance of the unrounded definition."""
     w = workloads.custom([700, 300, 65], 2, dtype=dtype, window=window, table_rows=1024,
                          seed=41)
     qkv, cos, sin = inputs(w)
@@ -389,7 +396,7 @@ def test_outlying_key_norms(dtype, factor, window):
             _say(f"case outlying keys {dtype} x{factor} W={window} br={br} prerotate={pre}")
             out, lse = run_gpu(w, qkv, cos, sin, br=br, prerotate=pre)
             compare(f"outlying keys {dtype} x{factor} W={window} br={br} pre={int(pre)}", w,
-                    out, lse, qkv, cos, sin)
+                    out, lse, qkv, cos, sin, mode_a=False)
 
 
 @functools.lru_cache(maxsize=1)

@@ -1,4 +1,5 @@
-"""Build libvlf.so in-tree: the gfx950 kernels (hipcc) and the host index code (g++).
+"""Build libvlf.so in-tree: the gfx950 kernels (hipcc) and the host index code (g++); and
+libvlf_probe.so, the matrix-unit probe the benchmark reads its measured peak from.
 
     python -m variable_length_flash_amd.build
 """
@@ -10,6 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libvlf.so")
+PROBE_LIBRARY = os.path.join(HERE, "libvlf_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 instructions stay off: hipcc forms them from ordinary float code otherwise.
@@ -36,6 +38,9 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", kernel_obj, host_obj, "-o", tmp],
          verbose)
     os.replace(tmp, LIBRARY)
+    tmp = PROBE_LIBRARY + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", os.path.join(CSRC, "vlf_probe.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIBRARY)
     return LIBRARY
 
 

@@ -1,0 +1,77 @@
+"""ctypes binding of libvlf_probe.so (include/vlf_probe.h): the matrix-unit probe the benchmark
+sets the forward's rate against. It is not part of the attention path."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libvlf_probe.so")
+EXPORTS = ("vlf_probe_mfma", "vlf_probe_last_error")
+FLOP_PER_MFMA = 32 * 32 * 16 * 2  # v_mfma_f32_32x32x16_bf16
+
+_lib = None
+
+
+def load_library():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is not built; run python -m "
+                               "variable_length_flash_amd.build")
+        lib = ctypes.CDLL(LIBRARY)
+        lib.vlf_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        lib.vlf_probe_mfma.restype = ctypes.c_int
+        lib.vlf_probe_last_error.argtypes = []
+        lib.vlf_probe_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def mfma_peak(device, iters: int = 20000, reps: int = 3):
+    """Sustained bf16 matrix rate and shader clock on ``device``: two four-wave workgroups per
+    CU issuing only v_mfma_f32_32x32x16_bf16 on independent accumulators. Returns a dict:
+    TFLOP/s of the fastest of ``reps`` launches (HIP events on the launch stream), the clock
+    (shader ticks over 100 MHz ticks, median over workgroups), the matrix clocks per
+    instruction and SIMD that rate and clock imply, and a workgroup's own loop time (equal to
+    the launch's when a CU's workgroups run side by side, half of it when they run in turn)."""
+    import torch
+    lib = load_library()
+    dev = torch.device(device)
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    blocks = 2 * cus
+    record = torch.zeros(4 * blocks, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch():
+        rc = lib.vlf_probe_mfma(int(iters), int(blocks), record.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(lib.vlf_probe_last_error().decode())
+
+    launch()  # warm-up
+    torch.cuda.synchronize(dev)
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch()
+        b.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    rec = record.view(blocks, 4).cpu()
+    ticks, real = rec[:, 0].double(), rec[:, 1].double()
+    clock = float((ticks / (real / 100e6)).median()) / 1e9
+    flop = blocks * 4 * iters * 8 * FLOP_PER_MFMA
+    tflops = flop / (best / 1e3) / 1e12
+    # matrix clocks per instruction on a SIMD over the whole launch: each SIMD issues
+    # blocks * 8 * iters / cus of them in the launch's time at the measured clock
+    per_simd = blocks * 8 * iters / cus
+    per_mfma = best / 1e3 * clock * 1e9 / per_simd
+    wg_ms = float((real / 100e6).median()) * 1e3
+    return {"tflops": round(tflops, 1), "clock_ghz": round(clock, 3),
+            "clocks_per_mfma": round(per_mfma, 2), "ms": round(best, 4),
+            "workgroup_ms_median": round(wg_ms, 4), "cus": cus, "workgroups": blocks,
+            "instruction": "v_mfma_f32_32x32x16_bf16"}
