@@ -242,6 +242,32 @@ int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_
                float scale, int32_t dtype, void *workspace, int64_t workspace_bytes, void *out,
                float *lse, void *stream);
 
+/* Bytes of the fixed device array vlf_attend_static uses as its key-tile workspace. */
+#define VLF_STATIC_WORKSPACE_BYTES (128LL << 20)
+
+/*
+ * vlf_attend on the key-tile workspace path, for callers that cannot allocate device memory
+ * (code under stream capture, serving loops and harnesses that forbid allocation): the
+ * workspace is a fixed array of VLF_STATIC_WORKSPACE_BYTES in the library's device memory,
+ * one per GPU, held until the process ends, instead of a caller's buffer. The call allocates
+ * and frees nothing. Arguments and results as in vlf_attend without `workspace` and
+ * `workspace_bytes`: the same two kernels on `stream` (key tiles, then the forward over them),
+ * so the same bits as vlf_attend with a workspace of its own. The array's address on the
+ * current device is looked up on the first call there.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap in time on one GPU
+ *   (other streams, other threads) race on it and must be ordered by the caller. Each call
+ *   writes every block and norm bound it reads before reading it, so nothing in the array
+ *   needs clearing and the previous call's contents never reach a result.
+ * Errors: as vlf_attend; VLF_EINVAL also when vlf_workspace_bytes(T, S, H) exceeds
+ * VLF_STATIC_WORKSPACE_BYTES (the message gives both sizes); VLF_EHIP when the array's device
+ * address cannot be obtained.
+ */
+int vlf_attend_static(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                      int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                      int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H,
+                      int32_t window, float scale, int32_t dtype, void *out, float *lse,
+                      void *stream);
+
 /*
  * The first half of vlf_attend with a workspace: rotate every key tile of cu once and write it,
  * with its values, into `workspace` (the blocks vlf_workspace_bytes describes; the rotation and

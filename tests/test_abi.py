@@ -246,6 +246,32 @@ def test_rotate_keys_with_no_tokens_is_a_no_op():
     assert _rotate_status(T=0, S=0, max_len=0, qkv=None, ws=None, ws_bytes=0)[0] == binding.VLF_OK
 
 
+def test_attend_static_rejects_a_workspace_beyond_its_array():
+    # the long workload's key tiles (541 MB) exceed the 128 MiB array: refused on the host with
+    # both sizes in the message, before the array's address is looked up or anything launched
+    lib = vlf.load_library()
+    T, S, H = 131072, 16, 16
+    assert vlf.workspace_bytes(T, S, H) > binding.STATIC_WORKSPACE_BYTES
+    rc = lib.vlf_attend_static(0x1000, 0x2000, 0x3000, 8192, 8192, 0x4000, 0x5000, 512, 256, T,
+                               S, H, 0, 0.125, binding.VLF_BF16, 0x6000, 0x7000, None)
+    msg = lib.vlf_last_error().decode()
+    assert rc == binding.VLF_EINVAL and "exceeds the static array" in msg
+    assert str(vlf.workspace_bytes(T, S, H)) in msg and str(binding.STATIC_WORKSPACE_BYTES) in msg
+    # argument errors of the forward come back the same way
+    rc = lib.vlf_attend_static(0x1000, 0x2000, 0x3000, 64, 60, 0x4000, 0x5000, 4, 64, 100, 2, 0,
+                               0, 0.125, binding.VLF_BF16, 0x6000, 0x7000, None)
+    assert rc == binding.VLF_EINVAL
+    # no work: nothing looked up, nothing launched
+    assert lib.vlf_attend_static(None, None, None, 0, 0, None, None, 0, 64, 0, 0, 2, 0, 0.125,
+                                 binding.VLF_BF16, None, None, None) == binding.VLF_OK
+
+
+def test_static_workspace_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "vlf.h")).read()
+    assert "#define VLF_STATIC_WORKSPACE_BYTES (128LL << 20)" in text
+    assert binding.STATIC_WORKSPACE_BYTES == 128 << 20
+
+
 def test_attend_rotated_needs_a_workspace():
     lib = vlf.load_library()
     rc = lib.vlf_attend_rotated(0x1000, 0x2000, 0x3000, 64, 60, 0x4000, 0x5000, 4, 64, 100, 2,

@@ -23,8 +23,8 @@ HEAD_DIM = 64
 EXPORTS = ("vlf_version", "vlf_last_error", "vlf_tile_count", "vlf_tile_table",
            "vlf_visible_pairs", "vlf_workspace_bytes", "vlf_schedule_rule", "vlf_typical_length",
            "vlf_choose_schedule", "vlf_choose_backward", "vlf_forward_kernel", "vlf_attend",
-           "vlf_rotate_keys", "vlf_attend_rotated", "vlf_backward_workspace_bytes",
-           "vlf_attend_backward", "vlf_rotate_qkv")
+           "vlf_attend_static", "vlf_rotate_keys", "vlf_attend_rotated",
+           "vlf_backward_workspace_bytes", "vlf_attend_backward", "vlf_rotate_qkv")
 
 
 class VlfError(RuntimeError):
@@ -77,6 +77,9 @@ def load_library():
     lib.vlf_attend.restype = ctypes.c_int
     lib.vlf_attend_rotated.argtypes = lib.vlf_attend.argtypes
     lib.vlf_attend_rotated.restype = ctypes.c_int
+    lib.vlf_attend_static.argtypes = [p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32,
+                                      ctypes.c_float, i32, p, p, p]
+    lib.vlf_attend_static.restype = ctypes.c_int
     lib.vlf_rotate_keys.argtypes = [p, p, p, i32, i32, p, i32, i32, i32, i32, p, i64, p]
     lib.vlf_rotate_keys.restype = ctypes.c_int
     lib.vlf_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, p]
@@ -377,6 +380,24 @@ def attend_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: flo
         batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens, batch.sequences, heads,
         int(window), float(scale), code, ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
         launch.cuda_stream))
+
+
+STATIC_WORKSPACE_BYTES = 128 << 20  # include/vlf.h, VLF_STATIC_WORKSPACE_BYTES
+
+
+def attend_static_into(batch: Batch, qkv, cos, sin, heads: int, window: int, scale: float, out,
+                       lse, stream=None):
+    """Queue the forward on the key-tile workspace path with the library's fixed device array
+    as the workspace (include/vlf.h, vlf_attend_static): nothing is allocated, here or in the
+    library. Batches whose workspace exceeds ``STATIC_WORKSPACE_BYTES`` are rejected; calls
+    that overlap in time on one GPU race on the array."""
+    code = _check_inputs(batch, qkv, cos, sin, heads, out, lse)
+    dev = qkv.device
+    _check(load_library().vlf_attend_static(
+        qkv.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0], batch.max_len,
+        batch.cu.data_ptr(), batch.tiles.data_ptr(), batch.num_tiles, batch.br, batch.tokens,
+        batch.sequences, heads, int(window), float(scale), code, out.data_ptr(), lse.data_ptr(),
+        _stream(stream, dev)))
 
 
 def rotate_keys(batch: Batch, qkv, cos, sin, heads: int, workspace, stream=None):

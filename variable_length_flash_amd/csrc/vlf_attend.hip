@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/vlf.h"
 #include "vlf_internal.h"
 
@@ -2866,6 +2868,38 @@ int launch_rotate_qkv_typed(const RotateArgs &a) {
     return VLF_OK;
 }
 }  // namespace
+
+// ---- the forward's key-tile workspace in a fixed device array ---------------------------------
+// For callers that cannot allocate device memory (code under stream capture, serving loops that
+// forbid it): vlf_attend_static runs the workspace path on this array instead of a caller's
+// workspace. Every GPU the library runs on holds its own copy, at its own address, until the
+// process ends. Host code never passes `scratch` itself to a kernel (in host code the name
+// stands for a host-side shadow, not device memory): the device address is looked up once per
+// device, with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[VLF_STATIC_WORKSPACE_BYTES];
+
+int static_scratch(void **ptr) {
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static void *addr[kDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(VLF_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kDevices)
+        return fail(VLF_EUNSUPPORTED, "device %d beyond the %d the library tracks", dev, kDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(VLF_EHIP, "device address of the static workspace on device %d: %s",
+                        dev, hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return VLF_OK;
+}
 
 int64_t backward_workspace_bytes(int32_t T, int32_t S, int32_t H, int32_t br) {
     if (T == 0)

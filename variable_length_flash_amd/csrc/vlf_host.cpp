@@ -383,6 +383,32 @@ int vlf_attend(const void *qkv, const void *cos, const void *sin, int32_t table_
                          workspace ? Launch::kBoth : Launch::kDirect);
 }
 
+int vlf_attend_static(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
+                      int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
+                      int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H,
+                      int32_t window, float scale, int32_t dtype, void *out, float *lse,
+                      void *stream) {
+    if (T < 0 || S < 0 || H < 1 || H > 65536)
+        return fail(VLF_EINVAL, "T = %d, S = %d, H = %d", T, S, H);
+    const int64_t need = workspace_bytes(T, S, H);
+    if (need > VLF_STATIC_WORKSPACE_BYTES)
+        return fail(VLF_EINVAL,
+                    "the key-tile workspace of %lld bytes (T=%d S=%d H=%d) exceeds the static "
+                    "array of %lld bytes; use vlf_attend with a workspace of its own",
+                    (long long)need, T, S, H, (long long)VLF_STATIC_WORKSPACE_BYTES);
+    void *ws = nullptr;
+    int64_t ws_bytes = 0;
+    if (T > 0 && num_tiles > 0) {
+        const int rc = static_scratch(&ws);
+        if (rc)
+            return rc;
+        ws_bytes = VLF_STATIC_WORKSPACE_BYTES;
+    }
+    return attend_common(qkv, cos, sin, table_rows, max_len, cu_dev, tiles_dev, num_tiles, br, T,
+                         S, H, window, scale, dtype, ws, ws_bytes, out, lse, stream,
+                         Launch::kBoth);
+}
+
 int vlf_attend_rotated(const void *qkv, const void *cos, const void *sin, int32_t table_rows,
                        int32_t max_len, const int32_t *cu_dev, const uint32_t *tiles_dev,
                        int32_t num_tiles, int32_t br, int32_t T, int32_t S, int32_t H,

@@ -49,6 +49,10 @@ enum class Launch {
 // Queue the forward kernels; returns a vlf_status.
 int launch_attend(const AttendArgs &a, Launch what);
 
+// The current device's address of the fixed workspace array (VLF_STATIC_WORKSPACE_BYTES),
+// looked up on the first call on that device; returns a vlf_status.
+int static_scratch(void **ptr);
+
 // The backward's arguments after validation; tiles are the tile table for br-row tiles.
 struct BackArgs {
     const void *qkv;
