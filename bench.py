@@ -420,6 +420,17 @@ def run_mfma_peak(args):
           flush=True)
 
 
+def run_overlap(args):
+    """``--overlap``: the overlap probe's loop time per role pair, one JSON line."""
+    import torch
+
+    from variable_length_flash_amd import probe
+    rows = probe.overlap(torch.device("cuda:0"))
+    print(json.dumps({"metric": "overlap probe: shader clocks per iteration of role pairs that "
+                                "share a SIMD (one eight-wave workgroup per CU)",
+                      "unit": "clocks", "pairs": rows}), flush=True)
+
+
 def run_backward(args, w, q, c, s, out, lse, stream):
     """``--backward``: the library's forward once (out, lse), then K timed backward calls
     (include/vlf.h, vlf_attend_backward: delta, back_kv, back_q) on a seeded dout.
@@ -697,6 +708,8 @@ def main():
                     help="skip the matrix probe in the default line")
     ap.add_argument("--mfma-peak", action="store_true",
                     help="run only the matrix probe (sustained bf16 MFMA rate and clock)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run only the overlap probe (matrix, vector and LDS work on one SIMD)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (vlf_attend_backward) instead of the forward")
     ap.add_argument("--causal", action="store_true",
@@ -716,6 +729,9 @@ def main():
         return
     if args.mfma_peak:
         run_mfma_peak(args)
+        return
+    if args.overlap:
+        run_overlap(args)
         return
     run(args)
 

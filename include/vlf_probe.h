@@ -34,6 +34,34 @@ extern "C" {
  */
 int vlf_probe_mfma(int32_t iters, int32_t blocks, uint64_t *record_dev, void *stream);
 
+/*
+ * Queue one launch of the overlap probe: `blocks` workgroups of eight waves; waves 0-3 (one per
+ * SIMD) run role `lo_role` and waves 4-7 (sharing those SIMDs) role `hi_role`, `iters` times:
+ *   0 nothing;
+ *   1 eight v_mfma_f32_32x32x16_bf16 on four independent accumulators (256 matrix clocks);
+ *   2 32 v_exp_f32;  3 32 v_fma_f32 (eight independent chains each);
+ *   4 the softmax of 32 scores per lane as the forward runs it: 32 fma, 32 exp, 32 add into a
+ *     row sum, 16 conversions to bf16 pairs;
+ *   5 roles 1 and 4 in one wave, with 16 products (one 32-row, 64-key attention step);
+ *   6 role 5 with the 16 products' A operands read from LDS (16 KiB per step), each read as
+ *     the compiler places it (just before its product);
+ *   7 role 6 with all 16 reads issued one step ahead of their products;
+ *   8 role 6 with each read issued four products ahead of its own;
+ *   9 role 6's 16 LDS reads alone (16 KiB per wave and iteration);
+ *  10 a 64-row step: role 8's 16 reads, each feeding two products (32 in all), and the softmax
+ *     of 64 scores per lane.
+ * Workgroup b records into record_dev[4b .. 4b + 3] (uint64): the shader-clock and 100 MHz
+ * ticks from the common start to the end of its last wave, then wave 0's and wave 4's own loop
+ * in shader clocks (a SIMD may run the older wave first, so one wave's loop alone does not show
+ * the pair's cost); sink_dev[512 b + thread] receives a checksum. With blocks = the CU count
+ * each CU runs one workgroup, so a pair of roles shares every SIMD. Asynchronous.
+ *   sink_dev    device, 512 * blocks floats.   record_dev  device, 4 * blocks uint64.
+ * Errors: -1 (a role outside 0 .. 10, iters or blocks out of range, null or misaligned
+ * buffers), -3 (launch).
+ */
+int vlf_probe_overlap(int32_t lo_role, int32_t hi_role, int32_t iters, int32_t blocks,
+                      float *sink_dev, uint64_t *record_dev, void *stream);
+
 /* Message for the last non-OK status on the calling thread ("" if none). */
 const char *vlf_probe_last_error(void);
 

@@ -66,6 +66,208 @@ __global__ void __launch_bounds__(256) mfma_probe(int32_t iters, uint64_t *recor
     }
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Byte offset of a lane's first operand in LDS at step i (the step's operands lie 1 KiB apart).
+__device__ __forceinline__ int base_of(int i, int lane) { return (i & 3) * 1024 + lane * 16; }
+
+// One role's loop (see vlf_probe_overlap). Every result feeds the returned checksum, so nothing
+// is dropped; the vector roles carry eight independent chains.
+template <int ROLE>
+__device__ __forceinline__ float role_loop(int iters, int lane, const uint8_t *lds) {
+    u32x4 a = {0x3c003c00u + lane, 0x3b003b00u, 0x3c00u, 0x3a00u}, b = a ^ 0x00010001u;
+    u32x4 a2 = a ^ 0x00020002u, b2 = b ^ 0x00040004u;
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {}, d0 = {}, d1 = {}, d2 = {}, d3 = {};
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        v[k] = -0.01f * (lane + k + 1);
+    float l = 0.f;
+    uint32_t acc = 0;
+    u32x4 ops[16];
+    if constexpr (ROLE == 7 || ROLE == 8 || ROLE == 10) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            ops[k] = *(const u32x4 *)(lds + ((base_of(0, lane) + k * 1024) & 16383));
+    }
+    for (int i = 0; i < iters; ++i) {
+        if constexpr (ROLE == 1 || ROLE == 5) {
+            c0 = mma(a, b, c0); c1 = mma(b, a, c1); c2 = mma(a2, b2, c2); c3 = mma(b2, a2, c3);
+            c0 = mma(a2, b, c0); c1 = mma(b2, a, c1); c2 = mma(a, b2, c2); c3 = mma(b, a2, c3);
+        }
+        if constexpr (ROLE == 5) {
+            c0 = mma(a, b2, c0); c1 = mma(b, a2, c1); c2 = mma(a2, b, c2); c3 = mma(b2, a, c3);
+            c0 = mma(a2, b2, c0); c1 = mma(b2, a2, c1); c2 = mma(a, b, c2); c3 = mma(b, a, c3);
+        }
+        if constexpr (ROLE == 6) {
+            // 16 products whose A operands come from LDS, one 16-byte read each
+            const int base = base_of(i, lane);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const u32x4 op = *(const u32x4 *)(lds + ((base + k * 1024) & 16383));
+                f32x16 &c = (k & 3) == 0 ? c0 : (k & 3) == 1 ? c1 : (k & 3) == 2 ? c2 : c3;
+                c = mma(op, b, c);
+            }
+        }
+        if constexpr (ROLE == 7) {
+            // the same 16 LDS operands, all read one step ahead of their products
+            const int nbase = ((i + 1) & 3) * 1024 + lane * 16;
+            u32x4 nxt[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                nxt[k] = *(const u32x4 *)(lds + ((nbase + k * 1024) & 16383));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                f32x16 &c = (k & 3) == 0 ? c0 : (k & 3) == 1 ? c1 : (k & 3) == 2 ? c2 : c3;
+                c = mma(ops[k], b, c);
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                ops[k] = nxt[k];
+        }
+        if constexpr (ROLE == 8) {
+            // the same 16 LDS operands, each read four products ahead of its own
+            const int nbase = ((i + 1) & 3) * 1024 + lane * 16;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                f32x16 &c = (k & 3) == 0 ? c0 : (k & 3) == 1 ? c1 : (k & 3) == 2 ? c2 : c3;
+                c = mma(ops[k & 3], b, c);
+                const int off = k < 12 ? base_of(i, lane) + (k + 4) * 1024 : nbase + (k - 12) * 1024;
+                ops[k & 3] = *(const u32x4 *)(lds + (off & 16383));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if constexpr (ROLE == 9) {
+            // the 16 LDS reads alone, all issued before the first is used
+            u32x4 r[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                r[k] = *(const u32x4 *)(lds + ((base_of(i, lane) + k * 1024) & 16383));
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                acc ^= r[k][0] ^ r[k][1] ^ r[k][2] ^ r[k][3];
+        }
+        if constexpr (ROLE == 10) {
+            // a 64-row step: every operand read (four products ahead) feeds two products, one
+            // per 32-row block, and the softmax covers 64 scores per lane
+            const int nbase = ((i + 1) & 3) * 1024 + lane * 16;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                f32x16 &c = (k & 3) == 0 ? c0 : (k & 3) == 1 ? c1 : (k & 3) == 2 ? c2 : c3;
+                f32x16 &d = (k & 3) == 0 ? d0 : (k & 3) == 1 ? d1 : (k & 3) == 2 ? d2 : d3;
+                c = mma(ops[k & 3], b, c);
+                d = mma(ops[k & 3], b2, d);
+                const int off = k < 12 ? base_of(i, lane) + (k + 4) * 1024 : nbase + (k - 12) * 1024;
+                ops[k & 3] = *(const u32x4 *)(lds + (off & 16383));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if constexpr (ROLE == 2) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    v[k] = __builtin_amdgcn_exp2f(v[k]);
+        }
+        if constexpr (ROLE == 3) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    v[k] = __builtin_fmaf(v[k], 0.999f, -0.001f);
+        }
+        if constexpr (ROLE >= 4 && ROLE != 9) {
+            // the softmax of 32 scores per lane (64 for the 64-row step): fma, exp2, row-sum
+            // add, bf16 pair conversion
+#pragma unroll
+            for (int r = 0; r < (ROLE == 10 ? 8 : 4); ++r) {
+                float e[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], 1.4427f, -0.5f));
+                    l += e[k];
+                }
+                asm volatile("" : "+v"(l));
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    acc ^= pack2(e[2 * k], e[2 * k + 1]);
+                v[r & 7] += __uint_as_float(acc & 0x3f800000u) * 1e-9f;
+            }
+        }
+    }
+    float s = l + __uint_as_float(acc);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        s += c0[k] + c1[k] + c2[k] + c3[k] + d0[k] + d1[k] + d2[k] + d3[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        s += v[k];
+    if constexpr (ROLE == 7 || ROLE == 8 || ROLE == 10) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            s += __uint_as_float(ops[k][0] & 0x3fffffffu);
+    }
+    return s;
+}
+
+template <int ROLE>
+__device__ __forceinline__ float run_role(int iters, int lane, const uint8_t *lds) {
+    return role_loop<ROLE>(iters, lane, lds);
+}
+
+__device__ __forceinline__ float dispatch_role(int role, int iters, int lane, const uint8_t *lds) {
+    switch (role) {
+    case 1: return run_role<1>(iters, lane, lds);
+    case 2: return run_role<2>(iters, lane, lds);
+    case 3: return run_role<3>(iters, lane, lds);
+    case 4: return run_role<4>(iters, lane, lds);
+    case 5: return run_role<5>(iters, lane, lds);
+    case 6: return run_role<6>(iters, lane, lds);
+    case 7: return run_role<7>(iters, lane, lds);
+    case 8: return run_role<8>(iters, lane, lds);
+    case 9: return run_role<9>(iters, lane, lds);
+    case 10: return run_role<10>(iters, lane, lds);
+    default: return 0.f;
+    }
+}
+
+__global__ void __launch_bounds__(512) overlap_probe(int32_t lo_role, int32_t hi_role,
+                                                     int32_t iters, float *sink,
+                                                     uint64_t *record) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[16384];
+    for (int i = threadIdx.x; i < 4096; i += 512)
+        ((uint32_t *)lds)[i] = 0x3c003c00u ^ (i & 0x00ff00ffu);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __syncthreads();
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    const float s = dispatch_role(wave < 4 ? lo_role : hi_role, iters, lane, lds);
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    sink[blockIdx.x * 512 + threadIdx.x] = s;
+    uint64_t *rec = record + 4 * (uint64_t)blockIdx.x;
+    if (threadIdx.x == 256)
+        rec[3] = t1 - t0;  // wave 4's own loop
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint64_t t2 = __builtin_amdgcn_s_memtime(), r2 = __builtin_amdgcn_s_memrealtime();
+        rec[0] = t2 - t0;  // both halves, to the last wave's end
+        rec[1] = r2 - r0;
+        rec[2] = t1 - t0;  // wave 0's own loop
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,6 +282,26 @@ int vlf_probe_mfma(int32_t iters, int32_t blocks, uint64_t *record_dev, void *st
     void *args[] = {(void *)&iters, (void *)&record_dev};
     const hipError_t e = hipLaunchKernel((const void *)mfma_probe, dim3((unsigned)blocks),
                                          dim3(256), args, 0, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(-3, "probe launch failed: %s", hipGetErrorString(e));
+    return 0;
+}
+
+int vlf_probe_overlap(int32_t lo_role, int32_t hi_role, int32_t iters, int32_t blocks,
+                      float *sink_dev, uint64_t *record_dev, void *stream) {
+    if (lo_role < 0 || lo_role > 10 || hi_role < 0 || hi_role > 10)
+        return fail(-1, "roles %d, %d outside 0 .. 10", lo_role, hi_role);
+    if (iters < 1 || iters > (1 << 24))
+        return fail(-1, "iters = %d outside 1 .. 2^24", iters);
+    if (blocks < 1 || blocks > (1 << 20))
+        return fail(-1, "blocks = %d outside 1 .. 2^20", blocks);
+    if (!sink_dev || ((uintptr_t)sink_dev & 3) != 0 || !record_dev ||
+        ((uintptr_t)record_dev & 7) != 0)
+        return fail(-1, "null or misaligned sink_dev / record_dev");
+    void *args[] = {(void *)&lo_role, (void *)&hi_role, (void *)&iters, (void *)&sink_dev,
+                    (void *)&record_dev};
+    const hipError_t e = hipLaunchKernel((const void *)overlap_probe, dim3((unsigned)blocks),
+                                         dim3(512), args, 0, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail(-3, "probe launch failed: %s", hipGetErrorString(e));
     return 0;

@@ -1,5 +1,6 @@
 """ctypes binding of libvlf_probe.so (include/vlf_probe.h): the matrix-unit probe the benchmark
-sets the forward's rate against. It is not part of the attention path."""
+sets the forward's rate against, and the overlap probe that measures how the matrix unit, the
+vector unit and LDS operand reads share a SIMD. It is not part of the attention path."""
 from __future__ import annotations
 
 import ctypes
@@ -7,7 +8,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libvlf_probe.so")
-EXPORTS = ("vlf_probe_mfma", "vlf_probe_last_error")
+EXPORTS = ("vlf_probe_mfma", "vlf_probe_overlap", "vlf_probe_last_error")
 FLOP_PER_MFMA = 32 * 32 * 16 * 2  # v_mfma_f32_32x32x16_bf16
 
 _lib = None
@@ -23,6 +24,8 @@ def load_library():
         lib.vlf_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p]
         lib.vlf_probe_mfma.restype = ctypes.c_int
+        lib.vlf_probe_overlap.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
+        lib.vlf_probe_overlap.restype = ctypes.c_int
         lib.vlf_probe_last_error.argtypes = []
         lib.vlf_probe_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -75,3 +78,44 @@ def mfma_peak(device, iters: int = 20000, reps: int = 3):
             "clocks_per_mfma": round(per_mfma, 2), "ms": round(best, 4),
             "workgroup_ms_median": round(wg_ms, 4), "cus": cus, "workgroups": blocks,
             "instruction": "v_mfma_f32_32x32x16_bf16"}
+
+
+ROLES = {0: "idle", 1: "mfma", 2: "exp", 3: "fma", 4: "softmax", 5: "step", 6: "step_lds",
+         7: "step_lds_step_ahead", 8: "step_lds_four_ahead", 9: "lds_reads",
+         10: "step64_lds_four_ahead"}
+# the pairs whose loop times describe the forward's wave step: each role alone (its partner
+# idle), then side by side on one SIMD
+OVERLAP_PAIRS = ((1, 0), (2, 0), (3, 0), (4, 0), (1, 1), (2, 2), (3, 3), (4, 4), (1, 2), (1, 4),
+                 (5, 0), (5, 5), (6, 0), (6, 6), (7, 0), (7, 7), (8, 0), (8, 8), (9, 0), (9, 9), (10, 0), (10, 10))
+
+
+def overlap(device, pairs=OVERLAP_PAIRS, iters: int = 4000):
+    """Loop time of the overlap probe (vlf_probe_overlap) for each (lo, hi) role pair, one
+    eight-wave workgroup per CU so that waves 0-3 and 4-7 pair up on the four SIMDs. Returns a
+    list of dicts: the roles, shader clocks per iteration from the common start to the last
+    wave's end and of each half's own loop (medians over workgroups), and the clock. A role's clocks per iteration alone, against two of it side by
+    side and against a pair of different roles, says how far the two units overlap."""
+    import torch
+    lib = load_library()
+    dev = torch.device(device)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(512 * cus, dtype=torch.float32, device=dev)
+    record = torch.zeros(4 * cus, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = []
+    for lo, hi in pairs:
+        for _ in range(2):  # the first launch warms the clock and the code
+            rc = lib.vlf_probe_overlap(int(lo), int(hi), int(iters), int(cus), sink.data_ptr(),
+                                       record.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(lib.vlf_probe_last_error().decode())
+        torch.cuda.synchronize(dev)
+        rec = record.view(cus, 4).cpu().double()
+        med = [float(rec[:, k].median()) for k in range(4)]
+        ghz = float((rec[:, 0] / (rec[:, 1] / 100e6)).median()) / 1e9
+        out.append({"lo": ROLES[lo], "hi": ROLES[hi],
+                    "clocks_per_iter": round(med[0] / iters, 1),
+                    "lo_clocks_per_iter": round(med[2] / iters, 1),
+                    "hi_clocks_per_iter": round(med[3] / iters, 1),
+                    "clock_ghz": round(ghz, 3)})
+    return out
