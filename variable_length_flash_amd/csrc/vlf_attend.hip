@@ -2304,6 +2304,41 @@ __device__ __forceinline__ bool back_full(int q0, int k0, int len, int back, int
     return q0 + 32 <= len && k0 + 32 <= len && q0 + 31 - k0 <= back && k0 + 31 - q0 <= ahead;
 }
 
+// The steps [fa, fb) of a sweep whose 64 streamed rows (it = a + 64 st, two 32-row blocks) and
+// the 32-row block at b0 are visible in every pair, for a sweep of `steps` steps: an interval of
+// st, since each condition of back_full bounds it on one side. Streamed rows are queries when
+// Q is true (back_kv: b0 is the wave's key block), keys otherwise (back_q: b0 its query block).
+// The bounds are taken in 64 bits (a reach may be INT32_MAX) and then checked with back_full
+// itself, so a step outside [fa, fb) is only ever masked when it need not be.
+template <bool Q>
+__device__ __forceinline__ void full_steps(int a, int steps, int b0, int len, int back, int ahead,
+                                           int &fa, int &fb) {
+    // streamed block x and fixed block b0: x + 32 <= len, b0 + 32 <= len, and the offset
+    // x - b0 (queries minus keys) within [-ahead + 31, back - 31] when Q, swapped otherwise
+    auto full = [&](int st) {
+        const int x = a + BS * st;
+        return Q ? back_full(x, b0, len, back, ahead) && back_full(x + 32, b0, len, back, ahead)
+                 : back_full(b0, x, len, back, ahead) && back_full(b0, x + 32, len, back, ahead);
+    };
+    const int64_t hi_q = Q ? (int64_t)b0 + back - 63 : (int64_t)b0 + ahead - 63;
+    const int64_t lo_q = Q ? (int64_t)b0 + 31 - ahead : (int64_t)b0 + 31 - back;
+    const int64_t top = min((int64_t)len - 64, hi_q);  // largest streamed start that fits
+    int64_t lo = lo_q - a <= 0 ? 0 : (lo_q - a + BS - 1) / BS;
+    int64_t hi = top - a < 0 ? 0 : (top - a) / BS + 1;
+    if (b0 + 32 > len)
+        hi = 0;
+    lo = min(lo, (int64_t)steps);
+    hi = min(hi, (int64_t)steps);
+    int f0 = (int)lo, f1 = (int)max(lo, hi);
+    while (f0 < f1 && !full(f0))
+        ++f0;
+    while (f1 > f0 && !full(f1 - 1))
+        --f1;
+    if (f0 >= f1)
+        f0 = f1 = steps;
+    fa = f0, fb = f1;
+}
+
 // Buffer resource over rows [r0, len) of a [*, ld] tensor from column col: rows past the
 // sequence read as zeros. Offsets stay below 64 rows, so 32 bits hold them.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t back_rows(const uint16_t *base, int64_t ld,
@@ -2492,7 +2527,11 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         ring_barrier<0>();
 
     f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
-    for (int st = 0; st < steps; ++st) {
+    // One step: the copy SL - 1 steps ahead, the products of step st (unless the wave is idle),
+    // the ring wait. The masked and unmasked steps run in loops of their own (below): with both
+    // bodies behind a branch in one loop the compiler gives the accumulators different
+    // registers in the two and copies all of them at the join, every step.
+    auto step = [&](int st, auto masked) __attribute__((always_inline)) {
         const int it = qa + st * BS;
         const bool more = st + SL - 1 < steps;
         if (more)
@@ -2502,8 +2541,8 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
             const uint8_t *os = qs + 3 * IMG;
             const float *nl = (const float *)(qs + 4 * IMG), *nd = nl + 64;
             // both 32-row blocks in one stretch, so that the softmax of one overlaps the
-            // products of the other; steps every pair of which is visible skip the mask
-            auto body = [&](auto masked) {
+            // products of the other
+            {
                 constexpr bool MASK = decltype(masked)::value;
                 f32x16 sc[2], dp[2];
 #pragma unroll
@@ -2541,18 +2580,23 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
                         dk1 = E::mfma(*(const u32x4 *)(qt + f1), pd[kc], dk1);
                     }
                 }
-            };
-            if (back_full(it, kw0, len, back, ahead) && back_full(it + 32, kw0, len, back, ahead))
-                body(Masked<false>{});
-            else
-                body(Masked<true>{});
+            }
         }
         // the next step's copies have landed (later steps' may still be in flight)
         if (more)
             ring_barrier<PIECES * (SL - 2)>();
         else
             ring_barrier<0>();
-    }
+    };
+    // steps [fa, fb) see every pair of the wave's keys and skip the mask
+    int fa, fb;
+    full_steps<true>(qa, steps, kw0, len, back, ahead, fa, fb);
+    for (int st = 0; st < fa; ++st)
+        step(st, Masked<true>{});
+    for (int st = fa; st < fb; ++st)
+        step(st, Masked<false>{});
+    for (int st = fb; st < steps; ++st)
+        step(st, Masked<true>{});
 
     // dK rotated back to the key's position, and dV; register i of block b holds dim
     // 32b + 8(i/4) + 4g + i%4 of key kj
@@ -2674,25 +2718,28 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         ring_barrier<0>();
 
     f32x16 dq0 = {}, dq1 = {};
-    for (int st = 0; st < steps; ++st) {
-        const int jt = ka + st * BS;
-        const bool more = st + SL - 1 < steps;
+    // One step (see back_kv: masked and unmasked steps run in loops of their own)
+    auto step = [&](int st_i, auto masked) __attribute__((always_inline)) {
+        const int jt = ka + st_i * BS;
+        const bool more = st_i + SL - 1 < steps;
         if (more)
-            copy(jt + (SL - 1) * BS, (st + SL - 1) % SL);
+            copy(jt + (SL - 1) * BS, (st_i + SL - 1) % SL);
         if (!idle) {
-            const uint8_t *ks = lds + (st % SL) * SLOT, *kt = ks + IMG, *vs = ks + 2 * IMG;
-            auto body = [&](auto masked) {
+            const uint8_t *ks = lds + (st_i % SL) * SLOT, *kt = ks + IMG, *vs = ks + 2 * IMG;
+            {
                 constexpr bool MASK = decltype(masked)::value;
                 f32x16 st[2], dp[2];
 #pragma unroll
                 for (int kb2 = 0; kb2 < 2; ++kb2) {
-                    // S^T - lse and dP^T - delta of keys jt + 32kb2 + 8(i/4) + 4g + i%4
-                    st[kb2] = nlv, dp[kb2] = ndv;
+                    // S^T - lse and dP^T - delta of keys jt + 32kb2 + 8(i/4) + 4g + i%4: the
+                    // first products add to -lse and -delta (nlv and ndv stay as they are)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int off = (32 * kb2 + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
-                        st[kb2] = E::mfma(*(const u32x4 *)(ks + off), qop[c], st[kb2]);
-                        dp[kb2] = E::mfma(*(const u32x4 *)(vs + off), oop[c], dp[kb2]);
+                        st[kb2] = E::mfma(*(const u32x4 *)(ks + off), qop[c],
+                                          c == 0 ? nlv : st[kb2]);
+                        dp[kb2] = E::mfma(*(const u32x4 *)(vs + off), oop[c],
+                                          c == 0 ? ndv : dp[kb2]);
                     }
                 }
 #pragma unroll
@@ -2710,17 +2757,22 @@ back_q(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
                             pd[kc], dq1);
                     }
                 }
-            };
-            if (back_full(qw0, jt, len, back, ahead) && back_full(qw0, jt + 32, len, back, ahead))
-                body(Masked<false>{});
-            else
-                body(Masked<true>{});
+            }
         }
         if (more)
             ring_barrier<PIECES * (SL - 2)>();
         else
             ring_barrier<0>();
-    }
+    };
+    // steps [fa, fb) see every pair of the wave's rows and skip the mask
+    int fa, fb;
+    full_steps<false>(ka, steps, qw0, len, back, ahead, fa, fb);
+    for (int st_i = 0; st_i < fa; ++st_i)
+        step(st_i, Masked<true>{});
+    for (int st_i = fa; st_i < fb; ++st_i)
+        step(st_i, Masked<false>{});
+    for (int st_i = fb; st_i < steps; ++st_i)
+        step(st_i, Masked<true>{});
 
     // dQ rotated back to the row's position (the transpose of the half-split rotation) and
     // scaled; register i of block b holds dim 32b + 8(i/4) + 4g + i%4 of row qi
