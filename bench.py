@@ -35,7 +35,11 @@ Other modes:
   --counters DIR ...   read rocprofv3 --pmc directories (any counters) and print, for one
                        kernel, each counter's average per dispatch with the derived matrix,
                        vector and LDS figures;
-  --mfma-peak          the matrix probe alone.
+  --trace DIR          read a rocprofv3 --kernel-trace --stats directory and print the kernel
+                       summary for profiles/ (per kernel: calls, total, average, min, max, and
+                       the average over the last --steps dispatches, the timed ones);
+  --mfma-peak          the matrix probe alone;
+  --overlap            the overlap probe alone (matrix, vector and LDS work sharing a SIMD).
 """
 from __future__ import annotations
 
@@ -605,6 +609,54 @@ def summarize(directories, workload: str, kernel: str):
     print(f"hbm_bytes_per_launch: {fetch + write:.0f}")
 
 
+def _short_kernel_name(name: str) -> str:
+    """'void ns::(anonymous namespace)::back_kv<ns::(anonymous namespace)::BF16, 4, 2, false>(...)'
+    -> 'back_kv<BF16, 4, 2, false>'."""
+    import re
+    name = re.sub(r"^void ", "", name)
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # drop the argument list: the first '(' outside <...>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not name.startswith("(anonymous", i):
+            cut = i
+            break
+    name = name[:cut]
+    return re.sub(r"[A-Za-z_0-9]+::\(anonymous namespace\)::", "", name)
+
+
+def trace_summary(directories, timed: int):
+    """Per-kernel summary of rocprofv3 --kernel-trace --stats directories: the stats table and
+    each kernel's average over its last ``timed`` dispatches (the timed steps)."""
+    stats, per = [], {}
+    for directory in directories:
+        for path in glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True):
+            with open(path) as f:
+                stats.extend(csv.DictReader(f))
+        for path in glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    per.setdefault(_short_kernel_name(r["Kernel_Name"]), []).append(
+                        (int(r["Dispatch_Id"]),
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {directories}")
+    print(f"kernel_source_sha256_16: {kernel_hash()}")
+    print("kernel | calls | total_ms | average_us | min_us | max_us | percent")
+    for r in stats:
+        print(f"{_short_kernel_name(r['Name'])} | {r['Calls']} | "
+              f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.2f}")
+    print(f"# average over the last {timed} dispatches of each kernel (the timed steps)")
+    for name, rows in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        rows.sort()
+        last = [d for _, d in rows[-timed:]]
+        print(f"{name} | timed_average_us {sum(last) / len(last):.2f} | over {len(last)}")
+
+
 def _kernel_rows(directories, kernel: str):
     """Per-dispatch sums of every counter of ``kernel`` in rocprofv3 --pmc directories."""
     import re
@@ -720,12 +772,18 @@ def main():
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", nargs="+")
     ap.add_argument("--counters", metavar="DIR", nargs="+")
+    ap.add_argument("--trace", metavar="DIR", nargs="+",
+                    help="summarize rocprofv3 --kernel-trace --stats output (last --steps "
+                         "dispatches of each kernel are the timed ones)")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.workload, args.kernel)
         return
     if args.counters:
         counters(args.counters, args.workload, args.kernel)
+        return
+    if args.trace:
+        trace_summary(args.trace, args.steps)
         return
     if args.mfma_peak:
         run_mfma_peak(args)
