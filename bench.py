@@ -190,7 +190,8 @@ class Forward:
         import variable_length_flash_amd as vlf
         self.vlf, self.w, self.dev = vlf, w, dev
         self.batch = vlf.prepare(w.cu, dev, br, prerotate, w.window)
-        self.kernel = vlf.forward_kernel(self.batch.br, self.batch.prerotate, w.window)
+        self.kernel = vlf.forward_kernel(self.batch.br, self.batch.prerotate, w.window,
+                                         self.batch.max_len)
         self.q, self.c, self.s = qkv.to(dev), cos.to(dev), sin.to(dev)
         self.out = torch.empty((w.tokens, w.heads * 64), dtype=self.q.dtype, device=dev)
         self.lse = torch.empty((w.heads, w.tokens), dtype=torch.float32, device=dev)

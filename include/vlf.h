@@ -56,7 +56,7 @@ enum vlf_dtype {
 /* Flag ORed into `window` for the causal sliding window (see the conventions above). */
 #define VLF_CAUSAL 0x40000000
 
-/* Library ABI version (this header: 4). */
+/* Library ABI version (this header: 5). */
 int32_t vlf_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). The pointer
@@ -122,8 +122,9 @@ int vlf_workspace_bytes(int32_t T, int32_t S, int32_t H, int64_t *bytes);
  *   window      as in vlf_attend.
  *   br_request  0: choose the tile height; 64, 128 or 256: take it and choose only the path.
  *   br          out: 64 when no sequence is longer than 64 (one key tile per query tile);
- *               256 under a window the direct path keeps in LDS (vlf_forward_kernel names
- *               attend_slide) once typical >= 256; 128 under other windows of at most 512;
+ *               256 once typical >= 256 where the direct path keeps every key a 256-row tile
+ *               reaches in LDS (vlf_forward_kernel names attend_slide: a window of at most
+ *               eight key tiles, or max_len <= 512); 128 under other windows of at most 512;
  *               for wider or full windows 256 once typical >= 448, else 128.
  *   prerotate   out: 1 to rotate keys once into a workspace (vlf_attend with a workspace),
  *               0 for the direct path. 1 when a query tile's key span (typical, or
@@ -170,14 +171,15 @@ int vlf_choose_backward(const int32_t *cu_host, int32_t S, int32_t T, int32_t H,
                         int32_t *br, int64_t *workspace_bytes);
 
 /*
- * Name of the forward kernel vlf_attend launches for a tile height, path and window (the
- * key-tile kernel prep_tiles runs before it when prerotate is 1): "attend_pre_ph" (workspace,
- * 256 rows), "attend_pre" (workspace, 64 or 128 rows), "attend_slide" (direct, 256 rows, a window
- * of at most eight key tiles kept in LDS: 1 <= W <= 129, or causal 1 <= W <= 257), "attend_one"
+ * Name of the forward kernel vlf_attend launches for a tile height, path, window and longest
+ * sequence (the key-tile kernel prep_tiles runs before it when prerotate is 1): "attend_pre_ph"
+ * (workspace, 256 rows), "attend_pre" (workspace, 64 or 128 rows), "attend_slide" (direct, 256
+ * rows, every key a tile reaches kept in an LDS ring of eight key tiles: a window with
+ * 1 <= W <= 129, or causal 1 <= W <= 257, or any window when max_len <= 512), "attend_one"
  * (direct, 64 rows) or "attend_fwd" (direct, 128 or 256 rows); "" for a tile height the library
- * does not run or a negative window. A static string.
+ * does not run, a negative window or a negative max_len. A static string.
  */
-const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window);
+const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window, int32_t max_len);
 
 /*
  * The forward pass (hanzo-kernel 0.2.42 src/packed.rs, `attend`): for each tile in tiles_dev

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_function():
     lib = vlf.load_library()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.vlf_version() == 4
+    assert lib.vlf_version() == 5
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -286,14 +286,16 @@ def test_attend_rotated_needs_a_workspace():
 
 
 @pytest.mark.parametrize("max_len,window,typical,br", [
-    (1, 0, None, 64), (64, 0, None, 64), (65, 0, None, 128), (447, 0, None, 128),
-    (448, 0, None, 256), (8192, 0, None, 256), (8192, 512, None, 128),
+    (1, 0, None, 64), (64, 0, None, 64), (65, 0, None, 128), (255, 0, None, 128),
+    (513, 0, 447.0, 128), (513, 0, 448.0, 256), (8192, 0, None, 256), (8192, 512, None, 128),
     (8192, 513, None, 256), (64, 128, None, 64),
     # windows of at most 129 keys: 256-row tiles on the key ring once sequences fill them
     (8192, 1, None, 256), (8192, 128, None, 256), (8192, 129, None, 256), (8192, 130, None, 128),
     (8192, 128, 255.0, 128), (300, 128, 256.0, 256),
+    # sequences of at most 512 tokens fit the key ring whole: 256-row tiles once typical >= 256
+    (256, 0, None, 256), (447, 0, None, 256), (512, 0, 343.0, 256), (512, 600, 300.0, 256),
     # the typical length decides, not the longest sequence
-    (512, 0, 343.0, 128), (512, 0, 512.0, 256), (8192, 0, 300.0, 128), (65, 0, 30.0, 128)])
+    (600, 0, 343.0, 128), (512, 0, 512.0, 256), (8192, 0, 300.0, 128), (65, 0, 30.0, 128)])
 def test_choose_br(max_len, window, typical, br):
     assert vlf.choose_br(max_len, window, typical) == br
 
@@ -341,7 +343,7 @@ def test_choose_schedule_of_the_workloads(name):
     assert max_len == max(w.lens)
     assert (br, pre) == vlf.schedule_rule(max_len, vlf.typical_length(w.cu), w.window)[:2]
     assert ws == (vlf.workspace_bytes(w.tokens, w.sequences, w.heads) if pre else 0)
-    want = {"tiny": (128, False), "encoder": (128, False), "sliding": (256, False),
+    want = {"tiny": (128, False), "encoder": (256, False), "sliding": (256, False),
             "many_short": (64, False), "long": (256, True)}[name]
     assert (br, pre) == want
     bbr, bws = vlf.choose_backward(w.cu, w.heads, w.window)
@@ -358,6 +360,26 @@ def test_choose_schedule_of_the_workloads(name):
     (128, False, -1, "")])
 def test_forward_kernel_names(br, pre, window, name):
     assert vlf.forward_kernel(br, pre, window) == name
+
+
+@pytest.mark.parametrize("br,pre,window,max_len,name", [
+    (256, False, 0, 512, "attend_slide"), (256, False, 0, 513, "attend_fwd"),
+    (256, False, 0 | vlf.CAUSAL, 512, "attend_slide"), (256, False, 600, 300, "attend_slide"),
+    (256, False, 600, 1000, "attend_fwd"), (256, False, 100, 100000, "attend_slide"),
+    (256, True, 0, 512, "attend_pre_ph"), (128, False, 0, 512, "attend_fwd"),
+    (64, False, 0, 64, "attend_one"), (256, False, 0, -1, "")])
+def test_forward_kernel_names_by_longest_sequence(br, pre, window, max_len, name):
+    # a batch whose sequences all fit eight key tiles keeps each one's whole key range in the
+    # ring of attend_slide, whatever the window
+    assert vlf.forward_kernel(br, pre, window, max_len) == name
+
+
+@pytest.mark.parametrize("max_len,typical,window,want", [
+    (512, 256.0, 0, (256, 0)), (512, 255.9, 0, (128, 0)), (513, 400.0, 0, (128, 1)),
+    (512, 300.0, 300, (256, 0)), (1000, 300.0, 300, (128, 0)), (512, 512.0, 0 | vlf.CAUSAL, (256, 0))])
+def test_rule_takes_the_ring_for_sequences_of_at_most_eight_tiles(max_len, typical, window, want):
+    br, pre, _ = vlf.schedule_rule(max_len, typical, window)
+    assert (br, int(pre)) == want
 
 
 def test_schedule_calls_reject_bad_arguments():

@@ -461,6 +461,25 @@ def test_window_runs_keep_keys(dtype, window):
     compare(f"window runs {dtype} W={window}", w, out, lse, qkv, cos, sin)
 
 
+# sequences of at most 512 tokens: every length class around the eight-tile ring's edges
+WHOLE_LENS = [512, 1, 0, 63, 64, 65, 255, 256, 257, 511, 300, 512, 129, 2, 448, 77] * 6
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("window", [0, 1, 100, 130, 300, 600, 0 | vlf.CAUSAL, 200 | vlf.CAUSAL])
+def test_whole_sequences_in_the_key_ring(dtype, window):
+    """No sequence longer than 512 tokens: the direct path at 256 rows keeps each (sequence,
+    head)'s whole key range in attend_slide's eight-tile ring, under any window (wider ones
+    than the ring's window bound included). The library names attend_slide for the batch;
+    every row of 96 sequences x 12 heads is compared."""
+    w = workloads.custom(WHOLE_LENS, 12, dtype=dtype, window=window, table_rows=512, seed=59)
+    assert vlf.forward_kernel(256, False, window, max(w.lens)) == "attend_slide"
+    qkv, cos, sin = inputs(w)
+    _say(f"case whole sequences in the key ring {dtype} W={window:#x}")
+    out, lse = run_gpu(w, qkv, cos, sin, br=256, prerotate=False)
+    compare(f"whole sequences in the ring {dtype} W={window:#x}", w, out, lse, qkv, cos, sin)
+
+
 @pytest.mark.parametrize("window", [1, 65])
 def test_window_runs_past_the_descriptor_cache(window):
     """20000 one-token sequences among longer ones, 2 heads: about 160 items per workgroup of

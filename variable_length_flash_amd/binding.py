@@ -70,7 +70,7 @@ def load_library():
     lib.vlf_choose_schedule.restype = ctypes.c_int
     lib.vlf_choose_backward.argtypes = [p, i32, i32, i32, i32, p, p]
     lib.vlf_choose_backward.restype = ctypes.c_int
-    lib.vlf_forward_kernel.argtypes = [i32, i32, i32]
+    lib.vlf_forward_kernel.argtypes = [i32, i32, i32, i32]
     lib.vlf_forward_kernel.restype = ctypes.c_char_p
     lib.vlf_attend.argtypes = [p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32,
                                ctypes.c_float, i32, p, i64, p, p, p]
@@ -180,10 +180,10 @@ def choose_br(max_len: int, window: int = 0, typical: float | None = None) -> in
     return schedule_rule(max_len, max_len if typical is None else typical, window)[0]
 
 
-def choose_prerotate(length: float, br: int, window: int = 0) -> bool:
+def choose_prerotate(length: float, br: int, window: int = 0, max_len: int = 0x7fffffff) -> bool:
     """Whether the library's rule takes the key-tile workspace at tile height ``br`` for a batch
-    of typical length ``length``."""
-    return schedule_rule(0, length, window, br)[1]
+    of typical length ``length`` (and longest sequence ``max_len``, unbounded by default)."""
+    return schedule_rule(max_len, length, window, br)[1]
 
 
 def choose_backward_br(typical: float) -> int:
@@ -215,10 +215,11 @@ def choose_backward(cu, heads: int, window: int = 0):
     return b.value, int(ws.value)
 
 
-def forward_kernel(br: int, prerotate: bool, window: int = 0) -> str:
-    """Name of the forward kernel the library launches for this schedule
-    (vlf_forward_kernel)."""
-    return load_library().vlf_forward_kernel(int(br), int(bool(prerotate)), int(window)).decode()
+def forward_kernel(br: int, prerotate: bool, window: int = 0, max_len: int = 0x7fffffff) -> str:
+    """Name of the forward kernel the library launches for this schedule and longest sequence
+    (vlf_forward_kernel; the default max_len names the kernel for any sequence length)."""
+    return load_library().vlf_forward_kernel(int(br), int(bool(prerotate)), int(window),
+                                             int(max_len)).decode()
 
 
 CAUSAL = 0x40000000  # ORed into a window: the causal sliding window (include/vlf.h, VLF_CAUSAL)

@@ -1586,6 +1586,9 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
 // ---- windows that fit in LDS: query tiles walked in table order, keys kept between them -------
 // With a window of at most 129 keys, the keys that a 256-row query tile reaches span at most
 // eight 64-key tiles, and the next query tile of the same sequence shares all but four of them.
+// attend_slide serves 256-row tiles whose reached keys span at most eight key tiles: a window of
+// at most 129 keys (causal: 257), or any window over sequences of at most 512 tokens, whose
+// whole key range then fits the ring.
 // attend_slide runs one 8-wave workgroup per CU over a contiguous run of the (head, tile) items:
 // an 8-slot LDS ring holds the current item's key tiles (key tile u of the sequence in slot
 // u % 8, as block images), each new key tile is rotated and staged once per run instead of once
@@ -2982,7 +2985,7 @@ int launch_attend(const AttendArgs &a, Launch what) {
     // rows) plus a tile past it to be reachable with a 31-bit byte offset.
     const int64_t rows = (int64_t)(a.table_rows < a.T ? a.table_rows : a.T) + 2 * BC;
     const bool fixed = rows * 3 * a.H * D * 2 < ((int64_t)1 << 31);
-    if (a.br == 256 && ring_fits(a.back, a.ahead)) {
+    if (a.br == 256 && ring_holds(a.back, a.ahead, a.max_len)) {
         if (bf)
             return fixed ? launch_slide<BF16, true>(a) : launch_slide<BF16, false>(a);
         return fixed ? launch_slide<F16, true>(a) : launch_slide<F16, false>(a);

@@ -73,6 +73,10 @@ bool ring_fits(int32_t back, int32_t ahead) {
     return (behind + 256 + ahead + 63) / 64 <= 8;
 }
 
+bool ring_holds(int32_t back, int32_t ahead, int32_t max_len) {
+    return ring_fits(back, ahead) || max_len <= 8 * 64;
+}
+
 // sum(L^2) / sum(L): the length of the sequence an average token sits in.
 static double typical_of(const int32_t *cu, int32_t S) {
     double sq = 0, total = 0;
@@ -89,21 +93,21 @@ static void rule(int32_t max_len, double typical, int32_t window, int32_t br_req
                  int32_t &br, int32_t &prerotate, int32_t &backward_br) {
     int32_t back, ahead;
     window_reaches(window, back, ahead);
-    const bool ring = ring_fits(back, ahead);
+    const bool ring = ring_holds(back, ahead, max_len);
     const int32_t W = window & ~VLF_CAUSAL;
     if (br_request) {
         br = br_request;
     } else if (max_len <= 64) {
         br = 64;  // one key tile per query tile: the unpipelined kernel
     } else if (ring && typical >= 256) {
-        br = 256;  // the window's keys stay in an LDS ring across consecutive tiles
+        br = 256;  // the reached keys stay in an LDS ring across consecutive tiles
     } else if (W > 0 && W <= 512) {
         br = 128;  // taller tiles would compute more masked pairs (span br + 2W - 1)
     } else {
         br = typical >= 448 ? 256 : 128;
     }
     if (br == 256 && ring) {
-        prerotate = 0;  // attend_slide keeps the window's keys in LDS already
+        prerotate = 0;  // attend_slide keeps the reached keys in LDS already
     } else {
         // a query tile's key span: the typical length, or the window's reach
         double span = typical;
@@ -122,7 +126,7 @@ using namespace vlf;
 
 extern "C" {
 
-int32_t vlf_version(void) { return 4; }
+int32_t vlf_version(void) { return 5; }
 
 const char *vlf_last_error(void) { return g_error.c_str(); }
 
@@ -283,14 +287,14 @@ int vlf_choose_backward(const int32_t *cu_host, int32_t S, int32_t T, int32_t H,
     return VLF_OK;
 }
 
-const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window) {
-    if (!supported_br(br) || window < 0)
+const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window, int32_t max_len) {
+    if (!supported_br(br) || window < 0 || max_len < 0)
         return "";
     if (prerotate)
         return br == 256 ? "attend_pre_ph" : "attend_pre";
     int32_t back, ahead;
     window_reaches(window, back, ahead);
-    if (br == 256 && ring_fits(back, ahead))
+    if (br == 256 && ring_holds(back, ahead, max_len))
         return "attend_slide";
     return br == 64 ? "attend_one" : "attend_fwd";
 }
@@ -367,8 +371,8 @@ static int attend_common(const void *qkv, const void *cos, const void *sin, int3
                     (const void *)tiles_dev, out, (void *)lse);
     int32_t back, ahead;
     window_reaches(window, back, ahead);
-    AttendArgs a{qkv,    cos,   sin,   table_rows, cu_dev, tiles_dev, num_tiles,
-                 br,     T,     S,     H,          back,   ahead,     scale,
+    AttendArgs a{qkv,    cos,   sin,   table_rows, max_len, cu_dev, tiles_dev, num_tiles,
+                 br,     T,     S,     H,          back,    ahead,  scale,
                  dtype,  const_cast<void *>(workspace), out, lse, stream};
     return launch_attend(a, what);
 }
@@ -505,8 +509,8 @@ int vlf_rotate_keys(const void *qkv, const void *cos, const void *sin, int32_t t
                           workspace_bytes_, T > 0, true);
     if (rc || T == 0)
         return rc;
-    AttendArgs a{qkv, cos, sin, table_rows, cu_dev, nullptr,   0,       0,       T, S,
-                 H,   0,   0,   1.f,        dtype,  workspace, nullptr, nullptr, stream};
+    AttendArgs a{qkv, cos, sin, table_rows, max_len, cu_dev,    nullptr, 0,       0, T,
+                 S,   H,   0,   0,          1.f,     dtype,     workspace, nullptr, nullptr, stream};
     return launch_attend(a, Launch::kRotate);
 }
 

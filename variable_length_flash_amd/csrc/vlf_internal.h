@@ -12,6 +12,7 @@ struct AttendArgs {
     const void *cos;
     const void *sin;
     int32_t table_rows;
+    int32_t max_len;  // the longest sequence (at most table_rows)
     const int32_t *cu;
     const uint32_t *tiles;
     int32_t num_tiles;
@@ -37,6 +38,11 @@ int64_t workspace_bytes(int32_t T, int32_t S, int32_t H);
 // i0 - 64 ceil(back / 64) (i0 a multiple of 64) to i0 + 255 + ahead. The direct path then runs
 // the kernel that keeps them in an LDS ring (attend_slide).
 bool ring_fits(int32_t back, int32_t ahead);
+
+// Whether every 256-row query tile's keys span at most eight 64-key tiles for a batch whose
+// longest sequence is max_len: the window fits (ring_fits), or no sequence is longer than eight
+// tiles, so the whole sequence fits. The direct path then runs attend_slide.
+bool ring_holds(int32_t back, int32_t ahead, int32_t max_len);
 
 // What launch_attend queues.
 enum class Launch {
