@@ -244,16 +244,17 @@ class Forward:
                 "rotate_ms": statistics.mean(rot), "rotate_ms_median": statistics.median(rot)}
 
 
-def tile_table_host_us(cu, br: int, reps: int = 50) -> float:
-    """Median host time of building the tile table through the library (vlf_tile_count, then
-    vlf_tile_table), microseconds."""
+def tile_table_host_us(cu, br: int, prerotate: bool = False, window: int = 0,
+                       reps: int = 50) -> float:
+    """Median host time of building the launch's tile table through the library
+    (vlf_tile_count, then vlf_launch_table), microseconds."""
     import statistics
 
     import variable_length_flash_amd as vlf
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        vlf.tile_table(cu, br)
+        vlf.launch_table(cu, br, prerotate, window)
         times.append((time.perf_counter() - t0) * 1e6)
     return statistics.median(times)
 
@@ -284,7 +285,8 @@ def secondary(args, dev):
             "tflops": round(flops / (t["step_ms"] / 1e3) / 1e12, 2),
             "hbm_gbs_algorithmic": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": nbytes, "effective_flop": flops,
-            "tile_table_host_us": round(tile_table_host_us(w.cu, f.batch.br), 1),
+            "tile_table_host_us": round(tile_table_host_us(w.cu, f.batch.br, f.batch.prerotate,
+                                                           w.window), 1),
         }
         del f
         torch.cuda.empty_cache()
@@ -384,7 +386,8 @@ def run(args):
                                     if batch.prerotate else {})},
             **({"rotate_hbm_gbs_algorithmic": round(rotate_bytes / (rotate_ms / 1e3) / 1e9, 1)}
                if batch.prerotate else {}),
-            "tile_table_host_us": round(tile_table_host_us(w.cu, batch.br), 1),
+            "tile_table_host_us": round(tile_table_host_us(w.cu, batch.br, batch.prerotate,
+                                                           w.window), 1),
             "visible_pairs_per_head": pairs, "effective_flop": flops,
             "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "achieved_hbm_gbs_algorithmic": round(alg_bytes / (kernel_ms / 1e3) / 1e9, 1),

@@ -87,6 +87,23 @@ int vlf_tile_table(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, uin
                    int64_t capacity);
 
 /*
+ * The tile table in the order vlf_attend runs it best at this schedule: the entries of
+ * vlf_tile_table (hanzo-kernel 0.2.42 src/packed.rs, `layout`), permuted. Where the direct path
+ * runs attend_slide (br = 256, prerotate 0, every tile's reached keys within eight key tiles,
+ * as vlf_forward_kernel names it), each CU takes an equal count of consecutive entries, so
+ * whole sequences (their entries kept adjacent and in row order) are ordered by the work of
+ * their entries: the most costly, the least costly, the second most, the second least, and so
+ * on (ties by sequence index). An entry's cost is 2 plus the 64-key tiles its 256 rows reach.
+ * Every other schedule gets the canonical order of vlf_tile_table.
+ *   cu_host, S, T, br   as in vlf_tile_table.
+ *   prerotate, window   as the batch will be run (vlf_choose_schedule, vlf_attend).
+ *   tiles_host          out, host, [num_tiles, 2] uint32.   capacity  as in vlf_tile_table.
+ * Host time O(S log S + num_tiles). Errors: those of vlf_tile_table; window < 0 (VLF_EINVAL).
+ */
+int vlf_launch_table(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, int32_t prerotate,
+                     int32_t window, uint32_t *tiles_host, int64_t capacity);
+
+/*
  * The number of (query, key) pairs one head computes: for each row i of each sequence, the
  * keys j of the same sequence the window admits (the masking of hanzo-kernel 0.2.42
  * src/packed.rs `attend`, or the causal window with VLF_CAUSAL). Effective FLOPs of one call
@@ -206,11 +223,12 @@ const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window, in
  *   tiles_dev  device, [num_tiles, 2] uint32 (sequence, first row) pairs built for the same cu
  *              and `br` (vlf_tile_table, or any permutation of it: the order is the launch
  *              order). Tiles naming a sequence >= S or a row beyond the sequence are skipped.
- *              Without a workspace, at br = 256 and a window that reaches at most eight key
- *              tiles (1 <= W <= 129, or causal 1 <= W <= 257), each CU walks a run
- *              of consecutive entries and keeps the keys that one entry shares with the
- *              next of the same sequence in LDS: any order gives the same results, and the
- *              canonical one is the fastest.
+ *              Without a workspace, at br = 256 where every tile's reached keys span at most
+ *              eight key tiles (1 <= W <= 129, causal 1 <= W <= 257, or max_len <= 512), each
+ *              CU walks a run of consecutive entries and keeps the keys that one entry shares
+ *              with the next of the same sequence in LDS: any order gives the same results;
+ *              vlf_launch_table's is the fastest (entries of a sequence adjacent and in row
+ *              order, sequences interleaved by cost).
  *   br         64, 128 or 256: rows per tile, as the table was built.
  *   T, S, H    tokens, sequences, heads (1 <= H <= 65536; T = 0 or num_tiles = 0 launches
  *              nothing).

@@ -326,6 +326,59 @@ def test_window_fits_ring():
     assert binding.window_fits_ring(129) and not binding.window_fits_ring(130)
 
 
+def test_launch_table_interleaves_whole_sequences_by_cost():
+    # by hand, full window, 256-row tiles, every sequence within eight key tiles: an entry costs
+    # 2 + the key tiles its rows reach (here the whole sequence). Sequence costs: 0 (512 rows,
+    # two entries of 2 + 8) 20, 1 (64) 3, 2 (300, two entries of 2 + 5) 14, 3 (100) 4, 4 (0)
+    # none. Most, least, second most, second least: 0, 1, 2, 3.
+    lens = [512, 64, 300, 100, 0]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    got = vlf.launch_table(cu, 256, False, 0)
+    want = np.array([[0, 0], [0, 256], [1, 0], [2, 0], [2, 256], [3, 0]], dtype=np.uint32)
+    np.testing.assert_array_equal(got, want)
+    # the other schedules keep the page's order
+    for br, pre, window in ((256, True, 0), (128, False, 0), (64, False, 0)):
+        np.testing.assert_array_equal(vlf.launch_table(cu, br, pre, window),
+                                      vlf.tile_table(cu, br))
+
+
+@pytest.mark.parametrize("window", [0, 1, 100, 129, 130, 300, 0 | vlf.CAUSAL])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_launch_table_is_a_permutation_with_sequences_whole(window, seed):
+    rng = np.random.default_rng(seed)
+    lens = list(rng.integers(0, 513, 60)) + ([3000, 9000] if seed else [])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    canon = vlf.tile_table(cu, 256)
+    got = vlf.launch_table(cu, 256, False, window)
+    assert got.shape == canon.shape
+    # the same entries
+    key = lambda t: t[:, 0].astype(np.int64) * 2 ** 32 + t[:, 1]
+    np.testing.assert_array_equal(np.sort(key(got)), np.sort(key(canon)))
+    # each sequence's entries adjacent and in row order
+    seqs = got[:, 0]
+    starts = np.nonzero(np.r_[True, seqs[1:] != seqs[:-1]])[0]
+    assert len(set(seqs[starts].tolist())) == len(starts)
+    for a, b in zip(starts, list(starts[1:]) + [len(got)]):
+        np.testing.assert_array_equal(got[a:b, 1], np.arange(b - a) * 256)
+    ring = vlf.forward_kernel(256, False, window, max(lens)) == "attend_slide"
+    if not ring:
+        np.testing.assert_array_equal(got, canon)
+
+
+def test_launch_table_rejects_what_the_tile_table_rejects():
+    lib = vlf.load_library()
+    cu = np.array([0, 5, 3], dtype=np.int32)
+    buf = np.zeros(16, dtype=np.uint32)
+    rc = lib.vlf_launch_table(cu.ctypes.data, 2, 3, 256, 0, 0, buf.ctypes.data, 16)
+    assert rc == binding.VLF_EINVAL
+    cu = np.array([0, 5], dtype=np.int32)
+    assert lib.vlf_launch_table(cu.ctypes.data, 1, 5, 256, 0, -1, buf.ctypes.data, 16) == \
+        binding.VLF_EINVAL
+    assert "window" in lib.vlf_last_error().decode()
+    assert lib.vlf_launch_table(cu.ctypes.data, 1, 5, 256, 0, 0, buf.ctypes.data, 1) == \
+        binding.VLF_EINVAL
+
+
 @pytest.mark.parametrize("lens,want", [([], 0.0), ([0, 0], 0.0), ([5], 5.0), ([100, 156],
                                        (100 ** 2 + 156 ** 2) / 256), ([512] * 32, 512.0)])
 def test_typical_length(lens, want):

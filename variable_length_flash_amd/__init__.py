@@ -8,8 +8,8 @@ loudly when it is missing: there is no fallback path.
 from .binding import (  # noqa: F401
     CAUSAL, Batch, VlfError, attend, attend_backward, attend_backward_into, attend_into,
     attend_rotated_into, backward_workspace_bytes, choose_backward, choose_backward_br, choose_br,
-    choose_prerotate, choose_schedule, forward_kernel, library_path, load_library, new_workspace,
-    prepare, rotate_keys, rotate_qkv_into, schedule_rule, tile_count, tile_table, typical_length,
-    visible_pairs, workspace_bytes,
+    choose_prerotate, choose_schedule, forward_kernel, launch_table, library_path, load_library,
+    new_workspace, prepare, rotate_keys, rotate_qkv_into, schedule_rule, tile_count, tile_table,
+    typical_length, visible_pairs, workspace_bytes,
 )
 from . import tune  # noqa: F401

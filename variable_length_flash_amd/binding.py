@@ -20,7 +20,7 @@ VLF_F16, VLF_BF16 = 0, 1
 HEAD_DIM = 64
 
 # every function include/vlf.h declares
-EXPORTS = ("vlf_version", "vlf_last_error", "vlf_tile_count", "vlf_tile_table",
+EXPORTS = ("vlf_version", "vlf_last_error", "vlf_tile_count", "vlf_tile_table", "vlf_launch_table",
            "vlf_visible_pairs", "vlf_workspace_bytes", "vlf_schedule_rule", "vlf_typical_length",
            "vlf_choose_schedule", "vlf_choose_backward", "vlf_forward_kernel", "vlf_attend",
            "vlf_attend_static", "vlf_rotate_keys", "vlf_attend_rotated",
@@ -58,6 +58,8 @@ def load_library():
     lib.vlf_tile_count.restype = ctypes.c_int
     lib.vlf_tile_table.argtypes = [p, i32, i32, i32, p, i64]
     lib.vlf_tile_table.restype = ctypes.c_int
+    lib.vlf_launch_table.argtypes = [p, i32, i32, i32, i32, i32, p, i64]
+    lib.vlf_launch_table.restype = ctypes.c_int
     lib.vlf_visible_pairs.argtypes = [p, i32, i32, i32, p]
     lib.vlf_visible_pairs.restype = ctypes.c_int
     lib.vlf_workspace_bytes.argtypes = [i32, i32, i32, p]
@@ -134,6 +136,18 @@ def tile_table(cu, br: int) -> np.ndarray:
     table = np.zeros((n, 2), dtype=np.uint32)
     _check(load_library().vlf_tile_table(_ptr(cu), cu.shape[0] - 1, int(cu[-1]), br,
                                           _ptr(table), 2 * n))
+    return table
+
+
+def launch_table(cu, br: int, prerotate: bool = False, window: int = 0) -> np.ndarray:
+    """The tile table in the library's launch order for this schedule (vlf_launch_table): the
+    entries of ``tile_table`` permuted, [NT, 2] uint32."""
+    cu = _host_cu(cu)
+    n, _ = tile_count(cu, br)
+    table = np.zeros((n, 2), dtype=np.uint32)
+    _check(load_library().vlf_launch_table(_ptr(cu), cu.shape[0] - 1, int(cu[-1]), br,
+                                            int(bool(prerotate)), int(window), _ptr(table),
+                                            2 * n))
     return table
 
 
@@ -268,7 +282,7 @@ def prepare(cu, device=None, br: int | None = None, prerotate: bool | None = Non
                                          0 if br is None else int(br))
     br = rule_br
     prerotate = rule_pre if prerotate is None else bool(prerotate)
-    table = tile_table(cu_host, br)
+    table = launch_table(cu_host, br, prerotate, window)
     return Batch(cu_host, torch.from_numpy(cu_host).to(device),
                  torch.from_numpy(table.view(np.int32)).to(device), table.shape[0], max_len, br,
                  prerotate)

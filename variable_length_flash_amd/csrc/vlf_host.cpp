@@ -5,12 +5,15 @@
 // (sequence, first row) pair per `br` query rows of every sequence, in sequence order. The pair
 // count follows the masking of that page's `attend` kernel: a query at position i sees key j of
 // its own sequence when the window is 0 or |i - j| < window.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/vlf.h"
+
 #include "vlf_internal.h"
 
 namespace vlf {
@@ -169,6 +172,61 @@ int vlf_tile_table(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, uin
             tiles_host[k++] = (uint32_t)i0;
         }
     }
+    return VLF_OK;
+}
+
+int vlf_launch_table(const int32_t *cu_host, int32_t S, int32_t T, int32_t br, int32_t prerotate,
+                     int32_t window, uint32_t *tiles_host, int64_t capacity) {
+    if (window < 0)
+        return fail(VLF_EINVAL, "window = %d < 0", window);
+    int32_t n = 0, max_len = 0;
+    int rc = vlf_tile_count(cu_host, S, T, br, &n, &max_len);
+    if (rc)
+        return rc;
+    rc = vlf_tile_table(cu_host, S, T, br, tiles_host, capacity);
+    if (rc)
+        return rc;
+    int32_t back, ahead;
+    window_reaches(window, back, ahead);
+    if (n == 0 || prerotate || br != 256 || !ring_holds(back, ahead, max_len))
+        return VLF_OK;  // one workgroup per entry: the canonical order
+    // attend_slide gives each CU an equal count of consecutive entries. Whole sequences (their
+    // entries stay adjacent, so the key ring still carries over between them) are ordered
+    // most costly, least costly, second most, second least, ..., so that every run mixes costly
+    // and cheap entries. The cost of an entry is what its waves sweep: a fixed 2 plus the key
+    // tiles its 256 rows reach (the kernel's key span).
+    std::vector<std::pair<int64_t, int32_t>> cost;  // (cost, sequence), sequences with rows
+    std::vector<int64_t> first((size_t)S + 1, 0);    // index of a sequence's first entry
+    int64_t k = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        first[s] = k;
+        const int32_t L = cu_host[s + 1] - cu_host[s];
+        int64_t c = 0;
+        for (int64_t i0 = 0; i0 < L; i0 += 256, ++k) {
+            const int64_t lo = i0 > back ? (i0 - back) / 64 * 64 : 0;
+            const int64_t hi = i0 + 256 + (int64_t)ahead < L ? i0 + 256 + ahead : L;
+            c += 2 + (hi - lo + 63) / 64;
+        }
+        if (L > 0)
+            cost.emplace_back(c, s);
+    }
+    first[S] = k;
+    std::stable_sort(cost.begin(), cost.end(),
+                     [](const std::pair<int64_t, int32_t> &a,
+                        const std::pair<int64_t, int32_t> &b) { return a.first > b.first; });
+    std::vector<uint32_t> out;
+    out.reserve(2 * (size_t)n);
+    size_t a = 0, b = cost.size();
+    bool front = true;
+    while (a < b) {
+        const int32_t s = front ? cost[a++].second : cost[--b].second;
+        front = !front;
+        for (int64_t e = first[s]; e < first[s + 1]; ++e) {
+            out.push_back((uint32_t)s);
+            out.push_back(tiles_host[2 * e + 1]);
+        }
+    }
+    std::copy(out.begin(), out.end(), tiles_host);
     return VLF_OK;
 }
 
