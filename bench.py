@@ -15,7 +15,9 @@ sixteen 8192-token sequences, 16 heads, bf16, full window. It prints one JSON li
   MI355X's dense bf16/fp16 matrix peak (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clock);
   traffic: HBM bytes per launch from rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled
   by the reading of a plain copy of known size), recorded in profiles/ with the hash of the
-  kernel source they were taken on (null when the source has changed since);
+  kernel source they were taken on (null when the source has changed since); step_traffic:
+  the same for every kernel of the step (the key-tile pass and the forward), against the
+  step's algorithmic bytes;
 * cpu_baseline: the float64 oracle (test infrastructure) on the host cores over a bounded
   sample of rows of the same workload, in the same unit (mode B, the parity gate; mode A on a
   quarter of the rows beside it), and its wall seconds over every row of the other workloads;
@@ -395,6 +397,15 @@ def run(args):
         "roofline": roofline(kernel, flops, alg_bytes, kernel_ms, traffic),
         "cpu_baseline": None,
     }
+    # the whole step's counted HBM bytes (the key-tile pass and the forward), beside the
+    # dominant kernel's own in roofline.traffic
+    step_kernels = ([("prep_tiles", rotate_ms)] if batch.prerotate else []) + [(kernel, kernel_ms)]
+    counted = [read_traffic(k, args.workload) for k, _ in step_kernels]
+    line["roofline"]["step_traffic"] = (
+        {"bytes": round(sum(counted)), "kernels": [k for k, _ in step_kernels],
+         "ratio_to_algorithmic": round(sum(counted) / alg_bytes, 3),
+         "gbs": round(sum(counted) / (sum(ms for _, ms in step_kernels) / 1e3) / 1e9, 1)}
+        if all(c is not None for c in counted) else None)
     del f
     torch.cuda.empty_cache()
     if not args.profile_run and not args.no_mfma_peak:
