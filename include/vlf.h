@@ -216,9 +216,12 @@ const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window, in
  *   cos, sin   device, [table_rows, 32] elements of `dtype`: entry [p][m] for position p.
  *   table_rows P, rows of the tables.
  *   max_len    the longest sequence of cu (vlf_tile_count's max_len). The call fails with
- *              VLF_EINVAL when P < max_len. Should a tile still name a sequence longer than P
- *              (a max_len that understates), the kernels skip it rather than read past the
- *              tables.
+ *              VLF_EINVAL when P < max_len. It also picks the kernel (vlf_forward_kernel): at
+ *              max_len <= 512 the direct path at 256 rows holds whole sequences in an LDS ring.
+ *              The library cannot read cu_dev to check it, so a max_len that understates is
+ *              the caller's error with a defined outcome: a tile naming a sequence longer than
+ *              P, or (on that ring) one whose keys span more than eight key tiles, is skipped
+ *              (its rows left unwritten) rather than read past the tables or the ring.
  *   cu_dev     device, [S+1] int32, the same values as the cu the tiles were built from.
  *   tiles_dev  device, [num_tiles, 2] uint32 (sequence, first row) pairs built for the same cu
  *              and `br` (vlf_tile_table, or any permutation of it: the order is the launch
