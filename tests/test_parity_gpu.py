@@ -480,6 +480,34 @@ def test_whole_sequences_in_the_key_ring(dtype, window):
     compare(f"whole sequences in the ring {dtype} W={window:#x}", w, out, lse, qkv, cos, sin)
 
 
+def test_understated_max_len_skips_what_the_ring_cannot_hold():
+    """max_len also picks the kernel, and the library cannot check it against cu on the device:
+    told 512 for a batch whose middle sequence has 1000 tokens (tables long enough for it), the
+    direct path at 256 rows runs the ring kernel, which must skip that sequence's tiles (their
+    keys span 16 key tiles) and leave its rows unwritten, while the other sequences are exact."""
+    import dataclasses
+    lens = [300, 1000, 64]
+    w = workloads.custom(lens, 2, dtype="bf16", window=0, table_rows=1000, seed=61)
+    qkv, cos, sin = inputs(w)
+    dev = torch.device("cuda:0")
+    batch = vlf.prepare(w.cu, dev, 256, False, 0)
+    assert batch.max_len == 1000
+    batch = dataclasses.replace(batch, max_len=512)
+    assert vlf.forward_kernel(256, False, 0, batch.max_len) == "attend_slide"
+    T, H = w.tokens, w.heads
+    out = torch.full((T, H * 64), float("nan"), dtype=qkv.dtype, device=dev)
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device=dev)
+    _say("case understated max_len on the key ring")
+    vlf.attend_into(batch, qkv.to(dev), cos.to(dev), sin.to(dev), H, 0, w.scale, out, lse)
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    skipped = np.arange(300, 1300)
+    assert np.isnan(out[skipped]).all() and np.isnan(lse[:, skipped]).all()
+    kept = np.r_[np.arange(0, 300), np.arange(1300, 1364)]
+    compare("understated max_len: the sequences the ring holds", w, out, lse, qkv, cos, sin,
+            rows=kept)
+
+
 @pytest.mark.parametrize("window", [1, 65])
 def test_window_runs_past_the_descriptor_cache(window):
     """20000 one-token sequences among longer ones, 2 heads: about 160 items per workgroup of
