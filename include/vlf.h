@@ -217,10 +217,12 @@ const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window, in
  *   table_rows P, rows of the tables.
  *   max_len    the longest sequence of cu (vlf_tile_count's max_len). The call fails with
  *              VLF_EINVAL when P < max_len. It also picks the kernel (vlf_forward_kernel): at
- *              max_len <= 512 the direct path at 256 rows holds whole sequences in an LDS ring.
+ *              max_len <= 512 the direct path at 256 rows holds whole sequences in an LDS ring,
+ *              and at max_len <= 64 the direct path at 64 rows sweeps one key tile per tile.
  *              The library cannot read cu_dev to check it, so a max_len that understates is
  *              the caller's error with a defined outcome: a tile naming a sequence longer than
- *              P, or (on that ring) one whose keys span more than eight key tiles, is skipped
+ *              P, or (on that ring) one whose keys span more than eight key tiles, or (at 64
+ *              rows with max_len <= 64) one whose keys span more than one key tile, is skipped
  *              (its rows left unwritten) rather than read past the tables or the ring.
  *   cu_dev     device, [S+1] int32, the same values as the cu the tiles were built from.
  *   tiles_dev  device, [num_tiles, 2] uint32 (sequence, first row) pairs built for the same cu

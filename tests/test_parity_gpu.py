@@ -155,7 +155,8 @@ def test_single_key_rows_are_exact(dtype, br, prerotate):
 
 @pytest.mark.parametrize("prerotate", PATHS)
 @pytest.mark.parametrize("lens", [[1], [1] * 300, [0, 0, 5, 0], [64] * 9, [128, 1, 128],
-                                  [2048], [0, 777, 0, 0, 1500]])
+                                  [2048], [0, 777, 0, 0, 1500], [3] * 700 + [300],
+                                  [0] * 400 + [70] + [0] * 200 + [1]])
 def test_edge_batches(lens, prerotate):
     w = workloads.custom(lens, 2, dtype="fp16", window=0, table_rows=max(lens + [1]), seed=3)
     qkv, cos, sin = inputs(w)
@@ -505,6 +506,31 @@ def test_understated_max_len_skips_what_the_ring_cannot_hold():
     assert np.isnan(out[skipped]).all() and np.isnan(lse[:, skipped]).all()
     kept = np.r_[np.arange(0, 300), np.arange(1300, 1364)]
     compare("understated max_len: the sequences the ring holds", w, out, lse, qkv, cos, sin,
+            rows=kept)
+
+
+def test_understated_max_len_on_single_key_tile_rows():
+    """At 64 rows a max_len of at most 64 runs attend_one's single-tile form, which sweeps one
+    key tile: told 64 for a batch with a 100-token sequence (tables long enough for it), that
+    sequence's two query tiles reach two key tiles and must be left unwritten, while the
+    sequences of at most 64 tokens are exact."""
+    import dataclasses
+    lens = [40, 100, 64, 1]
+    w = workloads.custom(lens, 2, dtype="fp16", window=0, table_rows=100, seed=62)
+    qkv, cos, sin = inputs(w)
+    dev = torch.device("cuda:0")
+    batch = dataclasses.replace(vlf.prepare(w.cu, dev, 64, False, 0), max_len=64)
+    T, H = w.tokens, w.heads
+    out = torch.full((T, H * 64), float("nan"), dtype=qkv.dtype, device=dev)
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device=dev)
+    _say("case understated max_len on single-tile rows")
+    vlf.attend_into(batch, qkv.to(dev), cos.to(dev), sin.to(dev), H, 0, w.scale, out, lse)
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    skipped = np.arange(40, 140)
+    assert np.isnan(out[skipped]).all() and np.isnan(lse[:, skipped]).all()
+    kept = np.r_[np.arange(0, 40), np.arange(140, 205)]
+    compare("understated max_len: the single-tile sequences", w, out, lse, qkv, cos, sin,
             rows=kept)
 
 

@@ -533,26 +533,42 @@ __device__ __forceinline__ float key_norm_max(const float *knorm, int kb, int nt
 }
 
 // Score of row qi with its own key (always visible), from the workspace block that holds it;
-// -inf for rows past the sequence. Shared by lanes n and n + 32.
-template <class E>
-__device__ __forceinline__ float own_score(const uint8_t *wblock, const u32x4 (&qop)[4], int qi,
-                                           int len, int g) {
-    float d = 0.f;
+// -inf for rows past the sequence. Shared by lanes n and n + 32. own_key reads the lane's half
+// of the key row (zero past the sequence), own_dot forms the score from it, so that the read
+// can be issued before the query operand exists.
+__device__ __forceinline__ void own_key(const uint8_t *wblock, int qi, int len, int g,
+                                        u32x4 (&kw)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        kw[c] = u32x4{0, 0, 0, 0};
     if (qi < len) {
         const int r = qi % BC;
         const uint8_t *krow = wblock + (int64_t)(qi / BC) * BLK + r * 128;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 kw = *(const u32x4 *)(krow + 16 * ((2 * c + g) ^ swz(r)));
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                d = __builtin_fmaf(E::lo(qop[c][w]), E::lo(kw[w]), d);
-                d = __builtin_fmaf(E::hi(qop[c][w]), E::hi(kw[w]), d);
-            }
-        }
+        for (int c = 0; c < 4; ++c)
+            kw[c] = *(const u32x4 *)(krow + 16 * ((2 * c + g) ^ swz(r)));
     }
+}
+template <class E>
+__device__ __forceinline__ float own_dot(const u32x4 (&kw)[4], const u32x4 (&qop)[4], int qi,
+                                         int len) {
+    float d = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            d = __builtin_fmaf(E::lo(qop[c][w]), E::lo(kw[c][w]), d);
+            d = __builtin_fmaf(E::hi(qop[c][w]), E::hi(kw[c][w]), d);
+        }
     d = pair_sum(d);
     return qi < len ? d : -__builtin_inff();
+}
+template <class E>
+__device__ __forceinline__ float own_score(const uint8_t *wblock, const u32x4 (&qop)[4], int qi,
+                                           int len, int g) {
+    u32x4 kw[4];
+    own_key(wblock, qi, len, g, kw);
+    return own_dot<E>(kw, qop, qi, len);
 }
 
 // The reference of each row of a wave: m_tile is the row maximum of one swept tile (masked),
@@ -604,18 +620,30 @@ prep_tiles(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            uint8_t *__restrict__ ws, int32_t NB, int32_t T, int32_t S, int32_t H, int32_t P) {
     __shared__ uint16_t vrow[64][72];
     __shared__ float wmax[4];
+    __shared__ int owner;
     const int h = (int)(blockIdx.x / (uint32_t)NB);
     const int b = (int)(blockIdx.x - (uint32_t)h * (uint32_t)NB);
-    // the sequence owning block b: the largest s with floor(cu[s] / 64) + s <= b
+    const int tid = (int)threadIdx.x;
+    // The sequence owning block b: the largest s with floor(cu[s] / 64) + s <= b, i.e. the one
+    // s with key(s) <= b < key(s + 1) for key(s) = floor(cu[s] / 64) + s, which rises with s.
+    // A search narrows it to at most 256 candidates, then one thread per candidate tests it:
+    // one memory round trip for batches of up to 256 sequences.
     int lo = 0, hi = S - 1;
-    while (lo < hi) {
+    while (hi - lo >= 256) {
         const int mid = (lo + hi + 1) >> 1;
         if (cu[mid] / 64 + mid <= b)
             lo = mid;
         else
             hi = mid - 1;
     }
-    const int s = lo;
+    if (tid == 0)
+        owner = lo;
+    __syncthreads();
+    if (tid > 0 && lo + tid <= hi && cu[lo + tid] / 64 + lo + tid <= b &&
+        (lo + tid == hi || cu[lo + tid + 1] / 64 + lo + tid + 1 > b))
+        owner = lo + tid;
+    __syncthreads();
+    const int s = owner;
     const int start = cu[s];
     const int len = cu[s + 1] - start;
     if (start < 0 || len <= 0 || len > P || (int64_t)start + len > T)
@@ -626,7 +654,6 @@ prep_tiles(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int j0 = BC * u;
     const int nvalid = min(BC, len - j0);
     const int64_t ld = 3LL * H * D;
-    const int tid = (int)threadIdx.x;
     uint8_t *blk = ws + ((int64_t)h * NB + b) * BLK;
 
     // thread (r, q): key row r, pairs m = 8q .. 8q+7 (dims m and m+32), value dims 16q .. 16q+15
@@ -978,8 +1005,26 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         }
     };
 
+    // Every global read of the prologue is issued before the first wait: the query rows and
+    // their table entries, the own key rows, the key norms and the copies of tiles 0 .. 2 (one
+    // memory latency in all rather than one after another).
+    QueryRaw qr;
+    query_load(qr, qkv, cos_t, sin_t, ld, start, qi, len, h, g);
+    u32x4 kw[4];
+    own_key(wblock, qi, len, g, kw);
+    // the blocks' key norm bounds: every score of tile t is at most qn * knorm[key(t) / BC]
+    const float *knorm = (const float *)(ws + (int64_t)H * NB * BLK) + (int64_t)h * NB +
+                         start / BC + (int)seq;
+    float kn0, kn1;
+    key_norm_reads(knorm, lo / BC, ntiles, lane, kn0, kn1);
+    asm volatile("" ::: "memory");
+    copy(0, 0);
+    if (ntiles > 1)
+        copy(1, 1);
+    if (ntiles > 2)
+        copy(2, 2);
     u32x4 qop[4];
-    query_operand<E>(qkv, cos_t, sin_t, ld, start, qi, len, h, g, scale, qop);
+    query_make<E>(qr, scale, qop);
     // upper bound of this row's rounded query norm (lanes n and n + 32 hold 32 elements each)
     float qn;
     {
@@ -994,19 +1039,9 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
             }
         qn = __builtin_sqrtf(pair_sum(sq)) * NORM_MARGIN;
     }
-    // the blocks' key norm bounds: every score of tile t is at most qn * knorm[key(t) / BC]
-    const float *knorm = (const float *)(ws + (int64_t)H * NB * BLK) + (int64_t)h * NB +
-                         start / BC + (int)seq;
-    float kn0, kn1;
-    key_norm_reads(knorm, lo / BC, ntiles, lane, kn0, kn1);
-    asm volatile("" ::: "memory");
-    copy(0, 0);
-    if (ntiles > 1)
-        copy(1, 1);
-    if (ntiles > 2)
-        copy(2, 2);
     // upper bound of every score of this row
     const float bq = qn * key_norm_max(knorm, lo / BC, ntiles, lane, kn0, kn1);
+    const float s_own = own_dot<E>(kw, qop, qi, len);
     if (ntiles > 2)
         ring_barrier<PIECES>();
     else
@@ -1045,7 +1080,7 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     if (edge(key(0)))
         mask_scores(sa0, sa1, key(0), len, back, ahead, qi, g);
     const float m_ref =
-        fixed_reference<E>(row_max(sa0, sa1), own_score<E>(wblock, qop, qi, len, g), bq,
+        fixed_reference<E>(row_max(sa0, sa1), s_own, bq,
                            qi < len, [&] {
                                return exact_row_max<E>(wblock, qop, cof, ntiles, key, edge, len,
                                                        back, ahead, qi, g);
@@ -1430,8 +1465,12 @@ int launch_pre(const AttendArgs &a) {
 // LDS (18 KB) stay small, so many workgroups share a CU, which is what batches of short
 // sequences need: most of their tiles see one key tile and are bound by load latency, not by
 // the matrix unit. Same arithmetic as attend_fwd, tile by tile.
-template <class E, bool FIXED>
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
+// SINGLE serves batches of sequences of at most 64 tokens, where every query tile reaches one
+// key tile: without a second tile to load ahead, the kernel fits 128 registers, so four waves
+// share a SIMD and eight workgroups a CU. A tile that reaches more keys (a sequence longer than
+// the caller's max_len said) is left unwritten.
+template <class E, bool FIXED, bool SINGLE>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(SINGLE ? 4 : 2)))
 attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            const uint32_t *__restrict__ tiles, uint16_t *__restrict__ out,
@@ -1470,6 +1509,8 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     int lo, hi;
     key_span(i0, BR, len, back, ahead, lo, hi);
     const int ntiles = (hi - lo + BC - 1) / BC;
+    if (SINGLE && ntiles > 1)
+        return;
 
     Staging<NTHR> sg;
     sg.init(tid, ld);
@@ -2023,10 +2064,12 @@ int launch_typed(const AttendArgs &a) {
                     (void *)&a.tiles, (void *)&out,   (void *)&a.lse, (void *)&num_tiles,
                     (void *)&T,   (void *)&S,         (void *)&H,  (void *)&P,
                     (void *)&Bk,  (void *)&Ah, (void *)&scale};
-    // 64-row tiles take the unpipelined kernel (short sequences), taller ones the pipeline
+    // 64-row tiles take the unpipelined kernel (short sequences; the single-tile form when no
+    // sequence is longer than one key tile), taller ones the pipeline
     const void *fn;
     if constexpr (NW == 2)
-        fn = (const void *)attend_one<E, FIXED>;
+        fn = a.max_len <= BC ? (const void *)attend_one<E, FIXED, true>
+                             : (const void *)attend_one<E, FIXED, false>;
     else
         fn = (const void *)attend_fwd<E, NW, FIXED>;
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(NW * 64), args, 0,
