@@ -41,7 +41,9 @@ Other modes:
                        summary for profiles/ (per kernel: calls, total, average, min, max, and
                        the average over the last --steps dispatches, the timed ones);
   --mfma-peak          the matrix probe alone;
-  --overlap            the overlap probe alone (matrix, vector and LDS work sharing a SIMD).
+  --overlap            the overlap probe alone (matrix, vector and LDS work sharing a SIMD);
+  --schedules          the phase-schedule probe (one product wave per SIMD) and the matrix
+                       unit's toll on vector work.
 """
 from __future__ import annotations
 
@@ -450,6 +452,17 @@ def run_overlap(args):
                       "unit": "clocks", "pairs": rows}), flush=True)
 
 
+def run_schedules(args):
+    """``--schedules``: the phase-schedule and matrix-toll probes, one JSON line."""
+    import torch
+
+    from variable_length_flash_amd import probe
+    res = probe.schedules(torch.device("cuda:0"))
+    print(json.dumps({"metric": "schedule probe: shader clocks per 32-row wave step with one "
+                                "product wave per SIMD, and the matrix unit's toll on vector work",
+                      "unit": "clocks", **res}), flush=True)
+
+
 def run_backward(args, w, q, c, s, out, lse, stream):
     """``--backward``: the library's forward once (out, lse), then K timed backward calls
     (include/vlf.h, vlf_attend_backward: delta, back_kv, back_q) on a seeded dout.
@@ -777,6 +790,8 @@ def main():
                     help="run only the matrix probe (sustained bf16 MFMA rate and clock)")
     ap.add_argument("--overlap", action="store_true",
                     help="run only the overlap probe (matrix, vector and LDS work on one SIMD)")
+    ap.add_argument("--schedules", action="store_true",
+                    help="run only the phase-schedule and matrix-toll probes")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (vlf_attend_backward) instead of the forward")
     ap.add_argument("--causal", action="store_true",
@@ -802,6 +817,9 @@ def main():
         return
     if args.mfma_peak:
         run_mfma_peak(args)
+        return
+    if args.schedules:
+        run_schedules(args)
         return
     if args.overlap:
         run_overlap(args)

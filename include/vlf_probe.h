@@ -62,6 +62,31 @@ int vlf_probe_mfma(int32_t iters, int32_t blocks, uint64_t *record_dev, void *st
 int vlf_probe_overlap(int32_t lo_role, int32_t hi_role, int32_t iters, int32_t blocks,
                       float *sink_dev, uint64_t *record_dev, void *stream);
 
+/*
+ * Queue one launch of a phase-schedule probe of the forward's 32-row, 64-key wave step, one
+ * workgroup per CU (`blocks` = the CU count), or of the matrix unit's toll on vector work.
+ * Kinds 0-5 run `steps` steps per wave with the forward's dataflow (scores from a K image in LDS
+ * and a query operand in registers, exp2 softmax with the row sum and bf16 pair conversions,
+ * output product from a V image in LDS), groups of four waves (one per SIMD) rotating roles at a
+ * barrier per phase, so that every SIMD holds one product wave and the rest softmax waves:
+ *   0 three groups (12 waves): product, softmax of half the step's scores, the other half;
+ *   1 kind 0 with the softmax phases left empty;   2 kind 0 with the products left empty;
+ *   3 four groups (16 waves), the softmax in thirds;   4, 5 kind 3 emptied as 1, 2.
+ *   record_dev[16 b] (uint64) gets workgroup b's shader clocks for the whole loop: per wave
+ *   step that is record / (groups * steps) on each SIMD.
+ * Kinds 6-9 run 12 waves per workgroup for `steps` iterations: waves 0-3 (one per SIMD) four
+ * v_mfma_f32_32x32x16_bf16 per iteration (kinds 7, 9) or nothing (6, 8); waves 4-11 (two per
+ * SIMD) 16 v_fma_f32 (6, 7) or v_exp_f32 (8, 9) on eight chains; record_dev[16 b + w] gets
+ * wave w's own loop in shader clocks.
+ * sink_dev receives checksums. Asynchronous; allocates nothing.
+ *   kind        0 .. 9.   steps  a multiple of 4 in 4 .. 2^22.   blocks  1 .. 2^20.
+ *   sink_dev    device, 1024 * blocks floats, 4-byte aligned.
+ *   record_dev  device, 16 * blocks uint64, 8-byte aligned.
+ * Errors: -1 (kind, steps or blocks out of range, null or misaligned buffers), -3 (launch).
+ */
+int vlf_probe_schedule(int32_t kind, int32_t steps, int32_t blocks, float *sink_dev,
+                       uint64_t *record_dev, void *stream);
+
 /* Message for the last non-OK status on the calling thread ("" if none). */
 const char *vlf_probe_last_error(void);
 

@@ -46,6 +46,12 @@ def test_probe_library_exports_its_header():
     assert "iters" in lib.vlf_probe_last_error().decode()
     assert lib.vlf_probe_overlap(1, 1, 10, 256, 0x1002, 0x1000, None) == -1
     assert "aligned" in lib.vlf_probe_last_error().decode()
+    assert lib.vlf_probe_schedule(10, 8, 256, 0x1000, 0x1000, None) == -1
+    assert "kind" in lib.vlf_probe_last_error().decode()
+    assert lib.vlf_probe_schedule(0, 6, 256, 0x1000, 0x1000, None) == -1
+    assert "steps" in lib.vlf_probe_last_error().decode()
+    assert lib.vlf_probe_schedule(0, 8, 256, 0x1000, 0x1004, None) == -1
+    assert "aligned" in lib.vlf_probe_last_error().decode()
 
 
 def test_library_exports_every_declared_function():

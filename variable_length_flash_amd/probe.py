@@ -8,7 +8,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libvlf_probe.so")
-EXPORTS = ("vlf_probe_mfma", "vlf_probe_overlap", "vlf_probe_last_error")
+EXPORTS = ("vlf_probe_mfma", "vlf_probe_overlap", "vlf_probe_schedule", "vlf_probe_last_error")
 FLOP_PER_MFMA = 32 * 32 * 16 * 2  # v_mfma_f32_32x32x16_bf16
 
 _lib = None
@@ -26,6 +26,8 @@ def load_library():
         lib.vlf_probe_mfma.restype = ctypes.c_int
         lib.vlf_probe_overlap.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
         lib.vlf_probe_overlap.restype = ctypes.c_int
+        lib.vlf_probe_schedule.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 3
+        lib.vlf_probe_schedule.restype = ctypes.c_int
         lib.vlf_probe_last_error.argtypes = []
         lib.vlf_probe_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -119,3 +121,50 @@ def overlap(device, pairs=OVERLAP_PAIRS, iters: int = 4000):
                     "hi_clocks_per_iter": round(med[3] / iters, 1),
                     "clock_ghz": round(ghz, 3)})
     return out
+
+
+SCHEDULES = {0: ("three groups", 3), 1: ("three groups, softmax phases empty", 3),
+             2: ("three groups, products empty", 3), 3: ("four groups", 4),
+             4: ("four groups, softmax phases empty", 4), 5: ("four groups, products empty", 4)}
+
+
+def schedules(device, steps: int = 2000):
+    """Shader clocks per 32-row wave step on one SIMD for the phase schedules of
+    vlf_probe_schedule (kinds 0-5, medians over one workgroup per CU), and the matrix unit's
+    toll on vector work (kinds 6-9): the clocks per iteration of the vector waves without and
+    beside a wave of back-to-back MFMAs, and the toll per MFMA that difference implies."""
+    import torch
+    lib = load_library()
+    dev = torch.device(device)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(1024 * cus, dtype=torch.float32, device=dev)
+    record = torch.zeros(16 * cus, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(kind):
+        for _ in range(2):  # the first launch warms the clock and the code
+            rc = lib.vlf_probe_schedule(int(kind), int(steps), int(cus), sink.data_ptr(),
+                                        record.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(lib.vlf_probe_last_error().decode())
+        torch.cuda.synchronize(dev)
+        return record.view(cus, 16).cpu().double()
+
+    rows = []
+    for kind, (name, groups) in SCHEDULES.items():
+        clocks = float(launch(kind)[:, 0].median()) / (groups * steps)
+        rows.append({"schedule": name, "waves_per_simd": groups,
+                     "clocks_per_wave_step": round(clocks, 1),
+                     "matrix_busy_pct": round(100 * 16 * 32 / clocks, 1)})
+    toll = []
+    for op, base, with_mfma in (("fma", 6, 7), ("exp", 8, 9)):
+        alone = float(launch(base)[:, 4:12].median()) / steps
+        rec = launch(with_mfma)
+        beside = float(rec[:, 4:12].median()) / steps
+        mfma_iter = float(rec[:, :4].median()) / steps  # clocks per four MFMAs
+        mfmas = 4 * beside / mfma_iter  # MFMAs issued on the SIMD during one vector iteration
+        toll.append({"vector_op": op, "clocks_per_16_alone": round(alone, 1),
+                     "clocks_per_16_beside_mfma": round(beside, 1),
+                     "mfma_clocks_per_instruction": round(mfma_iter / 4, 1),
+                     "toll_clocks_per_mfma": round((beside - alone) / mfmas, 1)})
+    return {"schedules": rows, "mfma_toll": toll}
