@@ -288,6 +288,11 @@ def secondary(args, dev):
             "step_ms_median": round(t["step_ms_median"], 4),
             "tflops": round(flops / (t["step_ms"] / 1e3) / 1e12, 2),
             "hbm_gbs_algorithmic": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            # the forward kernel alone (HIP events around its launch), as the main line's
+            # roofline takes it: the step's figures above include the key-tile pass if any and
+            # the launch gaps
+            "kernel_ms": round(t["kernel_ms"], 4),
+            "kernel_frac_of_hbm": round(nbytes / (t["kernel_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": nbytes, "effective_flop": flops,
             "tile_table_host_us": round(tile_table_host_us(w.cu, f.batch.br, f.batch.prerotate,
                                                            w.window), 1),

@@ -2421,11 +2421,13 @@ __device__ __forceinline__ void copy_block(const uint8_t *src, lds_u8 *dst, int 
     }
 }
 
-// 64 floats of rows [r0, r0 + 64) of a per-row float array into LDS (zeros past the sequence).
+// 64 floats of rows [r0, r0 + 64) of a per-row float array into LDS (zeros past the sequence;
+// a range that starts past it reads nothing and leaves zeros).
 __device__ __forceinline__ void copy_floats(const float *base, int start, int r0, int len,
                                             lds_u8 *dst, int lane) {
+    const int rows = len > r0 ? len - r0 : 0;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(base + start + r0), 0, 4 * (len - r0), RSRC_WORD3);
+        (void *)(base + start + (rows > 0 ? r0 : 0)), 0, 4 * rows, RSRC_WORD3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, 4 * lane, 0, 0, 0);
 }
 
@@ -2493,7 +2495,8 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         const uint32_t *__restrict__ tiles, const uint16_t *__restrict__ dout,
         const uint8_t *__restrict__ ws, uint16_t *__restrict__ dqkv, int32_t num_tiles,
         int32_t T, int32_t S, int32_t H, int32_t P, int32_t back, int32_t ahead, float scale) {
-    constexpr int SLOT = 4 * IMG + 512;  // Q~, Q~^T, dO^T, dO rows, -lse, -delta
+    // Q~, Q~^T, dO^T, dO rows, then -lse and -delta of the step's 64 rows and of the next 64
+    constexpr int SLOT = 4 * IMG + 1024;
     // buffer loads a wave issues per copy (waves 0 and 1 issue one more)
     constexpr int PIECES = 3 * IMG / 1024 / NW + 8 / NW;
     __shared__ __attribute__((aligned(16))) uint8_t lds[SL * SLOT];
@@ -2550,8 +2553,11 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
                 *(u32x4 *)(dg + 3 * IMG + r * 128 + 16 * (c4 ^ swz(r))) = y1;
                 *(u32x4 *)(dg + 3 * IMG + r * 128 + 16 * ((4 + c4) ^ swz(r))) = y2;
                 if (c4 == 0) {
-                    ((float *)(dg + 4 * IMG))[r] = i < len ? nlse[start + i] : 0.f;
-                    ((float *)(dg + 4 * IMG + 256))[r] = i < len ? ndelta[start + i] : 0.f;
+                    float *fl = (float *)(dg + 4 * IMG);
+                    fl[r] = i < len ? nlse[start + i] : 0.f;
+                    fl[64 + r] = i + BS < len ? nlse[start + i + BS] : 0.f;
+                    fl[128 + r] = i < len ? ndelta[start + i] : 0.f;
+                    fl[192 + r] = i + BS < len ? ndelta[start + i + BS] : 0.f;
                 }
             }
             return;
@@ -2559,10 +2565,15 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         lds_u8 *d = base + sl * SLOT;
         copy_block<NW, 3 * IMG>(imgs + (int64_t)(it / BC) * BIMG, d, wvu, lane);
         copy_rows<NW>(back_rows(dout + h * D, hd, start, it, len), hd, d + 3 * IMG, wvu, lane);
-        if (wvu == 0)
+        // the step's -lse and -delta, and the next step's (read at the end of this step)
+        if (wvu == 0) {
             copy_floats(nlse, start, it, len, d + 4 * IMG, lane);
-        if (wvu == 1)
-            copy_floats(ndelta, start, it, len, d + 4 * IMG + 256, lane);
+            copy_floats(nlse, start, it + BS, len, d + 4 * IMG + 256, lane);
+        }
+        if (wvu == 1) {
+            copy_floats(ndelta, start, it, len, d + 4 * IMG + 512, lane);
+            copy_floats(ndelta, start, it + BS, len, d + 4 * IMG + 768, lane);
+        }
     };
     const int steps = (qb - qa + BS - 1) / BS;
     for (int k = 0; k < SL - 1 && k < steps; ++k)
@@ -2573,6 +2584,27 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         ring_barrier<0>();
 
     f32x16 dv0 = {}, dv1 = {}, dk0 = {}, dk1 = {};
+    // S - lse and dP - delta of 32-row block rb of a step, register i holding query row
+    // 32rb + 8(i/4) + 4g + i%4: the accumulators start at -lse and -delta. A step's values are
+    // read from the LDS slot of the step before (its second half) as soon as that step's block
+    // rb has formed its P and dS, so that they have landed when the block's first products of
+    // the next step need them.
+    f32x16 sc[2], dp[2];
+    auto start_values = [&](const float *nl, const float *nd, int rb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const f32x4 x = *(const f32x4 *)(nl + 32 * rb + 8 * gi + 4 * g);
+            const f32x4 y = *(const f32x4 *)(nd + 32 * rb + 8 * gi + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sc[rb][4 * gi + e] = x[e], dp[rb][4 * gi + e] = y[e];
+        }
+    };
+    if (!idle && steps > 0) {
+        const float *nl = (const float *)(lds + 4 * IMG);
+        start_values(nl, nl + 128, 0);
+        start_values(nl, nl + 128, 1);
+    }
     // One step: the copy SL - 1 steps ahead, the products of step st (unless the wave is idle),
     // the ring wait. The masked and unmasked steps run in loops of their own (below): with both
     // bodies behind a branch in one loop the compiler gives the accumulators different
@@ -2585,24 +2617,14 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
         if (!idle) {
             const uint8_t *qs = lds + (st % SL) * SLOT, *qt = qs + IMG, *ot = qs + 2 * IMG;
             const uint8_t *os = qs + 3 * IMG;
-            const float *nl = (const float *)(qs + 4 * IMG), *nd = nl + 64;
+            // the next step's -lse and -delta (second halves of this slot's float arrays)
+            const float *nl = (const float *)(qs + 4 * IMG) + BS, *nd = nl + 128;
             // both 32-row blocks in one stretch, so that the softmax of one overlaps the
             // products of the other
             {
                 constexpr bool MASK = decltype(masked)::value;
-                f32x16 sc[2], dp[2];
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
-                    // S - lse and dP - delta of query rows it + 32rb + 8(i/4) + 4g + i%4
-                    // (register i): the accumulators start at -lse and -delta
-#pragma unroll
-                    for (int gi = 0; gi < 4; ++gi) {
-                        const f32x4 x = *(const f32x4 *)(nl + 32 * rb + 8 * gi + 4 * g);
-                        const f32x4 y = *(const f32x4 *)(nd + 32 * rb + 8 * gi + 4 * g);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sc[rb][4 * gi + e] = x[e], dp[rb][4 * gi + e] = y[e];
-                    }
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int off = (32 * rb + n) * 128 + 16 * ((2 * c + g) ^ swz(n));
@@ -2614,6 +2636,7 @@ back_kv(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
                 for (int rb = 0; rb < 2; ++rb) {
                     u32x4 pp[2], pd[2];
                     back_pds<E, MASK>(sc[rb], dp[rb], vlo - it - 32 * rb - 4 * g, span, pp, pd);
+                    start_values(nl, nd, rb);
                     // dV^T += dO^T P and dK^T += Q~^T dS (dims 0..31 and 32..63)
 #pragma unroll
                     for (int kc = 0; kc < 2; ++kc) {
