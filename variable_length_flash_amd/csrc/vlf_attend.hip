@@ -609,20 +609,25 @@ __device__ __forceinline__ float exact_row_max(const uint8_t *wblock,
     return mx;
 }
 
-// One workgroup per (block, head) writes that block: keys rotated and rounded exactly as the
-// staging of the other path does, values transposed; keys past the sequence are zero. It also
-// writes an upper bound of the largest Euclidean norm among the block's rounded keys into the
-// norm array that follows the blocks (index h * NB + block).
+// One workgroup per block and group of four heads writes those heads' blocks: keys rotated and
+// rounded exactly as the staging of the other path does, values transposed; keys past the
+// sequence are zero. The rotation table rows are read once for the four heads, and every key
+// and value row is requested before the first is used. It also writes an upper bound of the
+// largest Euclidean norm among each block's rounded keys into the norm array that follows the
+// blocks (index h * NB + block).
+constexpr int PREP_HEADS = 4;  // heads one prep_tiles workgroup rotates for its block
+
 template <class E>
 __global__ void __launch_bounds__(256)
 prep_tiles(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
            const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
            uint8_t *__restrict__ ws, int32_t NB, int32_t T, int32_t S, int32_t H, int32_t P) {
-    __shared__ uint16_t vrow[64][72];
-    __shared__ float wmax[4];
+    __shared__ uint16_t vrow[PREP_HEADS][64][72];
+    __shared__ float wmax[PREP_HEADS][4];
     __shared__ int owner;
-    const int h = (int)(blockIdx.x / (uint32_t)NB);
-    const int b = (int)(blockIdx.x - (uint32_t)h * (uint32_t)NB);
+    // block b of heads h0 .. h0 + PREP_HEADS - 1 (the table rows are read once for all of them)
+    const int b = (int)(blockIdx.x % (uint32_t)NB);
+    const int h0 = (int)(blockIdx.x / (uint32_t)NB) * PREP_HEADS;
     const int tid = (int)threadIdx.x;
     // The sequence owning block b: the largest s with floor(cu[s] / 64) + s <= b, i.e. the one
     // s with key(s) <= b < key(s + 1) for key(s) = floor(cu[s] / 64) + s, which rises with s.
@@ -654,68 +659,91 @@ prep_tiles(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int j0 = BC * u;
     const int nvalid = min(BC, len - j0);
     const int64_t ld = 3LL * H * D;
-    uint8_t *blk = ws + ((int64_t)h * NB + b) * BLK;
 
-    // thread (r, q): key row r, pairs m = 8q .. 8q+7 (dims m and m+32), value dims 16q .. 16q+15
+    // thread (r, q): key row r, pairs m = 8q .. 8q+7 (dims m and m+32), value dims 16q .. 16q+15;
+    // every head's rows and the table entries are requested before any is used
     const int r = tid >> 2, q = tid & 3;
-    u32x4 x1 = {0, 0, 0, 0}, x2 = {0, 0, 0, 0}, c = {0, 0, 0, 0}, sn = {0, 0, 0, 0};
-    u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+    u32x4 c = {0, 0, 0, 0}, sn = {0, 0, 0, 0};
+    u32x4 x1[PREP_HEADS], x2[PREP_HEADS], va[PREP_HEADS], vb[PREP_HEADS];
+#pragma unroll
+    for (int k = 0; k < PREP_HEADS; ++k)
+        x1[k] = x2[k] = va[k] = vb[k] = u32x4{0, 0, 0, 0};
     if (r < nvalid) {
-        const uint16_t *krow = qkv + (int64_t)(start + j0 + r) * ld + H * D + h * D;
-        const uint16_t *vrw = krow + H * D;
-        x1 = *(const u32x4 *)(krow + 8 * q);
-        x2 = *(const u32x4 *)(krow + 32 + 8 * q);
+        const uint16_t *krow = qkv + (int64_t)(start + j0 + r) * ld + H * D;
+#pragma unroll
+        for (int k = 0; k < PREP_HEADS; ++k) {
+            if (h0 + k < H) {
+                const uint16_t *kr = krow + (h0 + k) * D, *vr = kr + H * D;
+                x1[k] = *(const u32x4 *)(kr + 8 * q);
+                x2[k] = *(const u32x4 *)(kr + 32 + 8 * q);
+                va[k] = *(const u32x4 *)(vr + 16 * q);
+                vb[k] = *(const u32x4 *)(vr + 16 * q + 8);
+            }
+        }
         c = *(const u32x4 *)(cos_t + (j0 + r) * 32 + 8 * q);
         sn = *(const u32x4 *)(sin_t + (j0 + r) * 32 + 8 * q);
-        va = *(const u32x4 *)(vrw + 16 * q);
-        vb = *(const u32x4 *)(vrw + 16 * q + 8);
     }
-    uint32_t y1[4], y2[4];
-    {
-        const uint32_t a_[4] = {x1[0], x1[1], x1[2], x1[3]}, b_[4] = {x2[0], x2[1], x2[2], x2[3]};
-        const uint32_t c_[4] = {c[0], c[1], c[2], c[3]}, s_[4] = {sn[0], sn[1], sn[2], sn[3]};
-        rotate<E, 4>(a_, b_, c_, s_, 1.0f, y1, y2);
-    }
-    *(u32x4 *)(blk + r * 128 + 16 * (q ^ swz(r))) = u32x4{y1[0], y1[1], y1[2], y1[3]};
-    *(u32x4 *)(blk + r * 128 + 16 * ((4 + q) ^ swz(r))) = u32x4{y2[0], y2[1], y2[2], y2[3]};
-    *(u32x4 *)&vrow[r][16 * q] = va;
-    *(u32x4 *)&vrow[r][16 * q + 8] = vb;
-    // squared norm of key row r (its 64 rounded elements sit in lanes 4r .. 4r+3), then the
-    // largest over the wave's 16 rows
-    float sq = 0.f;
+    const uint32_t c_[4] = {c[0], c[1], c[2], c[3]}, s_[4] = {sn[0], sn[1], sn[2], sn[3]};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float a0 = E::lo(y1[k]), a1 = E::hi(y1[k]), b0 = E::lo(y2[k]), b1 = E::hi(y2[k]);
-        sq = __builtin_fmaf(a0, a0, sq);
-        sq = __builtin_fmaf(a1, a1, sq);
-        sq = __builtin_fmaf(b0, b0, sq);
-        sq = __builtin_fmaf(b1, b1, sq);
-    }
-    sq += __shfl_xor(sq, 1);
-    sq += __shfl_xor(sq, 2);
+    for (int k = 0; k < PREP_HEADS; ++k) {
+        if (h0 + k >= H)
+            break;  // uniform over the workgroup
+        uint8_t *blk = ws + ((int64_t)(h0 + k) * NB + b) * BLK;
+        uint32_t y1[4], y2[4];
+        {
+            const uint32_t a_[4] = {x1[k][0], x1[k][1], x1[k][2], x1[k][3]};
+            const uint32_t b_[4] = {x2[k][0], x2[k][1], x2[k][2], x2[k][3]};
+            rotate<E, 4>(a_, b_, c_, s_, 1.0f, y1, y2);
+        }
+        *(u32x4 *)(blk + r * 128 + 16 * (q ^ swz(r))) = u32x4{y1[0], y1[1], y1[2], y1[3]};
+        *(u32x4 *)(blk + r * 128 + 16 * ((4 + q) ^ swz(r))) = u32x4{y2[0], y2[1], y2[2], y2[3]};
+        *(u32x4 *)&vrow[k][r][16 * q] = va[k];
+        *(u32x4 *)&vrow[k][r][16 * q + 8] = vb[k];
+        // squared norm of key row r (its 64 rounded elements sit in lanes 4r .. 4r+3), then
+        // the largest over the wave's 16 rows
+        float sq = 0.f;
 #pragma unroll
-    for (int off = 4; off < 64; off <<= 1)
-        sq = fmaxf(sq, __shfl_xor(sq, off));
-    if ((tid & 63) == 0)
-        wmax[tid >> 6] = sq;
+        for (int e = 0; e < 4; ++e) {
+            const float a0 = E::lo(y1[e]), a1 = E::hi(y1[e]), b0 = E::lo(y2[e]), b1 = E::hi(y2[e]);
+            sq = __builtin_fmaf(a0, a0, sq);
+            sq = __builtin_fmaf(a1, a1, sq);
+            sq = __builtin_fmaf(b0, b0, sq);
+            sq = __builtin_fmaf(b1, b1, sq);
+        }
+        sq += __shfl_xor(sq, 1);
+        sq += __shfl_xor(sq, 2);
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1)
+            sq = fmaxf(sq, __shfl_xor(sq, off));
+        if ((tid & 63) == 0)
+            wmax[k][tid >> 6] = sq;
+    }
     __syncthreads();
-    if (tid == 0) {
-        const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        float *norms = (float *)(ws + (int64_t)H * NB * BLK);
-        norms[(int64_t)h * NB + b] = __builtin_sqrtf(m) * NORM_MARGIN;
-    }
-    // V^T: thread (d, q) writes chunks 2q and 2q+1 of row d; chunk ch holds slots 8ch .. 8ch+7
+    // V^T and the norm bound of each head's block
     const int d = tid >> 2;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int ch = 2 * q + e;
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k0 = vt_slot(8 * ch + 2 * j), k1 = vt_slot(8 * ch + 2 * j + 1);
-            w[j] = (uint32_t)vrow[k0][d] | ((uint32_t)vrow[k1][d] << 16);
+    for (int k = 0; k < PREP_HEADS; ++k) {
+        if (h0 + k >= H)
+            break;
+        uint8_t *blk = ws + ((int64_t)(h0 + k) * NB + b) * BLK;
+        if (tid == 0) {
+            const float m = fmaxf(fmaxf(wmax[k][0], wmax[k][1]), fmaxf(wmax[k][2], wmax[k][3]));
+            float *norms = (float *)(ws + (int64_t)H * NB * BLK);
+            norms[(int64_t)(h0 + k) * NB + b] = __builtin_sqrtf(m) * NORM_MARGIN;
         }
-        *(u32x4 *)(blk + IMG + d * 128 + 16 * (ch ^ swz(d))) = u32x4{w[0], w[1], w[2], w[3]};
+        // thread (d, q) writes chunks 2q and 2q+1 of row d; chunk ch holds slots 8ch .. 8ch+7
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int ch = 2 * q + e;
+            uint32_t wv4[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int k0 = vt_slot(8 * ch + 2 * jj), k1 = vt_slot(8 * ch + 2 * jj + 1);
+                wv4[jj] = (uint32_t)vrow[k][k0][d] | ((uint32_t)vrow[k][k1][d] << 16);
+            }
+            *(u32x4 *)(blk + IMG + d * 128 + 16 * (ch ^ swz(d))) =
+                u32x4{wv4[0], wv4[1], wv4[2], wv4[3]};
+        }
     }
 }
 
@@ -1167,7 +1195,7 @@ int64_t tile_blocks(const AttendArgs &a) { return (int64_t)(a.T / BC) + a.S; }
 template <class E>
 int launch_rotate(const AttendArgs &a) {
     const int64_t NB = tile_blocks(a);
-    const int64_t blocks = NB * a.H;
+    const int64_t blocks = NB * ((a.H + PREP_HEADS - 1) / PREP_HEADS);
     if (blocks > INT32_MAX)
         return fail(VLF_EINVAL, "%lld workgroups exceed the grid limit", (long long)blocks);
     const uint16_t *qkv = (const uint16_t *)a.qkv;
