@@ -233,7 +233,12 @@ const char *vlf_forward_kernel(int32_t br, int32_t prerotate, int32_t window, in
  *              CU walks a run of consecutive entries and keeps the keys that one entry shares
  *              with the next of the same sequence in LDS: any order gives the same results;
  *              vlf_launch_table's is the fastest (entries of a sequence adjacent and in row
- *              order, sequences interleaved by cost).
+ *              order, sequences interleaved by cost). There, when S <= 256, S * H is at least
+ *              twice the number of CUs and each CU's share of whole (sequence, head) runs fits
+ *              its list (ceil(S H / CUs) * ceil(table_rows / 256) <= 64), the kernel instead
+ *              ranks the sequences cu describes by cost and deals whole runs to the CUs in
+ *              snake order; the table's order is then not used (its entries must still be a
+ *              permutation of vlf_tile_table's).
  *   br         64, 128 or 256: rows per tile, as the table was built.
  *   T, S, H    tokens, sequences, heads (1 <= H <= 65536; T = 0 or num_tiles = 0 launches
  *              nothing).

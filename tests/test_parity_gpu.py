@@ -509,6 +509,89 @@ def test_understated_max_len_skips_what_the_ring_cannot_hold():
             rows=kept)
 
 
+# 80 sequences of 0 to 512 tokens x 8 heads: 640 (sequence, head) runs, at least two for each
+# of a 256-CU device's workgroups, so attend_slide deals whole runs in snake order
+SNAKE_LENS = [int(x) for x in np.random.default_rng(71).integers(0, 513, size=80)]
+SNAKE_LENS[5] = SNAKE_LENS[40] = 0
+SNAKE_LENS[6], SNAKE_LENS[7] = 1, 512
+
+
+def _with_table(batch, table, dev):
+    import dataclasses
+    tiles = torch.from_numpy(np.ascontiguousarray(table).astype(np.uint32).view(np.int32))
+    return dataclasses.replace(batch, tiles=tiles.to(dev).contiguous(), num_tiles=len(table))
+
+
+def _attend_nan(batch, w, qkv, cos, sin, dev):
+    T, H = w.tokens, w.heads
+    out = torch.full((T, H * 64), float("nan"), dtype=qkv.dtype, device=dev)
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device=dev)
+    vlf.attend_into(batch, qkv.to(dev), cos.to(dev), sin.to(dev), H, w.window, w.scale, out, lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def test_snake_order_ignores_the_table_order():
+    """With at least two whole (sequence, head) runs per workgroup and at most 256 sequences,
+    attend_slide ranks the sequences by cost from cu and deals the runs in snake order, so the
+    table's order does not matter: the canonical, reversed, shuffled and doubled tables give
+    bit-identical outputs, and the canonical one matches the oracle on every row."""
+    w = workloads.custom(SNAKE_LENS, 8, dtype="bf16", window=0, table_rows=512, seed=73)
+    assert vlf.forward_kernel(256, False, 0, max(w.lens)) == "attend_slide"
+    qkv, cos, sin = inputs(w)
+    dev = torch.device("cuda:0")
+    batch = vlf.prepare(w.cu, dev, 256, False, 0)
+    canon = vlf.tile_table(w.cu, 256).astype(np.int64)
+    _say("case snake order, canonical table")
+    ref = _attend_nan(_with_table(batch, canon, dev), w, qkv, cos, sin, dev)
+    compare("snake order, canonical table", w, ref[0], ref[1], qkv, cos, sin)
+    rng = np.random.default_rng(9)
+    for name, table in (("reversed", canon[::-1]), ("shuffled", canon[rng.permutation(len(canon))]),
+                        ("doubled", np.repeat(canon, 2, axis=0))):
+        _say(f"case snake order, {name} table")
+        got = _attend_nan(_with_table(batch, table, dev), w, qkv, cos, sin, dev)
+        assert np.array_equal(got[0], ref[0], equal_nan=True), name
+        assert np.array_equal(got[1], ref[1], equal_nan=True), name
+
+
+@pytest.mark.parametrize("count", [256, 257])
+def test_snake_order_at_its_sequence_bound(count):
+    """256 sequences is the most attend_slide ranks itself (snake order); 257 take equal runs of
+    the table. Both exact on every row, 2 heads, sequences of 0 to 300 tokens."""
+    lens = [int(x) for x in np.random.default_rng(count).integers(0, 301, size=count)]
+    w = workloads.custom(lens, 2, dtype="fp16", window=0, table_rows=300, seed=count)
+    qkv, cos, sin = inputs(w)
+    _say(f"case snake order bound, {count} sequences")
+    out, lse = run_gpu(w, qkv, cos, sin, br=256, prerotate=False)
+    compare(f"{count} sequences on the key ring", w, out, lse, qkv, cos, sin)
+
+
+def test_understated_max_len_in_snake_order():
+    """Snake order ranks only the sequences the tables reach: told max_len 300 (tables of 300
+    rows) for a batch with a 600-token sequence among 100 short ones, the ring kernel leaves the
+    long sequence's rows unwritten and the others exact (the oracle, which wants tables for
+    every sequence, gets 600 rows whose first 300 are the kernel's)."""
+    import dataclasses
+    lens = [int(x) for x in np.random.default_rng(75).integers(1, 201, size=100)]
+    lens[50] = 600
+    w = workloads.custom(lens, 8, dtype="bf16", window=0, table_rows=300, seed=75)
+    qkv, cos, sin = inputs(w)
+    w_full = workloads.custom(lens, 8, dtype="bf16", window=0, table_rows=600, seed=75)
+    cos_full, sin_full = workloads.rope_tables(w_full)
+    assert torch.equal(cos_full[:300], cos) and torch.equal(sin_full[:300], sin)
+    dev = torch.device("cuda:0")
+    batch = vlf.prepare(w.cu, dev, 256, False, 0)
+    batch = dataclasses.replace(batch, max_len=300)
+    assert vlf.forward_kernel(256, False, 0, batch.max_len) == "attend_slide"
+    _say("case understated max_len in snake order")
+    out, lse = _attend_nan(batch, w, qkv, cos, sin, dev)
+    a, b = int(w.cu[50]), int(w.cu[51])
+    assert np.isnan(out[a:b]).all() and np.isnan(lse[:, a:b]).all()
+    kept = np.r_[np.arange(0, a), np.arange(b, w.tokens)]
+    compare("understated max_len in snake order", w_full, out, lse, qkv, cos_full, sin_full,
+            rows=kept)
+
+
 def test_understated_max_len_on_single_key_tile_rows():
     """At 64 rows a max_len of at most 64 runs attend_one's single-tile form, which sweeps one
     key tile: told 64 for a batch with a 100-token sequence (tables long enough for it), that

@@ -1762,6 +1762,10 @@ __device__ __forceinline__ void slide_store_vals(const SlideVals &r, uint8_t *bl
     }
 }
 
+// Sequences attend_slide ranks itself for its snake order (larger batches take equal runs of
+// the table's order).
+constexpr int SNAKE_SEQ = 256;
+
 // One (head, query tile) item of attend_slide, with the key tiles [ta, tb) its window reaches.
 struct SlideItem {
     int h, seq, i0, start, len, ta, tb;
@@ -1774,25 +1778,87 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
              const uint16_t *__restrict__ sin_t, const int32_t *__restrict__ cu,
              const uint32_t *__restrict__ tiles, uint16_t *__restrict__ out,
              float *__restrict__ lse, int32_t num_tiles, int32_t T, int32_t S, int32_t H,
-             int32_t P, int32_t back, int32_t ahead, float scale) {
+             int32_t P, int32_t back, int32_t ahead, float scale, int32_t snake) {
     constexpr int NW = 8;
     constexpr int BR = 32 * NW;
     constexpr int RING = 8;   // key tiles held in LDS
     constexpr int DESC = 64;  // items described in LDS at a time
     __shared__ __attribute__((aligned(1024))) uint8_t ring[RING * BLK];
     __shared__ int32_t desc[DESC][8];  // seq (-1: skip), i0, start, len, h, ta, tb
+    __shared__ int32_t plist[DESC];    // snake order: seq << 24 | tile << 16 | h
+    __shared__ int32_t cost[SNAKE_SEQ], ranked[SNAKE_SEQ];
+    __shared__ int32_t plist_n;
 
-    // this workgroup's run of items u = h * num_tiles + tile (the host keeps the count below
-    // 2^31)
-    const int items = num_tiles * H;
     const int G = (int)gridDim.x, b = (int)blockIdx.x;
-    const int ua = (int)((int64_t)items * b / G), ub = (int)((int64_t)items * (b + 1) / G);
+    const int tid = (int)threadIdx.x;
+    int ua, ub;
+    if (snake && S <= SNAKE_SEQ) {
+        // Snake order: the sequences ranked by cost (tiles x key tiles they reach, most first,
+        // ties by index), run r = (rank floor(r / H), head r mod H) of all their tiles goes to
+        // workgroup r mod G, in rounds of G that alternate direction. The table's order is not
+        // used: the runs cover the tiles of every sequence cu describes, which is the set of
+        // the table's entries.
+        for (int x = tid; x < S; x += NW * 64) {
+            const int start = cu[x], len = cu[x + 1] - start;
+            int c = -1;
+            if (len > 0 && len <= P && start >= 0 && (int64_t)start + len <= T) {
+                c = 0;
+                for (int i0 = 0; i0 < len; i0 += BR) {
+                    int lo, hi;
+                    key_span(i0, BR, len, back, ahead, lo, hi);
+                    c += 2 + (hi - lo + BC - 1) / BC;
+                }
+            }
+            cost[x] = c;
+        }
+        __syncthreads();
+        for (int x = tid; x < S; x += NW * 64) {
+            const int c = cost[x];
+            if (c >= 0) {
+                int rank = 0;
+                for (int y = 0; y < S; ++y) {
+                    const int cy = cost[y];
+                    rank += cy > c || (cy == c && y < x);
+                }
+                ranked[rank] = x;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int sn = 0;
+            for (int y = 0; y < S; ++y)
+                sn += cost[y] >= 0;
+            const int runs = sn * H;
+            int np = 0;
+            for (int j = 0; j * G < runs; ++j) {
+                const int r = j * G + ((j & 1) ? G - 1 - b : b);
+                if (r >= runs)
+                    continue;
+                const int x = ranked[r / H], h = r - (r / H) * H;
+                const int len = cu[x + 1] - cu[x];
+                // (the host sizes the list for every run; the bound only guards it)
+                for (int tile = 0; tile * BR < len && np < DESC; ++tile)
+                    plist[np++] =
+                        (int32_t)(((uint32_t)x << 24) | ((uint32_t)tile << 16) | (uint32_t)h);
+            }
+            plist_n = np;
+        }
+        __syncthreads();
+        ua = 0;
+        ub = plist_n;
+    } else {
+        // this workgroup's run of items u = h * num_tiles + tile (the host keeps the count
+        // below 2^31)
+        snake = 0;
+        const int items = num_tiles * H;
+        ua = (int)((int64_t)items * b / G);
+        ub = (int)((int64_t)items * (b + 1) / G);
+    }
     if (ua >= ub)
         return;
 
     const int64_t ld = 3LL * H * D;
     const int hd = H * D;
-    const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, g = lane >> 5;
     const int t = tid & 255, gp = __builtin_amdgcn_readfirstlane(wv) >> 2;
@@ -1808,10 +1874,20 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
             int32_t e[8] = {-1, 0, 0, 0, 0, 0, 0, 0};
             const int u = from + tid;
             if (u < ub) {
-                const int h = u / num_tiles;
-                const int tile = u - h * num_tiles;
-                const uint32_t seq = tiles[2 * tile];
-                const int i0 = (int)tiles[2 * tile + 1];
+                int h;
+                uint32_t seq;
+                int i0;
+                if (snake) {
+                    const int pe = plist[u];
+                    seq = (uint32_t)pe >> 24;
+                    i0 = ((pe >> 16) & 255) * BR;
+                    h = pe & 0xffff;
+                } else {
+                    h = u / num_tiles;
+                    const int tile = u - h * num_tiles;
+                    seq = tiles[2 * tile];
+                    i0 = (int)tiles[2 * tile + 1];
+                }
                 if (seq < (uint32_t)S) {
                     const int start = cu[seq];
                     const int len = cu[seq + 1] - start;
@@ -2120,6 +2196,14 @@ int launch_slide(const AttendArgs &a) {
         return fail(VLF_EHIP, "device query failed: %s", hipGetErrorString(e));
     // one workgroup per CU (the 128 KB ring admits no second one)
     const int64_t grid = items < cus ? items : cus;
+    // Snake order where there are at least two runs of whole (sequence, head) pairs per
+    // workgroup and the sequences are few enough for each workgroup to rank them: a run per
+    // workgroup and round evens out the load far better than equal counts of consecutive
+    // entries. Each workgroup's list holds at most ceil(S H / grid) runs of at most
+    // ceil(P / 256) tiles (a longer sequence is skipped, as the tables do not reach it).
+    const int64_t runs = (int64_t)a.S * a.H;
+    const int64_t per = (runs + grid - 1) / grid, tiles_per = ((int64_t)a.table_rows + 255) / 256;
+    int32_t snake = a.S <= SNAKE_SEQ && runs >= 2 * grid && per * tiles_per <= 64;
     const uint16_t *qkv = (const uint16_t *)a.qkv;
     const uint16_t *cs = (const uint16_t *)a.cos;
     const uint16_t *sn = (const uint16_t *)a.sin;
@@ -2130,7 +2214,7 @@ int launch_slide(const AttendArgs &a) {
     void *args[] = {(void *)&qkv, (void *)&cs,        (void *)&sn, (void *)&a.cu,
                     (void *)&a.tiles, (void *)&out,   (void *)&a.lse, (void *)&num_tiles,
                     (void *)&T,   (void *)&S,         (void *)&H,  (void *)&P,
-                    (void *)&Bk,  (void *)&Ah, (void *)&scale};
+                    (void *)&Bk,  (void *)&Ah, (void *)&scale, (void *)&snake};
     e = hipLaunchKernel((const void *)attend_slide<E, FIXED>, dim3((unsigned)grid), dim3(512),
                         args, 0, (hipStream_t)a.stream);
     if (e != hipSuccess)
