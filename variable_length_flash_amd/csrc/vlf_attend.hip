@@ -2070,10 +2070,20 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
                 const int j0 = lo + tt * BC;
                 const uint8_t *kt = ring + ((j0 / BC) & (RING - 1)) * BLK;
                 f32x16 s0 = {}, s1 = {};
+                // Every operand read of a product goes out before its first MFMA (the
+                // scheduling barrier keeps them there): left to itself the compiler issued
+                // each read right before its MFMA and waited for it.
+                u32x4 op0[4], op1[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    s0 = E::mfma(*(const u32x4 *)(kt + cof[c]), qop[c], s0);
-                    s1 = E::mfma(*(const u32x4 *)(kt + 4096 + cof[c]), qop[c], s1);
+                    op0[c] = *(const u32x4 *)(kt + cof[c]);
+                    op1[c] = *(const u32x4 *)(kt + 4096 + cof[c]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    s0 = E::mfma(op0[c], qop[c], s0);
+                    s1 = E::mfma(op1[c], qop[c], s1);
                 }
                 if (tile_edge(w0, j0, len, back, ahead))
                     mask_band(s0, s1, jlo, jhi, j0, g);
@@ -2103,17 +2113,25 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
                     pk[2][k] = E::pack(s1[2 * k], s1[2 * k + 1]);
                     pk[3][k] = E::pack(s1[8 + 2 * k], s1[8 + 2 * k + 1]);
                 }
-                const uint8_t *vt = kt + IMG;
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    o0 = E::mfma(*(const u32x4 *)(vt + cof[kc]), pk[kc], o0);
-                    o1 = E::mfma(*(const u32x4 *)(vt + 4096 + cof[kc]), pk[kc], o1);
-                }
+                // the row sum before the output product, so the probabilities are dead by the
+                // time its operands arrive
                 float rs = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     rs += s0[i] + s1[i];
                 l_run += rs;
+                const uint8_t *vt = kt + IMG;
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    op0[kc] = *(const u32x4 *)(vt + cof[kc]);
+                    op1[kc] = *(const u32x4 *)(vt + 4096 + cof[kc]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    o0 = E::mfma(op0[kc], pk[kc], o0);
+                    o1 = E::mfma(op1[kc], pk[kc], o1);
+                }
             };
             // the first three key tiles, each after issuing a part of the next item's loads
             if (nt > 0) {
