@@ -783,7 +783,7 @@ attend_fwd(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, g = lane >> 5;
-    const int w0 = i0 + 32 * wv;  // first row of this wave
+    const int w0 = i0 + 32 * __builtin_amdgcn_readfirstlane(wv);  // first row of this wave
     const int qi = w0 + n;        // this lane's query position
 
     // ---- the key span this tile's window reaches (whole key tiles of BC)
@@ -1001,7 +1001,7 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, g = lane >> 5;
-    const int w0 = i0 + 32 * wv;
+    const int w0 = i0 + 32 * __builtin_amdgcn_readfirstlane(wv);
     const int qi = w0 + n;
 
     int lo, hi;
@@ -1251,7 +1251,7 @@ attend_pre_ph(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, g = lane >> 5;
-    const int w0 = i0 + 32 * wv;
+    const int w0 = i0 + 32 * __builtin_amdgcn_readfirstlane(wv);
     const int qi = w0 + n;
     int lo, hi;
     key_span(i0, BR, len, back, ahead, lo, hi);
@@ -1531,7 +1531,7 @@ attend_one(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, g = lane >> 5;
-    const int w0 = i0 + 32 * wv;
+    const int w0 = i0 + 32 * __builtin_amdgcn_readfirstlane(wv);
     const int qi = w0 + n;
 
     int lo, hi;
@@ -2052,7 +2052,7 @@ attend_slide(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_
             decode(u + 2, nn);
 
         // ---- this wave's 32 rows against the key tiles they reach
-        const int w0 = cur.i0 + 32 * wv;
+        const int w0 = cur.i0 + 32 * __builtin_amdgcn_readfirstlane(wv);
         if (cur.ok && w0 < cur.len) {
             const int len = cur.len;
             const int qi = w0 + n;
