@@ -191,9 +191,22 @@ __device__ __forceinline__ int vt_slot(int k) {
     return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+// A buffer resource over `bytes` bytes from base. Every resource here is built from
+// wave-uniform values (an item's, tile's or sequence's); they are read from the first lane so
+// that the compiler keeps the resource in scalar registers instead of wrapping each load that
+// uses it in a loop over the lanes' distinct values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes),
+                                             RSRC_WORD3);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)(uint32_t)n, RSRC_WORD3);
+    return make_rsrc(base, (uint32_t)n);
 }
 
 __device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t r, int off) {
@@ -1023,8 +1036,7 @@ attend_pre(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos_t,
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
     const int voff = 16 * lane;
     auto copy = [&](int t, int sl) {
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(wblock + (int64_t)(key(t) / BC) * BLK), 0, BLK, RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(wblock + (int64_t)(key(t) / BC) * BLK, BLK);
 #pragma unroll
         for (int j = 0; j < PIECES; ++j) {
             const int off = 1024 * (NW * j + wvu);
@@ -1270,8 +1282,7 @@ attend_pre_ph(const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ cos
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
     const int voff = 16 * lane;
     auto copy = [&](int t, int sl) {
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(wblock + (int64_t)(key(t) / BC) * BLK), 0, BLK, RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(wblock + (int64_t)(key(t) / BC) * BLK, BLK);
 #pragma unroll
         for (int j = 0; j < PIECES; ++j) {
             const int off = 1024 * (NW * j + wvu);
@@ -2519,8 +2530,11 @@ __device__ __forceinline__ void full_steps(int a, int steps, int b0, int len, in
 // sequence read as zeros. Offsets stay below 64 rows, so 32 bits hold them.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t back_rows(const uint16_t *base, int64_t ld,
                                                             int start, int r0, int len) {
-    const int64_t bytes = (int64_t)(len - r0 - 1) * ld * 2 + 128;
-    return rsrc(base + (int64_t)(start + r0) * ld, bytes);
+    // (wave-uniform: the arithmetic then stays on the scalar unit)
+    const int row = __builtin_amdgcn_readfirstlane(start + r0);
+    const int rows = __builtin_amdgcn_readfirstlane(len - r0);
+    const int64_t bytes = (int64_t)(rows - 1) * ld * 2 + 128;
+    return rsrc(base + (int64_t)row * ld, bytes);
 }
 
 // Copies 64 rows of a [*, ld] tensor (128 bytes each from the resource's column) into a row
@@ -2541,8 +2555,7 @@ __device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t r, int64_t ld, 
 // Copies `bytes` (a multiple of 1 KB) of a workspace block into LDS, 1 KB pieces by wave.
 template <int NW, int BYTES>
 __device__ __forceinline__ void copy_block(const uint8_t *src, lds_u8 *dst, int wvu, int lane) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, BYTES, RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, BYTES);
 #pragma unroll
     for (int j = 0; j < BYTES / 1024 / NW; ++j) {
         const int off = 1024 * (NW * j + wvu);
@@ -2556,8 +2569,7 @@ __device__ __forceinline__ void copy_block(const uint8_t *src, lds_u8 *dst, int 
 __device__ __forceinline__ void copy_floats(const float *base, int start, int r0, int len,
                                             lds_u8 *dst, int lane) {
     const int rows = len > r0 ? len - r0 : 0;
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(base + start + (rows > 0 ? r0 : 0)), 0, 4 * rows, RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + start + (rows > 0 ? r0 : 0), 4 * rows);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, 4 * lane, 0, 0, 0);
 }
 
